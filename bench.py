@@ -1,0 +1,203 @@
+"""Throughput of the KDA chunked forward pass on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+
+One step = one kda_fwd call (chunk table when packed, intra-chunk kernel,
+state-chain kernel) over the whole workload, with inputs already resident in
+HBM.  W untimed steps, then K timed steps between device synchronisations.
+Prints one JSON line.  Per-kernel device time comes from HIP events that
+kda_fwd records on its stream around each kernel.
+
+The default workload is the long single-sequence prefill: B=1, T=8192, H=32,
+K=V=128, bf16 inputs drawn N(0,1), lower_bound=-5, no initial state, bf16
+final state.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA, vendor figure
+# Algorithmic work per token-head (C = 64, K = V = 128):
+#   FLOPs 6KV + C(3K + 2V) = 139,264; bytes: q, k, v, g in (4 x 256) + beta (2) + out (256) = 1282
+F_ALG = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
+BYTES_ALG = 4 * 256 + 2 + 256
+# Interface bytes per token-head of each kernel, reading its inputs and writing
+# its outputs once (the chunk intermediates are 72.5 KiB per 64-token chunk
+# and head = 1160 B per token-head):
+INTER_BYTES = (4 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4) / 64.0
+KERNEL_BYTES = {
+    "kda_intra_kernel": 4 * 256 + 2 + INTER_BYTES,
+    "kda_chain_kernel": INTER_BYTES + 256,
+}
+
+
+def state_bytes(w) -> int:
+    per = w.N * w.H * w.K * w.V
+    b = 0
+    if w.initial_state is not None:
+        b += per * w.initial_state.element_size()
+    if w.final_state_dtype is not None:
+        b += per * (2 if w.final_state_dtype == torch.bfloat16 else 4)
+    return b
+
+
+def cpu_baseline(w, target_s: float = 12.0):
+    """Time the fp64 oracle on a bounded prefix of the same workload (all heads)."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    units = w.N * w.H
+    cores = min(threads, units)
+
+    def run(T_s):
+        q, k, v, g, b = (t[:, :T_s].contiguous() for t in (w.q, w.k, w.v, w.g, w.beta))
+        t0 = time.perf_counter()
+        oracle.fwd(q, k, v, g, b, w.scale, w.A_log, w.dt_bias, w.lower_bound,
+                   initial_state=w.initial_state, num_threads=threads)
+        return time.perf_counter() - t0
+
+    T_s = 64
+    dt = run(T_s)
+    while dt < 1.0 and T_s < w.T:
+        T_s = min(w.T, T_s * 4)
+        dt = run(T_s)
+    T_s = max(64, min(w.T, int(T_s * target_s / max(dt, 1e-3)) // 64 * 64))
+    dt = run(T_s)
+    tokens = w.B * T_s
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "first %d of %d tokens of every sequence, all %d heads, fp64 token recurrence, "
+                      "%d OpenMP threads, %.1f s" % (T_s, w.T, w.H, threads, dt)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, help="workload index 0..4 (default: T=8192, H=32)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the KDA forward shards by heads or sequences with "
+              "no communication, so no multi-GPU run is made (asked for %d GPUs)" % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    import gated_delta_rule_110_amd as kda
+    if not os.path.exists(kda.LIB_PATH):
+        kda.build()
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w_host = W.config(args.workload)
+    w = w_host.to(dev)
+    out = torch.empty((w.B, w.T, w.H, w.V), dtype=torch.bfloat16, device=dev)
+    final = None
+    if w.final_state_dtype is not None:
+        final = torch.empty((w.N, w.H, w.K, w.V), dtype=w.final_state_dtype, device=dev)
+    nbytes = kda.workspace_size(w.B, w.T, w.H, num_seqs=w.N)
+    workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    # 4 phase events per timed step (created by a first record)
+    stream = torch.cuda.current_stream(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize(dev)
+    ev_arrays = []
+    for row in evs:
+        arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in row])
+        ev_arrays.append(arr)
+
+    def step(ev=None):
+        kda.fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, out, w.A_log, w.dt_bias, w.lower_bound,
+                w.initial_state, final, w.cu_seqlens, workspace=workspace,
+                phase_events=None if ev is None else ctypes.cast(ev, ctypes.c_void_p))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev_arrays[i])
+    t_end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / args.steps
+
+    intra_ms = sum(r[1].elapsed_time(r[2]) for r in evs) / args.steps
+    chain_ms = sum(r[2].elapsed_time(r[3]) for r in evs) / args.steps
+    table_ms = sum(r[0].elapsed_time(r[1]) for r in evs) / args.steps
+    tok_heads = w.B * w.T * w.H
+    tokens = w.B * w.T
+    tokens_per_s = tokens / (ms / 1e3)
+    tflops = F_ALG * tok_heads / (ms / 1e3) / 1e12
+    path_bytes = BYTES_ALG * tok_heads + state_bytes(w)
+    gbs = path_bytes / (ms / 1e3) / 1e9
+
+    kernels = {"kda_intra_kernel": intra_ms, "kda_chain_kernel": chain_ms}
+    dom = max(kernels, key=kernels.get)
+    dom_bytes = KERNEL_BYTES[dom] * tok_heads + (state_bytes(w) if dom == "kda_chain_kernel" else 0)
+    achieved = dom_bytes / (kernels[dom] / 1e3) / 1e9
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "traffic_%s.json" % W.CONFIG_NAMES[args.workload])
+    if os.path.exists(prof):
+        with open(prof) as f:
+            tr = json.load(f)
+        traffic = tr.get(dom)
+
+    result = {
+        "metric": "KDA prefill tokens/s and MFMA TFLOP/s (% bf16 peak) at T=8K,H=32,K=V=128",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
+                   "num_seqs": w.N, "lower_bound": w.lower_bound,
+                   "initial_state": None if w.initial_state is None else str(w.initial_state.dtype),
+                   "final_state": None if w.final_state_dtype is None else str(w.final_state_dtype)},
+        "tflops_alg": round(tflops, 2),
+        "mfma_frac_alg": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "gbs_alg": round(gbs, 1),
+        "hbm_frac_alg": round(gbs / HBM_PEAK_GBS, 4),
+        "kernel_ms": {"kda_chunk_table_kernel": round(table_ms, 5),
+                      "kda_intra_kernel": round(intra_ms, 5), "kda_chain_kernel": round(chain_ms, 5)},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "wall_s": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w_host)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,180 @@
+"""libkda: the KDA chunked forward pass on gfx950, and its thin Python binding.
+
+The binding only marshals arguments: it checks dtypes, devices and
+contiguity, allocates the output and workspace with torch when the caller
+does not pass them, and calls ``kda_fwd`` from ``libkda.so`` through ctypes on
+torch's current HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no CPU or PyTorch fallback, and a missing library is an
+error.
+
+``fwd`` takes its arguments in the order of the forward call described on
+"Debajo del capó: CUTLASS en Hopper" (7minutos.es):
+q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+final_state, cu_seqlens.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+from ._build import LIB as LIB_PATH
+from ._build import build
+
+__all__ = ["fwd", "workspace_size", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16", "KDA_FP32"]
+
+KDA_BF16 = 1
+KDA_FP32 = 2
+HEAD_DIM = 128
+
+_STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
+                 4: "KDA_ERR_PARAM", 5: "KDA_ERR_DTYPE", 6: "KDA_ERR_ALIGN",
+                 7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP"}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (%d): %s" % (_STATUS_NAMES.get(status, "?"), status, message))
+        self.status = status
+
+
+class KdaDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("V", ctypes.c_int64), ("num_seqs", ctypes.c_int64),
+                ("initial_state_dtype", ctypes.c_int32), ("final_state_dtype", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("phase_events", ctypes.c_void_p)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libkda.so (built in-tree by ``build()``); raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libkda.so is not built (%s); run gated_delta_rule_110_amd.build()"
+                                   % LIB_PATH)
+            lib = ctypes.CDLL(LIB_PATH)
+            P = ctypes.c_void_p
+            lib.kda_fwd.restype = ctypes.c_int
+            lib.kda_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_float,
+                                    P, P, P, P, ctypes.POINTER(KdaDesc), P]
+            lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
+            lib.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(KdaDesc)]
+            lib.kda_status_string.restype = ctypes.c_char_p
+            lib.kda_status_string.argtypes = [ctypes.c_int]
+            _lib = lib
+    return _lib
+
+
+def _desc(B, T, H, N, h0_dtype=0, ht_dtype=0, workspace=None, nbytes=0) -> KdaDesc:
+    return KdaDesc(B, T, H, HEAD_DIM, HEAD_DIM, N, h0_dtype, ht_dtype,
+                   ctypes.c_void_p(workspace), nbytes, None)
+
+
+def workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None) -> int:
+    """Workspace bytes ``fwd`` needs for these shapes."""
+    d = _desc(B, T, H, B if num_seqs is None else num_seqs)
+    return int(library().kda_fwd_workspace_size(ctypes.byref(d)))
+
+
+def _state_dtype(t: Optional[torch.Tensor], name: str) -> int:
+    if t is None:
+        return 0
+    if t.dtype == torch.float32:
+        return KDA_FP32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise ValueError("%s must be bf16 or fp32, got %s" % (name, t.dtype))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+        scale: float, out: Optional[torch.Tensor], A_log: torch.Tensor, dt_bias: torch.Tensor,
+        lower_bound: float, initial_state: Optional[torch.Tensor] = None,
+        final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None,
+        phase_events=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """KDA forward on the current HIP stream.  Returns ``(out, final_state)``.
+
+    q, k, g: bf16 [B,T,H,128]; v: bf16 [B,T,H,128]; beta: bf16 logits [B,T,H];
+    A_log: fp32 [H]; dt_bias: fp32 [H,128]; lower_bound in [-5, 0];
+    initial_state / final_state: bf16 or fp32 [N,H,128,128] or None;
+    cu_seqlens: int64 [N+1] on the device (then B == 1) or None;
+    out: bf16 [B,T,H,128] or None (allocated); workspace: uint8 device tensor
+    of at least ``workspace_size`` bytes or None (allocated); phase_events:
+    None or the address of a caller-owned array of 4 hipEvent_t (instrumentation).
+    """
+    lib = library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("%s must be bfloat16, got %s" % (name, t.dtype))
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32:
+            raise ValueError("%s must be float32, got %s" % (name, t.dtype))
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,K]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or tuple(v.shape[:3]) != (B, T, H) or \
+            tuple(beta.shape) != (B, T, H):
+        raise ValueError("shape mismatch among q/k/v/g/beta")
+    if tuple(A_log.shape) != (H,) or tuple(dt_bias.shape) != (H, K):
+        raise ValueError("A_log must be [H] and dt_bias [H,K]")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int64 tensor")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=q.device)
+    tensors = [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out),
+               ("A_log", A_log), ("dt_bias", dt_bias), ("initial_state", initial_state),
+               ("final_state", final_state), ("cu_seqlens", cu_seqlens)]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a HIP device")
+    for name, t in tensors:
+        if t is None:
+            continue
+        if t.device != dev:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, T, H, V):
+        raise ValueError("out must be bf16 [B,T,H,V]")
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and tuple(t.shape) != (N, H, K, V):
+            raise ValueError("%s must be [N,H,K,V] = %s" % (name, (N, H, K, V)))
+    h0d = _state_dtype(initial_state, "initial_state")
+    htd = _state_dtype(final_state, "final_state")
+    d = _desc(B, T, H, N, h0d, htd)
+    d.K, d.V = K, V
+    need = int(lib.kda_fwd_workspace_size(ctypes.byref(d)))
+    with torch.cuda.device(dev):
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
+            raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
+        d.workspace = ctypes.c_void_p(workspace.data_ptr())
+        d.workspace_bytes = workspace.numel() * workspace.element_size()
+        d.phase_events = phase_events
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                         _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                         _ptr(final_state), _ptr(cu_seqlens), _ptr(out), ctypes.byref(d),
+                         ctypes.c_void_p(stream))
+    if st != 0:
+        raise KdaError(st, lib.kda_status_string(st).decode())
+    return out, final_state

@@ -1,0 +1,129 @@
+// kda_common.h -- internal definitions shared by the libkda HIP sources.
+// Not part of the public ABI (that is include/kda.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunk = 64;   // tokens per chunk
+constexpr int kK = 128;      // key / query head dim (the only one supported)
+constexpr int kV = 128;      // value head dim (the only one supported)
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef short s8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Per (chunk slot, head) intermediates written by the intra-chunk kernel and
+// consumed by the state-chain kernel, in fp16 unless stated.
+//   Wn  [64 tok][128 ch]   -W = -(I + A_kk)^-1 Diag(b) (gamma * K)      (negated)
+//   Qg  [64 tok][128 ch]   gamma * Qhat
+//   Kbt [128 ch][64 tok]   (exp(G_n - G_j) * khat_j) transposed
+//   Ut  [128 v][64 tok]    U^T, U = (I + A_kk)^-1 Diag(b) V
+//   Aqk [64 i][64 j]       causal decayed q.k products, zero above the diagonal
+//   gn  [128 ch] fp32      exp(G_n), the chunk's total per-channel decay
+constexpr int64_t kWnElems = kChunk * kK;
+constexpr int64_t kQgElems = kChunk * kK;
+constexpr int64_t kKbtElems = kK * kChunk;
+constexpr int64_t kUtElems = kV * kChunk;
+constexpr int64_t kAqkElems = kChunk * kChunk;
+constexpr int64_t kGnElems = kK;
+
+struct Geometry {
+    int64_t B, T, H, N;
+    int64_t nc_fixed;     // chunks per sequence when not packed
+    int64_t slots;        // chunk slots (upper bound when packed)
+    bool varlen;
+};
+
+struct WorkspaceLayout {
+    size_t off_chunk_off;  // int32 [N + 1] per-sequence first chunk slot (packed only)
+    size_t off_Wn, off_Qg, off_Kbt, off_Ut, off_Aqk, off_gn;
+    size_t total;
+};
+
+struct IntraArgs {
+    const uint16_t *q, *k, *v, *g, *beta;
+    const float *A_log, *dt_bias;
+    float lower_bound;
+    const int64_t *cu;          // packed: cumulative lengths, else nullptr
+    const int32_t *chunk_off;   // packed: [N + 1] first chunk slot of each sequence
+    int64_t T, H, N, nc_fixed;
+    _Float16 *Wn, *Qg, *Kbt, *Ut, *Aqk;
+    float *gn;
+};
+
+struct ChainArgs {
+    const _Float16 *Wn, *Qg, *Kbt, *Ut, *Aqk;
+    const float *gn;
+    const int64_t *cu;
+    const int32_t *chunk_off;
+    int64_t T, H, N, nc_fixed;
+    float scale;
+    const void *h0;      // initial state [N,H,K,V] or nullptr
+    void *ht;            // final state [N,H,K,V] or nullptr
+    int h0_bf16, ht_bf16;
+    uint16_t *out;       // [B,T,H,V] bf16
+};
+
+// ---- small numeric helpers --------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4 &r, float *o) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+// Split x into two bf16 values hi + lo (hi = RNE(x), lo = RNE(x - hi)).
+__device__ __forceinline__ void split_bf16(float x, short &hi, short &lo) {
+    uint16_t h = f32_to_bf16_bits(x);
+    float r = x - bf16_bits_to_f32(h);
+    hi = (short)h;
+    lo = (short)f32_to_bf16_bits(r);
+}
+
+__device__ __forceinline__ b8 as_b8(const s8 &s) { return __builtin_bit_cast(b8, s); }
+
+__device__ __forceinline__ f4 mfma16x16x32_f16(const h8 &a, const h8 &b, const f4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma16x16x32_bf16(const s8 &a, const s8 &b, const f4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_b8(a), as_b8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma16x16x16_f16(const h4 &a, const h4 &b, const f4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Resolve packed sequence index of a chunk slot: largest n with off[n] <= slot.
+__device__ __forceinline__ int64_t seq_of_slot(const int32_t *off, int64_t N, int64_t slot) {
+    int64_t lo = 0, hi = N;  // invariant: off[lo] <= slot < off[hi] (off[N] > slot)
+    while (hi - lo > 1) {
+        int64_t mid = (lo + hi) >> 1;
+        if (off[mid] <= slot) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+}  // namespace kda
+
+// Kernel launchers (defined in the .hip files).
+hipError_t kda_launch_chunk_table(const int64_t *cu, int64_t N, int32_t *chunk_off, hipStream_t s);
+hipError_t kda_launch_intra(const kda::IntraArgs &a, int64_t slots, hipStream_t s);
+hipError_t kda_launch_chain(const kda::ChainArgs &a, hipStream_t s);

@@ -1,0 +1,125 @@
+/*
+ * kda.h -- C ABI of libkda, the gfx950 (MI355X) forward pass of Kimi Delta
+ * Attention (KDA) in chunk-parallel form.
+ *
+ * The operation.  KDA is a delta-rule linear attention with a fixed-size state
+ * matrix per (sequence, head), a forget gate, and a per-channel decay that
+ * refines Gated DeltaNet ("What is Kimi Delta Attention (KDA)", Moonshot AI
+ * Open-Sources FlashKDA, kongchang.com/en; "¿Qué es la atención Kimi Delta y
+ * por qué es importante?", 7minutos.es).  For every token t of a sequence,
+ * with S a K x V fp32 state:
+ *
+ *   k_t <- k_t / sqrt(|k_t|^2 + 1e-6),  q_t likewise           (in-kernel L2 norm)
+ *   b_t  = sigmoid(beta_t)                                       (in-kernel sigmoid)
+ *   a_t[d] = max(lower_bound, -exp(A_log[h]) * softplus(g_t[d] + dt_bias[h,d]))
+ *   S_t = (I - b_t k_t k_t^T) Diag(exp(a_t)) S_{t-1} + b_t k_t v_t^T
+ *   o_t = scale * S_t^T q_t
+ *
+ * The in-kernel norm, sigmoid and gate flags are those of the backend call on
+ * "作为 FLA 后端的用法" (zuobiaodaohang.com FlashKDA page); the argument list,
+ * dtypes and the K = V = 128 restriction are those of the forward call on
+ * "Debajo del capó: CUTLASS en Hopper" (7minutos.es).  The gate formula is not
+ * printed on the pages: the one above is the plain reading of the parameter
+ * names, clamped to [lower_bound, 0].
+ *
+ * Every pointer argument is a DEVICE pointer on the current HIP device unless
+ * stated otherwise.  All tensors are row-major and contiguous, as the pages
+ * require ("性能与注意事项", zuobiaodaohang.com).  The library keeps no
+ * reference to any pointer after a call returns and has no global mutable
+ * state: calls on different streams may run concurrently if their buffers
+ * (including workspaces) are disjoint.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the optional recurrent states. */
+typedef enum { KDA_BF16 = 1, KDA_FP32 = 2 } kda_dtype_t;
+
+/* Status codes.  Everything except KDA_ERR_HIP is detected on the host before
+ * any work is enqueued; no output is touched in that case. */
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL (q,k,v,g,beta,out may be NULL when T == 0) */
+    KDA_ERR_SHAPE = 2,       /* B, H < 1, T < 0, num_seqs inconsistent, varlen with B != 1 */
+    KDA_ERR_UNSUPPORTED = 3, /* K != 128 or V != 128                               */
+    KDA_ERR_PARAM = 4,       /* lower_bound not finite or outside [-5, 0]; scale not finite */
+    KDA_ERR_DTYPE = 5,       /* a state dtype other than KDA_BF16 / KDA_FP32      */
+    KDA_ERR_ALIGN = 6,       /* a tensor pointer not 16-byte aligned (workspace: 256) */
+    KDA_ERR_WORKSPACE = 7,   /* workspace_bytes smaller than kda_fwd_workspace_size() */
+    KDA_ERR_HIP = 8          /* a HIP launch error                                 */
+} kda_status_t;
+
+/* Shapes and the caller-owned workspace of one call.
+ *   q, k, g : [B, T, H, K] bf16      v, out : [B, T, H, V] bf16     beta : [B, T, H] bf16
+ *   Without cu_seqlens, num_seqs must equal B and batch row n is one sequence.
+ *   With cu_seqlens, B must be 1, T is the total packed token count and
+ *   num_seqs = N is the number of packed sequences (cu_seqlens has N + 1 entries).
+ *   workspace: device memory of at least kda_fwd_workspace_size(desc) bytes,
+ *   256-byte aligned, owned by the caller, not read before it is written.  If
+ *   workspace is NULL the library takes and releases one with
+ *   hipMallocAsync / hipFreeAsync on the call's stream. */
+typedef struct {
+    int64_t B, T, H, K, V;
+    int64_t num_seqs;
+    int32_t initial_state_dtype;  /* kda_dtype_t; ignored when initial_state is NULL */
+    int32_t final_state_dtype;    /* kda_dtype_t; ignored when final_state is NULL   */
+    void *workspace;
+    size_t workspace_bytes;
+    /* Optional instrumentation: NULL, or an array of 4 hipEvent_t created by
+     * the caller.  kda_fwd records event 0 before its first kernel, 1 after
+     * the chunk-table kernel (packed batches only; otherwise right after 0),
+     * 2 after the intra-chunk kernel and 3 after the state-chain kernel, all
+     * on `stream`, so per-kernel device time can be measured. */
+    hipEvent_t *phase_events;
+} kda_desc_t;
+
+/* Bytes of workspace kda_fwd needs for these shapes (0 if the shapes are
+ * invalid).  Pure host arithmetic; needs no device.  Grows linearly with the
+ * number of 64-token chunks times H (about 72.5 KiB per chunk and head). */
+size_t kda_fwd_workspace_size(const kda_desc_t *desc);
+
+/* Enqueue the KDA forward pass on `stream` and return without synchronising.
+ *
+ *   q, k, g, v, beta : inputs as in kda_desc_t; g is the gate before activation,
+ *                      beta holds logits (the sigmoid is applied in-kernel).
+ *   scale            : fp32 factor applied to every output.
+ *   A_log            : fp32 [H], per-head log decay rate.
+ *   dt_bias          : fp32 [H, K], per-channel gate bias.
+ *   lower_bound      : fp32 in [-5, 0]; the per-channel log-decay is clamped to
+ *                      [lower_bound, 0] (values below -5 are refused: the chunked
+ *                      decay factorisation relies on them).
+ *   initial_state    : [N, H, K, V] of initial_state_dtype, or NULL for zeros.
+ *   final_state      : [N, H, K, V] of final_state_dtype, or NULL to skip it.
+ *                      It may alias initial_state when both dtypes match.
+ *   cu_seqlens       : device int64 [N + 1] cumulative lengths, or NULL.  Its
+ *                      contents must satisfy cu[0] = 0, cu[n] <= cu[n+1],
+ *                      cu[N] = T; they are not validated (no host sync).
+ *                      Empty sequences are allowed: their final state is their
+ *                      initial state.
+ *   out              : bf16 [B, T, H, V], caller-allocated, must not alias inputs.
+ *   desc             : shapes, state dtypes and workspace (host pointer).
+ *   stream           : HIP stream (0 = the null stream).
+ * Returns KDA_OK when the work was enqueued; device faults surface at the
+ * caller's next synchronisation. */
+kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, float scale, const float *A_log,
+                     const float *dt_bias, float lower_bound,
+                     const void *initial_state, void *final_state,
+                     const int64_t *cu_seqlens, void *out,
+                     const kda_desc_t *desc, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kda_status_string(kda_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

@@ -1,0 +1,110 @@
+"""The C ABI on the host: the library loads without a GPU, exports every
+function include/kda.h declares, and its synchronous validation paths return
+the documented status before any device work (no compute call is made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_110_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "kda.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\S.*?\b(kda_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        kda.build()
+    return kda.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) >= {"kda_fwd", "kda_fwd_workspace_size", "kda_status_string"}
+    dyn = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert hasattr(lib, n), n
+        assert re.search(r"\bT %s$" % n, dyn, flags=re.M), n
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert lib.kda_status_string(s)
+    assert lib.kda_status_string(99) == b"unknown status"
+
+
+def _desc(**kw):
+    d = kda.KdaDesc(1, 64, 2, 128, 128, 1, 2, 2, None, 0, None)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _call(lib, d, lb=-5.0, scale=0.1, null=(), align=None, cu=None):
+    ptrs = {n: ctypes.c_void_p(FAKE) for n in ("q", "k", "v", "g", "beta", "A_log", "dt_bias", "out")}
+    for n in null:
+        ptrs[n] = None
+    if align:
+        ptrs[align] = ctypes.c_void_p(FAKE + 2)
+    return lib.kda_fwd(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["g"], ptrs["beta"], scale, ptrs["A_log"],
+                       ptrs["dt_bias"], lb, None, None, cu, ptrs["out"], ctypes.byref(d), None)
+
+
+def test_validation_errors(lib):
+    ws = kda.workspace_size(1, 64, 2)
+    ok_ws = dict(workspace=ctypes.c_void_p(0x100000), workspace_bytes=0)  # too small on purpose
+    assert _call(lib, _desc(K=64)) == 3
+    assert _call(lib, _desc(V=256)) == 3
+    assert _call(lib, _desc(B=0)) == 2
+    assert _call(lib, _desc(H=0)) == 2
+    assert _call(lib, _desc(T=-1)) == 2
+    assert _call(lib, _desc(num_seqs=3)) == 2                 # unpacked: num_seqs must equal B
+    assert _call(lib, _desc(B=2, num_seqs=2), cu=ctypes.c_void_p(FAKE)) == 2  # packed needs B == 1
+    assert _call(lib, _desc(), lb=-5.5) == 4
+    assert _call(lib, _desc(), lb=0.25) == 4
+    assert _call(lib, _desc(), lb=float("nan")) == 4
+    assert _call(lib, _desc(), scale=float("inf")) == 4
+    for n in ("q", "k", "v", "g", "beta", "out", "A_log", "dt_bias"):
+        assert _call(lib, _desc(), null=(n,)) == 1, n
+    for n in ("q", "k", "v", "g", "out", "dt_bias"):
+        assert _call(lib, _desc(), align=n) == 6, n
+    d = _desc(**ok_ws)
+    assert _call(lib, d) == 7
+    d = _desc(workspace=ctypes.c_void_p(0x100010), workspace_bytes=ws)  # not 256-aligned
+    assert _call(lib, d) == 6
+    # bad state dtype
+    d = _desc(final_state_dtype=7)
+    assert lib.kda_fwd(*([ctypes.c_void_p(FAKE)] * 5), 0.1, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), -5.0,
+                       None, ctypes.c_void_p(FAKE), None, ctypes.c_void_p(FAKE), ctypes.byref(d), None) == 5
+
+
+def test_workspace_size_monotone(lib):
+    prev = 0
+    for T in (0, 1, 64, 65, 1000, 8192):
+        s = kda.workspace_size(1, T, 4)
+        assert s >= prev and s % 256 == 0
+        prev = s
+    assert kda.workspace_size(1, 8192, 32, num_seqs=10) > kda.workspace_size(1, 8192, 32)
+    assert kda.workspace_size(2, 64, 2, num_seqs=3) == 0          # invalid shapes -> 0
+    # about 72.5 KiB per (64-token chunk, head)
+    per = (kda.workspace_size(4, 64 * 100, 8) - kda.workspace_size(4, 64 * 50, 8)) / (4 * 50 * 8)
+    assert abs(per - 72.5 * 1024) < 512
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kda.fwd(x, x, x, x, torch.zeros((1, 64, 2), dtype=torch.bfloat16), 0.1, None,
+                torch.zeros(2), torch.zeros(2, 128), -5.0)
