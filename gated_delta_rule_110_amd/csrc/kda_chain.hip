@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_chain_kernel(ChainArgs a) {
                 sv[2] = (_Float16)S[rt][ct][2]; sv[3] = (_Float16)S[rt][ct][3];
                 *reinterpret_cast<h4 *>(&sm.sSt[(16 * ct + r16) * kSPad + 32 * w + 16 * rt + 4 * cg]) = sv;
             }
-        __syncthreads();
+        lds_barrier();
 
         // (b) waves 0,1: Ut = U - W S (rows 32w..);  waves 2,3: Qg S (rows 32(w-2)..)
         f4 X[2][2];
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_chain_kernel(ChainArgs a) {
                     *reinterpret_cast<h4 *>(&sm.sUt[(16 * ct + r16) * kUPad + 32 * w + 16 * rt + 4 * cg]) = uv;
                 }
         }
-        __syncthreads();
+        lds_barrier();
 
         // (c) S <- Diag(exp(G_n)) S + Kbar^T Ut ;  (d) waves 2,3: O = scale (Qg S + A_qk Ut)
 #pragma unroll
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_chain_kernel(ChainArgs a) {
                         sm.sO[(32 * (w - 2) + 16 * rt + 4 * cg + e) * kOPad + 16 * ct + r16] =
                             f32_to_bf16_bits(a.scale * X[rt][ct][e]);
         }
-        __syncthreads();
+        lds_barrier();
 
         // output rows of this chunk: 64 rows x 32 columns, 16 bytes per thread
         {

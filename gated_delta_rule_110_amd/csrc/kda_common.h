@@ -74,12 +74,9 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+// fp32 -> bf16 bits, round to nearest even (hardware conversion; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ void unpack_bf16x8(const uint4 &r, float *o) {
@@ -91,12 +88,41 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 &r, float *o) {
     }
 }
 
-// Split x into two bf16 values hi + lo (hi = RNE(x), lo = RNE(x - hi)).
+// Split x into two bf16 values hi + lo (hi = RNE(x), lo = RNE(x - hi)), using
+// the hardware fp32 -> bf16 conversion (round to nearest even).
 __device__ __forceinline__ void split_bf16(float x, short &hi, short &lo) {
-    uint16_t h = f32_to_bf16_bits(x);
-    float r = x - bf16_bits_to_f32(h);
-    hi = (short)h;
-    lo = (short)f32_to_bf16_bits(r);
+    const __bf16 h = (__bf16)x;
+    const short hs = __builtin_bit_cast(short, h);
+    const float r = x - __uint_as_float((uint32_t)(uint16_t)hs << 16);
+    hi = hs;
+    lo = __builtin_bit_cast(short, (__bf16)r);
+}
+
+// Hardware transcendental approximations (about 1 ulp on normal values).
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_logf(x) * 0.6931471805599453f; }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// DPP lane moves within 16-lane rows.
+__device__ __forceinline__ float dpp_row_shr(float x, float fill, int s) {
+    // lanes whose source lies before the row start keep `fill`
+    switch (s) {
+        case 1: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), 0x111, 0xf, 0xf, false));
+        case 2: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), 0x112, 0xf, 0xf, false));
+        case 4: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), 0x114, 0xf, 0xf, false));
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), 0x118, 0xf, 0xf, false));
+    }
+}
+__device__ __forceinline__ float dpp_row_bcast15(float x) {
+    // every lane of a 16-lane row receives the row's lane 15
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xf, 0xf, false));
+}
+
+// Barrier that orders LDS traffic only: outstanding global loads (prefetches)
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ b8 as_b8(const s8 &s) { return __builtin_bit_cast(b8, s); }

@@ -37,22 +37,12 @@ namespace {
 constexpr int kThreads = 256;
 
 struct __align__(16) IntraSmem {
-    float yt[48 * 128];      // rows of blocks 0..2: exp(G_e - G_j) * khat_j, e = block end; later Kbar^T staging
+    float yt[48 * 128];      // rows of blocks 0..2: exp(G_e - G_j) * khat_j, e = block end of the row
     float L[64 * 64];        // A_kk (b-scaled, strictly lower), overwritten in place by T
     _Float16 kgT[128 * 64];  // (b * gamma * khat)^T, [channel][token]
     _Float16 vbT[128 * 64];  // (b * v)^T,            [value column][token]
     float pblk[4 * 128];     // per 16-row block: product of the block's decays, per channel
 };
-
-__device__ __forceinline__ void load_row8(const uint16_t *p, bool valid, float *o) {
-    if (valid) {
-        uint4 r = *reinterpret_cast<const uint4 *>(p);
-        unpack_bf16x8(r, o);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = 0.f;
-    }
-}
 
 __device__ __forceinline__ h4 to_h4(const f4 &x) {
     h4 r;
@@ -75,6 +65,86 @@ __device__ __forceinline__ f4 mfma_split16(const h4 &ah, const h4 &al, const h4 
     c = mfma16x16x16_f16(ah, bl, c);
     c = mfma16x16x16_f16(al, bh, c);
     return c;
+}
+
+// Gram tiles of row block W, computed transposed (D[j][i], j in block jb,
+// i = this wave's rows): A_kk (b-scaled, strictly lower) to LDS in fp32 and
+// A_qk (lower incl. diagonal) to global in fp16.  Blocks above the diagonal
+// are written as zeros.
+template <int W>
+__device__ __forceinline__ void gram_tiles(IntraSmem &sm, const float *kv, const float *qv, const float *yd,
+                                           float b, int row, int r16, int cg, _Float16 *Aqk) {
+    f4 akk_o[W > 0 ? W : 1], aqk_o[W > 0 ? W : 1];
+    f4 akk_d = f4{0, 0, 0, 0}, aqk_d = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < (W > 0 ? W : 1); ++t) { akk_o[t] = f4{0, 0, 0, 0}; aqk_o[t] = f4{0, 0, 0, 0}; }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int c0 = 32 * kk + 8 * cg;
+        s8 xhi, xlo, qhi, qlo, ydhi, ydlo;
+        h8 xh, qh;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int idx = 8 * kk + e;
+            short th, tl;
+            split_bf16(kv[idx], th, tl); xhi[e] = th; xlo[e] = tl;
+            split_bf16(qv[idx], th, tl); qhi[e] = th; qlo[e] = tl;
+            split_bf16(yd[idx], th, tl); ydhi[e] = th; ydlo[e] = tl;
+            xh[e] = (_Float16)kv[idx];
+            qh[e] = (_Float16)qv[idx];
+        }
+        // diagonal block: factors span up to exp(+-80), so bf16 hi+lo (3 MFMAs)
+        akk_d = mfma16x16x32_bf16(ydhi, xhi, akk_d);
+        akk_d = mfma16x16x32_bf16(ydhi, xlo, akk_d);
+        akk_d = mfma16x16x32_bf16(ydlo, xhi, akk_d);
+        aqk_d = mfma16x16x32_bf16(ydhi, qhi, aqk_d);
+        aqk_d = mfma16x16x32_bf16(ydhi, qlo, aqk_d);
+        aqk_d = mfma16x16x32_bf16(ydlo, qhi, aqk_d);
+        if constexpr (W > 0) {
+            // off-diagonal blocks jb < W: A = [prod_{jb < w' < W} pblk[w']] * yt_j  (<= 1, fp16)
+            float m[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m[e] = 1.f;
+#pragma unroll
+            for (int jb = W - 1; jb >= 0; --jb) {
+                if (jb < W - 1) {
+                    const float4 p0 = *reinterpret_cast<const float4 *>(&sm.pblk[(jb + 1) * 128 + c0]);
+                    const float4 p1 = *reinterpret_cast<const float4 *>(&sm.pblk[(jb + 1) * 128 + c0 + 4]);
+                    m[0] *= p0.x; m[1] *= p0.y; m[2] *= p0.z; m[3] *= p0.w;
+                    m[4] *= p1.x; m[5] *= p1.y; m[6] *= p1.z; m[7] *= p1.w;
+                }
+                const float4 y0 = *reinterpret_cast<const float4 *>(&sm.yt[(16 * jb + r16) * 128 + c0]);
+                const float4 y1 = *reinterpret_cast<const float4 *>(&sm.yt[(16 * jb + r16) * 128 + c0 + 4]);
+                h8 yh;
+                yh[0] = (_Float16)(y0.x * m[0]); yh[1] = (_Float16)(y0.y * m[1]);
+                yh[2] = (_Float16)(y0.z * m[2]); yh[3] = (_Float16)(y0.w * m[3]);
+                yh[4] = (_Float16)(y1.x * m[4]); yh[5] = (_Float16)(y1.y * m[5]);
+                yh[6] = (_Float16)(y1.z * m[6]); yh[7] = (_Float16)(y1.w * m[7]);
+                akk_o[jb] = mfma16x16x32_f16(yh, xh, akk_o[jb]);
+                aqk_o[jb] = mfma16x16x32_f16(yh, qh, aqk_o[jb]);
+            }
+        }
+    }
+    // Lane holds D[j = 16 jb + 4 cg + e][i = row].
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        f4 dk, dq;
+        if (jb < W) { dk = akk_o[jb < W ? jb : 0]; dq = aqk_o[jb < W ? jb : 0]; }
+        else if (jb == W) {
+            dk = akk_d; dq = aqk_d;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int jj = 4 * cg + e;
+                if (!(jj < r16)) dk[e] = 0.f;
+                if (!(jj <= r16)) dq[e] = 0.f;
+            }
+        } else { dk = f4{0, 0, 0, 0}; dq = f4{0, 0, 0, 0}; }
+        dk = dk * b;
+        *reinterpret_cast<f4 *>(&sm.L[row * 64 + 16 * jb + 4 * cg]) = dk;
+        h4 qq;
+        qq[0] = (_Float16)dq[0]; qq[1] = (_Float16)dq[1]; qq[2] = (_Float16)dq[2]; qq[3] = (_Float16)dq[3];
+        *reinterpret_cast<h4 *>(Aqk + row * 64 + 16 * jb + 4 * cg) = qq;
+    }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
@@ -121,16 +191,24 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
 
     // ---- P0: load, normalise, gate, block-local decay products ------------
     // Lane owns row `row`, channels ch(kk, e) = 32 kk + 8 cg + e.
-    float qv[32], kv[32], gv[32], vv[32];
+    float qv[32], kv[32];
+    uint4 graw[4], vraw[4];
     {
         const int64_t base = ((t0 + row) * H + h) * kK;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int c0 = 32 * kk + 8 * cg;
-            load_row8(a.q + base + c0, valid, qv + 8 * kk);
-            load_row8(a.k + base + c0, valid, kv + 8 * kk);
-            load_row8(a.g + base + c0, valid, gv + 8 * kk);
-            load_row8(a.v + base + c0, valid, vv + 8 * kk);
+            uint4 qr = make_uint4(0, 0, 0, 0), kr = qr, gr = qr, vr = qr;
+            if (valid) {
+                qr = *reinterpret_cast<const uint4 *>(a.q + base + c0);
+                kr = *reinterpret_cast<const uint4 *>(a.k + base + c0);
+                gr = *reinterpret_cast<const uint4 *>(a.g + base + c0);
+                vr = *reinterpret_cast<const uint4 *>(a.v + base + c0);
+            }
+            unpack_bf16x8(qr, qv + 8 * kk);
+            unpack_bf16x8(kr, kv + 8 * kk);
+            graw[kk] = gr;
+            vraw[kk] = vr;
         }
     }
     float ssq = 0.f, ssk = 0.f;
@@ -138,16 +216,16 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     for (int e = 0; e < 32; ++e) { ssq += qv[e] * qv[e]; ssk += kv[e] * kv[e]; }
     ssq += __shfl_xor(ssq, 16); ssq += __shfl_xor(ssq, 32);
     ssk += __shfl_xor(ssk, 16); ssk += __shfl_xor(ssk, 32);
-    const float rq = 1.0f / sqrtf(ssq + 1e-6f);
-    const float rk = 1.0f / sqrtf(ssk + 1e-6f);
+    const float rq = fast_rsqrt(ssq + 1e-6f);
+    const float rk = fast_rsqrt(ssk + 1e-6f);
     float b = 0.f;
-    if (valid) {
-        const float x = bf16_bits_to_f32(a.beta[(t0 + row) * H + h]);
-        b = 1.0f / (1.0f + expf(-x));
-    }
-    // gate: d = exp(max(lb, -exp(A_log) * softplus(g + dt_bias)))
+    if (valid) b = fast_rcp(1.0f + fast_exp(-bf16_bits_to_f32(a.beta[(t0 + row) * H + h])));
+
+    // gate: d = exp(max(lb, -exp(A_log) softplus(g + dt_bias))), then the
+    // inclusive product over the block's rows: P_i = exp(G_i - G_{r-1}).
+    float P[32];
     {
-        const float Aexp = expf(a.A_log[h]);
+        const float Aexp = fast_exp(a.A_log[h]);
         const float lb = a.lower_bound;
         const float *dtb = a.dt_bias + h * kK;
 #pragma unroll
@@ -156,157 +234,103 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
             const float4 d0 = *reinterpret_cast<const float4 *>(dtb + c0);
             const float4 d1 = *reinterpret_cast<const float4 *>(dtb + c0 + 4);
             const float db[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            float gf[8];
+            unpack_bf16x8(graw[kk], gf);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = gv[8 * kk + e] + db[e];
-                const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+                const float x = gf[e] + db[e];
+                // softplus(x) = max(x,0) + log1p(u), u = exp(-|x|) in (0, 1]; a short
+                // series for small u keeps log1p accurate where 1 + u would round
+                const float u = fast_exp(-fabsf(x));
+                const float small = u * (1.0f - u * (0.5f - u * (1.0f / 3.0f)));
+                const float sp = fmaxf(x, 0.f) + (u < (1.0f / 128.0f) ? small : fast_log(1.0f + u));
                 const float lg = fmaxf(lb, -Aexp * sp);
-                gv[8 * kk + e] = valid ? expf(lg) : 1.0f;
+                P[8 * kk + e] = valid ? fast_exp(lg) : 1.0f;
             }
         }
     }
-    // inclusive product scan over the 16 rows of the block (lanes of one 16-lane row)
 #pragma unroll
     for (int s = 1; s < 16; s <<= 1) {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            const float t = __shfl_up(gv[e], s, 16);
-            if (r16 >= s) gv[e] *= t;
-        }
+        for (int e = 0; e < 32; ++e) P[e] *= dpp_row_shr(P[e], 1.0f, s);
     }
-    // gv = P_i = exp(G_i - G_{r-1});  pe = P at the block end
-    float yd[32], ytk[32];
+    // yd = exp(G_{r-1} - G_j) khat_j (>= khat; used by the diagonal blocks), and
+    // exp(G_e - G_j) khat_j = pe * yd with e the block end and pe the block total
+    float yd[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-        const float pe = __shfl(gv[e], 15, 16);
+        const float pe = dpp_row_bcast15(P[e]);
         const float kh = kv[e] * rk;
-        const float qh = qv[e] * rq;
-        const float P = gv[e];
-        const float inv = 1.0f / P;
-        ytk[e] = kh * (pe * inv);  // exp(G_e - G_j) khat_j
-        yd[e] = kh * inv;          // exp(G_{r-1} - G_j) khat_j  (>= khat, diagonal blocks only)
-        kv[e] = kh * P;            // X_i = exp(G_i - G_{r-1}) khat_i
-        qv[e] = qh * P;            // Q'_i = exp(G_i - G_{r-1}) qhat_i
+        yd[e] = kh * fast_rcp(P[e]);
+        kv[e] = kh * P[e];         // X_i = exp(G_i - G_{r-1}) khat_i
+        qv[e] = qv[e] * rq * P[e]; // Q'_i = exp(G_i - G_{r-1}) qhat_i
+        P[e] = pe;
     }
     if (w < 3) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            const int i0 = 8 * kk;
             float4 *dst = reinterpret_cast<float4 *>(&sm.yt[row * 128 + 32 * kk + 8 * cg]);
-            dst[0] = make_float4(ytk[8 * kk + 0], ytk[8 * kk + 1], ytk[8 * kk + 2], ytk[8 * kk + 3]);
-            dst[1] = make_float4(ytk[8 * kk + 4], ytk[8 * kk + 5], ytk[8 * kk + 6], ytk[8 * kk + 7]);
+            dst[0] = make_float4(P[i0 + 0] * yd[i0 + 0], P[i0 + 1] * yd[i0 + 1], P[i0 + 2] * yd[i0 + 2], P[i0 + 3] * yd[i0 + 3]);
+            dst[1] = make_float4(P[i0 + 4] * yd[i0 + 4], P[i0 + 5] * yd[i0 + 5], P[i0 + 6] * yd[i0 + 6], P[i0 + 7] * yd[i0 + 7]);
         }
     }
     if (r16 == 15) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm.pblk[w * 128 + 32 * kk + 8 * cg + e] = gv[8 * kk + e];
+        for (int kk = 0; kk < 4; ++kk) {
+            float4 *dst = reinterpret_cast<float4 *>(&sm.pblk[w * 128 + 32 * kk + 8 * cg]);
+            dst[0] = make_float4(P[8 * kk + 0], P[8 * kk + 1], P[8 * kk + 2], P[8 * kk + 3]);
+            dst[1] = make_float4(P[8 * kk + 4], P[8 * kk + 5], P[8 * kk + 6], P[8 * kk + 7]);
+        }
     }
-    __syncthreads();  // B1
+    lds_barrier();  // B1
 
     // ---- P1: cross-block decays, outputs that need only gamma, Gram tiles --
-    _Float16 kbar[32];
-    {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            h8 qg8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int ch = 32 * kk + 8 * cg + e;
-                const float p0 = sm.pblk[ch], p1 = sm.pblk[128 + ch];
-                const float p2 = sm.pblk[256 + ch], p3 = sm.pblk[384 + ch];
-                const float gb = (w > 0 ? p0 : 1.f) * (w > 1 ? p1 : 1.f) * (w > 2 ? p2 : 1.f);
-                const float ga = (w < 1 ? p1 : 1.f) * (w < 2 ? p2 : 1.f) * (w < 3 ? p3 : 1.f);
-                const int idx = 8 * kk + e;
-                qg8[e] = (_Float16)(gb * qv[idx]);                                   // gamma_i qhat_i
-                sm.kgT[ch * 64 + row] = (_Float16)(b * gb * kv[idx]);                // b gamma khat
-                sm.vbT[ch * 64 + row] = (_Float16)(b * vv[idx]);                     // b v
-                kbar[idx] = (_Float16)(ga * ytk[idx]);                               // exp(G_n - G_j) khat_j
-                if (w == 0 && r16 == 0) gn[ch] = p0 * p1 * p2 * p3;                  // exp(G_n)
-            }
-            *reinterpret_cast<h8 *>(Qg + row * kK + 32 * kk + 8 * cg) = qg8;
-        }
-    }
-
-    // Gram tiles of row block w, computed transposed: D[j][i] for j in block jb.
-    f4 akk_o[3], aqk_o[3], akk_d, aqk_d;
-#pragma unroll
-    for (int t = 0; t < 3; ++t) { akk_o[t] = f4{0, 0, 0, 0}; aqk_o[t] = f4{0, 0, 0, 0}; }
-    akk_d = f4{0, 0, 0, 0};
-    aqk_d = f4{0, 0, 0, 0};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        h8 xh, qh;
-        s8 xhi, xlo, qhi, qlo, ydhi, ydlo;
+        const int c0 = 32 * kk + 8 * cg;
+        float pb[4][8];
+#pragma unroll
+        for (int wp = 0; wp < 4; ++wp) {
+            const float4 x0 = *reinterpret_cast<const float4 *>(&sm.pblk[wp * 128 + c0]);
+            const float4 x1 = *reinterpret_cast<const float4 *>(&sm.pblk[wp * 128 + c0 + 4]);
+            pb[wp][0] = x0.x; pb[wp][1] = x0.y; pb[wp][2] = x0.z; pb[wp][3] = x0.w;
+            pb[wp][4] = x1.x; pb[wp][5] = x1.y; pb[wp][6] = x1.z; pb[wp][7] = x1.w;
+        }
+        float vf[8];
+        unpack_bf16x8(vraw[kk], vf);
+        h8 qg8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
+            const int ch = c0 + e;
+            const float gb = (w > 0 ? pb[0][e] : 1.f) * (w > 1 ? pb[1][e] : 1.f) * (w > 2 ? pb[2][e] : 1.f);
+            const float ga = (w < 1 ? pb[1][e] : 1.f) * (w < 2 ? pb[2][e] : 1.f) * (w < 3 ? pb[3][e] : 1.f);
             const int idx = 8 * kk + e;
-            xh[e] = (_Float16)kv[idx];
-            qh[e] = (_Float16)qv[idx];
-            short th, tl;
-            split_bf16(kv[idx], th, tl); xhi[e] = th; xlo[e] = tl;
-            split_bf16(qv[idx], th, tl); qhi[e] = th; qlo[e] = tl;
-            split_bf16(yd[idx], th, tl); ydhi[e] = th; ydlo[e] = tl;
+            qg8[e] = (_Float16)(gb * qv[idx]);                        // gamma_i qhat_i
+            sm.kgT[ch * 64 + row] = (_Float16)(b * gb * kv[idx]);     // b gamma khat
+            sm.vbT[ch * 64 + row] = (_Float16)(b * vf[e]);            // b v
+            Kbt[ch * 64 + row] = (_Float16)(ga * (P[idx] * yd[idx]));  // exp(G_n - G_j) khat_j, transposed
         }
-        // diagonal block: A = Yd (rows j), B = X or Q' (columns i)
-        akk_d = mfma16x16x32_bf16(ydhi, xhi, akk_d);
-        akk_d = mfma16x16x32_bf16(ydhi, xlo, akk_d);
-        akk_d = mfma16x16x32_bf16(ydlo, xhi, akk_d);
-        aqk_d = mfma16x16x32_bf16(ydhi, qhi, aqk_d);
-        aqk_d = mfma16x16x32_bf16(ydhi, qlo, aqk_d);
-        aqk_d = mfma16x16x32_bf16(ydlo, qhi, aqk_d);
-        // off-diagonal blocks jb < w: A = exp(G_{r-1} - G_j) khat_j
-        //   = [prod_{jb < w' < w} pblk[w']] * yt_j
-#pragma unroll
-        for (int jb = 0; jb < 3; ++jb) {
-            if (jb < w) {
-                const int c0 = 32 * kk + 8 * cg;
-                const float4 y0 = *reinterpret_cast<const float4 *>(&sm.yt[(16 * jb + r16) * 128 + c0]);
-                const float4 y1 = *reinterpret_cast<const float4 *>(&sm.yt[(16 * jb + r16) * 128 + c0 + 4]);
-                float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-                for (int wp = jb + 1; wp < w; ++wp) {
-                    const float4 m0 = *reinterpret_cast<const float4 *>(&sm.pblk[wp * 128 + c0]);
-                    const float4 m1 = *reinterpret_cast<const float4 *>(&sm.pblk[wp * 128 + c0 + 4]);
-                    y[0] *= m0.x; y[1] *= m0.y; y[2] *= m0.z; y[3] *= m0.w;
-                    y[4] *= m1.x; y[5] *= m1.y; y[6] *= m1.z; y[7] *= m1.w;
-                }
-                h8 yh;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) yh[e] = (_Float16)y[e];
-                akk_o[jb] = mfma16x16x32_f16(yh, xh, akk_o[jb]);
-                aqk_o[jb] = mfma16x16x32_f16(yh, qh, aqk_o[jb]);
-            }
+        if (w == 0 && r16 == 0) {
+            *reinterpret_cast<float4 *>(gn + c0) = make_float4(
+                pb[0][0] * pb[1][0] * pb[2][0] * pb[3][0], pb[0][1] * pb[1][1] * pb[2][1] * pb[3][1],
+                pb[0][2] * pb[1][2] * pb[2][2] * pb[3][2], pb[0][3] * pb[1][3] * pb[2][3] * pb[3][3]);
+            *reinterpret_cast<float4 *>(gn + c0 + 4) = make_float4(
+                pb[0][4] * pb[1][4] * pb[2][4] * pb[3][4], pb[0][5] * pb[1][5] * pb[2][5] * pb[3][5],
+                pb[0][6] * pb[1][6] * pb[2][6] * pb[3][6], pb[0][7] * pb[1][7] * pb[2][7] * pb[3][7]);
         }
+        *reinterpret_cast<h8 *>(Qg + row * kK + c0) = qg8;
     }
-    // Write tiles.  Lane holds D[j = 16 jb + 4 cg + e][i = row].
-    {
-        const int i = row;
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            f4 dk, dq;
-            if (jb < w) { dk = akk_o[jb < 3 ? jb : 0]; dq = aqk_o[jb < 3 ? jb : 0]; }
-            else if (jb == w) {
-                dk = akk_d; dq = aqk_d;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int jj = 4 * cg + e;
-                    if (!(jj < r16)) dk[e] = 0.f;
-                    if (!(jj <= r16)) dq[e] = 0.f;
-                }
-            } else { dk = f4{0, 0, 0, 0}; dq = f4{0, 0, 0, 0}; }
-            dk = dk * b;
-            *reinterpret_cast<f4 *>(&sm.L[i * 64 + 16 * jb + 4 * cg]) = dk;
-            *reinterpret_cast<h4 *>(Aqk + i * 64 + 16 * jb + 4 * cg) = to_h4(dq);
-        }
-    }
-    __syncthreads();  // B2: L complete, yt free, kgT/vbT complete
 
-    // ---- P2: stage Kbar^T, invert the diagonal 16x16 blocks of (I + A_kk) --
-    _Float16 *sKbT = reinterpret_cast<_Float16 *>(sm.yt);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sKbT[(32 * kk + 8 * cg + e) * 64 + row] = kbar[8 * kk + e];
+    switch (w) {
+        case 0: gram_tiles<0>(sm, kv, qv, yd, b, row, r16, cg, Aqk); break;
+        case 1: gram_tiles<1>(sm, kv, qv, yd, b, row, r16, cg, Aqk); break;
+        case 2: gram_tiles<2>(sm, kv, qv, yd, b, row, r16, cg, Aqk); break;
+        default: gram_tiles<3>(sm, kv, qv, yd, b, row, r16, cg, Aqk); break;
+    }
+    lds_barrier();  // B2: L complete, yt free, kgT/vbT complete
+
+    // ---- P2: invert the diagonal 16x16 blocks of (I + A_kk) -----------------
     if (cg == 0) {
         // lane r16 = column j of T_ww; left-looking forward substitution in fp32
         const int j = r16;
@@ -324,14 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sm.L[(16 * w + r) * 64 + 16 * w + j] = x[r];
     }
-    __syncthreads();  // B3
-
-    // Kbar^T to global, coalesced 16-byte stores
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int q16 = tid + 256 * m;
-        reinterpret_cast<uint4 *>(Kbt)[q16] = reinterpret_cast<const uint4 *>(sKbT)[q16];
-    }
+    lds_barrier();  // B3
 
     // ---- P3: off-diagonal blocks of T, row block by row block -------------
     //   T_ij = -T_ii * sum_{k=j}^{i-1} L_ik T_kj  (16x16 blocks, split-fp16 MFMA)
@@ -361,12 +378,12 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
             split_h4(bv, bh, bl);
             tij = mfma_split16(ah, al, bh, bl, tij);
         }
-        __syncthreads();
+        lds_barrier();
         if (w < ib) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) sm.L[(16 * ib + 4 * cg + e) * 64 + 16 * w + r16] = -tij[e];
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- P4: W^T = (Kg)^T T^T and U = T Vb on MFMA --------------------------
