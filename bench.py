@@ -90,12 +90,25 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, help="workload index 0..4 (default: T=8192, H=32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (the "
+                         "reference kernel that scales FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the KDA forward shards by heads or sequences with "
               "no communication, so no multi-GPU run is made (asked for %d GPUs)" % args.gpus,
               file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return 0
 
     import gated_delta_rule_110_amd as kda
     if not os.path.exists(kda.LIB_PATH):

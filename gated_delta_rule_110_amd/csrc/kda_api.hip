@@ -43,11 +43,11 @@ WorkspaceLayout make_layout(const Geometry &g) {
     const size_t per = (size_t)g.slots * (size_t)g.H;
     size_t o = 0;
     L.off_chunk_off = o; o = align_up(o + (g.varlen ? sizeof(int32_t) * (size_t)(g.N + 1) : 0), 256);
-    L.off_Wn = o;  o = align_up(o + per * kWnElems * 2, 256);
-    L.off_Qg = o;  o = align_up(o + per * kQgElems * 2, 256);
-    L.off_Kbt = o; o = align_up(o + per * kKbtElems * 2, 256);
-    L.off_Ut = o;  o = align_up(o + per * kUtElems * 2, 256);
-    L.off_Aqk = o; o = align_up(o + per * kAqkElems * 2, 256);
+    L.off_Wf = o; o = align_up(o + per * kWfElems * 2, 256);
+    L.off_Qf = o; o = align_up(o + per * kQfElems * 2, 256);
+    L.off_Kf = o; o = align_up(o + per * kKfElems * 2, 256);
+    L.off_Af = o; o = align_up(o + per * kAfElems * 2, 256);
+    L.off_Uf = o; o = align_up(o + per * kUfElems * 2, 256);
     L.off_gn = o;  o = align_up(o + per * kGnElems * 4, 256);
     L.total = o;
     return L;
@@ -136,17 +136,17 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
     ia.A_log = A_log; ia.dt_bias = dt_bias; ia.lower_bound = lower_bound;
     ia.cu = cu_seqlens; ia.chunk_off = chunk_off;
     ia.T = geo.T; ia.H = geo.H; ia.N = geo.N; ia.nc_fixed = geo.nc_fixed;
-    ia.Wn = reinterpret_cast<_Float16 *>(ws + lay.off_Wn);
-    ia.Qg = reinterpret_cast<_Float16 *>(ws + lay.off_Qg);
-    ia.Kbt = reinterpret_cast<_Float16 *>(ws + lay.off_Kbt);
-    ia.Ut = reinterpret_cast<_Float16 *>(ws + lay.off_Ut);
-    ia.Aqk = reinterpret_cast<_Float16 *>(ws + lay.off_Aqk);
+    ia.Wf = reinterpret_cast<_Float16 *>(ws + lay.off_Wf);
+    ia.Qf = reinterpret_cast<_Float16 *>(ws + lay.off_Qf);
+    ia.Kf = reinterpret_cast<_Float16 *>(ws + lay.off_Kf);
+    ia.Af = reinterpret_cast<_Float16 *>(ws + lay.off_Af);
+    ia.Uf = reinterpret_cast<_Float16 *>(ws + lay.off_Uf);
     ia.gn = reinterpret_cast<float *>(ws + lay.off_gn);
     if (err == hipSuccess && geo.T > 0) err = kda_launch_intra(ia, geo.slots, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[2], stream);
 
     ChainArgs ca{};
-    ca.Wn = ia.Wn; ca.Qg = ia.Qg; ca.Kbt = ia.Kbt; ca.Ut = ia.Ut; ca.Aqk = ia.Aqk; ca.gn = ia.gn;
+    ca.Wf = ia.Wf; ca.Qf = ia.Qf; ca.Kf = ia.Kf; ca.Af = ia.Af; ca.Uf = ia.Uf; ca.gn = ia.gn;
     ca.cu = cu_seqlens; ca.chunk_off = chunk_off;
     ca.T = geo.T; ca.H = geo.H; ca.N = geo.N; ca.nc_fixed = geo.nc_fixed;
     ca.scale = scale;

@@ -9,79 +9,166 @@
 //   O_c  = scale * (Qg S + A_qk Ut_c)      (outputs of the chunk's tokens)
 //   S   <- Diag(exp(G_n)) S + Kbar^T Ut_c  (state leaving the chunk)
 //
-// The state's V columns evolve independently, so each 256-thread workgroup
-// owns one (sequence, head, 32-column V block); the state slice (128 x 32
-// fp32) lives in MFMA accumulators and is shared through LDS as fp16 each
-// step.  The four V-block workgroups of a head are placed on the same XCD
-// (same blockIdx % 8) so that they share the head's per-chunk operands in
-// that XCD's L2.  The optional initial state seeds S and the final state is
-// written after the last chunk; passing one call's final state as the next
-// call's initial state continues a sequence, which is the multi-turn state
-// carry the forward call exposes ("¿Qué es la atención Kimi Delta…",
-// 7minutos.es).
+// The state's V columns evolve independently, so each workgroup owns one
+// (sequence, head, 16-column V block).  Its first wave runs the chain: the
+// 128 x 16 fp32 state slice lives in eight MFMA accumulator tiles, and because
+// the intermediates are stored in fragment order with a matching k
+// permutation, a pair of accumulator tiles converted to fp16 is directly the B
+// operand of the next product -- no LDS round trip sits on the serial path.
+// The second wave computes the outputs from the fp16 state and pseudo-value
+// fragments the chain wave hands over through a double-buffered LDS slot, one
+// barrier per chunk.  Each wave prefetches the next chunk's operands into
+// registers while it works on the current one.
+//
+// The eight V-block workgroups of a head are placed on one XCD (same
+// blockIdx % 8), so the head's per-chunk operands are fetched from HBM once
+// into that XCD's L2 and shared.  The optional initial state seeds S and the
+// final state is written after the last chunk; passing one call's final state
+// as the next call's initial state continues a sequence, which is the
+// multi-turn state carry the forward call exposes ("¿Qué es la atención Kimi
+// Delta…", 7minutos.es).
 #include "kda_common.h"
 
 using namespace kda;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kVB = 32;              // value columns per workgroup
+constexpr int kThreads = 128;        // wave 0: state chain, wave 1: outputs
+constexpr int kVB = 16;              // value columns per workgroup
 constexpr int kNVB = kV / kVB;       // workgroups per (sequence, head)
-constexpr int kSPad = kK + 8;        // LDS row pitches (halves)
-constexpr int kUPad = kChunk + 8;
-constexpr int kOPad = kVB + 8;
 
 struct __align__(16) ChainSmem {
-    _Float16 sSt[kVB * kSPad];       // S^T in fp16, [v][channel]
-    _Float16 sUt[kVB * kUPad];       // Ut^T in fp16, [v][token]
-    uint16_t sO[kChunk * kOPad];     // output tile, bf16 [token][v]
+    h8 sS[2][4][64];   // state as fp16 B fragments [slot][k-block][lane]
+    h8 sU[2][2][64];   // pseudo-values as fp16 B fragments
 };
 
-struct StepOps {
-    h8 A[2][4];    // rows of -W (waves 0,1) or Qg (waves 2,3): [row tile][k step]
-    h4 U[2][2];    // waves 0,1: U tile in accumulator layout [row tile][col tile]
-    h8 Aq[2][2];   // waves 2,3: A_qk rows [row tile][k step]
-    h8 Kb[2][2];   // Kbar^T rows [row tile][k step]
-    f4 g[2];       // exp(G_n) for the lane's state rows [row tile]
+struct ChainOps {      // the chain wave's operands for one chunk
+    h8 W[4][4];        // -W  [row tile][k-block]
+    h8 K[8][2];        // Kbar^T [channel tile][k-block]
+    h4 U[4];           // U in accumulator layout [row tile]
 };
 
-__device__ __forceinline__ void load_step(StepOps &o, const ChainArgs &a, int64_t ws, int w, int vb,
-                                          int r16, int cg) {
-    const _Float16 *rows = (w < 2 ? a.Wn + ws * kWnElems : a.Qg + ws * kQgElems);
-    const int rbase = 32 * (w & 1);
+struct OutOps {        // the output wave's operands for one chunk
+    h8 Q[4][4];        // Qg  [row tile][k-block]
+    h8 A[4][2];        // A_qk [row tile][k-block]
+};
+
+__device__ __forceinline__ void load_chain_ops(ChainOps &o, const ChainArgs &a, int64_t ws, int vb,
+                                               int lane) {
+    const h8 *W = reinterpret_cast<const h8 *>(a.Wf + ws * kWfElems) + lane;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int it = 0; it < 4; ++it)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            o.A[rt][ks] = *reinterpret_cast<const h8 *>(rows + (rbase + 16 * rt + r16) * kK + 32 * ks + 8 * cg);
-    if (w < 2) {
-        const _Float16 *ut = a.Ut + ws * kUtElems;
+        for (int kb = 0; kb < 4; ++kb) o.W[it][kb] = W[(it * 4 + kb) * 64];
+    const h8 *K = reinterpret_cast<const h8 *>(a.Kf + ws * kKfElems) + lane;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+    for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-                o.U[rt][ct] = *reinterpret_cast<const h4 *>(ut + (kVB * vb + 16 * ct + r16) * kChunk + rbase + 16 * rt + 4 * cg);
-    } else {
-        const _Float16 *aq = a.Aqk + ws * kAqkElems;
+        for (int kb = 0; kb < 2; ++kb) o.K[ct][kb] = K[(ct * 2 + kb) * 64];
+    const h4 *U = reinterpret_cast<const h4 *>(a.Uf + ws * kUfElems) + vb * 4 * 64 + lane;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                o.Aq[rt][ks] = *reinterpret_cast<const h8 *>(aq + (rbase + 16 * rt + r16) * kChunk + 32 * ks + 8 * cg);
-    }
-    const _Float16 *kb = a.Kbt + ws * kKbtElems;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            o.Kb[rt][ks] = *reinterpret_cast<const h8 *>(kb + (32 * w + 16 * rt + r16) * kChunk + 32 * ks + 8 * cg);
-    const float *gn = a.gn + ws * kGnElems;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) o.g[rt] = *reinterpret_cast<const f4 *>(gn + 32 * w + 16 * rt + 4 * cg);
+    for (int it = 0; it < 4; ++it) o.U[it] = U[it * 64];
 }
 
-__global__ __launch_bounds__(kThreads, 2) void kda_chain_kernel(ChainArgs a) {
+__device__ __forceinline__ void load_out_ops(OutOps &o, const ChainArgs &a, int64_t ws, int lane) {
+    const h8 *Q = reinterpret_cast<const h8 *>(a.Qf + ws * kQfElems) + lane;
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) o.Q[it][kb] = Q[(it * 4 + kb) * 64];
+    const h8 *A = reinterpret_cast<const h8 *>(a.Af + ws * kAfElems) + lane;
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) o.A[it][kb] = A[(it * 2 + kb) * 64];
+}
+
+// Two accumulator tiles (rows 4g+e of tile 2p and of tile 2p+1) -> one fp16 B
+// fragment of k-block p.
+__device__ __forceinline__ h8 pack_frag(const f4 &t0, const f4 &t1) {
+    h8 r;
+    r[0] = (_Float16)t0[0]; r[1] = (_Float16)t0[1]; r[2] = (_Float16)t0[2]; r[3] = (_Float16)t0[3];
+    r[4] = (_Float16)t1[0]; r[5] = (_Float16)t1[1]; r[6] = (_Float16)t1[2]; r[7] = (_Float16)t1[3];
+    return r;
+}
+
+// One chunk of the state chain.  S[ct] holds S[16 ct + 4 g + e][16 vb + r].
+__device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], const ChainOps &op, const float *gn,
+                                           int slot, int lane) {
+    // exp(G_n) for the lane's state rows, needed only after the barrier
+    f4 gd[8];
+    const f4 *G = reinterpret_cast<const f4 *>(gn) + (lane >> 4);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) gd[ct] = G[4 * ct];
+    h8 Sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        Sb[kb] = pack_frag(S[2 * kb], S[2 * kb + 1]);
+        sm.sS[slot][kb][lane] = Sb[kb];
+    }
+    // Ut = U - W S: X[it] holds Ut[16 it + 4 g + e][16 vb + r]
+    f4 X[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        X[it][0] = (float)op.U[it][0]; X[it][1] = (float)op.U[it][1];
+        X[it][2] = (float)op.U[it][2]; X[it][3] = (float)op.U[it][3];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) X[it] = mfma16x16x32_f16(op.W[it][kb], Sb[kb], X[it]);
+    h8 Ub[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        Ub[kb] = pack_frag(X[2 * kb], X[2 * kb + 1]);
+        sm.sU[slot][kb][lane] = Ub[kb];
+    }
+    lds_barrier();
+    // S <- Diag(exp(G_n)) S + Kbar^T Ut
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) S[ct] = S[ct] * gd[ct];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) S[ct] = mfma16x16x32_f16(op.K[ct][kb], Ub[kb], S[ct]);
+}
+
+// Outputs of one chunk, computed transposed so that each lane ends up with four
+// consecutive value columns of one token: O^T = S^T Qg^T + Ut^T A_qk^T.
+__device__ __forceinline__ void out_step(ChainSmem &sm, const OutOps &op, int slot, int lane, float scale,
+                                         uint16_t *out_chunk, int64_t row_stride, int64_t rows) {
+    lds_barrier();
+    h8 Sb[4], Ub[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) Sb[kb] = sm.sS[slot][kb][lane];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) Ub[kb] = sm.sU[slot][kb][lane];
+    f4 O[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) O[it] = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) O[it] = mfma16x16x32_f16(Sb[kb], op.Q[it][kb], O[it]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) O[it] = mfma16x16x32_f16(Ub[kb], op.A[it][kb], O[it]);
+    // lane (r, g) holds O[16 it + r][16 vb + 4 g + e]
+    const int r = lane & 15;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int row = 16 * it + r;
+        if (row < rows) {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16_bits(scale * O[it][0]) | ((uint32_t)f32_to_bf16_bits(scale * O[it][1]) << 16);
+            pk.y = (uint32_t)f32_to_bf16_bits(scale * O[it][2]) | ((uint32_t)f32_to_bf16_bits(scale * O[it][3]) << 16);
+            *reinterpret_cast<uint2 *>(out_chunk + row * row_stride) = pk;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
     __shared__ ChainSmem sm;
 
     const int64_t H = a.H;
@@ -108,135 +195,58 @@ __global__ __launch_bounds__(kThreads, 2) void kda_chain_kernel(ChainArgs a) {
         seqlen = a.T;
     }
 
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int lane = tid & 63;
-    const int r16 = lane & 15;
-    const int cg = lane >> 4;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15;
+    const int g = lane >> 4;
 
-    // state fragment: S[c = 32 w + 16 rt + 4 cg + e][v = 32 vb + 16 ct + r16]
-    f4 S[2][2];
-    const int64_t sbase = (n * H + h) * (int64_t)kK * kV;
+    if (wave == 0) {
+        // ---- state chain ---------------------------------------------------
+        f4 S[8];
+        const int64_t sbase = (n * H + h) * (int64_t)kK * kV + kVB * vb + r;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t idx = sbase + (int64_t)(32 * w + 16 * rt + 4 * cg + e) * kV + kVB * vb + 16 * ct + r16;
+                const int64_t idx = sbase + (int64_t)(16 * ct + 4 * g + e) * kV;
                 float s = 0.f;
                 if (a.h0) s = a.h0_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.h0)[idx])
                                         : reinterpret_cast<const float *>(a.h0)[idx];
-                S[rt][ct][e] = s;
+                S[ct][e] = s;
             }
-
-    StepOps cur, nxt;
-    if (nchunks > 0) load_step(cur, a, c0 * H + h, w, vb, r16, cg);
-
-    for (int64_t s = 0; s < nchunks; ++s) {
-        if (s + 1 < nchunks) load_step(nxt, a, (c0 + s + 1) * H + h, w, vb, r16, cg);
-
-        // (a) S -> LDS as fp16, transposed
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                h4 sv;
-                sv[0] = (_Float16)S[rt][ct][0]; sv[1] = (_Float16)S[rt][ct][1];
-                sv[2] = (_Float16)S[rt][ct][2]; sv[3] = (_Float16)S[rt][ct][3];
-                *reinterpret_cast<h4 *>(&sm.sSt[(16 * ct + r16) * kSPad + 32 * w + 16 * rt + 4 * cg]) = sv;
-            }
-        lds_barrier();
-
-        // (b) waves 0,1: Ut = U - W S (rows 32w..);  waves 2,3: Qg S (rows 32(w-2)..)
-        f4 X[2][2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                if (w < 2) {
-                    X[rt][ct][0] = (float)cur.U[rt][ct][0]; X[rt][ct][1] = (float)cur.U[rt][ct][1];
-                    X[rt][ct][2] = (float)cur.U[rt][ct][2]; X[rt][ct][3] = (float)cur.U[rt][ct][3];
-                } else {
-                    X[rt][ct] = f4{0, 0, 0, 0};
-                }
-            }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const h8 bs = *reinterpret_cast<const h8 *>(&sm.sSt[(16 * ct + r16) * kSPad + 32 * ks + 8 * cg]);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) X[rt][ct] = mfma16x16x32_f16(cur.A[rt][ks], bs, X[rt][ct]);
-            }
+        ChainOps A, B;
+        if (nchunks > 0) load_chain_ops(A, a, c0 * H + h, vb, lane);
+        for (int64_t s = 0; s < nchunks; s += 2) {
+            if (s + 1 < nchunks) load_chain_ops(B, a, (c0 + s + 1) * H + h, vb, lane);
+            chain_step(sm, S, A, a.gn + ((c0 + s) * H + h) * kGnElems, 0, lane);
+            if (s + 1 >= nchunks) break;
+            if (s + 2 < nchunks) load_chain_ops(A, a, (c0 + s + 2) * H + h, vb, lane);
+            chain_step(sm, S, B, a.gn + ((c0 + s + 1) * H + h) * kGnElems, 1, lane);
         }
-        if (w < 2) {
+        if (a.ht) {
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    h4 uv;
-                    uv[0] = (_Float16)X[rt][ct][0]; uv[1] = (_Float16)X[rt][ct][1];
-                    uv[2] = (_Float16)X[rt][ct][2]; uv[3] = (_Float16)X[rt][ct][3];
-                    *reinterpret_cast<h4 *>(&sm.sUt[(16 * ct + r16) * kUPad + 32 * w + 16 * rt + 4 * cg]) = uv;
-                }
-        }
-        lds_barrier();
-
-        // (c) S <- Diag(exp(G_n)) S + Kbar^T Ut ;  (d) waves 2,3: O = scale (Qg S + A_qk Ut)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) S[rt][ct] = S[rt][ct] * cur.g[rt];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const h8 bu = *reinterpret_cast<const h8 *>(&sm.sUt[(16 * ct + r16) * kUPad + 32 * ks + 8 * cg]);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) S[rt][ct] = mfma16x16x32_f16(cur.Kb[rt][ks], bu, S[rt][ct]);
-                if (w >= 2) {
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) X[rt][ct] = mfma16x16x32_f16(cur.Aq[rt][ks], bu, X[rt][ct]);
-                }
-            }
-        }
-        if (w >= 2) {
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sm.sO[(32 * (w - 2) + 16 * rt + 4 * cg + e) * kOPad + 16 * ct + r16] =
-                            f32_to_bf16_bits(a.scale * X[rt][ct][e]);
-        }
-        lds_barrier();
-
-        // output rows of this chunk: 64 rows x 32 columns, 16 bytes per thread
-        {
-            const int orow = tid >> 2, part = tid & 3;
-            const int64_t rem = seqlen - kChunk * s;
-            if (orow < rem) {
-                const int64_t tok = tseq + kChunk * s + orow;
-                uint4 val = *reinterpret_cast<const uint4 *>(&sm.sO[orow * kOPad + 8 * part]);
-                *reinterpret_cast<uint4 *>(a.out + (tok * H + h) * kV + kVB * vb + 8 * part) = val;
-            }
-        }
-        if (s + 1 < nchunks) cur = nxt;
-    }
-
-    if (a.ht) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int64_t idx = sbase + (int64_t)(32 * w + 16 * rt + 4 * cg + e) * kV + kVB * vb + 16 * ct + r16;
-                    if (a.ht_bf16) reinterpret_cast<uint16_t *>(a.ht)[idx] = f32_to_bf16_bits(S[rt][ct][e]);
-                    else reinterpret_cast<float *>(a.ht)[idx] = S[rt][ct][e];
+                    const int64_t idx = sbase + (int64_t)(16 * ct + 4 * g + e) * kV;
+                    if (a.ht_bf16) reinterpret_cast<uint16_t *>(a.ht)[idx] = f32_to_bf16_bits(S[ct][e]);
+                    else reinterpret_cast<float *>(a.ht)[idx] = S[ct][e];
                 }
+        }
+    } else {
+        // ---- outputs -------------------------------------------------------
+        const int64_t row_stride = H * kV;
+        uint16_t *out0 = a.out + (tseq * H + h) * kV + kVB * vb + 4 * g;
+        OutOps A, B;
+        if (nchunks > 0) load_out_ops(A, a, c0 * H + h, lane);
+        for (int64_t s = 0; s < nchunks; s += 2) {
+            if (s + 1 < nchunks) load_out_ops(B, a, (c0 + s + 1) * H + h, lane);
+            out_step(sm, A, 0, lane, a.scale, out0 + kChunk * s * row_stride, row_stride, seqlen - kChunk * s);
+            if (s + 1 >= nchunks) break;
+            if (s + 2 < nchunks) load_out_ops(A, a, (c0 + s + 2) * H + h, lane);
+            out_step(sm, B, 1, lane, a.scale, out0 + kChunk * (s + 1) * row_stride, row_stride,
+                     seqlen - kChunk * (s + 1));
+        }
     }
 }
 

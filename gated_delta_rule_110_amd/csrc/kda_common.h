@@ -17,18 +17,33 @@ typedef short s8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 // Per (chunk slot, head) intermediates written by the intra-chunk kernel and
-// consumed by the state-chain kernel, in fp16 unless stated.
-//   Wn  [64 tok][128 ch]   -W = -(I + A_kk)^-1 Diag(b) (gamma * K)      (negated)
-//   Qg  [64 tok][128 ch]   gamma * Qhat
-//   Kbt [128 ch][64 tok]   (exp(G_n - G_j) * khat_j) transposed
-//   Ut  [128 v][64 tok]    U^T, U = (I + A_kk)^-1 Diag(b) V
-//   Aqk [64 i][64 j]       causal decayed q.k products, zero above the diagonal
-//   gn  [128 ch] fp32      exp(G_n), the chunk's total per-channel decay
-constexpr int64_t kWnElems = kChunk * kK;
-constexpr int64_t kQgElems = kChunk * kK;
-constexpr int64_t kKbtElems = kK * kChunk;
-constexpr int64_t kUtElems = kV * kChunk;
-constexpr int64_t kAqkElems = kChunk * kChunk;
+// read by the state-chain kernel, fp16 unless stated.  They are stored in
+// MFMA fragment order: each 16-byte (or 8-byte) group is exactly what one lane
+// of a 16x16x32 MFMA holds, so every load and store moves 1 KiB (512 B) of
+// contiguous memory per wave instruction.
+//
+// Lane l of a wave is (r = l & 15, g = l >> 4).  The state S and the chunk's
+// pseudo-values live in MFMA accumulators, where lane (r, g) of tile t holds
+// rows 16 t + 4 g + e (e = 0..3) of column r.  A pair of accumulator tiles
+// (2 p, 2 p + 1) is fed straight back as the B operand of the 32-deep k-block
+// p, so inside a k-block the lane's eight k slots j = 0..7 stand for the rows
+//   perm(p, g, j) = 32 p + 4 g + j          (j < 4)
+//                   32 p + 16 + 4 g + j - 4  (j >= 4)
+// and every A operand that meets such a B operand is stored with its k index
+// permuted the same way.
+//
+//   Wf [4 it][4 kb][64 lane][8]  -W[16 it + r][perm(kb, g, j)]            (negated)
+//   Qf [4 it][4 kb][64 lane][8]   Qg[16 it + r][perm(kb, g, j)],  Qg = gamma * qhat
+//   Kf [8 ct][2 kb][64 lane][8]   Kbar[perm(kb, g, j)][16 ct + r], Kbar_j = exp(G_n - G_j) khat_j
+//   Af [4 it][2 kb][64 lane][8]   A_qk[16 it + r][perm(kb, g, j)]
+//   Uf [8 vb][4 it][64 lane][4]   U[16 it + 4 g + e][16 vb + r]
+//   gn [128] fp32                 exp(G_n), the chunk's total per-channel decay
+// with W = (I + A_kk)^-1 Diag(b) (gamma * Khat) and U = (I + A_kk)^-1 Diag(b) V.
+constexpr int64_t kWfElems = kChunk * kK;
+constexpr int64_t kQfElems = kChunk * kK;
+constexpr int64_t kKfElems = kK * kChunk;
+constexpr int64_t kAfElems = kChunk * kChunk;
+constexpr int64_t kUfElems = kChunk * kV;
 constexpr int64_t kGnElems = kK;
 
 struct Geometry {
@@ -40,7 +55,7 @@ struct Geometry {
 
 struct WorkspaceLayout {
     size_t off_chunk_off;  // int32 [N + 1] per-sequence first chunk slot (packed only)
-    size_t off_Wn, off_Qg, off_Kbt, off_Ut, off_Aqk, off_gn;
+    size_t off_Wf, off_Qf, off_Kf, off_Af, off_Uf, off_gn;
     size_t total;
 };
 
@@ -51,12 +66,12 @@ struct IntraArgs {
     const int64_t *cu;          // packed: cumulative lengths, else nullptr
     const int32_t *chunk_off;   // packed: [N + 1] first chunk slot of each sequence
     int64_t T, H, N, nc_fixed;
-    _Float16 *Wn, *Qg, *Kbt, *Ut, *Aqk;
+    _Float16 *Wf, *Qf, *Kf, *Af, *Uf;
     float *gn;
 };
 
 struct ChainArgs {
-    const _Float16 *Wn, *Qg, *Kbt, *Ut, *Aqk;
+    const _Float16 *Wf, *Qf, *Kf, *Af, *Uf;
     const float *gn;
     const int64_t *cu;
     const int32_t *chunk_off;

@@ -15,19 +15,30 @@
 // (the WY/UT representation of products of Householder-like factors, as used
 // for delta-rule attention by Yang et al., "Parallelizing Linear Transformers
 // with the Delta Rule over Sequence Length", extended here to a per-channel
-// decay).  The state chain kernel consumes W, U, Kbar, Qg, A_qk, exp(G_n).
+// decay).  The state-chain kernel consumes W, U, Kbar, Qg, A_qk and exp(G_n),
+// which this kernel writes in MFMA fragment order (see kda_common.h).
+//
+// Wave w owns rows 16 w .. 16 w + 15; lane (r, g) holds row 16 w + r and the
+// channels 32 kk + 8 g + e (kk = 0..3, e = 0..7), which is the A/B operand
+// layout of a 16x16x32 MFMA over channels.
 //
 // Decay factors exp(G_i - G_j) are never formed as exp(G_i) * exp(-G_j) over a
 // whole chunk (that overflows): within each 16-row block r..r+15 the kernel
 // keeps P_i = exp(G_i - G_{r-1}) (a product of at most 16 factors >= exp(-5),
 // so >= exp(-80) > FLT_MIN), and off-diagonal 16x16 blocks use the row
-// block's start as the reference so that both MFMA factors are <= 1.  That is
-// what the lower bound of -5 on the log-decay buys.
+// block's start as the reference so that both MFMA factors are <= 1 (fp16).
+// The diagonal blocks, whose factors span up to exp(+-80), use bf16 hi + lo
+// splits (three bf16 MFMAs).  That is what the lower bound of -5 on the
+// log-decay buys.
 //
-// Matrix products run on MFMA with fp16 operands and fp32 accumulation; the
-// diagonal 16x16 blocks of the two Gram matrices, whose factors span up to
-// exp(+-80), use bf16 hi+lo splits (three bf16 MFMAs); the triangular inverse
-// is done in fp32 (diagonal blocks) and split-fp16 MFMA (off-diagonal blocks).
+// Layout changes between the token-major rows a lane holds and the
+// channel-major or 4-token fragments the products need are done on the matrix
+// cores: an MFMA against a 0/1 selection matrix moves fp16 values exactly.
+//
+// The triangular inverse: the 16x16 diagonal blocks by forward substitution
+// in fp32, then the off-diagonal blocks column block by column block, each
+// wave keeping its column of T in MFMA registers (split-fp16 products), so no
+// barrier separates the block rows.
 #include "kda_common.h"
 
 using namespace kda;
@@ -35,13 +46,22 @@ using namespace kda;
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kYP = 132;   // row pitch (floats) of the decayed-key rows
+constexpr int kLP = 68;    // row pitch (floats) of A_kk / T
+constexpr int kTP = 72;    // row pitch (halves) of the transposed operands and of T in fp16
+constexpr float kLog2e = 1.4426950408889634f;
 
 struct __align__(16) IntraSmem {
-    float yt[48 * 128];      // rows of blocks 0..2: exp(G_e - G_j) * khat_j, e = block end of the row
-    float L[64 * 64];        // A_kk (b-scaled, strictly lower), overwritten in place by T
-    _Float16 kgT[128 * 64];  // (b * gamma * khat)^T, [channel][token]
-    _Float16 vbT[128 * 64];  // (b * v)^T,            [value column][token]
-    float pblk[4 * 128];     // per 16-row block: product of the block's decays, per channel
+    union {
+        float yt[64 * kYP];  // Y_j = exp(G_{r-1} - G_j) * khat_j, r = start of j's 16-row block
+        struct {
+            _Float16 kg[128 * kTP];  // (b * gamma * khat)^T   [channel][token]
+            _Float16 vb[128 * kTP];  // (b * v)^T              [value column][token]
+        } t;
+    } u;
+    float L[64 * kLP];      // b-scaled A_kk (strictly lower); diagonal blocks overwritten by T
+    _Float16 Th[64 * kTP];  // T = (I + A_kk)^-1 in fp16, zeros above the diagonal
+    float pblk[4 * 128];    // per 16-row block: product of the block's decays, per channel
 };
 
 __device__ __forceinline__ h4 to_h4(const f4 &x) {
@@ -50,100 +70,55 @@ __device__ __forceinline__ h4 to_h4(const f4 &x) {
     return r;
 }
 
+__device__ __forceinline__ h8 to_h8(const f4 &a, const f4 &b) {
+    h8 r;
+    r[0] = (_Float16)a[0]; r[1] = (_Float16)a[1]; r[2] = (_Float16)a[2]; r[3] = (_Float16)a[3];
+    r[4] = (_Float16)b[0]; r[5] = (_Float16)b[1]; r[6] = (_Float16)b[2]; r[7] = (_Float16)b[3];
+    return r;
+}
+
 // fp16 hi + lo split of four floats.
-__device__ __forceinline__ void split_h4(const float *x, h4 &hi, h4 &lo) {
+__device__ __forceinline__ void split_h4(const f4 &x, h4 &hi, h4 &lo) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        _Float16 h = (_Float16)x[e];
+        const _Float16 h = (_Float16)x[e];
         hi[e] = h;
         lo[e] = (_Float16)(x[e] - (float)h);
     }
 }
 
-__device__ __forceinline__ f4 mfma_split16(const h4 &ah, const h4 &al, const h4 &bh, const h4 &bl, f4 c) {
+// a * b with both operands split into fp16 hi + lo (three MFMAs, ~22-bit products).
+__device__ __forceinline__ f4 mfma_split16(const f4 &a, const f4 &b, f4 c) {
+    h4 ah, al, bh, bl;
+    split_h4(a, ah, al);
+    split_h4(b, bh, bl);
     c = mfma16x16x16_f16(ah, bh, c);
     c = mfma16x16x16_f16(ah, bl, c);
     c = mfma16x16x16_f16(al, bh, c);
     return c;
 }
 
-// Gram tiles of row block W, computed transposed (D[j][i], j in block jb,
-// i = this wave's rows): A_kk (b-scaled, strictly lower) to LDS in fp32 and
-// A_qk (lower incl. diagonal) to global in fp16.  Blocks above the diagonal
-// are written as zeros.
-template <int W>
-__device__ __forceinline__ void gram_tiles(IntraSmem &sm, const float *kv, const float *qv, const float *yd,
-                                           float b, int row, int r16, int cg, _Float16 *Aqk) {
-    f4 akk_o[W > 0 ? W : 1], aqk_o[W > 0 ? W : 1];
-    f4 akk_d = f4{0, 0, 0, 0}, aqk_d = f4{0, 0, 0, 0};
+// Off-diagonal blocks of T = (I + A_kk)^-1 in column block J (wave J):
+//   T_ij = -T_ii * sum_{k=j}^{i-1} L_ik T_kj   (16x16 blocks, split-fp16 MFMA),
+// with the column's blocks kept in registers in accumulator layout
+// (Tc[k][e] = T[16 k + 4 cg + e][16 J + r16]), which is also their B-operand layout.
+template <int J>
+__device__ __forceinline__ void offdiag_column(IntraSmem &sm, int r16, int cg) {
+    f4 Tc[4];
 #pragma unroll
-    for (int t = 0; t < (W > 0 ? W : 1); ++t) { akk_o[t] = f4{0, 0, 0, 0}; aqk_o[t] = f4{0, 0, 0, 0}; }
+    for (int e = 0; e < 4; ++e) Tc[J][e] = sm.L[(16 * J + 4 * cg + e) * kLP + 16 * J + r16];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int c0 = 32 * kk + 8 * cg;
-        s8 xhi, xlo, qhi, qlo, ydhi, ydlo;
-        h8 xh, qh;
+    for (int ib = J + 1; ib < 4; ++ib) {
+        f4 R = f4{0, 0, 0, 0};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int idx = 8 * kk + e;
-            short th, tl;
-            split_bf16(kv[idx], th, tl); xhi[e] = th; xlo[e] = tl;
-            split_bf16(qv[idx], th, tl); qhi[e] = th; qlo[e] = tl;
-            split_bf16(yd[idx], th, tl); ydhi[e] = th; ydlo[e] = tl;
-            xh[e] = (_Float16)kv[idx];
-            qh[e] = (_Float16)qv[idx];
+        for (int kb = J; kb < ib; ++kb) {
+            const f4 la = *reinterpret_cast<const f4 *>(&sm.L[(16 * ib + r16) * kLP + 16 * kb + 4 * cg]);
+            R = mfma_split16(la, Tc[kb], R);
         }
-        // diagonal block: factors span up to exp(+-80), so bf16 hi+lo (3 MFMAs)
-        akk_d = mfma16x16x32_bf16(ydhi, xhi, akk_d);
-        akk_d = mfma16x16x32_bf16(ydhi, xlo, akk_d);
-        akk_d = mfma16x16x32_bf16(ydlo, xhi, akk_d);
-        aqk_d = mfma16x16x32_bf16(ydhi, qhi, aqk_d);
-        aqk_d = mfma16x16x32_bf16(ydhi, qlo, aqk_d);
-        aqk_d = mfma16x16x32_bf16(ydlo, qhi, aqk_d);
-        if constexpr (W > 0) {
-            // off-diagonal blocks jb < W: A = [prod_{jb < w' < W} pblk[w']] * yt_j  (<= 1, fp16)
-            float m[8];
+        const f4 ta = *reinterpret_cast<const f4 *>(&sm.L[(16 * ib + r16) * kLP + 16 * ib + 4 * cg]);
+        Tc[ib] = -mfma_split16(ta, R, f4{0, 0, 0, 0});
 #pragma unroll
-            for (int e = 0; e < 8; ++e) m[e] = 1.f;
-#pragma unroll
-            for (int jb = W - 1; jb >= 0; --jb) {
-                if (jb < W - 1) {
-                    const float4 p0 = *reinterpret_cast<const float4 *>(&sm.pblk[(jb + 1) * 128 + c0]);
-                    const float4 p1 = *reinterpret_cast<const float4 *>(&sm.pblk[(jb + 1) * 128 + c0 + 4]);
-                    m[0] *= p0.x; m[1] *= p0.y; m[2] *= p0.z; m[3] *= p0.w;
-                    m[4] *= p1.x; m[5] *= p1.y; m[6] *= p1.z; m[7] *= p1.w;
-                }
-                const float4 y0 = *reinterpret_cast<const float4 *>(&sm.yt[(16 * jb + r16) * 128 + c0]);
-                const float4 y1 = *reinterpret_cast<const float4 *>(&sm.yt[(16 * jb + r16) * 128 + c0 + 4]);
-                h8 yh;
-                yh[0] = (_Float16)(y0.x * m[0]); yh[1] = (_Float16)(y0.y * m[1]);
-                yh[2] = (_Float16)(y0.z * m[2]); yh[3] = (_Float16)(y0.w * m[3]);
-                yh[4] = (_Float16)(y1.x * m[4]); yh[5] = (_Float16)(y1.y * m[5]);
-                yh[6] = (_Float16)(y1.z * m[6]); yh[7] = (_Float16)(y1.w * m[7]);
-                akk_o[jb] = mfma16x16x32_f16(yh, xh, akk_o[jb]);
-                aqk_o[jb] = mfma16x16x32_f16(yh, qh, aqk_o[jb]);
-            }
-        }
-    }
-    // Lane holds D[j = 16 jb + 4 cg + e][i = row].
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-        f4 dk, dq;
-        if (jb < W) { dk = akk_o[jb < W ? jb : 0]; dq = aqk_o[jb < W ? jb : 0]; }
-        else if (jb == W) {
-            dk = akk_d; dq = aqk_d;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int jj = 4 * cg + e;
-                if (!(jj < r16)) dk[e] = 0.f;
-                if (!(jj <= r16)) dq[e] = 0.f;
-            }
-        } else { dk = f4{0, 0, 0, 0}; dq = f4{0, 0, 0, 0}; }
-        dk = dk * b;
-        *reinterpret_cast<f4 *>(&sm.L[row * 64 + 16 * jb + 4 * cg]) = dk;
-        h4 qq;
-        qq[0] = (_Float16)dq[0]; qq[1] = (_Float16)dq[1]; qq[2] = (_Float16)dq[2]; qq[3] = (_Float16)dq[3];
-        *reinterpret_cast<h4 *>(Aqk + row * 64 + 16 * jb + 4 * cg) = qq;
+        for (int e = 0; e < 4; ++e) sm.Th[(16 * ib + 4 * cg + e) * kTP + 16 * J + r16] = (_Float16)Tc[ib][e];
     }
 }
 
@@ -182,15 +157,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     const bool valid = row < L;
 
     const int64_t ws = slot * H + h;  // workspace index of this (chunk, head)
-    _Float16 *Wn = a.Wn + ws * kWnElems;
-    _Float16 *Qg = a.Qg + ws * kQgElems;
-    _Float16 *Kbt = a.Kbt + ws * kKbtElems;
-    _Float16 *Ut = a.Ut + ws * kUtElems;
-    _Float16 *Aqk = a.Aqk + ws * kAqkElems;
-    float *gn = a.gn + ws * kGnElems;
 
     // ---- P0: load, normalise, gate, block-local decay products ------------
-    // Lane owns row `row`, channels ch(kk, e) = 32 kk + 8 cg + e.
     float qv[32], kv[32];
     uint4 graw[4], vraw[4];
     {
@@ -221,12 +189,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     float b = 0.f;
     if (valid) b = fast_rcp(1.0f + fast_exp(-bf16_bits_to_f32(a.beta[(t0 + row) * H + h])));
 
-    // gate: d = exp(max(lb, -exp(A_log) softplus(g + dt_bias))), then the
-    // inclusive product over the block's rows: P_i = exp(G_i - G_{r-1}).
+    // gate in base 2: log2 d = max(lb log2e, -exp(A_log) log2(1 + 2^(x log2e))), x = g + dt_bias,
+    // i.e. d = exp(max(lb, -exp(A_log) softplus(x))); then the inclusive product
+    // over the block's rows: P_i = exp(G_i - G_{r-1}).
     float P[32];
     {
-        const float Aexp = fast_exp(a.A_log[h]);
-        const float lb = a.lower_bound;
+        const float nA = -fast_exp(a.A_log[h]);
+        const float lb2 = a.lower_bound * kLog2e;
         const float *dtb = a.dt_bias + h * kK;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -238,14 +207,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
             unpack_bf16x8(graw[kk], gf);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = gf[e] + db[e];
-                // softplus(x) = max(x,0) + log1p(u), u = exp(-|x|) in (0, 1]; a short
-                // series for small u keeps log1p accurate where 1 + u would round
-                const float u = fast_exp(-fabsf(x));
-                const float small = u * (1.0f - u * (0.5f - u * (1.0f / 3.0f)));
-                const float sp = fmaxf(x, 0.f) + (u < (1.0f / 128.0f) ? small : fast_log(1.0f + u));
-                const float lg = fmaxf(lb, -Aexp * sp);
-                P[8 * kk + e] = valid ? fast_exp(lg) : 1.0f;
+                const float t = __builtin_amdgcn_exp2f((gf[e] + db[e]) * kLog2e);
+                const float l2 = fmaxf(lb2, nA * __builtin_amdgcn_logf(1.0f + t));
+                P[8 * kk + e] = valid ? __builtin_amdgcn_exp2f(l2) : 1.0f;
             }
         }
     }
@@ -254,28 +218,35 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
 #pragma unroll
         for (int e = 0; e < 32; ++e) P[e] *= dpp_row_shr(P[e], 1.0f, s);
     }
-    // yd = exp(G_{r-1} - G_j) khat_j (>= khat; used by the diagonal blocks), and
-    // exp(G_e - G_j) khat_j = pe * yd with e the block end and pe the block total
-    float yd[32];
+    // X_i = P_i khat_i and Q'_i = P_i qhat_i stay in registers; Y_j = khat_j / P_j
+    // (<= exp(80) khat_j) goes to LDS; P becomes the block total pe.
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        const float pe = dpp_row_bcast15(P[e]);
-        const float kh = kv[e] * rk;
-        yd[e] = kh * fast_rcp(P[e]);
-        kv[e] = kh * P[e];         // X_i = exp(G_i - G_{r-1}) khat_i
-        qv[e] = qv[e] * rq * P[e]; // Q'_i = exp(G_i - G_{r-1}) qhat_i
-        P[e] = pe;
-    }
-    if (w < 3) {
+    for (int kk = 0; kk < 4; ++kk) {
+        float yv[8];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int i0 = 8 * kk;
-            float4 *dst = reinterpret_cast<float4 *>(&sm.yt[row * 128 + 32 * kk + 8 * cg]);
-            dst[0] = make_float4(P[i0 + 0] * yd[i0 + 0], P[i0 + 1] * yd[i0 + 1], P[i0 + 2] * yd[i0 + 2], P[i0 + 3] * yd[i0 + 3]);
-            dst[1] = make_float4(P[i0 + 4] * yd[i0 + 4], P[i0 + 5] * yd[i0 + 5], P[i0 + 6] * yd[i0 + 6], P[i0 + 7] * yd[i0 + 7]);
+        for (int e = 0; e < 8; ++e) {
+            const int idx = 8 * kk + e;
+            const float pe = dpp_row_bcast15(P[idx]);
+            const float kh = kv[idx] * rk;
+            yv[e] = kh * fast_rcp(P[idx]);
+            kv[idx] = kh * P[idx];          // X
+            qv[idx] = qv[idx] * rq * P[idx];  // Q'
+            P[idx] = pe;
         }
+        float4 *dst = reinterpret_cast<float4 *>(&sm.u.yt[row * kYP + 32 * kk + 8 * cg]);
+        dst[0] = make_float4(yv[0], yv[1], yv[2], yv[3]);
+        dst[1] = make_float4(yv[4], yv[5], yv[6], yv[7]);
     }
-    if (r16 == 15) {
+    // b v in fp16 (natural layout)
+    h8 vbF[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        float vf[8];
+        unpack_bf16x8(vraw[kk], vf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vbF[kk][e] = (_Float16)(b * vf[e]);
+    }
+    if (r16 == 0) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             float4 *dst = reinterpret_cast<float4 *>(&sm.pblk[w * 128 + 32 * kk + 8 * cg]);
@@ -283,9 +254,22 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
             dst[1] = make_float4(P[8 * kk + 4], P[8 * kk + 5], P[8 * kk + 6], P[8 * kk + 7]);
         }
     }
-    lds_barrier();  // B1
+    lds_barrier();  // B1: block totals and decayed key rows visible
 
-    // ---- P1: cross-block decays, outputs that need only gamma, Gram tiles --
+    // ---- P1: cross-block decays, chunk outputs, Gram tiles ----------------
+    // The 0/1 selection matrices: lane (r, g) slot j is 1 where 8 g + j == r + 16 half.
+    h8 sel[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sel[hf][j] = (8 * cg + j == r16 + 16 * hf) ? (_Float16)1.0f : (_Float16)0.0f;
+
+    h8 kgF[4];                          // b gamma khat (natural layout, fp16)
+    f4 akk_o[3], aqk_o[3], akk_d = f4{0, 0, 0, 0}, aqk_d = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < 3; ++t) { akk_o[t] = f4{0, 0, 0, 0}; aqk_o[t] = f4{0, 0, 0, 0}; }
+    _Float16 *Kf = a.Kf + ws * kKfElems;
+    _Float16 *Qf = a.Qf + ws * kQfElems;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const int c0 = 32 * kk + 8 * cg;
@@ -297,39 +281,116 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
             pb[wp][0] = x0.x; pb[wp][1] = x0.y; pb[wp][2] = x0.z; pb[wp][3] = x0.w;
             pb[wp][4] = x1.x; pb[wp][5] = x1.y; pb[wp][6] = x1.z; pb[wp][7] = x1.w;
         }
-        float vf[8];
-        unpack_bf16x8(vraw[kk], vf);
-        h8 qg8;
+        float yv[8];
+        {
+            const float4 y0 = *reinterpret_cast<const float4 *>(&sm.u.yt[row * kYP + c0]);
+            const float4 y1 = *reinterpret_cast<const float4 *>(&sm.u.yt[row * kYP + c0 + 4]);
+            yv[0] = y0.x; yv[1] = y0.y; yv[2] = y0.z; yv[3] = y0.w;
+            yv[4] = y1.x; yv[5] = y1.y; yv[6] = y1.z; yv[7] = y1.w;
+        }
+        h8 qg8, kb8, xh, qh;
+        s8 xhi, xlo, qhi, qlo, yhi, ylo;
+        float gnv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int ch = c0 + e;
-            const float gb = (w > 0 ? pb[0][e] : 1.f) * (w > 1 ? pb[1][e] : 1.f) * (w > 2 ? pb[2][e] : 1.f);
-            const float ga = (w < 1 ? pb[1][e] : 1.f) * (w < 2 ? pb[2][e] : 1.f) * (w < 3 ? pb[3][e] : 1.f);
             const int idx = 8 * kk + e;
-            qg8[e] = (_Float16)(gb * qv[idx]);                        // gamma_i qhat_i
-            sm.kgT[ch * 64 + row] = (_Float16)(b * gb * kv[idx]);     // b gamma khat
-            sm.vbT[ch * 64 + row] = (_Float16)(b * vf[e]);            // b v
-            Kbt[ch * 64 + row] = (_Float16)(ga * (P[idx] * yd[idx]));  // exp(G_n - G_j) khat_j, transposed
+            // bef = exp(G_{r-1}) (blocks before this one), aft = exp(G_n - G_{r-1}) (this block and later)
+            const float bef = (w > 0 ? pb[0][e] : 1.f) * (w > 1 ? pb[1][e] : 1.f) * (w > 2 ? pb[2][e] : 1.f);
+            const float aft = (w < 1 ? pb[0][e] : 1.f) * (w < 2 ? pb[1][e] : 1.f) * (w < 3 ? pb[2][e] : 1.f) * pb[3][e];
+            gnv[e] = pb[0][e] * pb[1][e] * pb[2][e] * pb[3][e];
+            qg8[e] = (_Float16)(bef * qv[idx]);           // gamma_i qhat_i
+            kgF[kk][e] = (_Float16)(b * bef * kv[idx]);   // b gamma khat
+            kb8[e] = (_Float16)(aft * yv[e]);             // exp(G_n - G_j) khat_j
+            xh[e] = (_Float16)kv[idx];
+            qh[e] = (_Float16)qv[idx];
+            short th, tl;
+            split_bf16(kv[idx], th, tl); xhi[e] = th; xlo[e] = tl;
+            split_bf16(qv[idx], th, tl); qhi[e] = th; qlo[e] = tl;
+            split_bf16(yv[e], th, tl); yhi[e] = th; ylo[e] = tl;
         }
         if (w == 0 && r16 == 0) {
-            *reinterpret_cast<float4 *>(gn + c0) = make_float4(
-                pb[0][0] * pb[1][0] * pb[2][0] * pb[3][0], pb[0][1] * pb[1][1] * pb[2][1] * pb[3][1],
-                pb[0][2] * pb[1][2] * pb[2][2] * pb[3][2], pb[0][3] * pb[1][3] * pb[2][3] * pb[3][3]);
-            *reinterpret_cast<float4 *>(gn + c0 + 4) = make_float4(
-                pb[0][4] * pb[1][4] * pb[2][4] * pb[3][4], pb[0][5] * pb[1][5] * pb[2][5] * pb[3][5],
-                pb[0][6] * pb[1][6] * pb[2][6] * pb[3][6], pb[0][7] * pb[1][7] * pb[2][7] * pb[3][7]);
+            *reinterpret_cast<float4 *>(a.gn + ws * kGnElems + c0) = make_float4(gnv[0], gnv[1], gnv[2], gnv[3]);
+            *reinterpret_cast<float4 *>(a.gn + ws * kGnElems + c0 + 4) = make_float4(gnv[4], gnv[5], gnv[6], gnv[7]);
         }
-        *reinterpret_cast<h8 *>(Qg + row * kK + c0) = qg8;
+        // Qf[w][kk]: lane (r, g) <- Qg[16 w + r][32 kk + 16 half + 4 g + e]   (Sel x Qg^T)
+        {
+            const f4 lo = mfma16x16x32_f16(sel[0], qg8, f4{0, 0, 0, 0});
+            const f4 hi = mfma16x16x32_f16(sel[1], qg8, f4{0, 0, 0, 0});
+            *reinterpret_cast<h8 *>(Qf + ((w * 4 + kk) * 64 + lane) * 8) = to_h8(lo, hi);
+        }
+        // Kf[2 kk + half][w / 2]: lane (r, g) <- Kbar[16 w + 4 g + e][32 kk + 16 half + r]   (Kbar x Sel)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const f4 d = mfma16x16x32_f16(kb8, sel[hf], f4{0, 0, 0, 0});
+            *reinterpret_cast<h4 *>(Kf + (((2 * kk + hf) * 2 + (w >> 1)) * 64 + lane) * 8 + 4 * (w & 1)) = to_h4(d);
+        }
+        // Gram tiles, computed transposed: D[j][i], j in block jb, i = this lane's row.
+        // Diagonal block: factors span up to exp(+-80), so bf16 hi + lo (three MFMAs).
+        akk_d = mfma16x16x32_bf16(yhi, xhi, akk_d);
+        akk_d = mfma16x16x32_bf16(yhi, xlo, akk_d);
+        akk_d = mfma16x16x32_bf16(ylo, xhi, akk_d);
+        aqk_d = mfma16x16x32_bf16(yhi, qhi, aqk_d);
+        aqk_d = mfma16x16x32_bf16(yhi, qlo, aqk_d);
+        aqk_d = mfma16x16x32_bf16(ylo, qhi, aqk_d);
+        // Off-diagonal blocks jb < w: A = [prod_{jb <= w' < w} pblk[w']] * Y_j = exp(G_{r-1} - G_j) khat_j
+        // (<= 1, fp16), with r the start of this wave's block.
+        float m[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] = 1.f;
+#pragma unroll
+        for (int jb = 2; jb >= 0; --jb) {
+            if (jb < w) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m[e] *= pb[jb][e];
+                const float4 y0 = *reinterpret_cast<const float4 *>(&sm.u.yt[(16 * jb + r16) * kYP + c0]);
+                const float4 y1 = *reinterpret_cast<const float4 *>(&sm.u.yt[(16 * jb + r16) * kYP + c0 + 4]);
+                h8 yh;
+                yh[0] = (_Float16)(y0.x * m[0]); yh[1] = (_Float16)(y0.y * m[1]);
+                yh[2] = (_Float16)(y0.z * m[2]); yh[3] = (_Float16)(y0.w * m[3]);
+                yh[4] = (_Float16)(y1.x * m[4]); yh[5] = (_Float16)(y1.y * m[5]);
+                yh[6] = (_Float16)(y1.z * m[6]); yh[7] = (_Float16)(y1.w * m[7]);
+                akk_o[jb] = mfma16x16x32_f16(yh, xh, akk_o[jb]);
+                aqk_o[jb] = mfma16x16x32_f16(yh, qh, aqk_o[jb]);
+            }
+        }
     }
-
-    switch (w) {
-        case 0: gram_tiles<0>(sm, kv, qv, yd, b, row, r16, cg, Aqk); break;
-        case 1: gram_tiles<1>(sm, kv, qv, yd, b, row, r16, cg, Aqk); break;
-        case 2: gram_tiles<2>(sm, kv, qv, yd, b, row, r16, cg, Aqk); break;
-        default: gram_tiles<3>(sm, kv, qv, yd, b, row, r16, cg, Aqk); break;
+    // Lane holds D[j = 16 jb + 4 cg + e][i = row]: A_kk (b-scaled) to LDS, A_qk to Af.
+    {
+        f4 dq[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            f4 dk;
+            if (jb < w) { dk = akk_o[jb < 3 ? jb : 0]; dq[jb] = aqk_o[jb < 3 ? jb : 0]; }
+            else if (jb == w) {
+                dk = akk_d; dq[jb] = aqk_d;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int jj = 4 * cg + e;
+                    if (!(jj < r16)) dk[e] = 0.f;
+                    if (!(jj <= r16)) dq[jb][e] = 0.f;
+                }
+            } else { dk = f4{0, 0, 0, 0}; dq[jb] = f4{0, 0, 0, 0}; }
+            *reinterpret_cast<f4 *>(&sm.L[row * kLP + 16 * jb + 4 * cg]) = dk * b;
+        }
+        _Float16 *Af = a.Af + ws * kAfElems;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            *reinterpret_cast<h8 *>(Af + ((w * 2 + kb) * 64 + lane) * 8) = to_h8(dq[2 * kb], dq[2 * kb + 1]);
     }
-    lds_barrier();  // B2: L complete, yt free, kgT/vbT complete
+    lds_barrier();  // B2: L complete; the decayed key rows are no longer read
 
+    // ---- P1b: transposed operands of the W / U products into LDS ----------
+    //   kg[32 kk + 16 half + r][16 w + 4 g + e] = (b gamma khat)[16 w + 4 g + e][32 kk + 16 half + r]
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int ch = 32 * kk + 16 * hf + r16;
+            const f4 dk = mfma16x16x32_f16(kgF[kk], sel[hf], f4{0, 0, 0, 0});
+            *reinterpret_cast<h4 *>(&sm.u.t.kg[ch * kTP + 16 * w + 4 * cg]) = to_h4(dk);
+            const f4 dv = mfma16x16x32_f16(vbF[kk], sel[hf], f4{0, 0, 0, 0});
+            *reinterpret_cast<h4 *>(&sm.u.t.vb[ch * kTP + 16 * w + 4 * cg]) = to_h4(dv);
+        }
     // ---- P2: invert the diagonal 16x16 blocks of (I + A_kk) -----------------
     if (cg == 0) {
         // lane r16 = column j of T_ww; left-looking forward substitution in fp32
@@ -337,94 +398,66 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
-        const float *Lw = sm.L + (16 * w) * 64 + 16 * w;
+        const float *Lw = sm.L + (16 * w) * kLP + 16 * w;
 #pragma unroll
         for (int r = 1; r < 16; ++r) {
             float acc = x[r];
 #pragma unroll
-            for (int kq = 0; kq < r; ++kq) acc -= Lw[r * 64 + kq] * x[kq];
+            for (int kq = 0; kq < r; ++kq) acc -= Lw[r * kLP + kq] * x[kq];
             x[r] = acc;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm.L[(16 * w + r) * 64 + 16 * w + j] = x[r];
-    }
-    lds_barrier();  // B3
-
-    // ---- P3: off-diagonal blocks of T, row block by row block -------------
-    //   T_ij = -T_ii * sum_{k=j}^{i-1} L_ik T_kj  (16x16 blocks, split-fp16 MFMA)
-#pragma unroll
-    for (int ib = 1; ib < 4; ++ib) {
-        f4 tij = f4{0, 0, 0, 0};
-        if (w < ib) {
-            const int jb = w;
-            f4 R = f4{0, 0, 0, 0};
-            for (int kb = jb; kb < ib; ++kb) {
-                float av[4], bv[4];
-                const float4 la = *reinterpret_cast<const float4 *>(&sm.L[(16 * ib + r16) * 64 + 16 * kb + 4 * cg]);
-                av[0] = la.x; av[1] = la.y; av[2] = la.z; av[3] = la.w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bv[e] = sm.L[(16 * kb + 4 * cg + e) * 64 + 16 * jb + r16];
-                h4 ah, al, bh, bl;
-                split_h4(av, ah, al);
-                split_h4(bv, bh, bl);
-                R = mfma_split16(ah, al, bh, bl, R);
-            }
-            float av[4], bv[4];
-            const float4 ta = *reinterpret_cast<const float4 *>(&sm.L[(16 * ib + r16) * 64 + 16 * ib + 4 * cg]);
-            av[0] = ta.x; av[1] = ta.y; av[2] = ta.z; av[3] = ta.w;
-            bv[0] = R[0]; bv[1] = R[1]; bv[2] = R[2]; bv[3] = R[3];
-            h4 ah, al, bh, bl;
-            split_h4(av, ah, al);
-            split_h4(bv, bh, bl);
-            tij = mfma_split16(ah, al, bh, bl, tij);
+        for (int r = 0; r < 16; ++r) {
+            sm.L[(16 * w + r) * kLP + 16 * w + j] = x[r];
+            sm.Th[(16 * w + r) * kTP + 16 * w + j] = (_Float16)x[r];
         }
-        lds_barrier();
-        if (w < ib) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sm.L[(16 * ib + 4 * cg + e) * 64 + 16 * w + r16] = -tij[e];
-        }
-        lds_barrier();
     }
+    // zeros above the diagonal of T
+#pragma unroll
+    for (int jb = 1; jb < 4; ++jb)
+        if (jb > w) *reinterpret_cast<h4 *>(&sm.Th[row * kTP + 16 * jb + 4 * cg]) = h4{0, 0, 0, 0};
+    lds_barrier();  // B3: diagonal blocks of T, kg, vb complete
 
-    // ---- P4: W^T = (Kg)^T T^T and U = T Vb on MFMA --------------------------
-    f4 accW[4][2], accU[4][2];
+    // ---- P3: off-diagonal blocks of T, one column block per wave ----------
+    switch (w) {
+        case 0: offdiag_column<0>(sm, r16, cg); break;
+        case 1: offdiag_column<1>(sm, r16, cg); break;
+        case 2: offdiag_column<2>(sm, r16, cg); break;
+        default: break;
+    }
+    lds_barrier();  // B4: T complete
+
+    // ---- P4: W^T = (b gamma K)^T T^T and U = T (b V) on MFMA ---------------
+    {
+        const int nkb = w < 2 ? 1 : 2;   // T[i][j] = 0 for j > i
+        h8 tf[2];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+        for (int kb = 0; kb < 2; ++kb)
+            tf[kb] = *reinterpret_cast<const h8 *>(&sm.Th[row * kTP + 32 * kb + 8 * cg]);
+        f4 accW[8], accU[8];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) { accW[ib][t] = f4{0, 0, 0, 0}; accU[ib][t] = f4{0, 0, 0, 0}; }
+        for (int t = 0; t < 8; ++t) { accW[t] = f4{0, 0, 0, 0}; accU[t] = f4{0, 0, 0, 0}; }
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
+        for (int kb = 0; kb < 2; ++kb) {
+            if (kb >= nkb) continue;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ks == 1 && ib < 2) continue;
-            // T[i = 16 ib + r16][j = 32 ks + 8 cg + e]
-            const float *tp = &sm.L[(16 * ib + r16) * 64 + 32 * ks + 8 * cg];
-            const float4 t0v = *reinterpret_cast<const float4 *>(tp);
-            const float4 t1v = *reinterpret_cast<const float4 *>(tp + 4);
-            h8 tf;
-            tf[0] = (_Float16)t0v.x; tf[1] = (_Float16)t0v.y; tf[2] = (_Float16)t0v.z; tf[3] = (_Float16)t0v.w;
-            tf[4] = (_Float16)t1v.x; tf[5] = (_Float16)t1v.y; tf[6] = (_Float16)t1v.z; tf[7] = (_Float16)t1v.w;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int rt = 2 * w + t;  // channel tile (W^T rows) and value-column tile (U columns)
-                const h8 ka = *reinterpret_cast<const h8 *>(&sm.kgT[(16 * rt + r16) * 64 + 32 * ks + 8 * cg]);
-                accW[ib][t] = mfma16x16x32_f16(ka, tf, accW[ib][t]);
-                const h8 vb = *reinterpret_cast<const h8 *>(&sm.vbT[(16 * rt + r16) * 64 + 32 * ks + 8 * cg]);
-                accU[ib][t] = mfma16x16x32_f16(tf, vb, accU[ib][t]);
+            for (int t = 0; t < 8; ++t) {
+                const h8 ka = *reinterpret_cast<const h8 *>(&sm.u.t.kg[(16 * t + r16) * kTP + 32 * kb + 8 * cg]);
+                accW[t] = mfma16x16x32_f16(ka, tf[kb], accW[t]);
+                const h8 vv = *reinterpret_cast<const h8 *>(&sm.u.t.vb[(16 * t + r16) * kTP + 32 * kb + 8 * cg]);
+                accU[t] = mfma16x16x32_f16(tf[kb], vv, accU[t]);
             }
         }
-    }
+        // accW[ct]: W[16 w + r][16 ct + 4 cg + e] -> Wf[w][kb] = -(tiles 2 kb, 2 kb + 1)
+        _Float16 *Wf = a.Wf + ws * kWfElems;
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
+        for (int kb = 0; kb < 4; ++kb)
+            *reinterpret_cast<h8 *>(Wf + ((w * 4 + kb) * 64 + lane) * 8) = to_h8(-accW[2 * kb], -accW[2 * kb + 1]);
+        // accU[vt]: U[16 w + 4 cg + e][16 vt + r] -> Uf[vt][w]
+        _Float16 *Uf = a.Uf + ws * kUfElems;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int rt = 2 * w + t;
-            // accW: D[c = 16 rt + 4 cg + e][i = 16 ib + r16]  ->  Wn[i][c..c+3] = -W
-            const f4 wv = -accW[ib][t];
-            *reinterpret_cast<h4 *>(Wn + (16 * ib + r16) * kK + 16 * rt + 4 * cg) = to_h4(wv);
-            // accU: D[i = 16 ib + 4 cg + e][v = 16 rt + r16]  ->  Ut[v][i..i+3]
-            *reinterpret_cast<h4 *>(Ut + (16 * rt + r16) * kChunk + 16 * ib + 4 * cg) = to_h4(accU[ib][t]);
-        }
+        for (int vt = 0; vt < 8; ++vt)
+            *reinterpret_cast<h4 *>(Uf + ((vt * 4 + w) * 64 + lane) * 4) = to_h4(accU[vt]);
     }
 }
 
