@@ -33,7 +33,12 @@ using namespace kda;
 
 namespace {
 
-constexpr int kThreads = 128;        // wave 0: state chain, wave 1: outputs
+constexpr int kThreads = 192;        // wave 0: state chain, wave 1: outputs, wave 2: L2 prefetch
+#ifndef KDA_CHAIN_AHEAD
+#define KDA_CHAIN_AHEAD 8
+#endif
+constexpr int kAhead = KDA_CHAIN_AHEAD;  // chunks the prefetch wave runs ahead of the chain
+constexpr int kRing = 8;                 // chunks between a prefetch load and its use
 constexpr int kVB = 16;              // value columns per workgroup
 constexpr int kNVB = kV / kVB;       // workgroups per (sequence, head)
 
@@ -83,6 +88,40 @@ __device__ __forceinline__ void load_out_ops(OutOps &o, const ChainArgs &a, int6
         for (int kb = 0; kb < 2; ++kb) o.A[it][kb] = A[(it * 2 + kb) * 64];
 }
 
+// exp(G_n) for the lane's state rows S[16 ct + 4 g + e][.].
+__device__ __forceinline__ void load_decay(f4 (&gd)[8], const float *gn, int lane) {
+    const f4 *G = reinterpret_cast<const f4 *>(gn) + (lane >> 4);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) gd[ct] = G[4 * ct];
+}
+
+// Load this workgroup's share of one chunk's operands so that they are in the
+// XCD's L2 when the chain and output waves load them a few chunks later.  The
+// eight V-block workgroups of a head split the head's cache lines (one dword
+// per 128-byte line).  The values are consumed kRing chunks later (folded
+// into a checksum that is only stored through a null sink pointer), so the
+// wave waits for each load long after issuing it, and loads complete in order.
+__device__ __forceinline__ void touch_lines(const ChainArgs &a, int64_t ws, int vb, int lane, uint32_t &t0,
+                                            uint32_t &t1) {
+    const char *wf = reinterpret_cast<const char *>(a.Wf + ws * kWfElems);
+    const char *qf = reinterpret_cast<const char *>(a.Qf + ws * kQfElems);
+    const char *kf = reinterpret_cast<const char *>(a.Kf + ws * kKfElems);
+    const char *af = reinterpret_cast<const char *>(a.Af + ws * kAfElems);
+    const char *uf = reinterpret_cast<const char *>(a.Uf + ws * kUfElems);
+    const char *gn = reinterpret_cast<const char *>(a.gn + ws * kGnElems);
+    const int l = lane;
+    const char *p0;  // lines 0..63 of the share: W, Qg, Kbar, U
+    if (l < 16) p0 = wf + (16 * vb + l) * 128;
+    else if (l < 32) p0 = qf + (16 * vb + l - 16) * 128;
+    else if (l < 48) p0 = kf + (16 * vb + l - 32) * 128;
+    else p0 = uf + (16 * vb + l - 48) * 128;
+    const char *p1;  // lines 64..72: A_qk and exp(G_n) (lanes >= 8 share one line)
+    if (l < 8) p1 = af + (8 * vb + l) * 128;
+    else p1 = gn + (vb & 3) * 128;
+    t0 = *reinterpret_cast<const uint32_t *>(p0);
+    t1 = *reinterpret_cast<const uint32_t *>(p1);
+}
+
 // Two accumulator tiles (rows 4g+e of tile 2p and of tile 2p+1) -> one fp16 B
 // fragment of k-block p.
 __device__ __forceinline__ h8 pack_frag(const f4 &t0, const f4 &t1) {
@@ -93,13 +132,8 @@ __device__ __forceinline__ h8 pack_frag(const f4 &t0, const f4 &t1) {
 }
 
 // One chunk of the state chain.  S[ct] holds S[16 ct + 4 g + e][16 vb + r].
-__device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], const ChainOps &op, const float *gn,
+__device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], const ChainOps &op, const f4 (&gd)[8],
                                            int slot, int lane) {
-    // exp(G_n) for the lane's state rows, needed only after the barrier
-    f4 gd[8];
-    const f4 *G = reinterpret_cast<const f4 *>(gn) + (lane >> 4);
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) gd[ct] = G[4 * ct];
     h8 Sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -214,14 +248,25 @@ __global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
                                         : reinterpret_cast<const float *>(a.h0)[idx];
                 S[ct][e] = s;
             }
+        // Per step: the decay vector of this chunk is loaded first, then the
+        // next chunk's operands; loads complete in order, so waiting for the
+        // decay vector never waits for the prefetch.  The prefetch is issued
+        // on every step (the last step reloads its own chunk) so that the
+        // compiler's wait counts never have to cover a path without it.
         ChainOps A, B;
+        f4 gd[8];
+        const int64_t last = nchunks - 1;
         if (nchunks > 0) load_chain_ops(A, a, c0 * H + h, vb, lane);
         for (int64_t s = 0; s < nchunks; s += 2) {
-            if (s + 1 < nchunks) load_chain_ops(B, a, (c0 + s + 1) * H + h, vb, lane);
-            chain_step(sm, S, A, a.gn + ((c0 + s) * H + h) * kGnElems, 0, lane);
+            load_decay(gd, a.gn + ((c0 + s) * H + h) * kGnElems, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            load_chain_ops(B, a, (c0 + (s + 1 < last ? s + 1 : last)) * H + h, vb, lane);
+            chain_step(sm, S, A, gd, 0, lane);
             if (s + 1 >= nchunks) break;
-            if (s + 2 < nchunks) load_chain_ops(A, a, (c0 + s + 2) * H + h, vb, lane);
-            chain_step(sm, S, B, a.gn + ((c0 + s + 1) * H + h) * kGnElems, 1, lane);
+            load_decay(gd, a.gn + ((c0 + s + 1) * H + h) * kGnElems, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            load_chain_ops(A, a, (c0 + (s + 2 < last ? s + 2 : last)) * H + h, vb, lane);
+            chain_step(sm, S, B, gd, 1, lane);
         }
         if (a.ht) {
 #pragma unroll
@@ -233,17 +278,40 @@ __global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
                     else reinterpret_cast<float *>(a.ht)[idx] = S[ct][e];
                 }
         }
+    } else if (wave == 2) {
+        // ---- L2 prefetch: chunk s + kAhead while the others work on chunk s --
+        // Virtual step u touches chunk u + 1; steps u >= kAhead - 1 coincide with
+        // chain step s = u - kAhead + 1 and end at that step's barrier.
+        uint32_t acc = 0, r0[kRing], r1[kRing];
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) { r0[j] = 0u; r1[j] = 0u; }
+        const int64_t nu = nchunks > 0 ? nchunks + kAhead - 1 : 0;
+        for (int64_t ub = 0; ub < nu; ub += kRing) {
+#pragma unroll
+            for (int j = 0; j < kRing; ++j) {
+                const int64_t u = ub + j;
+                // past the end, the last chunk is touched again (harmless, keeps the loads unconditional)
+                const int64_t c = u + 1 < nchunks ? u + 1 : nchunks - 1;
+                acc ^= r0[j] ^ r1[j];
+                touch_lines(a, (c0 + c) * H + h, vb, lane, r0[j], r1[j]);
+                if (u >= kAhead - 1 && u < nu) lds_barrier();
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) acc ^= r0[j] ^ r1[j];
+        if (a.sink) a.sink[lane] = acc;
     } else {
         // ---- outputs -------------------------------------------------------
         const int64_t row_stride = H * kV;
         uint16_t *out0 = a.out + (tseq * H + h) * kV + kVB * vb + 4 * g;
         OutOps A, B;
+        const int64_t last = nchunks - 1;
         if (nchunks > 0) load_out_ops(A, a, c0 * H + h, lane);
         for (int64_t s = 0; s < nchunks; s += 2) {
-            if (s + 1 < nchunks) load_out_ops(B, a, (c0 + s + 1) * H + h, lane);
+            load_out_ops(B, a, (c0 + (s + 1 < last ? s + 1 : last)) * H + h, lane);
             out_step(sm, A, 0, lane, a.scale, out0 + kChunk * s * row_stride, row_stride, seqlen - kChunk * s);
             if (s + 1 >= nchunks) break;
-            if (s + 2 < nchunks) load_out_ops(A, a, (c0 + s + 2) * H + h, lane);
+            load_out_ops(A, a, (c0 + (s + 2 < last ? s + 2 : last)) * H + h, lane);
             out_step(sm, B, 1, lane, a.scale, out0 + kChunk * (s + 1) * row_stride, row_stride,
                      seqlen - kChunk * (s + 1));
         }

@@ -81,6 +81,7 @@ struct ChainArgs {
     void *ht;            // final state [N,H,K,V] or nullptr
     int h0_bf16, ht_bf16;
     uint16_t *out;       // [B,T,H,V] bf16
+    uint32_t *sink;      // always nullptr: keeps the prefetch loads observable
 };
 
 // ---- small numeric helpers --------------------------------------------------
