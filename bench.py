@@ -56,8 +56,11 @@ def state_bytes(w) -> int:
     return b
 
 
-def cpu_baseline(w, target_s: float = 12.0):
-    """Time the fp64 oracle on a bounded prefix of the same workload (all heads)."""
+def cpu_baseline(w, target_s: float = 10.0):
+    """Time the fp64 oracle (the plain token recurrence, as it stands) on the host cores.
+
+    The sample is the first T_s tokens of every sequence and all heads, run
+    repeatedly until about ``target_s`` seconds of wall time have passed."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
     units = w.N * w.H
@@ -75,12 +78,91 @@ def cpu_baseline(w, target_s: float = 12.0):
     while dt < 1.0 and T_s < w.T:
         T_s = min(w.T, T_s * 4)
         dt = run(T_s)
-    T_s = max(64, min(w.T, int(T_s * target_s / max(dt, 1e-3)) // 64 * 64))
-    dt = run(T_s)
-    tokens = w.B * T_s
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    reps, total = 1, dt
+    while total < target_s:
+        total += run(T_s)
+        reps += 1
+    tokens = w.B * T_s * reps
+    return {"value": round(tokens / total, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": "first %d of %d tokens of every sequence, all %d heads, fp64 token recurrence, "
-                      "%d OpenMP threads, %.1f s" % (T_s, w.T, w.H, threads, dt)}
+                      "%d repetitions, %d OpenMP threads, %.1f s" % (T_s, w.T, w.H, reps, threads, total)}
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources and headers the library is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_110_amd", "csrc")
+    for name in sorted(os.listdir(csrc)) + ["../../include/kda.h"]:
+        path = os.path.normpath(os.path.join(csrc, name))
+        if os.path.isfile(path):
+            h.update(name.encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload_name: str) -> str:
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload_name)
+
+
+def write_traffic(pmc_dir: str, workload_name: str) -> dict:
+    """Summarise rocprofv3 --pmc runs into profiles/traffic_<workload>.json.
+
+    pmc_dir holds four rocprofv3 CSV output folders: fetch/ (FETCH_SIZE on
+    bench.py), write/ (WRITE_SIZE on bench.py), calf/ and calw/ (the same
+    counters on ``bench.py --copy-calibration MIB``).  Both counters are in KiB
+    per dispatch; each is scaled by (copy bytes) / (counter bytes of the copy
+    kernel), so that a plain copy of known size reads as its true size."""
+    import csv
+    import glob
+
+    def per_kernel(sub):
+        sums, counts = {}, {}
+        for f in glob.glob(os.path.join(pmc_dir, sub, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                name = r["Kernel_Name"]
+                key = None
+                for kn in ("kda_intra_kernel", "kda_chain_kernel", "kda_chunk_table_kernel", "copyBuffer"):
+                    if kn in name:
+                        key = kn
+                if key is None:
+                    continue
+                sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
+                counts[key] = counts.get(key, 0) + 1
+        return {k: sums[k] / counts[k] for k in sums}
+
+    with open(os.path.join(pmc_dir, "calibration_bytes.txt")) as f:
+        cal_bytes = float(f.read().strip())
+    cf, cw = per_kernel("calf"), per_kernel("calw")
+    scale_f = cal_bytes / (cf["copyBuffer"] * 1024.0)
+    scale_w = cal_bytes / (cw["copyBuffer"] * 1024.0)
+    fe, wr = per_kernel("fetch"), per_kernel("write")
+    res = {"workload": workload_name, "source_sha256": source_digest(),
+           "fetch_scale": round(scale_f, 4), "write_scale": round(scale_w, 4), "kernels": {}}
+    for k in fe:
+        if k == "copyBuffer":
+            continue
+        rb = fe[k] * 1024.0 * scale_f
+        wb = wr.get(k, 0.0) * 1024.0 * scale_w
+        res["kernels"][k] = {"read_bytes": round(rb), "write_bytes": round(wb), "bytes": round(rb + wb)}
+    with open(traffic_path(workload_name), "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
+def load_traffic(workload_name: str, kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    path = traffic_path(workload_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("source_sha256") != source_digest():
+        return None
+    k = tr.get("kernels", {}).get(kernel)
+    return None if k is None else k["bytes"]
 
 
 def main(argv=None) -> int:
@@ -90,6 +172,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, help="workload index 0..4 (default: T=8192, H=32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV folders in DIR and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
                          "reference kernel that scales FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -100,6 +184,9 @@ def main(argv=None) -> int:
               file=sys.stderr)
         return 2
 
+    if args.traffic_from:
+        print(json.dumps(write_traffic(args.traffic_from, W.CONFIG_NAMES[args.workload])))
+        return 0
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
@@ -171,12 +258,7 @@ def main(argv=None) -> int:
     dom = max(kernels, key=kernels.get)
     dom_bytes = KERNEL_BYTES[dom] * tok_heads + (state_bytes(w) if dom == "kda_chain_kernel" else 0)
     achieved = dom_bytes / (kernels[dom] / 1e3) / 1e9
-    traffic = None
-    prof = os.path.join(ROOT, "profiles", "traffic_%s.json" % W.CONFIG_NAMES[args.workload])
-    if os.path.exists(prof):
-        with open(prof) as f:
-            tr = json.load(f)
-        traffic = tr.get(dom)
+    traffic = load_traffic(W.CONFIG_NAMES[args.workload], dom)
 
     result = {
         "metric": "KDA prefill tokens/s and MFMA TFLOP/s (% bf16 peak) at T=8K,H=32,K=V=128",

@@ -10,47 +10,60 @@
 //   S   <- Diag(exp(G_n)) S + Kbar^T Ut_c  (state leaving the chunk)
 //
 // The state's V columns evolve independently, so each workgroup owns one
-// (sequence, head, 16-column V block).  Its first wave runs the chain: the
-// 128 x 16 fp32 state slice lives in eight MFMA accumulator tiles, and because
-// the intermediates are stored in fragment order with a matching k
-// permutation, a pair of accumulator tiles converted to fp16 is directly the B
-// operand of the next product -- no LDS round trip sits on the serial path.
-// The second wave computes the outputs from the fp16 state and pseudo-value
-// fragments the chain wave hands over through a double-buffered LDS slot, one
-// barrier per chunk.  Each wave prefetches the next chunk's operands into
-// registers while it works on the current one.
+// (sequence, head, 16-column V block), with three waves:
+//
+//   wave 0 (chain)  keeps the 128 x 16 fp32 state slice in eight MFMA
+//                   accumulator tiles.  The intermediates are stored in
+//                   fragment order with a k permutation matching the
+//                   accumulator layout, so two accumulator tiles converted to
+//                   fp16 are directly the B operand of the next product -- no
+//                   LDS round trip sits on the serial path.  It reads W and
+//                   Kbar^T from an LDS ring and loads only U and exp(G_n)
+//                   itself.
+//   wave 1 (output) computes O from the fp16 state and pseudo-value fragments
+//                   the chain wave hands over through a double-buffered LDS
+//                   slot, with Qg and A_qk prefetched three chunks ahead in
+//                   registers.
+//   wave 2 (loader) streams W and Kbar^T into a three-slot LDS ring (global
+//                   loads issued three chunks ahead) and loads this
+//                   workgroup's share of the head's operands eight chunks ahead
+//                   into the XCD's L2.
+//
+// One barrier per chunk orders the LDS hand-overs.  Vector-memory loads
+// complete in order within a wave, so each wave only waits for loads that are
+// older than the ones it issues for later chunks, and every prefetch is
+// unconditional (past the end the last chunk is reloaded) so that the
+// compiler's wait counts never cover a path without it.
 //
 // The eight V-block workgroups of a head are placed on one XCD (same
-// blockIdx % 8), so the head's per-chunk operands are fetched from HBM once
-// into that XCD's L2 and shared.  The optional initial state seeds S and the
-// final state is written after the last chunk; passing one call's final state
-// as the next call's initial state continues a sequence, which is the
-// multi-turn state carry the forward call exposes ("¿Qué es la atención Kimi
-// Delta…", 7minutos.es).
+// blockIdx % 8), so the head's per-chunk operands come from HBM once into that
+// XCD's L2.  The optional initial state seeds S and the final state is
+// written after the last chunk; passing one call's final state as the next
+// call's initial state continues a sequence, which is the multi-turn state
+// carry the forward call exposes ("¿Qué es la atención Kimi Delta…",
+// 7minutos.es).
 #include "kda_common.h"
 
 using namespace kda;
 
 namespace {
 
-constexpr int kThreads = 192;        // wave 0: state chain, wave 1: outputs, wave 2: L2 prefetch
+constexpr int kThreads = 256;        // wave 0: state chain, 1: outputs, 2: LDS loader, 3: L2 prefetch
 #ifndef KDA_CHAIN_AHEAD
 #define KDA_CHAIN_AHEAD 8
 #endif
-constexpr int kAhead = KDA_CHAIN_AHEAD;  // chunks the prefetch wave runs ahead of the chain
-constexpr int kRing = 8;                 // chunks between a prefetch load and its use
-constexpr int kVB = 16;              // value columns per workgroup
-constexpr int kNVB = kV / kVB;       // workgroups per (sequence, head)
+constexpr int kAhead = KDA_CHAIN_AHEAD;  // chunks the L2 prefetch runs ahead of the chain
+constexpr int kRing = 8;                 // chunks between an L2 prefetch load and its use (multiple of 4)
+constexpr int kVB = 16;                  // value columns per workgroup
+constexpr int kNVB = kV / kVB;           // workgroups per (sequence, head)
+constexpr int kSlots = 4;                // LDS ring slots for -W / Kbar^T
 
 struct __align__(16) ChainSmem {
-    h8 sS[2][4][64];   // state as fp16 B fragments [slot][k-block][lane]
-    h8 sU[2][2][64];   // pseudo-values as fp16 B fragments
-};
-
-struct ChainOps {      // the chain wave's operands for one chunk
-    h8 W[4][4];        // -W  [row tile][k-block]
-    h8 K[8][2];        // Kbar^T [channel tile][k-block]
-    h4 U[4];           // U in accumulator layout [row tile]
+    // per slot: -W frags [it*4+kb] (0..15), Kbar^T frags [16 + ct*2+kb] (16..31), this
+    // workgroup's U block (32..33, [it][lane] of 8 bytes), exp(G_n) (34, 128 floats)
+    h8 ring[kSlots][35][64];
+    h8 sS[2][4][64];           // state as fp16 B fragments [slot][k-block][lane]
+    h8 sU[2][2][64];           // pseudo-values as fp16 B fragments
 };
 
 struct OutOps {        // the output wave's operands for one chunk
@@ -58,22 +71,7 @@ struct OutOps {        // the output wave's operands for one chunk
     h8 A[4][2];        // A_qk [row tile][k-block]
 };
 
-__device__ __forceinline__ void load_chain_ops(ChainOps &o, const ChainArgs &a, int64_t ws, int vb,
-                                               int lane) {
-    const h8 *W = reinterpret_cast<const h8 *>(a.Wf + ws * kWfElems) + lane;
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) o.W[it][kb] = W[(it * 4 + kb) * 64];
-    const h8 *K = reinterpret_cast<const h8 *>(a.Kf + ws * kKfElems) + lane;
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) o.K[ct][kb] = K[(ct * 2 + kb) * 64];
-    const h4 *U = reinterpret_cast<const h4 *>(a.Uf + ws * kUfElems) + vb * 4 * 64 + lane;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) o.U[it] = U[it * 64];
-}
+__device__ __forceinline__ int64_t clamp_chunk(int64_t s, int64_t last) { return s < last ? s : last; }
 
 __device__ __forceinline__ void load_out_ops(OutOps &o, const ChainArgs &a, int64_t ws, int lane) {
     const h8 *Q = reinterpret_cast<const h8 *>(a.Qf + ws * kQfElems) + lane;
@@ -88,19 +86,40 @@ __device__ __forceinline__ void load_out_ops(OutOps &o, const ChainArgs &a, int6
         for (int kb = 0; kb < 2; ++kb) o.A[it][kb] = A[(it * 2 + kb) * 64];
 }
 
-// exp(G_n) for the lane's state rows S[16 ct + 4 g + e][.].
-__device__ __forceinline__ void load_decay(f4 (&gd)[8], const float *gn, int lane) {
-    const f4 *G = reinterpret_cast<const f4 *>(gn) + (lane >> 4);
+// Copy one chunk's -W and Kbar^T fragments (32 KiB), this workgroup's U block
+// (2 KiB) and exp(G_n) (512 B) straight from global memory into ring slot
+// `slot`, 35 vector-memory instructions with no registers: each lane's 16 bytes
+// land at fragment base + lane * 16, the fragment order of the buffers.
+constexpr int kDmaPerChunk = 35;
+__device__ __forceinline__ void dma_ring(ChainSmem &sm, const ChainArgs &a, int64_t ws, int vb, int slot, int lane) {
+    const h8 *W = reinterpret_cast<const h8 *>(a.Wf + ws * kWfElems) + lane;
+    const h8 *K = reinterpret_cast<const h8 *>(a.Kf + ws * kKfElems) + lane;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) gd[ct] = G[4 * ct];
+    for (int f = 0; f < 16; ++f)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(W + f * 64),
+                                         (__attribute__((address_space(3))) void *)&sm.ring[slot][f][0], 16, 0, 0);
+#pragma unroll
+    for (int f = 0; f < 16; ++f)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(K + f * 64),
+                                         (__attribute__((address_space(3))) void *)&sm.ring[slot][16 + f][0], 16, 0, 0);
+    const h8 *U = reinterpret_cast<const h8 *>(a.Uf + ws * kUfElems + vb * 4 * 64 * 4) + lane;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(U + f * 64),
+                                         (__attribute__((address_space(3))) void *)&sm.ring[slot][32 + f][0], 16, 0, 0);
+    if (lane < 32) {
+        const h8 *G = reinterpret_cast<const h8 *>(a.gn + ws * kGnElems) + lane;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)G,
+                                         (__attribute__((address_space(3))) void *)&sm.ring[slot][34][0], 16, 0, 0);
+    }
 }
 
 // Load this workgroup's share of one chunk's operands so that they are in the
-// XCD's L2 when the chain and output waves load them a few chunks later.  The
-// eight V-block workgroups of a head split the head's cache lines (one dword
-// per 128-byte line).  The values are consumed kRing chunks later (folded
-// into a checksum that is only stored through a null sink pointer), so the
-// wave waits for each load long after issuing it, and loads complete in order.
+// XCD's L2 when the other waves load them a few chunks later.  The eight
+// V-block workgroups of a head split the head's cache lines (one dword per
+// 128-byte line).  The values are consumed kRing chunks later (folded into a
+// checksum that is only stored through a null sink pointer), so the compiler
+// tracks these loads and waits for each long after issuing it.
 __device__ __forceinline__ void touch_lines(const ChainArgs &a, int64_t ws, int vb, int lane, uint32_t &t0,
                                             uint32_t &t1) {
     const char *wf = reinterpret_cast<const char *>(a.Wf + ws * kWfElems);
@@ -131,9 +150,12 @@ __device__ __forceinline__ h8 pack_frag(const f4 &t0, const f4 &t1) {
     return r;
 }
 
-// One chunk of the state chain.  S[ct] holds S[16 ct + 4 g + e][16 vb + r].
-__device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], const ChainOps &op, const f4 (&gd)[8],
-                                           int slot, int lane) {
+// One chunk of the state chain.  S[ct] holds S[16 ct + 4 g + e][16 vb + r];
+// the chunk's -W and Kbar^T fragments are in ring slot `rs`.
+__device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], int rs, int slot, int lane) {
+    h8 W[16];
+#pragma unroll
+    for (int f = 0; f < 16; ++f) W[f] = sm.ring[rs][f][lane];
     h8 Sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -142,15 +164,19 @@ __device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], const Chai
     }
     // Ut = U - W S: X[it] holds Ut[16 it + 4 g + e][16 vb + r]
     f4 X[4];
+    const h4 *Ul = reinterpret_cast<const h4 *>(&sm.ring[rs][32][0]) + lane;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        X[it][0] = (float)op.U[it][0]; X[it][1] = (float)op.U[it][1];
-        X[it][2] = (float)op.U[it][2]; X[it][3] = (float)op.U[it][3];
+        const h4 u = Ul[it * 64];
+        X[it][0] = (float)u[0]; X[it][1] = (float)u[1]; X[it][2] = (float)u[2]; X[it][3] = (float)u[3];
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int it = 0; it < 4; ++it) X[it] = mfma16x16x32_f16(op.W[it][kb], Sb[kb], X[it]);
+        for (int it = 0; it < 4; ++it) X[it] = mfma16x16x32_f16(W[it * 4 + kb], Sb[kb], X[it]);
+    h8 K[16];   // read while the products above drain (the ring slot is stable until two barriers on)
+#pragma unroll
+    for (int f = 0; f < 16; ++f) K[f] = sm.ring[rs][16 + f][lane];
     h8 Ub[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -158,13 +184,14 @@ __device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], const Chai
         sm.sU[slot][kb][lane] = Ub[kb];
     }
     lds_barrier();
-    // S <- Diag(exp(G_n)) S + Kbar^T Ut
+    // S <- Diag(exp(G_n)) S + Kbar^T Ut;  exp(G_n)[16 ct + 4 g .. + 3] for the lane's rows
+    const f4 *Gl = reinterpret_cast<const f4 *>(&sm.ring[rs][34][0]) + (lane >> 4);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) S[ct] = S[ct] * gd[ct];
+    for (int ct = 0; ct < 8; ++ct) S[ct] = S[ct] * Gl[4 * ct];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) S[ct] = mfma16x16x32_f16(op.K[ct][kb], Ub[kb], S[ct]);
+        for (int ct = 0; ct < 8; ++ct) S[ct] = mfma16x16x32_f16(K[ct * 2 + kb], Ub[kb], S[ct]);
 }
 
 // Outputs of one chunk, computed transposed so that each lane ends up with four
@@ -228,6 +255,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
         tseq = n * a.T;
         seqlen = a.T;
     }
+    const int64_t last = nchunks - 1;
+    auto wsof = [&](int64_t s) { return (c0 + clamp_chunk(s, last)) * H + h; };
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -243,30 +272,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t idx = sbase + (int64_t)(16 * ct + 4 * g + e) * kV;
-                float s = 0.f;
-                if (a.h0) s = a.h0_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.h0)[idx])
+                float v = 0.f;
+                if (a.h0) v = a.h0_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.h0)[idx])
                                         : reinterpret_cast<const float *>(a.h0)[idx];
-                S[ct][e] = s;
+                S[ct][e] = v;
             }
-        // Per step: the decay vector of this chunk is loaded first, then the
-        // next chunk's operands; loads complete in order, so waiting for the
-        // decay vector never waits for the prefetch.  The prefetch is issued
-        // on every step (the last step reloads its own chunk) so that the
-        // compiler's wait counts never have to cover a path without it.
-        ChainOps A, B;
-        f4 gd[8];
-        const int64_t last = nchunks - 1;
-        if (nchunks > 0) load_chain_ops(A, a, c0 * H + h, vb, lane);
-        for (int64_t s = 0; s < nchunks; s += 2) {
-            load_decay(gd, a.gn + ((c0 + s) * H + h) * kGnElems, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            load_chain_ops(B, a, (c0 + (s + 1 < last ? s + 1 : last)) * H + h, vb, lane);
-            chain_step(sm, S, A, gd, 0, lane);
-            if (s + 1 >= nchunks) break;
-            load_decay(gd, a.gn + ((c0 + s + 1) * H + h) * kGnElems, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            load_chain_ops(A, a, (c0 + (s + 2 < last ? s + 2 : last)) * H + h, vb, lane);
-            chain_step(sm, S, B, gd, 1, lane);
+        if (nchunks > 0) {
+            lds_barrier();  // ring slot 0 written by the loader
+            for (int64_t s = 0; s < nchunks; ++s) chain_step(sm, S, (int)(s & 3), (int)(s & 1), lane);
         }
         if (a.ht) {
 #pragma unroll
@@ -278,42 +291,81 @@ __global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
                     else reinterpret_cast<float *>(a.ht)[idx] = S[ct][e];
                 }
         }
-    } else if (wave == 2) {
-        // ---- L2 prefetch: chunk s + kAhead while the others work on chunk s --
-        // Virtual step u touches chunk u + 1; steps u >= kAhead - 1 coincide with
-        // chain step s = u - kAhead + 1 and end at that step's barrier.
-        uint32_t acc = 0, r0[kRing], r1[kRing];
-#pragma unroll
-        for (int j = 0; j < kRing; ++j) { r0[j] = 0u; r1[j] = 0u; }
-        const int64_t nu = nchunks > 0 ? nchunks + kAhead - 1 : 0;
-        for (int64_t ub = 0; ub < nu; ub += kRing) {
-#pragma unroll
-            for (int j = 0; j < kRing; ++j) {
-                const int64_t u = ub + j;
-                // past the end, the last chunk is touched again (harmless, keeps the loads unconditional)
-                const int64_t c = u + 1 < nchunks ? u + 1 : nchunks - 1;
-                acc ^= r0[j] ^ r1[j];
-                touch_lines(a, (c0 + c) * H + h, vb, lane, r0[j], r1[j]);
-                if (u >= kAhead - 1 && u < nu) lds_barrier();
+    } else if (wave == 1) {
+        // ---- outputs -------------------------------------------------------
+        if (nchunks > 0) {
+            const int64_t row_stride = H * kV;
+            uint16_t *out0 = a.out + (tseq * H + h) * kV + kVB * vb + 4 * g;
+            auto out_at = [&](int64_t s) { return out0 + kChunk * s * row_stride; };
+            OutOps A, B, C;
+            load_out_ops(A, a, wsof(0), lane);
+            load_out_ops(B, a, wsof(1), lane);
+            lds_barrier();
+            for (int64_t s = 0; s < nchunks; s += 3) {
+                load_out_ops(C, a, wsof(s + 2), lane);
+                out_step(sm, A, (int)(s & 1), lane, a.scale, out_at(s), row_stride, seqlen - kChunk * s);
+                if (s + 1 >= nchunks) break;
+                load_out_ops(A, a, wsof(s + 3), lane);
+                out_step(sm, B, (int)((s + 1) & 1), lane, a.scale, out_at(s + 1), row_stride,
+                         seqlen - kChunk * (s + 1));
+                if (s + 2 >= nchunks) break;
+                load_out_ops(B, a, wsof(s + 4), lane);
+                out_step(sm, C, (int)((s + 2) & 1), lane, a.scale, out_at(s + 2), row_stride,
+                         seqlen - kChunk * (s + 2));
             }
         }
+    } else if (wave == 2) {
+        // ---- loader: W / Kbar^T into the LDS ring ---------------------------
+        // Iteration u (between barriers u - 1 and u) starts the copy of chunk
+        // u + 2 into slot (u + 2) % 4 -- the chunk that last used that slot was
+        // read before barrier u - 2 -- then waits for the copy of chunk u + 1
+        // (issued one iteration earlier) so that barrier u publishes it for
+        // chain step u + 1.  This wave issues no other vector-memory loads, and
+        // they complete in order, so "at most kDmaPerChunk outstanding" means
+        // exactly that every copy but those of chunk u + 2 has landed.
+        if (nchunks > 0) {
+            dma_ring(sm, a, wsof(0), vb, 0, lane);
+            dma_ring(sm, a, wsof(1), vb, 1, lane);
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaPerChunk) : "memory");
+            lds_barrier();  // ring slot 0 visible to the chain wave
+            for (int64_t s = 0; s < nchunks; s += 4) {
 #pragma unroll
-        for (int j = 0; j < kRing; ++j) acc ^= r0[j] ^ r1[j];
-        if (a.sink) a.sink[lane] = acc;
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t u = s + j;  // s is a multiple of 4
+                    dma_ring(sm, a, wsof(u + 2), vb, (j + 2) & 3, lane);
+                    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaPerChunk) : "memory");
+                    if (u < nchunks) lds_barrier();
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
     } else {
-        // ---- outputs -------------------------------------------------------
-        const int64_t row_stride = H * kV;
-        uint16_t *out0 = a.out + (tseq * H + h) * kV + kVB * vb + 4 * g;
-        OutOps A, B;
-        const int64_t last = nchunks - 1;
-        if (nchunks > 0) load_out_ops(A, a, c0 * H + h, lane);
-        for (int64_t s = 0; s < nchunks; s += 2) {
-            load_out_ops(B, a, (c0 + (s + 1 < last ? s + 1 : last)) * H + h, lane);
-            out_step(sm, A, 0, lane, a.scale, out0 + kChunk * s * row_stride, row_stride, seqlen - kChunk * s);
-            if (s + 1 >= nchunks) break;
-            load_out_ops(A, a, (c0 + (s + 2 < last ? s + 2 : last)) * H + h, lane);
-            out_step(sm, B, 1, lane, a.scale, out0 + kChunk * (s + 1) * row_stride, row_stride,
-                     seqlen - kChunk * (s + 1));
+        // ---- L2 prefetch: chunk s + kAhead while the others work on chunk s --
+        // Virtual step u touches chunk u + 1; steps u >= kAhead - 1 coincide with
+        // chain step u - kAhead + 1 and end at that step's barrier (after the
+        // prologue barrier the other waves pass first).
+        if (nchunks > 0) {
+            uint32_t acc = 0, r0[kRing], r1[kRing];
+#pragma unroll
+            for (int j = 0; j < kRing; ++j) { r0[j] = 0u; r1[j] = 0u; }
+            const int64_t nu = nchunks + kAhead - 1;
+            bool prologue_done = false;
+            for (int64_t ub = 0; ub < nu; ub += kRing) {
+#pragma unroll
+                for (int j = 0; j < kRing; ++j) {
+                    const int64_t u = ub + j;
+                    acc ^= r0[j] ^ r1[j];
+                    touch_lines(a, wsof(u + 1), vb, lane, r0[j], r1[j]);
+                    if (u >= kAhead - 1 && u < nu) {
+                        if (!prologue_done) { lds_barrier(); prologue_done = true; }
+                        lds_barrier();
+                    }
+                }
+            }
+            if (!prologue_done) lds_barrier();
+#pragma unroll
+            for (int j = 0; j < kRing; ++j) acc ^= r0[j] ^ r1[j];
+            if (a.sink) a.sink[lane] = acc;
         }
     }
 }

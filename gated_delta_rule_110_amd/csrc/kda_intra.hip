@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     }
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;          // wave = 16-row block
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave = 16-row block (wave-uniform)
     const int lane = tid & 63;
     const int r16 = lane & 15;       // row within the block
     const int cg = lane >> 4;        // 8-channel group within each 32-channel step
@@ -288,29 +288,42 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
             yv[0] = y0.x; yv[1] = y0.y; yv[2] = y0.z; yv[3] = y0.w;
             yv[4] = y1.x; yv[5] = y1.y; yv[6] = y1.z; yv[7] = y1.w;
         }
+        // bef = exp(G_{r-1}) (blocks before this one), aft = exp(G_n - G_{r-1}) (this block
+        // and later), per channel; w is wave-uniform, so these are scalar branches.
+        float bef[8], aft[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { bef[e] = pb[0][e]; aft[e] = pb[3][e]; }
+        if (w == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { bef[e] = 1.f; aft[e] *= pb[2][e] * pb[1][e] * pb[0][e]; }
+            if (r16 == 0) {
+                *reinterpret_cast<float4 *>(a.gn + ws * kGnElems + c0) = make_float4(aft[0], aft[1], aft[2], aft[3]);
+                *reinterpret_cast<float4 *>(a.gn + ws * kGnElems + c0 + 4) = make_float4(aft[4], aft[5], aft[6], aft[7]);
+            }
+        } else if (w == 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) aft[e] *= pb[2][e] * pb[1][e];
+        } else if (w == 2) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { bef[e] *= pb[1][e]; aft[e] *= pb[2][e]; }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bef[e] *= pb[1][e] * pb[2][e];
+        }
         h8 qg8, kb8, xh, qh;
         s8 xhi, xlo, qhi, qlo, yhi, ylo;
-        float gnv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int idx = 8 * kk + e;
-            // bef = exp(G_{r-1}) (blocks before this one), aft = exp(G_n - G_{r-1}) (this block and later)
-            const float bef = (w > 0 ? pb[0][e] : 1.f) * (w > 1 ? pb[1][e] : 1.f) * (w > 2 ? pb[2][e] : 1.f);
-            const float aft = (w < 1 ? pb[0][e] : 1.f) * (w < 2 ? pb[1][e] : 1.f) * (w < 3 ? pb[2][e] : 1.f) * pb[3][e];
-            gnv[e] = pb[0][e] * pb[1][e] * pb[2][e] * pb[3][e];
-            qg8[e] = (_Float16)(bef * qv[idx]);           // gamma_i qhat_i
-            kgF[kk][e] = (_Float16)(b * bef * kv[idx]);   // b gamma khat
-            kb8[e] = (_Float16)(aft * yv[e]);             // exp(G_n - G_j) khat_j
+            qg8[e] = (_Float16)(bef[e] * qv[idx]);            // gamma_i qhat_i
+            kgF[kk][e] = (_Float16)(b * bef[e] * kv[idx]);    // b gamma khat
+            kb8[e] = (_Float16)(aft[e] * yv[e]);              // exp(G_n - G_j) khat_j
             xh[e] = (_Float16)kv[idx];
             qh[e] = (_Float16)qv[idx];
             short th, tl;
             split_bf16(kv[idx], th, tl); xhi[e] = th; xlo[e] = tl;
             split_bf16(qv[idx], th, tl); qhi[e] = th; qlo[e] = tl;
             split_bf16(yv[e], th, tl); yhi[e] = th; ylo[e] = tl;
-        }
-        if (w == 0 && r16 == 0) {
-            *reinterpret_cast<float4 *>(a.gn + ws * kGnElems + c0) = make_float4(gnv[0], gnv[1], gnv[2], gnv[3]);
-            *reinterpret_cast<float4 *>(a.gn + ws * kGnElems + c0 + 4) = make_float4(gnv[4], gnv[5], gnv[6], gnv[7]);
         }
         // Qf[w][kk]: lane (r, g) <- Qg[16 w + r][32 kk + 16 half + 4 g + e]   (Sel x Qg^T)
         {
