@@ -159,35 +159,24 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     const int64_t ws = slot * H + h;  // workspace index of this (chunk, head)
 
     // ---- P0: load, normalise, gate, block-local decay products ------------
-    float qv[32], kv[32];
-    uint4 graw[4], vraw[4];
+    // Loads are issued g first (rows past the end reload the last row, zeroed
+    // below): they complete in order, so the gate math starts as soon as g
+    // arrives while q, k, v are still in flight.
+    uint4 graw[4], kraw[4], qraw[4], vraw[4];
+    float bl;
     {
-        const int64_t base = ((t0 + row) * H + h) * kK;
+        const int64_t base = ((t0 + (valid ? row : L - 1)) * H + h) * kK;
+        bl = bf16_bits_to_f32(a.beta[(t0 + (valid ? row : L - 1)) * H + h]);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int c0 = 32 * kk + 8 * cg;
-            uint4 qr = make_uint4(0, 0, 0, 0), kr = qr, gr = qr, vr = qr;
-            if (valid) {
-                qr = *reinterpret_cast<const uint4 *>(a.q + base + c0);
-                kr = *reinterpret_cast<const uint4 *>(a.k + base + c0);
-                gr = *reinterpret_cast<const uint4 *>(a.g + base + c0);
-                vr = *reinterpret_cast<const uint4 *>(a.v + base + c0);
-            }
-            unpack_bf16x8(qr, qv + 8 * kk);
-            unpack_bf16x8(kr, kv + 8 * kk);
-            graw[kk] = gr;
-            vraw[kk] = vr;
-        }
+        for (int kk = 0; kk < 4; ++kk) graw[kk] = *reinterpret_cast<const uint4 *>(a.g + base + 32 * kk + 8 * cg);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kraw[kk] = *reinterpret_cast<const uint4 *>(a.k + base + 32 * kk + 8 * cg);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qraw[kk] = *reinterpret_cast<const uint4 *>(a.q + base + 32 * kk + 8 * cg);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) vraw[kk] = *reinterpret_cast<const uint4 *>(a.v + base + 32 * kk + 8 * cg);
     }
-    float ssq = 0.f, ssk = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) { ssq += qv[e] * qv[e]; ssk += kv[e] * kv[e]; }
-    ssq += __shfl_xor(ssq, 16); ssq += __shfl_xor(ssq, 32);
-    ssk += __shfl_xor(ssk, 16); ssk += __shfl_xor(ssk, 32);
-    const float rq = fast_rsqrt(ssq + 1e-6f);
-    const float rk = fast_rsqrt(ssk + 1e-6f);
-    float b = 0.f;
-    if (valid) b = fast_rcp(1.0f + fast_exp(-bf16_bits_to_f32(a.beta[(t0 + row) * H + h])));
 
     // gate in base 2: log2 d = max(lb log2e, -exp(A_log) log2(1 + 2^(x log2e))), x = g + dt_bias,
     // i.e. d = exp(max(lb, -exp(A_log) softplus(x))); then the inclusive product
@@ -218,6 +207,28 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
 #pragma unroll
         for (int e = 0; e < 32; ++e) P[e] *= dpp_row_shr(P[e], 1.0f, s);
     }
+    // L2 norms (rows past the end are zeroed: no key, no query, b = 0)
+    if (!valid) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            kraw[kk] = make_uint4(0, 0, 0, 0); qraw[kk] = kraw[kk]; vraw[kk] = kraw[kk];
+        }
+    }
+    float qv[32], kv[32];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        unpack_bf16x8(kraw[kk], kv + 8 * kk);
+        unpack_bf16x8(qraw[kk], qv + 8 * kk);
+    }
+    float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) { ssq += qv[e] * qv[e]; ssk += kv[e] * kv[e]; }
+    ssq += __shfl_xor(ssq, 16); ssq += __shfl_xor(ssq, 32);
+    ssk += __shfl_xor(ssk, 16); ssk += __shfl_xor(ssk, 32);
+    const float rq = fast_rsqrt(ssq + 1e-6f);
+    const float rk = fast_rsqrt(ssk + 1e-6f);
+    const float b = valid ? fast_rcp(1.0f + fast_exp(-bl)) : 0.f;
+
     // X_i = P_i khat_i and Q'_i = P_i qhat_i stay in registers; Y_j = khat_j / P_j
     // (<= exp(80) khat_j) goes to LDS; P becomes the block total pe.
 #pragma unroll
