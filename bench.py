@@ -67,13 +67,17 @@ def cpu_baseline(w, target_s: float = 10.0):
     cores = min(threads, units)
 
     def run(T_s):
-        q, k, v, g, b = (t[:, :T_s].contiguous() for t in (w.q, w.k, w.v, w.g, w.beta))
         t0 = time.perf_counter()
-        oracle.fwd(q, k, v, g, b, w.scale, w.A_log, w.dt_bias, w.lower_bound,
-                   initial_state=w.initial_state, num_threads=threads)
+        if w.cu_seqlens is not None:  # packed batch: always the whole batch
+            oracle.fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, w.A_log, w.dt_bias, w.lower_bound,
+                       initial_state=w.initial_state, cu_seqlens=w.cu_seqlens, num_threads=threads)
+        else:
+            q, k, v, g, b = (t[:, :T_s].contiguous() for t in (w.q, w.k, w.v, w.g, w.beta))
+            oracle.fwd(q, k, v, g, b, w.scale, w.A_log, w.dt_bias, w.lower_bound,
+                       initial_state=w.initial_state, num_threads=threads)
         return time.perf_counter() - t0
 
-    T_s = 64
+    T_s = 64 if w.cu_seqlens is None else w.T
     dt = run(T_s)
     while dt < 1.0 and T_s < w.T:
         T_s = min(w.T, T_s * 4)
@@ -165,13 +169,53 @@ def load_traffic(workload_name: str, kernel: str):
     return None if k is None else k["bytes"]
 
 
+def bench_decode(kda, args, dev, H) -> int:
+    """Decode step: N sequences x H heads, one token each, fp32 state in place.
+    Algorithmic HBM bytes per step: the state read and written (2 x 64 KiB per
+    head) plus q, k, v, g (4 x 256 B), beta (2 B) and out (256 B) per head."""
+    N = args.decode
+    w = W.make("decode_N%d_H%d" % (N, H), N, 1, H, 6000 + N, lower_bound=-5.0, init="fp32", final="fp32").to(dev)
+    st = w.initial_state.clone()
+    out = torch.empty((N, 1, H, 128), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        kda.decode(w.q, w.k, w.v, w.g, w.beta, w.scale, out, w.A_log, w.dt_bias, w.lower_bound, st, st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize(dev)
+    ms = t0.elapsed_time(t1) / args.steps
+    nbytes = N * H * (2 * 128 * 128 * 4 + 4 * 256 + 2 + 256)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    print(json.dumps({"metric": "KDA decode tokens/s (one token per sequence, fp32 state in place)",
+                      "value": round(N / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "decode", "N": N, "H": H, "K": 128, "V": 128},
+                      "roofline": {"kernel": "kda_decode_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "traffic": None}}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, help="workload index 0..4 (default: T=8192, H=32)")
+    ap.add_argument("--workload", default="2",
+                    help="workload index 0..4 (default 2: T=8192, H=32) or a name from workloads.PAGES_NAMES "
+                         "(the pages' H=96 / H=64 shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", type=int, default=0, metavar="N",
+                    help="time the single-token recurrent step (kda_decode) for N sequences of the "
+                         "chosen workload's head count, fp32 state updated in place, and exit")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV folders in DIR and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -184,8 +228,9 @@ def main(argv=None) -> int:
               file=sys.stderr)
         return 2
 
+    wname = W.CONFIG_NAMES[int(args.workload)] if args.workload.isdigit() else args.workload
     if args.traffic_from:
-        print(json.dumps(write_traffic(args.traffic_from, W.CONFIG_NAMES[args.workload])))
+        print(json.dumps(write_traffic(args.traffic_from, wname)))
         return 0
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
@@ -203,7 +248,9 @@ def main(argv=None) -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w_host = W.config(args.workload)
+    if args.decode:
+        return bench_decode(kda, args, dev, W.by_name(wname).H)
+    w_host = W.by_name(wname)
     w = w_host.to(dev)
     out = torch.empty((w.B, w.T, w.H, w.V), dtype=torch.bfloat16, device=dev)
     final = None
@@ -258,7 +305,7 @@ def main(argv=None) -> int:
     dom = max(kernels, key=kernels.get)
     dom_bytes = KERNEL_BYTES[dom] * tok_heads + (state_bytes(w) if dom == "kda_chain_kernel" else 0)
     achieved = dom_bytes / (kernels[dom] / 1e3) / 1e9
-    traffic = load_traffic(W.CONFIG_NAMES[args.workload], dom)
+    traffic = load_traffic(wname, dom)
 
     result = {
         "metric": "KDA prefill tokens/s and MFMA TFLOP/s (% bf16 peak) at T=8K,H=32,K=V=128",

@@ -24,7 +24,8 @@ import torch
 from ._build import LIB as LIB_PATH
 from ._build import build
 
-__all__ = ["fwd", "workspace_size", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16", "KDA_FP32"]
+__all__ = ["fwd", "decode", "workspace_size", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
+           "KDA_FP32"]
 
 KDA_BF16 = 1
 KDA_FP32 = 2
@@ -66,6 +67,9 @@ def library() -> ctypes.CDLL:
             lib.kda_fwd.restype = ctypes.c_int
             lib.kda_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_float,
                                     P, P, P, P, ctypes.POINTER(KdaDesc), P]
+            lib.kda_decode.restype = ctypes.c_int
+            lib.kda_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_float,
+                                       P, P, P, ctypes.POINTER(KdaDesc), P]
             lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
             lib.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(KdaDesc)]
             lib.kda_status_string.restype = ctypes.c_char_p
@@ -175,6 +179,62 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
                          _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
                          _ptr(final_state), _ptr(cu_seqlens), _ptr(out), ctypes.byref(d),
                          ctypes.c_void_p(stream))
+    if st != 0:
+        raise KdaError(st, lib.kda_status_string(st).decode())
+    return out, final_state
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+           scale: float, out: Optional[torch.Tensor], A_log: torch.Tensor, dt_bias: torch.Tensor,
+           lower_bound: float, initial_state: Optional[torch.Tensor] = None,
+           final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One recurrent KDA step per sequence on the current HIP stream.
+
+    q, k, g, v: bf16 [N,1,H,128]; beta: bf16 [N,1,H]; states: bf16 or fp32
+    [N,H,128,128] or None (final_state may be the same tensor as
+    initial_state for an in-place update); out: bf16 [N,1,H,128] or None.
+    Returns ``(out, final_state)``."""
+    lib = library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("%s must be bfloat16, got %s" % (name, t.dtype))
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32:
+            raise ValueError("%s must be float32, got %s" % (name, t.dtype))
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError("q must be [N,1,H,K]")
+    N, _, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or tuple(v.shape[:3]) != (N, 1, H) or \
+            tuple(beta.shape) != (N, 1, H):
+        raise ValueError("shape mismatch among q/k/v/g/beta")
+    if tuple(A_log.shape) != (H,) or tuple(dt_bias.shape) != (H, K):
+        raise ValueError("A_log must be [H] and dt_bias [H,K]")
+    if out is None:
+        out = torch.empty((N, 1, H, V), dtype=torch.bfloat16, device=q.device)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a HIP device")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out), ("A_log", A_log),
+                    ("dt_bias", dt_bias), ("initial_state", initial_state), ("final_state", final_state)):
+        if t is None:
+            continue
+        if t.device != dev:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (N, 1, H, V):
+        raise ValueError("out must be bf16 [N,1,H,V]")
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and tuple(t.shape) != (N, H, K, V):
+            raise ValueError("%s must be [N,H,K,V] = %s" % (name, (N, H, K, V)))
+    d = _desc(N, 1, H, N, _state_dtype(initial_state, "initial_state"), _state_dtype(final_state, "final_state"))
+    d.K, d.V = K, V
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
+                            _ptr(dt_bias), float(lower_bound), _ptr(initial_state), _ptr(final_state),
+                            _ptr(out), ctypes.byref(d), ctypes.c_void_p(stream))
     if st != 0:
         raise KdaError(st, lib.kda_status_string(st).decode())
     return out, final_state

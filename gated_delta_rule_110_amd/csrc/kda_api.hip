@@ -163,3 +163,36 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
     }
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
+
+extern "C" kda_status_t kda_decode(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, float scale, const float *A_log,
+                                   const float *dt_bias, float lower_bound,
+                                   const void *initial_state, void *final_state, void *out,
+                                   const kda_desc_t *desc, hipStream_t stream) {
+    if (!desc || !A_log || !dt_bias) return KDA_ERR_NULL;
+    if (desc->B < 1 || desc->H < 1 || desc->T != 1 || desc->num_seqs != desc->B) return KDA_ERR_SHAPE;
+    if (desc->K != kK || desc->V != kV) return KDA_ERR_UNSUPPORTED;
+    if (desc->B * desc->H > 0xffffffffLL) return KDA_ERR_SHAPE;
+    if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_NULL;
+    if (!(lower_bound >= -5.0f && lower_bound <= 0.0f)) return KDA_ERR_PARAM;
+    if (!isfinite(scale)) return KDA_ERR_PARAM;
+    if (initial_state && desc->initial_state_dtype != KDA_BF16 && desc->initial_state_dtype != KDA_FP32)
+        return KDA_ERR_DTYPE;
+    if (final_state && desc->final_state_dtype != KDA_BF16 && desc->final_state_dtype != KDA_FP32)
+        return KDA_ERR_DTYPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(out, 16) ||
+        !aligned(dt_bias, 16) || !aligned(beta, 2) || !aligned(A_log, 4) ||
+        (initial_state && !aligned(initial_state, 8)) || (final_state && !aligned(final_state, 8)))
+        return KDA_ERR_ALIGN;
+    DecodeArgs da{};
+    da.q = static_cast<const uint16_t *>(q); da.k = static_cast<const uint16_t *>(k);
+    da.v = static_cast<const uint16_t *>(v); da.g = static_cast<const uint16_t *>(g);
+    da.beta = static_cast<const uint16_t *>(beta);
+    da.A_log = A_log; da.dt_bias = dt_bias; da.lower_bound = lower_bound; da.scale = scale;
+    da.N = desc->B; da.H = desc->H;
+    da.h0 = initial_state; da.ht = final_state;
+    da.h0_bf16 = desc->initial_state_dtype == KDA_BF16;
+    da.ht_bf16 = desc->final_state_dtype == KDA_BF16;
+    da.out = static_cast<uint16_t *>(out);
+    return kda_launch_decode(da, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}

@@ -84,6 +84,17 @@ struct ChainArgs {
     uint32_t *sink;      // always nullptr: keeps the prefetch loads observable
 };
 
+struct DecodeArgs {
+    const uint16_t *q, *k, *v, *g, *beta;   // [N,H,K] / [N,H,V] / [N,H] bf16
+    const float *A_log, *dt_bias;
+    float lower_bound, scale;
+    int64_t N, H;
+    const void *h0;      // state in [N,H,K,V] or nullptr (zeros)
+    void *ht;            // state out [N,H,K,V] or nullptr; may alias h0
+    int h0_bf16, ht_bf16;
+    uint16_t *out;       // [N,H,V] bf16
+};
+
 // ---- small numeric helpers --------------------------------------------------
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
@@ -169,3 +180,4 @@ __device__ __forceinline__ int64_t seq_of_slot(const int32_t *off, int64_t N, in
 hipError_t kda_launch_chunk_table(const int64_t *cu, int64_t N, int32_t *chunk_off, hipStream_t s);
 hipError_t kda_launch_intra(const kda::IntraArgs &a, int64_t slots, hipStream_t s);
 hipError_t kda_launch_chain(const kda::ChainArgs &a, hipStream_t s);
+hipError_t kda_launch_decode(const kda::DecodeArgs &a, hipStream_t s);

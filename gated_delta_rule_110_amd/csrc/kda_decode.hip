@@ -1,0 +1,160 @@
+// kda_decode.hip -- one recurrent KDA step per sequence (gfx950).
+//
+// The recurrent form of the method processes one token per step, which is
+// how generation proceeds ("¿Qué es la atención Kimi Delta y por qué es
+// importante?", 7minutos.es).  For every (sequence n, head h), with the K x V
+// state S read from initial_state (or zero):
+//
+//   S' = (I - b k k^T) Diag(exp(a)) S + b k v^T,    o = scale * S'^T q
+//
+// with the same in-kernel L2 norms, sigmoid and gate as the chunked forward.
+// Writing D = Diag(exp(a)) S, the step needs two reductions over the K rows
+// of D -- D^T k and D^T q -- after which
+//
+//   u = b (v - D^T k),   S' = D + k u^T,   o = scale (D^T q + u (k . q)).
+//
+// So the state is read once, decayed in registers, reduced, and written once:
+// the step is bound by the state's HBM traffic (2 x 64 KiB per head in fp32).
+//
+// One 256-thread workgroup per (sequence, head).  Thread (wave w, lane l)
+// holds rows 32 w .. 32 w + 31 and columns 2 l, 2 l + 1 of S, so each row is
+// one coalesced 512-byte (fp32) or 256-byte (bf16) access per wave.
+#include "kda_common.h"
+
+using namespace kda;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct __align__(16) DecodeSmem {
+    float kh[kK];          // normalised key
+    float qh[kK];          // normalised query
+    float dec[kK];         // exp(a), per channel
+    float part[4][kV][2];  // per-wave partial sums of D^T k and D^T q
+    float scal[4];         // b, k.q
+};
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+__global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
+    __shared__ DecodeSmem sm;
+    const int64_t n = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63;
+    const int64_t row = n * a.H + h;  // token row of this (sequence, head)
+
+    // ---- per-token vectors: L2 norms (waves 0, 1), gate (waves 2, 3) ------
+    if (w < 2) {
+        const uint16_t *src = (w == 0 ? a.k : a.q) + row * kK;
+        const uint32_t pair = *reinterpret_cast<const uint32_t *>(src + 2 * lane);
+        const float x0 = bf16_bits_to_f32(pair & 0xffffu), x1 = bf16_bits_to_f32(pair >> 16);
+        const float r = fast_rsqrt(wave_sum(x0 * x0 + x1 * x1) + 1e-6f);
+        float *dst = w == 0 ? sm.kh : sm.qh;
+        dst[2 * lane] = x0 * r;
+        dst[2 * lane + 1] = x1 * r;
+    } else {
+        const int c = 64 * (w - 2) + lane;
+        const float x = bf16_bits_to_f32(a.g[row * kK + c]) + a.dt_bias[h * kK + c];
+        const float nA = -fast_exp(a.A_log[h]);
+        const float l2 = fmaxf(a.lower_bound * kLog2e, nA * __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(x * kLog2e)));
+        sm.dec[c] = __builtin_amdgcn_exp2f(l2);
+        if (w == 2 && lane == 0) sm.scal[0] = fast_rcp(1.0f + fast_exp(-bf16_bits_to_f32(a.beta[row])));
+    }
+    __syncthreads();
+    if (w == 0) {
+        const float kq = wave_sum(sm.kh[2 * lane] * sm.qh[2 * lane] + sm.kh[2 * lane + 1] * sm.qh[2 * lane + 1]);
+        if (lane == 0) sm.scal[1] = kq;
+    }
+
+    // ---- state pass: D = Diag(exp(a)) S, partial D^T k and D^T q ----------
+    const int64_t sbase = (n * a.H + h) * (int64_t)kK * kV + 2 * lane;
+    float D[32][2];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int c = 32 * w + i;
+        const int64_t idx = sbase + (int64_t)c * kV;
+        float s0 = 0.f, s1 = 0.f;
+        if (a.h0) {
+            if (a.h0_bf16) {
+                const uint32_t pr = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(a.h0) + idx);
+                s0 = bf16_bits_to_f32(pr & 0xffffu);
+                s1 = bf16_bits_to_f32(pr >> 16);
+            } else {
+                const float2 pr = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(a.h0) + idx);
+                s0 = pr.x;
+                s1 = pr.y;
+            }
+        }
+        D[i][0] = s0;
+        D[i][1] = s1;
+    }
+    float pk0 = 0.f, pk1 = 0.f, pq0 = 0.f, pq1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int c = 32 * w + i;
+        const float d = sm.dec[c], kc = sm.kh[c], qc = sm.qh[c];
+        D[i][0] *= d;
+        D[i][1] *= d;
+        pk0 += D[i][0] * kc; pk1 += D[i][1] * kc;
+        pq0 += D[i][0] * qc; pq1 += D[i][1] * qc;
+    }
+    *reinterpret_cast<float2 *>(&sm.part[w][2 * lane][0]) = make_float2(pk0, pq0);
+    *reinterpret_cast<float2 *>(&sm.part[w][2 * lane + 1][0]) = make_float2(pk1, pq1);
+    __syncthreads();
+
+    // ---- u = b (v - D^T k) for this thread's two columns; output by wave 0 --
+    float u[2];
+    const float b = sm.scal[0];
+    const uint32_t vpair = *reinterpret_cast<const uint32_t *>(a.v + row * kV + 2 * lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int col = 2 * lane + j;
+        const float dk = sm.part[0][col][0] + sm.part[1][col][0] + sm.part[2][col][0] + sm.part[3][col][0];
+        const float vj = bf16_bits_to_f32(j == 0 ? (vpair & 0xffffu) : (vpair >> 16));
+        u[j] = b * (vj - dk);
+    }
+    if (w == 0) {
+        const float kq = sm.scal[1];
+        float o[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = 2 * lane + j;
+            const float dq = sm.part[0][col][1] + sm.part[1][col][1] + sm.part[2][col][1] + sm.part[3][col][1];
+            o[j] = a.scale * (dq + u[j] * kq);
+        }
+        *reinterpret_cast<uint32_t *>(a.out + row * kV + 2 * lane) =
+            (uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
+    }
+
+    // ---- S' = D + k u^T ----------------------------------------------------
+    if (a.ht) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int c = 32 * w + i;
+            const float kc = sm.kh[c];
+            const float s0 = D[i][0] + kc * u[0], s1 = D[i][1] + kc * u[1];
+            const int64_t idx = sbase + (int64_t)c * kV;
+            if (a.ht_bf16) {
+                *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(a.ht) + idx) =
+                    (uint32_t)f32_to_bf16_bits(s0) | ((uint32_t)f32_to_bf16_bits(s1) << 16);
+            } else {
+                *reinterpret_cast<float2 *>(reinterpret_cast<float *>(a.ht) + idx) = make_float2(s0, s1);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t kda_launch_decode(const DecodeArgs &a, hipStream_t s) {
+    const int64_t units = a.N * a.H;
+    if (units <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_decode_kernel, dim3((unsigned)units), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}

@@ -116,6 +116,31 @@ kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
                      const int64_t *cu_seqlens, void *out,
                      const kda_desc_t *desc, hipStream_t stream);
 
+/* One recurrent step per sequence -- the token-by-token form used during
+ * generation ("¿Qué es la atención Kimi Delta y por qué es importante?",
+ * 7minutos.es).  For every sequence n and head h, with S the K x V state read
+ * from initial_state (zeros when NULL) and the same in-kernel norms, sigmoid
+ * and gate as kda_fwd:
+ *
+ *   S' = (I - b k k^T) Diag(exp(a)) S + b k v^T,   out = scale * S'^T q
+ *
+ *   desc             : B = N sequences, T = 1, num_seqs = N, K = V = 128;
+ *                      workspace and phase_events are ignored.
+ *   q, k, g, v       : [N, 1, H, 128] bf16 (one token per sequence); beta [N, 1, H] bf16.
+ *   initial_state    : [N, H, K, V] of initial_state_dtype, or NULL for zeros.
+ *   final_state      : [N, H, K, V] of final_state_dtype, or NULL to skip it;
+ *                      it may alias initial_state (in-place update) when both
+ *                      dtypes match.
+ *   out              : [N, 1, H, 128] bf16.
+ * Feeding kda_fwd's final_state in as initial_state continues a prefilled
+ * sequence.  Errors as for kda_fwd (KDA_ERR_SHAPE when T != 1).  One kernel,
+ * no workspace, no allocation; enqueued on `stream`. */
+kda_status_t kda_decode(const void *q, const void *k, const void *v, const void *g,
+                        const void *beta, float scale, const float *A_log,
+                        const float *dt_bias, float lower_bound,
+                        const void *initial_state, void *final_state, void *out,
+                        const kda_desc_t *desc, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(kda_status_t status);
 

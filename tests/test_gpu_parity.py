@@ -38,6 +38,13 @@ def test_config_full(idx):
     _check(w, W.CONFIG_NAMES[idx])
 
 
+@pytest.mark.parametrize("name", W.PAGES_NAMES)
+def test_pages_workloads(name):
+    # the pages' benchmark shapes: T = 8192, H = 96 / 64, fixed length and 8 x 1024 packed
+    w = W.pages_workload(name)
+    _check(w, name)
+
+
 def test_config4_sampled_heads():
     w = W.config(4)
     _check(w, W.CONFIG_NAMES[4], heads=[0, 31])

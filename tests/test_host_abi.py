@@ -108,3 +108,37 @@ def test_python_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         kda.fwd(x, x, x, x, torch.zeros((1, 64, 2), dtype=torch.bfloat16), 0.1, None,
                 torch.zeros(2), torch.zeros(2, 128), -5.0)
+
+
+def _call_decode(lib, d, lb=-5.0, scale=0.1, null=(), align=None, h0=None, ht=None):
+    ptrs = {n: ctypes.c_void_p(FAKE) for n in ("q", "k", "v", "g", "beta", "A_log", "dt_bias", "out")}
+    for n in null:
+        ptrs[n] = None
+    if align:
+        ptrs[align] = ctypes.c_void_p(FAKE + 2)
+    return lib.kda_decode(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["g"], ptrs["beta"], scale, ptrs["A_log"],
+                          ptrs["dt_bias"], lb, h0, ht, ptrs["out"], ctypes.byref(d), None)
+
+
+def test_decode_validation_errors(lib):
+    one = dict(T=1, B=3, num_seqs=3)
+    assert _call_decode(lib, _desc(**dict(one, T=2))) == 2          # one token per sequence
+    assert _call_decode(lib, _desc(**dict(one, num_seqs=2))) == 2
+    assert _call_decode(lib, _desc(**dict(one, B=0, num_seqs=0))) == 2
+    assert _call_decode(lib, _desc(**dict(one, K=64))) == 3
+    assert _call_decode(lib, _desc(**one), lb=-6.0) == 4
+    assert _call_decode(lib, _desc(**one), scale=float("nan")) == 4
+    for n in ("q", "k", "v", "g", "beta", "out", "A_log", "dt_bias"):
+        assert _call_decode(lib, _desc(**one), null=(n,)) == 1, n
+    for n in ("q", "k", "v", "g", "out", "dt_bias"):
+        assert _call_decode(lib, _desc(**one), align=n) == 6, n
+    assert _call_decode(lib, _desc(**dict(one, initial_state_dtype=9)), h0=ctypes.c_void_p(FAKE)) == 5
+    assert _call_decode(lib, _desc(**one), ht=ctypes.c_void_p(FAKE + 4)) == 6
+
+
+def test_python_decode_rejects_bad_shapes():
+    import torch
+    x = torch.zeros((2, 2, 3, 128), dtype=torch.bfloat16)   # two tokens: not a decode step
+    with pytest.raises(ValueError):
+        kda.decode(x, x, x, x, torch.zeros((2, 2, 3), dtype=torch.bfloat16), 0.1, None,
+                   torch.zeros(3), torch.zeros(3, 128), -5.0)

@@ -174,6 +174,31 @@ def config(i: int) -> Workload:
     raise ValueError("config index must be 0..4")
 
 
+# The pages' own benchmark shapes: T = 8192 tokens, head dim 128, H = 96 and
+# H = 64, as one fixed-length sequence and as eight packed sequences of 1024
+# tokens (the uniform-varlen scenario).  The pages do not state the initial
+# state, lower bound or gate statistics of these runs; the recipe of the
+# T = 8192 workload above is reused (no initial state, lower_bound = -5,
+# fp32 final state).
+PAGES_NAMES = ["pages_H96_fixed8192", "pages_H96_varlen1024x8", "pages_H64_fixed8192", "pages_H64_varlen1024x8"]
+
+
+def pages_workload(name: str) -> Workload:
+    i = PAGES_NAMES.index(name)
+    H = 96 if i < 2 else 64
+    seed = 2000 + i
+    if i % 2 == 0:
+        return make(name, 1, 8192, H, seed, lower_bound=-5.0, init=None, final="fp32")
+    return make(name, 1, 8192, H, seed, lower_bound=-5.0, init=None, final="fp32", seqlens=[1024] * 8)
+
+
+def by_name(name: str) -> Workload:
+    """Any workload by name: CONFIG_NAMES or PAGES_NAMES."""
+    if name in CONFIG_NAMES:
+        return config(CONFIG_NAMES.index(name))
+    return pages_workload(name)
+
+
 def config_shape(i: int) -> dict:
     """Shapes of a workload without drawing it."""
     shapes = {0: (1, 512, 4), 1: (4, 2048, 32), 2: (1, 8192, 32), 3: (1, 32768, 32), 4: (1, 131072, 32)}
