@@ -28,18 +28,46 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into gated_delta_rule_110_amd/libkda.so (always rebuilds)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE] + srcs + ["-o", tmp]
+# Per-source additions.  The state chain keeps its MFMA accumulators in
+# ordinary VGPRs: the state update multiplies them by the decay every chunk, and
+# accumulator-register copies around that multiply would sit on the serial path.
+EXTRA_FLAGS = {"kda_chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into gated_delta_rule_110_amd/libkda.so (always rebuilds)."""
+    tag = "%d" % os.getpid()
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(CSRC, src.replace(".hip", ".o%s" % tag))
+        cmd = ([hipcc()] + [f for f in HIPCC_FLAGS if f != "-shared"] + EXTRA_FLAGS.get(src, [])
+               + ["-c", "-I", INCLUDE, os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+        procs.append(_run(cmd, verbose))
     # the host pass warns that it does not know the packed-fp32 feature: harmless
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
-    if res.returncode != 0:
+    msgs, ok = [], True
+    for p in procs:
+        out = p.communicate()[0]
+        msgs += [ln for ln in out.splitlines() if noise not in ln]
+        ok = ok and p.returncode == 0
+    tmp = LIB + ".tmp" + tag
+    try:
+        if ok:
+            link = _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+            msgs += [ln for ln in link.communicate()[0].splitlines() if noise not in ln]
+            ok = link.returncode == 0
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+    if not ok:
         if os.path.exists(tmp):
             os.remove(tmp)
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
