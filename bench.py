@@ -93,11 +93,11 @@ def cpu_baseline(w, target_s: float = 10.0):
 
 
 def source_digest() -> str:
-    """sha256 over the HIP sources and headers the library is built from."""
+    """sha256 over the HIP sources, headers and build flags the library is built from."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_110_amd", "csrc")
-    for name in sorted(os.listdir(csrc)) + ["../../include/kda.h"]:
+    for name in sorted(os.listdir(csrc)) + ["../../include/kda.h", "../_build.py"]:
         path = os.path.normpath(os.path.join(csrc, name))
         if os.path.isfile(path):
             h.update(name.encode())
