@@ -141,6 +141,15 @@ __device__ __forceinline__ float dpp_row_shr(float x, float fill, int s) {
         default: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), 0x118, 0xf, 0xf, false));
     }
 }
+__device__ __forceinline__ float dpp_row_shr_zero(float x, int s) {
+    // lanes whose source lies before the row start read 0 (bound_ctrl)
+    switch (s) {
+        case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+        case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+        case 4: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
+    }
+}
 __device__ __forceinline__ float dpp_row_bcast15(float x) {
     // every lane of a 16-lane row receives the row's lane 15
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xf, 0xf, false));

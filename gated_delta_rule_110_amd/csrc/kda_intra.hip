@@ -198,15 +198,19 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
             for (int e = 0; e < 8; ++e) {
                 const float t = __builtin_amdgcn_exp2f((gf[e] + db[e]) * kLog2e);
                 const float l2 = fmaxf(lb2, nA * __builtin_amdgcn_logf(1.0f + t));
-                P[8 * kk + e] = valid ? __builtin_amdgcn_exp2f(l2) : 1.0f;
+                P[8 * kk + e] = valid ? l2 : 0.0f;  // log2 of the decay
             }
         }
     }
+    // inclusive prefix sums of the log2 decays over the block's rows (one DPP
+    // row = 16 lanes = the block), then P = 2^sum; one DPP add per step
 #pragma unroll
     for (int s = 1; s < 16; s <<= 1) {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) P[e] *= dpp_row_shr(P[e], 1.0f, s);
+        for (int e = 0; e < 32; ++e) P[e] += dpp_row_shr_zero(P[e], s);
     }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) P[e] = __builtin_amdgcn_exp2f(P[e]);
     // L2 norms (rows past the end are zeroed: no key, no query, b = 0)
     if (!valid) {
 #pragma unroll
