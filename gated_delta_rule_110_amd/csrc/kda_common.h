@@ -68,6 +68,7 @@ struct IntraArgs {
     int64_t T, H, N, nc_fixed;
     _Float16 *Wf, *Qf, *Kf, *Af, *Uf;
     float *gn;
+    int heads_fast;             // grid (H, slots) rather than (slots, H); set by the launcher
 };
 
 struct ChainArgs {

@@ -125,8 +125,11 @@ __device__ __forceinline__ void offdiag_column(IntraSmem &sm, int r16, int cg) {
 __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     __shared__ IntraSmem sm;
 
-    const int64_t slot = blockIdx.x;
-    const int64_t h = blockIdx.y;
+    // Heads fastest where the grid allows (gridDim.y <= 65535 chunk slots): the
+    // workgroups in flight together then cover whole token rows, and the chain
+    // kernel that runs next reads the intermediates measurably faster.
+    const int64_t slot = a.heads_fast ? blockIdx.y : blockIdx.x;
+    const int64_t h = a.heads_fast ? blockIdx.x : blockIdx.y;
     const int64_t H = a.H;
 
     // ---- which tokens this chunk covers -----------------------------------
@@ -493,7 +496,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
 
 hipError_t kda_launch_intra(const IntraArgs &a, int64_t slots, hipStream_t s) {
     if (slots <= 0) return hipSuccess;
-    dim3 grid((unsigned)slots, (unsigned)a.H);
-    hipLaunchKernelGGL(kda_intra_kernel, grid, dim3(kThreads), 0, s, a);
+    IntraArgs b = a;
+    b.heads_fast = slots <= 65535 && a.H <= 65535;
+    const dim3 grid = b.heads_fast ? dim3((unsigned)a.H, (unsigned)slots) : dim3((unsigned)slots, (unsigned)a.H);
+    hipLaunchKernelGGL(kda_intra_kernel, grid, dim3(kThreads), 0, s, b);
     return hipGetLastError();
 }
