@@ -10,30 +10,35 @@
 //   S   <- Diag(exp(G_n)) S + Kbar^T Ut_c  (state leaving the chunk)
 //
 // The state's V columns evolve independently, so each workgroup owns one
-// (sequence, head, 16-column V block), with three waves:
+// (sequence, head, 16-column V block), with four waves:
 //
 //   wave 0 (chain)  keeps the 128 x 16 fp32 state slice in eight MFMA
 //                   accumulator tiles.  The intermediates are stored in
 //                   fragment order with a k permutation matching the
 //                   accumulator layout, so two accumulator tiles converted to
 //                   fp16 are directly the B operand of the next product -- no
-//                   LDS round trip sits on the serial path.  It reads W and
-//                   Kbar^T from an LDS ring and loads only U and exp(G_n)
-//                   itself.
+//                   LDS round trip sits on the serial path.  It reads -W,
+//                   Kbar^T, its U block and exp(G_n) from a four-slot LDS ring.
 //   wave 1 (output) computes O from the fp16 state and pseudo-value fragments
 //                   the chain wave hands over through a double-buffered LDS
-//                   slot, with Qg and A_qk prefetched three chunks ahead in
+//                   slot, with Qg and A_qk loaded three chunks ahead into
 //                   registers.
-//   wave 2 (loader) streams W and Kbar^T into a three-slot LDS ring (global
-//                   loads issued three chunks ahead) and loads this
-//                   workgroup's share of the head's operands eight chunks ahead
-//                   into the XCD's L2.
+//   wave 2 (loader) copies each chunk's ring operands straight from global
+//                   memory into the ring (global_load_lds, no registers), two
+//                   chunks ahead of the chain.
+//   wave 3 (L2)     loads this workgroup's share of the head's cache lines
+//                   kAhead chunks ahead of the chain into the XCD's L2.
 //
 // One barrier per chunk orders the LDS hand-overs.  Vector-memory loads
 // complete in order within a wave, so each wave only waits for loads that are
 // older than the ones it issues for later chunks, and every prefetch is
 // unconditional (past the end the last chunk is reloaded) so that the
 // compiler's wait counts never cover a path without it.
+//
+// What bounds a chunk step is the CU's vector-memory path: each workgroup
+// moves about 61 KiB per chunk through it (every V block needs the head's
+// whole W, Kbar, Qg and A_qk), which takes about 1.2 us at the rate one CU
+// sustains, longer than the chain wave's own arithmetic.
 //
 // The eight V-block workgroups of a head are placed on one XCD (same
 // blockIdx % 8), so the head's per-chunk operands come from HBM once into that
