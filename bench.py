@@ -37,9 +37,11 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA, vendor figure
 F_ALG = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
 BYTES_ALG = 4 * 256 + 2 + 256
 # Interface bytes per token-head of each kernel, reading its inputs and writing
-# its outputs once (the chunk intermediates are 72.5 KiB per 64-token chunk
-# and head = 1160 B per token-head):
-INTER_BYTES = (4 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4) / 64.0
+# its outputs once.  The chunk intermediates are W, Qg, Kbar^T, U (64 x 128
+# fp16 each), the 6 of 8 A_qk fragments that are not identically zero (rows
+# 0..31 have no entries in columns 32..63) and exp(G_n) (128 fp32): 70.5 KiB per
+# 64-token chunk and head = 1128 B per token-head.
+INTER_BYTES = (4 * 64 * 128 * 2 + 6 * 1024 + 128 * 4) / 64.0
 KERNEL_BYTES = {
     "kda_intra_kernel": 4 * 256 + 2 + INTER_BYTES,
     "kda_chain_kernel": INTER_BYTES + 256,

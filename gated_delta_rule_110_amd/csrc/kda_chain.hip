@@ -73,7 +73,7 @@ struct __align__(16) ChainSmem {
 
 struct OutOps {        // the output wave's operands for one chunk
     h8 Q[4][4];        // Qg  [row tile][k-block]
-    h8 A[4][2];        // A_qk [row tile][k-block]
+    h8 A[4][2];        // A_qk [row tile][k-block]; [0][1] and [1][1] are zero and never loaded
 };
 
 __device__ __forceinline__ int64_t clamp_chunk(int64_t s, int64_t last) { return s < last ? s : last; }
@@ -88,7 +88,8 @@ __device__ __forceinline__ void load_out_ops(OutOps &o, const ChainArgs &a, int6
 #pragma unroll
     for (int it = 0; it < 4; ++it)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) o.A[it][kb] = A[(it * 2 + kb) * 64];
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb == 0 || it >= 2) o.A[it][kb] = A[(it * 2 + kb) * 64];  // A_qk[i][j] = 0 for j > i
 }
 
 // Copy one chunk's -W and Kbar^T fragments (32 KiB), this workgroup's U block
@@ -219,7 +220,8 @@ __device__ __forceinline__ void out_step(ChainSmem &sm, const OutOps &op, int sl
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int it = 0; it < 4; ++it) O[it] = mfma16x16x32_f16(Ub[kb], op.A[it][kb], O[it]);
+        for (int it = 0; it < 4; ++it)
+            if (kb == 0 || it >= 2) O[it] = mfma16x16x32_f16(Ub[kb], op.A[it][kb], O[it]);
     // lane (r, g) holds O[16 it + r][16 vb + 4 g + e]
     const int r = lane & 15;
 #pragma unroll

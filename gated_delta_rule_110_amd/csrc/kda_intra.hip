@@ -406,7 +406,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
         _Float16 *Af = a.Af + ws * kAfElems;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-            *reinterpret_cast<h8 *>(Af + ((w * 2 + kb) * 64 + lane) * 8) = to_h8(dq[2 * kb], dq[2 * kb + 1]);
+            if (kb == 0 || w >= 2)  // rows 0..31 have no A_qk entries in columns 32..63 (never read)
+                *reinterpret_cast<h8 *>(Af + ((w * 2 + kb) * 64 + lane) * 8) = to_h8(dq[2 * kb], dq[2 * kb + 1]);
     }
     lds_barrier();  // B2: L complete; the decayed key rows are no longer read
 

@@ -26,16 +26,18 @@ def test_algorithmic_constants():
     assert bench.F_ALG == 139264
     # q, k, v, g in (bf16, 128 each), beta in (bf16), out (bf16, 128)
     assert bench.BYTES_ALG == 1282
-    # W, Qg, Kbar^T, U (64 x 128 fp16 each), A_qk (64 x 64 fp16), exp(G_n) (128 fp32) per chunk-head
-    assert bench.INTER_BYTES * 64 == 72.5 * 1024
+    # W, Qg, Kbar^T, U (64 x 128 fp16 each), the nonzero 3/4 of A_qk (64 x 64 fp16), exp(G_n)
+    # (128 fp32) per chunk-head
+    assert bench.INTER_BYTES * 64 == 70.5 * 1024
 
 
 def test_intermediates_match_the_library_workspace():
     kda = pytest.importorskip("gated_delta_rule_110_amd")
     sizes = [kda.workspace_size(1, 64 * chunks, 3) for chunks in (1, 2)]
-    # one more chunk of three heads adds three chunk-heads of intermediates (plus alignment)
+    # one more chunk of three heads adds three chunk-heads of intermediates: the workspace keeps
+    # room for all 8 A_qk fragments (2 KiB more than is ever written or read), plus alignment
     per = (sizes[1] - sizes[0]) / 3
-    assert bench.INTER_BYTES * 64 <= per <= bench.INTER_BYTES * 64 + 1024
+    assert bench.INTER_BYTES * 64 + 2048 <= per <= bench.INTER_BYTES * 64 + 2048 + 1024
 
 
 def _write_counter_csv(folder, rows):
