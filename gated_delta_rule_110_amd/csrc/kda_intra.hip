@@ -425,19 +425,24 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
         }
     // ---- P2: invert the diagonal 16x16 blocks of (I + A_kk) -----------------
     if (cg == 0) {
-        // lane r16 = column j of T_ww; left-looking forward substitution in fp32
+        // lane r16 = column j of T_ww: forward substitution in fp32.  The strict
+        // lower triangle of the block (120 values) is read first, then the
+        // substitution runs column by column (x[c] is final when column c is
+        // applied), so only one multiply-add per column is on the serial path.
         const int j = r16;
+        const float *Lw = sm.L + (16 * w) * kLP + 16 * w;
+        float Lt[120];  // L[r][c], c < r, row r at offset r (r - 1) / 2
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+#pragma unroll
+            for (int c = 0; c < r; ++c) Lt[r * (r - 1) / 2 + c] = Lw[r * kLP + c];
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
-        const float *Lw = sm.L + (16 * w) * kLP + 16 * w;
 #pragma unroll
-        for (int r = 1; r < 16; ++r) {
-            float acc = x[r];
+        for (int c = 0; c < 15; ++c)
 #pragma unroll
-            for (int kq = 0; kq < r; ++kq) acc -= Lw[r * kLP + kq] * x[kq];
-            x[r] = acc;
-        }
+            for (int r = c + 1; r < 16; ++r) x[r] -= Lt[r * (r - 1) / 2 + c] * x[c];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             sm.L[(16 * w + r) * kLP + 16 * w + j] = x[r];
