@@ -57,6 +57,16 @@ def test_ragged_varlen(lens):
     _check(w, "ragged%s" % lens)
 
 
+def test_many_short_sequences():
+    # more sequences than one workgroup of the chunk-table scan covers (1024), with empty ones:
+    # the scan's carry across blocks, and thousands of (sequence, head) chains
+    rng = np.random.Generator(np.random.PCG64(4242))
+    lens = [int(x) for x in rng.integers(0, 41, size=1100)]
+    lens[0] = lens[500] = lens[1024] = lens[-1] = 0
+    w = W.make("many", 1, sum(lens), 2, 4243, lower_bound=-4.0, init="fp32", final="fp32", seqlens=lens)
+    _check(w, "many%d" % len(lens))
+
+
 @pytest.mark.parametrize("T", [1, 63, 65, 200])
 def test_fixed_ragged_tail(T):
     w = W.make("tail", 2, T, 3, 3000 + T, init="bf16", final="fp32")
