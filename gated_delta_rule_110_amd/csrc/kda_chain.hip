@@ -55,9 +55,9 @@ namespace {
 
 constexpr int kThreads = 256;        // wave 0: state chain, 1: outputs, 2: LDS loader, 3: L2 prefetch
 #ifndef KDA_CHAIN_AHEAD
-#define KDA_CHAIN_AHEAD 8
+#define KDA_CHAIN_AHEAD 3
 #endif
-constexpr int kAhead = KDA_CHAIN_AHEAD;  // chunks the L2 prefetch runs ahead of the chain
+constexpr int kAhead = KDA_CHAIN_AHEAD;  // chunks the L2 prefetch runs ahead of the chain (measured: 3 beats 2 and 4-16)
 constexpr int kRing = 8;                 // chunks between an L2 prefetch load and its use (multiple of 4)
 constexpr int kVB = 16;                  // value columns per workgroup
 constexpr int kNVB = kV / kVB;           // workgroups per (sequence, head)
