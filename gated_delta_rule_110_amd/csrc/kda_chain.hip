@@ -58,7 +58,7 @@ constexpr int kThreads = 256;        // wave 0: state chain, 1: outputs, 2: LDS 
 #define KDA_CHAIN_AHEAD 3
 #endif
 constexpr int kAhead = KDA_CHAIN_AHEAD;  // chunks the L2 prefetch runs ahead of the chain (measured: 3 beats 2 and 4-16)
-constexpr int kRing = 8;                 // chunks between an L2 prefetch load and its use (multiple of 4)
+constexpr int kTouchInFlight = 8;        // L2 prefetch copies allowed in flight (two per chunk)
 constexpr int kVB = 16;                  // value columns per workgroup
 constexpr int kNVB = kV / kVB;           // workgroups per (sequence, head)
 constexpr int kSlots = 4;                // LDS ring slots for -W / Kbar^T
@@ -69,6 +69,7 @@ struct __align__(16) ChainSmem {
     h8 ring[kSlots][35][64];
     h8 sS[2][4][64];           // state as fp16 B fragments [slot][k-block][lane]
     h8 sU[2][2][64];           // pseudo-values as fp16 B fragments
+    uint32_t dump[2][64];      // landing place of the L2 prefetch copies (never read)
 };
 
 struct OutOps {        // the output wave's operands for one chunk
@@ -123,11 +124,10 @@ __device__ __forceinline__ void dma_ring(ChainSmem &sm, const ChainArgs &a, int6
 // Load this workgroup's share of one chunk's operands so that they are in the
 // XCD's L2 when the other waves load them a few chunks later.  The eight
 // V-block workgroups of a head split the head's cache lines (one dword per
-// 128-byte line).  The values are consumed kRing chunks later (folded into a
-// checksum that is only stored through a null sink pointer), so the compiler
-// tracks these loads and waits for each long after issuing it.
-__device__ __forceinline__ void touch_lines(const ChainArgs &a, int64_t ws, int vb, int lane, uint32_t &t0,
-                                            uint32_t &t1) {
+// 128-byte line).  The loads copy into an LDS area nobody reads: no
+// destination registers, so this wave never has to wait for one except to
+// bound how many are in flight.
+__device__ __forceinline__ void touch_lines(ChainSmem &sm, const ChainArgs &a, int64_t ws, int vb, int lane) {
     const char *wf = reinterpret_cast<const char *>(a.Wf + ws * kWfElems);
     const char *qf = reinterpret_cast<const char *>(a.Qf + ws * kQfElems);
     const char *kf = reinterpret_cast<const char *>(a.Kf + ws * kKfElems);
@@ -143,8 +143,8 @@ __device__ __forceinline__ void touch_lines(const ChainArgs &a, int64_t ws, int 
     const char *p1;  // lines 64..72: A_qk and exp(G_n) (lanes >= 8 share one line)
     if (l < 8) p1 = af + (8 * vb + l) * 128;
     else p1 = gn + (vb & 3) * 128;
-    t0 = *reinterpret_cast<const uint32_t *>(p0);
-    t1 = *reinterpret_cast<const uint32_t *>(p1);
+    lds_copy4(p0, lds_addr(&sm.dump[0][0]));
+    lds_copy4(p1, lds_addr(&sm.dump[1][0]));
 }
 
 // Two accumulator tiles (rows 4g+e of tile 2p and of tile 2p+1) -> one fp16 B
@@ -352,27 +352,18 @@ __global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
         // chain step u - kAhead + 1 and end at that step's barrier (after the
         // prologue barrier the other waves pass first).
         if (nchunks > 0) {
-            uint32_t acc = 0, r0[kRing], r1[kRing];
-#pragma unroll
-            for (int j = 0; j < kRing; ++j) { r0[j] = 0u; r1[j] = 0u; }
             const int64_t nu = nchunks + kAhead - 1;
             bool prologue_done = false;
-            for (int64_t ub = 0; ub < nu; ub += kRing) {
-#pragma unroll
-                for (int j = 0; j < kRing; ++j) {
-                    const int64_t u = ub + j;
-                    acc ^= r0[j] ^ r1[j];
-                    touch_lines(a, wsof(u + 1), vb, lane, r0[j], r1[j]);
-                    if (u >= kAhead - 1 && u < nu) {
-                        if (!prologue_done) { lds_barrier(); prologue_done = true; }
-                        lds_barrier();
-                    }
+            for (int64_t u = 0; u < nu; ++u) {
+                touch_lines(sm, a, wsof(u + 1), vb, lane);
+                asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTouchInFlight) : "memory");
+                if (u >= kAhead - 1) {
+                    if (!prologue_done) { lds_barrier(); prologue_done = true; }
+                    lds_barrier();
                 }
             }
             if (!prologue_done) lds_barrier();
-#pragma unroll
-            for (int j = 0; j < kRing; ++j) acc ^= r0[j] ^ r1[j];
-            if (a.sink) a.sink[lane] = acc;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
     }
 }

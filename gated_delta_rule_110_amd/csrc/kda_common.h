@@ -82,7 +82,6 @@ struct ChainArgs {
     void *ht;            // final state [N,H,K,V] or nullptr
     int h0_bf16, ht_bf16;
     uint16_t *out;       // [B,T,H,V] bf16
-    uint32_t *sink;      // always nullptr: keeps the prefetch loads observable
 };
 
 struct DecodeArgs {
@@ -175,6 +174,22 @@ __device__ __forceinline__ f4 mfma16x16x16_f16(const h4 &a, const h4 &b, const f
 }
 
 // Resolve packed sequence index of a chunk slot: largest n with off[n] <= slot.
+// LDS byte address of a __shared__ object (what M0 and the ds_* instructions take).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)(p);
+}
+
+// Each lane copies 4 bytes from global memory at p to LDS at lds + 4 * lane
+// (global_load_lds; M0 holds the LDS base, and the s_nop is the wait state an
+// M0 write needs before such a copy).  Used to pull cache lines into L2 ahead
+// of their use: the copy has no destination register, and it is issued
+// through inline asm, so the compiler neither waits for it nor makes later
+// LDS accesses wait for it.  Only this wave's younger loads complete after it
+// (vector-memory loads complete in order).
+__device__ __forceinline__ void lds_copy4(const void *p, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(p), "{m0}"(lds) : "memory");
+}
+
 __device__ __forceinline__ int64_t seq_of_slot(const int32_t *off, int64_t N, int64_t slot) {
     int64_t lo = 0, hi = N;  // invariant: off[lo] <= slot < off[hi] (off[N] > slot)
     while (hi - lo > 1) {
