@@ -58,7 +58,8 @@ constexpr int kThreads = 256;        // wave 0: state chain, 1: outputs, 2: LDS 
 #define KDA_CHAIN_AHEAD 3
 #endif
 constexpr int kAhead = KDA_CHAIN_AHEAD;  // chunks the L2 prefetch runs ahead of the chain (measured: 3 beats 2 and 4-16)
-constexpr int kTouchInFlight = 8;        // L2 prefetch copies allowed in flight (two per chunk)
+constexpr int kTouchInFlight = 32;       // L2 prefetch copies allowed in flight (two per chunk): a
+                                         // tighter bound stalls this wave, and the barrier, on HBM latency
 constexpr int kVB = 16;                  // value columns per workgroup
 constexpr int kNVB = kV / kVB;           // workgroups per (sequence, head)
 constexpr int kSlots = 4;                // LDS ring slots for -W / Kbar^T
