@@ -21,8 +21,8 @@
 //                   Kbar^T, its U block and exp(G_n) from a four-slot LDS ring.
 //   wave 1 (output) computes O from the fp16 state and pseudo-value fragments
 //                   the chain wave hands over through a double-buffered LDS
-//                   slot, with Qg and A_qk loaded three chunks ahead into
-//                   registers.
+//                   slot, loading the chunk's Qg and A_qk into registers just
+//                   before the barrier that hands the fragments over.
 //   wave 2 (loader) copies each chunk's ring operands straight from global
 //                   memory into the ring (global_load_lds, no registers), two
 //                   chunks ahead of the chain.
@@ -305,21 +305,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
             const int64_t row_stride = H * kV;
             uint16_t *out0 = a.out + (tseq * H + h) * kV + kVB * vb + 4 * g;
             auto out_at = [&](int64_t s) { return out0 + kChunk * s * row_stride; };
-            OutOps A, B, C;
-            load_out_ops(A, a, wsof(0), lane);
-            load_out_ops(B, a, wsof(1), lane);
+            // Qg and A_qk of a chunk are loaded just before the barrier that
+            // hands over its fragments: the per-CU load path is the bottleneck, and
+            // deeper register prefetch (two or three chunks ahead) only adds
+            // loads in flight (measured equal or slower)
+            OutOps A;
             lds_barrier();
-            for (int64_t s = 0; s < nchunks; s += 3) {
-                load_out_ops(C, a, wsof(s + 2), lane);
+            for (int64_t s = 0; s < nchunks; ++s) {
+                load_out_ops(A, a, wsof(s), lane);
                 out_step(sm, A, (int)(s & 1), lane, a.scale, out_at(s), row_stride, seqlen - kChunk * s);
-                if (s + 1 >= nchunks) break;
-                load_out_ops(A, a, wsof(s + 3), lane);
-                out_step(sm, B, (int)((s + 1) & 1), lane, a.scale, out_at(s + 1), row_stride,
-                         seqlen - kChunk * (s + 1));
-                if (s + 2 >= nchunks) break;
-                load_out_ops(B, a, wsof(s + 4), lane);
-                out_step(sm, C, (int)((s + 2) & 1), lane, a.scale, out_at(s + 2), row_stride,
-                         seqlen - kChunk * (s + 2));
             }
         }
     } else if (wave == 2) {
