@@ -162,13 +162,20 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     const int64_t ws = slot * H + h;  // workspace index of this (chunk, head)
 
     // ---- P0: load, normalise, gate, block-local decay products ------------
-    // Loads are issued g first (rows past the end reload the last row, zeroed
-    // below): they complete in order, so the gate math starts as soon as g
-    // arrives while q, k, v are still in flight.
+    // Loads are issued dt_bias and g first (rows past the end reload the last
+    // row, zeroed below): they complete in order, so the gate math starts as
+    // soon as these arrive while q, k, v are still in flight.
     uint4 graw[4], kraw[4], qraw[4], vraw[4];
+    float4 dtb4[8];  // dt_bias[h][32 kk + 8 cg + 0..7] as two float4 per kk
     float bl;
     {
         const int64_t base = ((t0 + (valid ? row : L - 1)) * H + h) * kK;
+        const float *dtb = a.dt_bias + h * kK;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            dtb4[2 * kk] = *reinterpret_cast<const float4 *>(dtb + 32 * kk + 8 * cg);
+            dtb4[2 * kk + 1] = *reinterpret_cast<const float4 *>(dtb + 32 * kk + 8 * cg + 4);
+        }
         bl = bf16_bits_to_f32(a.beta[(t0 + (valid ? row : L - 1)) * H + h]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) graw[kk] = *reinterpret_cast<const uint4 *>(a.g + base + 32 * kk + 8 * cg);
@@ -179,6 +186,10 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
         for (int kk = 0; kk < 4; ++kk) qraw[kk] = *reinterpret_cast<const uint4 *>(a.q + base + 32 * kk + 8 * cg);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) vraw[kk] = *reinterpret_cast<const uint4 *>(a.v + base + 32 * kk + 8 * cg);
+        // every load is issued before any of them is used: otherwise the
+        // scheduler starts unpacking g early, and the register reuse that
+        // follows makes the k, q, v loads wait for the first g load to land
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // gate in base 2: log2 d = max(lb log2e, -exp(A_log) log2(1 + 2^(x log2e))), x = g + dt_bias,
@@ -188,12 +199,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     {
         const float nA = -fast_exp(a.A_log[h]);
         const float lb2 = a.lower_bound * kLog2e;
-        const float *dtb = a.dt_bias + h * kK;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const int c0 = 32 * kk + 8 * cg;
-            const float4 d0 = *reinterpret_cast<const float4 *>(dtb + c0);
-            const float4 d1 = *reinterpret_cast<const float4 *>(dtb + c0 + 4);
+            const float4 d0 = dtb4[2 * kk], d1 = dtb4[2 * kk + 1];
             const float db[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
             float gf[8];
             unpack_bf16x8(graw[kk], gf);
