@@ -417,21 +417,10 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
             if (kb == 0 || w >= 2)  // rows 0..31 have no A_qk entries in columns 32..63 (never read)
                 *reinterpret_cast<h8 *>(Af + ((w * 2 + kb) * 64 + lane) * 8) = to_h8(dq[2 * kb], dq[2 * kb + 1]);
     }
-    lds_barrier();  // B2: L complete; the decayed key rows are no longer read
-
-    // ---- P1b: transposed operands of the W / U products into LDS ----------
-    //   kg[32 kk + 16 half + r][16 w + 4 g + e] = (b gamma khat)[16 w + 4 g + e][32 kk + 16 half + r]
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int ch = 32 * kk + 16 * hf + r16;
-            const f4 dk = mfma16x16x32_f16(kgF[kk], sel[hf], f4{0, 0, 0, 0});
-            *reinterpret_cast<h4 *>(&sm.u.t.kg[ch * kTP + 16 * w + 4 * cg]) = to_h4(dk);
-            const f4 dv = mfma16x16x32_f16(vbF[kk], sel[hf], f4{0, 0, 0, 0});
-            *reinterpret_cast<h4 *>(&sm.u.t.vb[ch * kTP + 16 * w + 4 * cg]) = to_h4(dv);
-        }
     // ---- P2: invert the diagonal 16x16 blocks of (I + A_kk) -----------------
+    // Each wave inverts its own block from the rows it has just written (one
+    // wave's LDS accesses execute in order), so this needs no barrier and fills
+    // the time the waves with fewer Gram tiles would spend waiting at B2.
     if (cg == 0) {
         // lane r16 = column j of T_ww: forward substitution in fp32.  The strict
         // lower triangle of the block (120 values) is read first, then the
@@ -461,7 +450,20 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
 #pragma unroll
     for (int jb = 1; jb < 4; ++jb)
         if (jb > w) *reinterpret_cast<h4 *>(&sm.Th[row * kTP + 16 * jb + 4 * cg]) = h4{0, 0, 0, 0};
-    lds_barrier();  // B3: diagonal blocks of T, kg, vb complete
+    lds_barrier();  // B2: L and the diagonal blocks of T complete; the decayed key rows are no longer read
+
+    // ---- P1b: transposed operands of the W / U products into LDS ----------
+    //   kg[32 kk + 16 half + r][16 w + 4 g + e] = (b gamma khat)[16 w + 4 g + e][32 kk + 16 half + r]
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int ch = 32 * kk + 16 * hf + r16;
+            const f4 dk = mfma16x16x32_f16(kgF[kk], sel[hf], f4{0, 0, 0, 0});
+            *reinterpret_cast<h4 *>(&sm.u.t.kg[ch * kTP + 16 * w + 4 * cg]) = to_h4(dk);
+            const f4 dv = mfma16x16x32_f16(vbF[kk], sel[hf], f4{0, 0, 0, 0});
+            *reinterpret_cast<h4 *>(&sm.u.t.vb[ch * kTP + 16 * w + 4 * cg]) = to_h4(dv);
+        }
 
     // ---- P3: off-diagonal blocks of T, one column block per wave ----------
     switch (w) {
