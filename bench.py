@@ -45,7 +45,13 @@ INTER_BYTES = (4 * 64 * 128 * 2 + 6 * 1024 + 128 * 4) / 64.0
 KERNEL_BYTES = {
     "kda_intra_kernel": 4 * 256 + 2 + INTER_BYTES,
     "kda_chain_kernel": INTER_BYTES + 256,
+    # split chains (the map pass, the scan over segments and the chain with outputs, timed
+    # together): the intermediates are read twice, once per chain pass
+    "split_chain": 2 * INTER_BYTES + 256,
 }
+# Split chains also move, per (batch row, segment, head), the two fp32 maps (written by the
+# map pass, read by the scan) and the entering state (written by the scan, read by the chain).
+SPLIT_BYTES_PER_SEGMENT_HEAD = 2 * (2 * 128 * 128 * 4) + 2 * (128 * 128 * 4)
 
 
 def state_bytes(w) -> int:
@@ -213,7 +219,10 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="2",
                     help="workload index 0..4 (default 2: T=8192, H=32) or a name from workloads.PAGES_NAMES "
-                         "(the pages' H=96 / H=64 shapes)")
+                         "(the pages' H=96 / H=64 shapes) or workloads.SPLIT_NAMES (one long sequence, few heads)")
+    ap.add_argument("--chain-segments", type=int, default=0, metavar="N",
+                    help="split each state chain into N segments (0: the library's automatic choice, "
+                         "1: never; batches without cu_seqlens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="time the single-token recurrent step (kda_decode) for N sequences of the "
@@ -258,7 +267,8 @@ def main(argv=None) -> int:
     final = None
     if w.final_state_dtype is not None:
         final = torch.empty((w.N, w.H, w.K, w.V), dtype=w.final_state_dtype, device=dev)
-    nbytes = kda.workspace_size(w.B, w.T, w.H, num_seqs=w.N)
+    segs = 1 if w.cu_seqlens is not None else kda.chain_segments_for(w.B, w.T, w.H, args.chain_segments)
+    nbytes = kda.workspace_size(w.B, w.T, w.H, num_seqs=w.N, chain_segments=args.chain_segments)
     workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
     # 4 phase events per timed step (created by a first record)
@@ -276,7 +286,8 @@ def main(argv=None) -> int:
     def step(ev=None):
         kda.fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, out, w.A_log, w.dt_bias, w.lower_bound,
                 w.initial_state, final, w.cu_seqlens, workspace=workspace,
-                phase_events=None if ev is None else ctypes.cast(ev, ctypes.c_void_p))
+                phase_events=None if ev is None else ctypes.cast(ev, ctypes.c_void_p),
+                chain_segments=args.chain_segments)
 
     for _ in range(args.warmup):
         step()
@@ -303,9 +314,14 @@ def main(argv=None) -> int:
     path_bytes = BYTES_ALG * tok_heads + state_bytes(w)
     gbs = path_bytes / (ms / 1e3) / 1e9
 
-    kernels = {"kda_intra_kernel": intra_ms, "kda_chain_kernel": chain_ms}
+    chain_key = "split_chain" if segs > 1 else "kda_chain_kernel"
+    kernels = {"kda_intra_kernel": intra_ms, chain_key: chain_ms}
     dom = max(kernels, key=kernels.get)
-    dom_bytes = KERNEL_BYTES[dom] * tok_heads + (state_bytes(w) if dom == "kda_chain_kernel" else 0)
+    dom_bytes = KERNEL_BYTES[dom] * tok_heads
+    if dom != "kda_intra_kernel":
+        dom_bytes += state_bytes(w)
+    if dom == "split_chain":
+        dom_bytes += SPLIT_BYTES_PER_SEGMENT_HEAD * w.B * segs * w.H
     achieved = dom_bytes / (kernels[dom] / 1e3) / 1e9
     traffic = load_traffic(wname, dom)
 
@@ -325,13 +341,14 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
                    "num_seqs": w.N, "lower_bound": w.lower_bound,
                    "initial_state": None if w.initial_state is None else str(w.initial_state.dtype),
-                   "final_state": None if w.final_state_dtype is None else str(w.final_state_dtype)},
+                   "final_state": None if w.final_state_dtype is None else str(w.final_state_dtype),
+                   "chain_segments": segs},
         "tflops_alg": round(tflops, 2),
         "mfma_frac_alg": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "gbs_alg": round(gbs, 1),
         "hbm_frac_alg": round(gbs / HBM_PEAK_GBS, 4),
         "kernel_ms": {"kda_chunk_table_kernel": round(table_ms, 5),
-                      "kda_intra_kernel": round(intra_ms, 5), "kda_chain_kernel": round(chain_ms, 5)},
+                      "kda_intra_kernel": round(intra_ms, 5), chain_key: round(chain_ms, 5)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

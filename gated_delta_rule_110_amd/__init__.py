@@ -24,7 +24,7 @@ import torch
 from ._build import LIB as LIB_PATH
 from ._build import build
 
-__all__ = ["fwd", "decode", "workspace_size", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
+__all__ = ["fwd", "decode", "workspace_size", "chain_segments_for", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
            "KDA_FP32"]
 
 KDA_BF16 = 1
@@ -47,7 +47,7 @@ class KdaDesc(ctypes.Structure):
                 ("K", ctypes.c_int64), ("V", ctypes.c_int64), ("num_seqs", ctypes.c_int64),
                 ("initial_state_dtype", ctypes.c_int32), ("final_state_dtype", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("phase_events", ctypes.c_void_p)]
+                ("phase_events", ctypes.c_void_p), ("chain_segments", ctypes.c_int64)]
 
 
 _lock = threading.Lock()
@@ -72,21 +72,29 @@ def library() -> ctypes.CDLL:
                                        P, P, P, ctypes.POINTER(KdaDesc), P]
             lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
             lib.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(KdaDesc)]
+            lib.kda_fwd_chain_segments.restype = ctypes.c_int64
+            lib.kda_fwd_chain_segments.argtypes = [ctypes.POINTER(KdaDesc)]
             lib.kda_status_string.restype = ctypes.c_char_p
             lib.kda_status_string.argtypes = [ctypes.c_int]
             _lib = lib
     return _lib
 
 
-def _desc(B, T, H, N, h0_dtype=0, ht_dtype=0, workspace=None, nbytes=0) -> KdaDesc:
+def _desc(B, T, H, N, h0_dtype=0, ht_dtype=0, workspace=None, nbytes=0, chain_segments=0) -> KdaDesc:
     return KdaDesc(B, T, H, HEAD_DIM, HEAD_DIM, N, h0_dtype, ht_dtype,
-                   ctypes.c_void_p(workspace), nbytes, None)
+                   ctypes.c_void_p(workspace), nbytes, None, chain_segments)
 
 
-def workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None) -> int:
-    """Workspace bytes ``fwd`` needs for these shapes."""
-    d = _desc(B, T, H, B if num_seqs is None else num_seqs)
+def workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None, chain_segments: int = 0) -> int:
+    """Workspace bytes ``fwd`` needs for these shapes (and chain split)."""
+    d = _desc(B, T, H, B if num_seqs is None else num_seqs, chain_segments=chain_segments)
     return int(library().kda_fwd_workspace_size(ctypes.byref(d)))
+
+
+def chain_segments_for(B: int, T: int, H: int, chain_segments: int = 0) -> int:
+    """Segments ``fwd`` splits each state chain into for these shapes without cu_seqlens."""
+    d = _desc(B, T, H, B, chain_segments=chain_segments)
+    return int(library().kda_fwd_chain_segments(ctypes.byref(d)))
 
 
 def _state_dtype(t: Optional[torch.Tensor], name: str) -> int:
@@ -108,7 +116,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         lower_bound: float, initial_state: Optional[torch.Tensor] = None,
         final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None,
-        phase_events=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        phase_events=None, chain_segments: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KDA forward on the current HIP stream.  Returns ``(out, final_state)``.
 
     q, k, g: bf16 [B,T,H,128]; v: bf16 [B,T,H,128]; beta: bf16 logits [B,T,H];
@@ -117,7 +125,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     cu_seqlens: int64 [N+1] on the device (then B == 1) or None;
     out: bf16 [B,T,H,128] or None (allocated); workspace: uint8 device tensor
     of at least ``workspace_size`` bytes or None (allocated); phase_events:
-    None or the address of a caller-owned array of 4 hipEvent_t (instrumentation).
+    None or the address of a caller-owned array of 4 hipEvent_t (instrumentation);
+    chain_segments: 0 (automatic), 1 (never) or the number of segments each
+    sequence's state chain is split into (batches without cu_seqlens).
     """
     lib = library()
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -163,7 +173,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
             raise ValueError("%s must be [N,H,K,V] = %s" % (name, (N, H, K, V)))
     h0d = _state_dtype(initial_state, "initial_state")
     htd = _state_dtype(final_state, "final_state")
-    d = _desc(B, T, H, N, h0d, htd)
+    d = _desc(B, T, H, N, h0d, htd, chain_segments=int(chain_segments))
     d.K, d.V = K, V
     need = int(lib.kda_fwd_workspace_size(ctypes.byref(d)))
     with torch.cuda.device(dev):

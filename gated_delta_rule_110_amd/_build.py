@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_intra.hip", "kda_chain.hip", "kda_decode.hip", "kda_api.hip"]
+SOURCES = ["kda_intra.hip", "kda_chain.hip", "kda_segment.hip", "kda_decode.hip", "kda_api.hip"]
 HEADERS = [os.path.join(CSRC, "kda_common.h"), os.path.join(INCLUDE, "kda.h")]
 
 # -packed-fp32-ops off: hipcc must not emit packed fp32 VALU instructions.

@@ -16,6 +16,33 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// How many segments each sequence's state chain is cut into (kda.h,
+// kda_desc_t::chain_segments).  Automatic splitting aims at 8 workgroups per
+// segment and head filling the 256 CUs, keeping at least 32 chunks per segment
+// so that the extra map and scan work stays small next to the chain.
+constexpr int64_t kCUs = 256;
+constexpr int64_t kChainWorkgroups = 8;
+constexpr int64_t kMinSegmentChunks = 32;
+
+kda_status_t choose_segments(const kda_desc_t *d, Geometry &g) {
+    g.segs = 1;
+    g.segc = g.nc_fixed;
+    const int64_t req = d->chain_segments;
+    if (req < 0) return KDA_ERR_PARAM;
+    if (g.varlen) return req >= 2 ? KDA_ERR_UNSUPPORTED : KDA_OK;
+    const int64_t nc = g.nc_fixed;
+    int64_t want = req;
+    if (req == 0) {
+        want = kCUs / kChainWorkgroups / (g.B * g.H);
+        if (want > nc / kMinSegmentChunks) want = nc / kMinSegmentChunks;
+    }
+    if (want > nc) want = nc;
+    if (want < 2) return KDA_OK;
+    g.segc = (nc + want - 1) / want;
+    g.segs = (nc + g.segc - 1) / g.segc;  // >= 2: segc < nc when 2 <= want <= nc
+    return KDA_OK;
+}
+
 // Fills geometry; returns KDA_OK or the shape error.
 kda_status_t make_geometry(const kda_desc_t *d, bool varlen, Geometry &g) {
     if (d->B < 1 || d->H < 1 || d->T < 0) return KDA_ERR_SHAPE;
@@ -35,7 +62,7 @@ kda_status_t make_geometry(const kda_desc_t *d, bool varlen, Geometry &g) {
         g.slots = g.N * nc;
     }
     if (g.slots > 0x7fffffffLL || g.N > 0x7fffffffLL) return KDA_ERR_SHAPE;
-    return KDA_OK;
+    return choose_segments(d, g);
 }
 
 WorkspaceLayout make_layout(const Geometry &g) {
@@ -49,6 +76,15 @@ WorkspaceLayout make_layout(const Geometry &g) {
     L.off_Af = o; o = align_up(o + per * kAfElems * 2, 256);
     L.off_Uf = o; o = align_up(o + per * kUfElems * 2, 256);
     L.off_gn = o;  o = align_up(o + per * kGnElems * 4, 256);
+    if (g.segs > 1) {
+        const size_t ns = (size_t)(g.B * g.segs);
+        const size_t maps = ns * (size_t)g.H * (size_t)(kK * kV) * 4;
+        L.off_seg_cu = o;  o = align_up(o + (ns + 1) * sizeof(int64_t), 256);
+        L.off_seg_off = o; o = align_up(o + (ns + 1) * sizeof(int32_t), 256);
+        L.off_mapM = o;    o = align_up(o + maps, 256);
+        L.off_mapN = o;    o = align_up(o + maps, 256);
+        L.off_sin = o;     o = align_up(o + maps, 256);
+    }
     L.total = o;
     return L;
 }
@@ -69,6 +105,13 @@ extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc) {
         ok = true;
     }
     return ok ? need : 0;
+}
+
+extern "C" int64_t kda_fwd_chain_segments(const kda_desc_t *desc) {
+    if (!desc) return -1;
+    Geometry g;
+    if (make_geometry(desc, false, g) != KDA_OK) return -1;
+    return g.segs;
 }
 
 extern "C" const char *kda_status_string(kda_status_t s) {
@@ -154,7 +197,32 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
     ca.h0_bf16 = desc->initial_state_dtype == KDA_BF16;
     ca.ht_bf16 = desc->final_state_dtype == KDA_BF16;
     ca.out = static_cast<uint16_t *>(out);
-    if (err == hipSuccess) err = kda_launch_chain(ca, stream);
+    if (geo.segs > 1) {
+        // split chains: every segment is a packed sequence of the chain kernel
+        int64_t *seg_cu = reinterpret_cast<int64_t *>(ws + lay.off_seg_cu);
+        int32_t *seg_off = reinterpret_cast<int32_t *>(ws + lay.off_seg_off);
+        float *mapM = reinterpret_cast<float *>(ws + lay.off_mapM);
+        float *mapN = reinterpret_cast<float *>(ws + lay.off_mapN);
+        float *sin = reinterpret_cast<float *>(ws + lay.off_sin);
+        ChainArgs seg = ca;
+        seg.cu = seg_cu; seg.chunk_off = seg_off;
+        seg.N = geo.B * geo.segs; seg.nc_fixed = 0;
+        if (err == hipSuccess) err = kda_launch_seg_table(geo.B, geo.T, geo.segs, geo.segc, seg_cu, seg_off, stream);
+        ChainArgs maps = seg;  // 1. the map of every segment
+        maps.h0 = nullptr; maps.ht = nullptr; maps.out = nullptr;
+        maps.map_mode = 1; maps.mapM = mapM; maps.mapN = mapN;
+        if (err == hipSuccess) err = kda_launch_chain(maps, stream);
+        ScanArgs sa{};     // 2. entering states and the final state
+        sa.mapM = mapM; sa.mapN = mapN; sa.sin = sin;
+        sa.h0 = initial_state; sa.ht = final_state;
+        sa.h0_bf16 = ca.h0_bf16; sa.ht_bf16 = ca.ht_bf16;
+        sa.B = geo.B; sa.H = geo.H; sa.segs = geo.segs;
+        if (err == hipSuccess) err = kda_launch_seg_scan(sa, stream);
+        seg.h0 = sin; seg.h0_bf16 = 0; seg.ht = nullptr;  // 3. outputs
+        if (err == hipSuccess) err = kda_launch_chain(seg, stream);
+    } else if (err == hipSuccess) {
+        err = kda_launch_chain(ca, stream);
+    }
     if (ev && err == hipSuccess) err = hipEventRecord(ev[3], stream);
 
     if (owned) {

@@ -47,6 +47,11 @@
 // call's initial state continues a sequence, which is the multi-turn state
 // carry the forward call exposes ("¿Qué es la atención Kimi Delta…",
 // 7minutos.es).
+//
+// kda_chain_map_kernel is the same chain without outputs, used to split long
+// chains (kda_segment.hip): it gives every chain its affine map S -> M S + N,
+// with 16 workgroups per chain, eight carrying N (from S = 0) and eight
+// carrying M (from S = I with the chunks' U taken as zero).
 #include "kda_common.h"
 
 using namespace kda;
@@ -158,7 +163,9 @@ __device__ __forceinline__ h8 pack_frag(const f4 &t0, const f4 &t1) {
 }
 
 // One chunk of the state chain.  S[ct] holds S[16 ct + 4 g + e][16 vb + r];
-// the chunk's -W and Kbar^T fragments are in ring slot `rs`.
+// the chunk's -W and Kbar^T fragments are in ring slot `rs`.  With kNoU the
+// chunk's U is taken as zero (the linear part of the chunk map).
+template <bool kNoU>
 __device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], int rs, int slot, int lane) {
     h8 W[16];
 #pragma unroll
@@ -171,11 +178,16 @@ __device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], int rs, in
     }
     // Ut = U - W S: X[it] holds Ut[16 it + 4 g + e][16 vb + r]
     f4 X[4];
-    const h4 *Ul = reinterpret_cast<const h4 *>(&sm.ring[rs][32][0]) + lane;
+    if (kNoU) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const h4 u = Ul[it * 64];
-        X[it][0] = (float)u[0]; X[it][1] = (float)u[1]; X[it][2] = (float)u[2]; X[it][3] = (float)u[3];
+        for (int it = 0; it < 4; ++it) X[it] = f4{0, 0, 0, 0};
+    } else {
+        const h4 *Ul = reinterpret_cast<const h4 *>(&sm.ring[rs][32][0]) + lane;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const h4 u = Ul[it * 64];
+            X[it][0] = (float)u[0]; X[it][1] = (float)u[1]; X[it][2] = (float)u[2]; X[it][3] = (float)u[3];
+        }
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -237,17 +249,25 @@ __device__ __forceinline__ void out_step(ChainSmem &sm, const OutOps &op, int sl
     }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
-    __shared__ ChainSmem sm;
+// The chain kernel's body; kMap selects map mode (ChainArgs::map_mode), which
+// is a kernel of its own so that the ordinary chain is compiled without it.
+__shared__ ChainSmem sm;  // each of the two kernels below gets its own
+
+template <bool kMap>
+__device__ __forceinline__ void chain_body(const ChainArgs &a) {
 
     const int64_t H = a.H;
     const int64_t NH = a.N * H;
-    // blockIdx -> (chain, V block) with all V blocks of a chain on one XCD
+    // blockIdx -> (chain, V block) with all V blocks of a chain on one XCD; in
+    // map mode a chain has 16 workgroups, the second 8 propagating the identity
     const int64_t x = blockIdx.x;
     const int64_t xcd = x & 7;
     const int64_t sx = x >> 3;
-    const int vb = (int)(sx % kNVB);
-    const int64_t chain = (sx / kNVB) * 8 + xcd;
+    constexpr int nvb = kMap ? 2 * kNVB : kNVB;
+    const int vbx = (int)(sx % nvb);
+    const int vb = vbx & (kNVB - 1);
+    const bool linear_part = kMap && vbx >= kNVB;
+    const int64_t chain = (sx / nvb) * 8 + xcd;
     if (chain >= NH) return;
     const int64_t n = chain / H, h = chain - (chain / H) * H;
 
@@ -281,15 +301,26 @@ __global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
             for (int e = 0; e < 4; ++e) {
                 const int64_t idx = sbase + (int64_t)(16 * ct + 4 * g + e) * kV;
                 float v = 0.f;
-                if (a.h0) v = a.h0_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.h0)[idx])
-                                        : reinterpret_cast<const float *>(a.h0)[idx];
+                if (kMap) v = (linear_part && 16 * ct + 4 * g + e == kVB * vb + r) ? 1.f : 0.f;
+                else if (a.h0) v = a.h0_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.h0)[idx])
+                                             : reinterpret_cast<const float *>(a.h0)[idx];
                 S[ct][e] = v;
             }
         if (nchunks > 0) {
             lds_barrier();  // ring slot 0 written by the loader
-            for (int64_t s = 0; s < nchunks; ++s) chain_step(sm, S, (int)(s & 3), (int)(s & 1), lane);
+            if (kMap && linear_part) {
+                for (int64_t s = 0; s < nchunks; ++s) chain_step<true>(sm, S, (int)(s & 3), (int)(s & 1), lane);
+            } else {
+                for (int64_t s = 0; s < nchunks; ++s) chain_step<false>(sm, S, (int)(s & 3), (int)(s & 1), lane);
+            }
         }
-        if (a.ht) {
+        if (kMap) {
+            float *dst = linear_part ? a.mapM : a.mapN;
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[sbase + (int64_t)(16 * ct + 4 * g + e) * kV] = S[ct][e];
+        } else if (a.ht) {
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
@@ -301,7 +332,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
         }
     } else if (wave == 1) {
         // ---- outputs -------------------------------------------------------
-        if (nchunks > 0) {
+        if (kMap) {
+            // no outputs: only the barriers the other waves count on
+            if (nchunks > 0) {
+                lds_barrier();
+                for (int64_t s = 0; s < nchunks; ++s) lds_barrier();
+            }
+        } else if (nchunks > 0) {
             const int64_t row_stride = H * kV;
             uint16_t *out0 = a.out + (tseq * H + h) * kV + kVB * vb + 4 * g;
             auto out_at = [&](int64_t s) { return out0 + kChunk * s * row_stride; };
@@ -363,6 +400,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) {
     }
 }
 
+__global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) { chain_body<false>(a); }
+__global__ __launch_bounds__(kThreads, 1) void kda_chain_map_kernel(ChainArgs a) { chain_body<true>(a); }
+
 // Packed batches: first chunk slot of each sequence, off[n] = sum_{m<n} ceil(len_m / 64).
 __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int64_t *cu, int64_t N, int32_t *off) {
     __shared__ int64_t part[1024];
@@ -399,8 +439,10 @@ hipError_t kda_launch_chain(const ChainArgs &a, hipStream_t s) {
     const int64_t NH = a.N * a.H;
     if (NH <= 0) return hipSuccess;
     const int64_t groups = (NH + 7) / 8;
-    const int64_t blocks = groups * 8 * kNVB;
-    hipLaunchKernelGGL(kda_chain_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    if (a.map_mode)
+        hipLaunchKernelGGL(kda_chain_map_kernel, dim3((unsigned)(groups * 8 * 2 * kNVB)), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(kda_chain_kernel, dim3((unsigned)(groups * 8 * kNVB)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

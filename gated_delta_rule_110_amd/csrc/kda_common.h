@@ -51,11 +51,18 @@ struct Geometry {
     int64_t nc_fixed;     // chunks per sequence when not packed
     int64_t slots;        // chunk slots (upper bound when packed)
     bool varlen;
+    int64_t segs;         // segments each sequence's chunk chain is split into (1 = not split)
+    int64_t segc;         // chunks per segment (the last one may hold fewer)
 };
 
 struct WorkspaceLayout {
     size_t off_chunk_off;  // int32 [N + 1] per-sequence first chunk slot (packed only)
     size_t off_Wf, off_Qf, off_Kf, off_Af, off_Uf, off_gn;
+    // split chains only: the segments as packed sequences (int64 [B segs + 1]
+    // token offsets, int32 [B segs + 1] first chunk slots), the affine map of
+    // every segment (fp32 [B segs, H, K, K] linear part, [B segs, H, K, V]
+    // offset) and the state entering every segment (fp32 [B segs, H, K, V])
+    size_t off_seg_cu, off_seg_off, off_mapM, off_mapN, off_sin;
     size_t total;
 };
 
@@ -82,6 +89,26 @@ struct ChainArgs {
     void *ht;            // final state [N,H,K,V] or nullptr
     int h0_bf16, ht_bf16;
     uint16_t *out;       // [B,T,H,V] bf16
+    // Map mode (map_mode != 0): no outputs and no h0 / ht.  Each chain gets 16
+    // workgroups instead of 8: V blocks 0..7 run the chain from S = 0 and
+    // write the result to mapN, V blocks 8..15 run it from S = I with U taken
+    // as 0 and write the result to mapM, both fp32 [N,H,K,128].  These are
+    // the offset and the linear part of the chain's affine map S -> M S + N.
+    int map_mode;
+    float *mapM, *mapN;
+};
+
+// The sequential pass over the segments of split chains: for batch row b and
+// head h, S_0 = h0[b, h] (zeros when h0 is null) and, for s = 0 .. segs - 1,
+// S_{s+1} = M_s S_s + N_s with (M_s, N_s) the map of segment s; S_s (s < segs)
+// goes to sin, S_segs to ht.
+struct ScanArgs {
+    const float *mapM, *mapN;   // [B segs, H, K, K] / [B segs, H, K, V] fp32
+    float *sin;                 // [B segs, H, K, V] fp32
+    const void *h0;             // [B, H, K, V] or nullptr
+    void *ht;                   // [B, H, K, V] or nullptr
+    int h0_bf16, ht_bf16;
+    int64_t B, H, segs;
 };
 
 struct DecodeArgs {
@@ -173,7 +200,6 @@ __device__ __forceinline__ f4 mfma16x16x16_f16(const h4 &a, const h4 &b, const f
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// Resolve packed sequence index of a chunk slot: largest n with off[n] <= slot.
 // LDS byte address of a __shared__ object (what M0 and the ds_* instructions take).
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)(p);
@@ -190,6 +216,7 @@ __device__ __forceinline__ void lds_copy4(const void *p, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(p), "{m0}"(lds) : "memory");
 }
 
+// Resolve packed sequence index of a chunk slot: largest n with off[n] <= slot.
 __device__ __forceinline__ int64_t seq_of_slot(const int32_t *off, int64_t N, int64_t slot) {
     int64_t lo = 0, hi = N;  // invariant: off[lo] <= slot < off[hi] (off[N] > slot)
     while (hi - lo > 1) {
@@ -205,4 +232,7 @@ __device__ __forceinline__ int64_t seq_of_slot(const int32_t *off, int64_t N, in
 hipError_t kda_launch_chunk_table(const int64_t *cu, int64_t N, int32_t *chunk_off, hipStream_t s);
 hipError_t kda_launch_intra(const kda::IntraArgs &a, int64_t slots, hipStream_t s);
 hipError_t kda_launch_chain(const kda::ChainArgs &a, hipStream_t s);
+hipError_t kda_launch_seg_table(int64_t B, int64_t T, int64_t segs, int64_t segc, int64_t *cu, int32_t *off,
+                                hipStream_t s);
+hipError_t kda_launch_seg_scan(const kda::ScanArgs &a, hipStream_t s);
 hipError_t kda_launch_decode(const kda::DecodeArgs &a, hipStream_t s);

@@ -77,14 +77,37 @@ typedef struct {
      * the caller.  kda_fwd records event 0 before its first kernel, 1 after
      * the chunk-table kernel (packed batches only; otherwise right after 0),
      * 2 after the intra-chunk kernel and 3 after the state-chain kernel, all
-     * on `stream`, so per-kernel device time can be measured. */
+     * on `stream`, so per-kernel device time can be measured (with split
+     * chains, event 3 follows the last of the three chain-side launches). */
     hipEvent_t *phase_events;
+    /* Split state chains (batches without cu_seqlens only).  The chunks of a
+     * sequence form a serial chain; every chunk maps the state entering it
+     * affinely, so a long chain can be cut into segments whose maps are
+     * computed in parallel and then composed in order (see kda_fwd).
+     *   0  : automatic -- split when the chains alone cannot fill the GPU:
+     *        segments = min(32 / (B * H), chunks / 32) when that is >= 2
+     *        (sized for the 256 CUs of an MI355X, 8 workgroups per chain),
+     *        otherwise no split;
+     *   1  : never split;
+     *   >= 2 : split every sequence into that many segments (at most one per
+     *        64-token chunk; fewer when the chunks do not divide evenly).
+     * Negative values are KDA_ERR_PARAM; a value >= 2 with cu_seqlens is
+     * KDA_ERR_UNSUPPORTED.  The result is the same function of the inputs
+     * either way, up to rounding. */
+    int64_t chain_segments;
 } kda_desc_t;
 
 /* Bytes of workspace kda_fwd needs for these shapes (0 if the shapes are
  * invalid).  Pure host arithmetic; needs no device.  Grows linearly with the
- * number of 64-token chunks times H (about 72.5 KiB per chunk and head). */
+ * number of 64-token chunks times H (about 72.5 KiB per chunk and head), plus
+ * 192 KiB per (segment, head) when chains are split. */
 size_t kda_fwd_workspace_size(const kda_desc_t *desc);
+
+/* Number of segments kda_fwd splits each sequence's state chain into for
+ * these shapes when called without cu_seqlens (1 = not split; calls with
+ * cu_seqlens never split), or -1 if the descriptor is invalid.  Pure host
+ * arithmetic. */
+int64_t kda_fwd_chain_segments(const kda_desc_t *desc);
 
 /* Enqueue the KDA forward pass on `stream` and return without synchronising.
  *
@@ -108,7 +131,12 @@ size_t kda_fwd_workspace_size(const kda_desc_t *desc);
  *   desc             : shapes, state dtypes and workspace (host pointer).
  *   stream           : HIP stream (0 = the null stream).
  * Returns KDA_OK when the work was enqueued; device faults surface at the
- * caller's next synchronisation. */
+ * caller's next synchronisation.
+ *
+ * With split chains (desc->chain_segments) the state chain of every sequence
+ * runs in three launches instead of one: the map of every segment, an fp32
+ * scan over the segments (the entering states and the final state), and the
+ * chain with outputs from each segment's entering state. */
 kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
                      const void *beta, float scale, const float *A_log,
                      const float *dt_bias, float lower_bound,

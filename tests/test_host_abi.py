@@ -102,6 +102,33 @@ def test_workspace_size_monotone(lib):
     assert abs(per - 72.5 * 1024) < 512
 
 
+def test_chain_segments_rule(lib):
+    # automatic: split only when the B*H chains (8 workgroups each) leave CUs idle and the
+    # chain is long enough (at least 32 chunks per segment)
+    assert kda.chain_segments_for(1, 8192, 32) == 1
+    assert kda.chain_segments_for(1, 131072, 32) == 1
+    assert kda.chain_segments_for(1, 131072, 4) == 8
+    assert kda.chain_segments_for(1, 131072, 1) == 32
+    assert kda.chain_segments_for(2, 131072, 1) == 16
+    assert kda.chain_segments_for(1, 4096, 4) == 2
+    assert kda.chain_segments_for(1, 1024, 1) == 1
+    # forced: equal segments of ceil(chunks / n) chunks, at most one per chunk
+    assert kda.chain_segments_for(1, 64 * 40 + 17, 2, 4) == 4   # 41 chunks: 11, 11, 11, 8
+    assert kda.chain_segments_for(1, 64 * 10, 2, 3) == 3        # 4, 4, 2
+    assert kda.chain_segments_for(1, 64 * 9, 2, 4) == 3         # 3, 3, 3
+    assert kda.chain_segments_for(1, 64 * 5 + 1, 2, 100) == 6
+    assert kda.chain_segments_for(1, 8192, 4, 1) == 1
+    assert kda.chain_segments_for(1, 0, 4, 4) == 1
+    assert kda.chain_segments_for(1, 8192, 4, -1) == -1
+    # errors: a negative count; a split asked for together with cu_seqlens
+    assert _call(lib, _desc(chain_segments=-2)) == 4
+    assert _call(lib, _desc(chain_segments=2), cu=ctypes.c_void_p(FAKE)) == 3
+    # 192 KiB of workspace per (batch row, segment, head): two maps and the entering state,
+    # fp32 128 x 128 each (B = 2: only the unpacked layout counts)
+    extra = kda.workspace_size(2, 64 * 40, 2, chain_segments=4) - kda.workspace_size(2, 64 * 40, 2, chain_segments=1)
+    assert 2 * 4 * 2 * 192 * 1024 <= extra <= 2 * 4 * 2 * 192 * 1024 + 1024
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16)

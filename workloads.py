@@ -192,10 +192,24 @@ def pages_workload(name: str) -> Workload:
     return make(name, 1, 8192, H, seed, lower_bound=-5.0, init=None, final="fp32", seqlens=[1024] * 8)
 
 
+# One long sequence with few heads: the state chains alone occupy few CUs, so
+# the forward pass splits them into segments.  Same recipe as the 128K-token
+# workload above (g ~ N(-1, 1), lower_bound = -5, fp32 initial and final
+# states) with H = 4.
+SPLIT_NAMES = ["long_T131072_H4"]
+
+
+def split_workload(name: str) -> Workload:
+    i = SPLIT_NAMES.index(name)
+    return make(name, 1, 131072, 4, 3000 + i, lower_bound=-5.0, g_mean=-1.0, init="fp32", final="fp32")
+
+
 def by_name(name: str) -> Workload:
-    """Any workload by name: CONFIG_NAMES or PAGES_NAMES."""
+    """Any workload by name: CONFIG_NAMES, PAGES_NAMES or SPLIT_NAMES."""
     if name in CONFIG_NAMES:
         return config(CONFIG_NAMES.index(name))
+    if name in SPLIT_NAMES:
+        return split_workload(name)
     return pages_workload(name)
 
 
