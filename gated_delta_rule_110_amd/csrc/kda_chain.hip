@@ -49,9 +49,10 @@
 // 7minutos.es).
 //
 // kda_chain_map_kernel is the same chain without outputs, used to split long
-// chains (kda_segment.hip): it gives every chain its affine map S -> M S + N,
-// with 16 workgroups per chain, eight carrying N (from S = 0) and eight
-// carrying M (from S = I with the chunks' U taken as zero).
+// chains (kda_segment.hip): it gives every chain its affine map S -> M S + N.
+// Its wave 1 is a second chain wave: in each V-block workgroup wave 0 carries
+// the block's columns of N (from S = 0) and wave 1 those of M (from S = I with
+// the chunks' U taken as zero), both reading the same operand ring.
 #include "kda_common.h"
 
 using namespace kda;
@@ -164,8 +165,9 @@ __device__ __forceinline__ h8 pack_frag(const f4 &t0, const f4 &t1) {
 
 // One chunk of the state chain.  S[ct] holds S[16 ct + 4 g + e][16 vb + r];
 // the chunk's -W and Kbar^T fragments are in ring slot `rs`.  With kNoU the
-// chunk's U is taken as zero (the linear part of the chunk map).
-template <bool kNoU>
+// chunk's U is taken as zero (the linear part of the chunk map); kHandOver
+// writes the fp16 state and pseudo-values for the output wave.
+template <bool kNoU, bool kHandOver>
 __device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], int rs, int slot, int lane) {
     h8 W[16];
 #pragma unroll
@@ -174,7 +176,7 @@ __device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], int rs, in
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         Sb[kb] = pack_frag(S[2 * kb], S[2 * kb + 1]);
-        sm.sS[slot][kb][lane] = Sb[kb];
+        if (kHandOver) sm.sS[slot][kb][lane] = Sb[kb];
     }
     // Ut = U - W S: X[it] holds Ut[16 it + 4 g + e][16 vb + r]
     f4 X[4];
@@ -200,7 +202,7 @@ __device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], int rs, in
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         Ub[kb] = pack_frag(X[2 * kb], X[2 * kb + 1]);
-        sm.sU[slot][kb][lane] = Ub[kb];
+        if (kHandOver) sm.sU[slot][kb][lane] = Ub[kb];
     }
     lds_barrier();
     // S <- Diag(exp(G_n)) S + Kbar^T Ut;  exp(G_n)[16 ct + 4 g .. + 3] for the lane's rows
@@ -258,16 +260,12 @@ __device__ __forceinline__ void chain_body(const ChainArgs &a) {
 
     const int64_t H = a.H;
     const int64_t NH = a.N * H;
-    // blockIdx -> (chain, V block) with all V blocks of a chain on one XCD; in
-    // map mode a chain has 16 workgroups, the second 8 propagating the identity
+    // blockIdx -> (chain, V block) with all V blocks of a chain on one XCD
     const int64_t x = blockIdx.x;
     const int64_t xcd = x & 7;
     const int64_t sx = x >> 3;
-    constexpr int nvb = kMap ? 2 * kNVB : kNVB;
-    const int vbx = (int)(sx % nvb);
-    const int vb = vbx & (kNVB - 1);
-    const bool linear_part = kMap && vbx >= kNVB;
-    const int64_t chain = (sx / nvb) * 8 + xcd;
+    const int vb = (int)(sx % kNVB);
+    const int64_t chain = (sx / kNVB) * 8 + xcd;
     if (chain >= NH) return;
     const int64_t n = chain / H, h = chain - (chain / H) * H;
 
@@ -291,8 +289,11 @@ __device__ __forceinline__ void chain_body(const ChainArgs &a) {
     const int r = lane & 15;
     const int g = lane >> 4;
 
-    if (wave == 0) {
+    if (wave == 0 || (kMap && wave == 1)) {
         // ---- state chain ---------------------------------------------------
+        // (map mode: wave 0 carries N from S = 0, wave 1 carries M from S = I
+        // with U = 0; both read the same ring)
+        const bool linear_part = kMap && wave == 1;
         f4 S[8];
         const int64_t sbase = (n * H + h) * (int64_t)kK * kV + kVB * vb + r;
 #pragma unroll
@@ -308,10 +309,15 @@ __device__ __forceinline__ void chain_body(const ChainArgs &a) {
             }
         if (nchunks > 0) {
             lds_barrier();  // ring slot 0 written by the loader
-            if (kMap && linear_part) {
-                for (int64_t s = 0; s < nchunks; ++s) chain_step<true>(sm, S, (int)(s & 3), (int)(s & 1), lane);
+            if (!kMap) {
+                for (int64_t s = 0; s < nchunks; ++s)
+                    chain_step<false, true>(sm, S, (int)(s & 3), (int)(s & 1), lane);
+            } else if (linear_part) {
+                for (int64_t s = 0; s < nchunks; ++s)
+                    chain_step<true, false>(sm, S, (int)(s & 3), (int)(s & 1), lane);
             } else {
-                for (int64_t s = 0; s < nchunks; ++s) chain_step<false>(sm, S, (int)(s & 3), (int)(s & 1), lane);
+                for (int64_t s = 0; s < nchunks; ++s)
+                    chain_step<false, false>(sm, S, (int)(s & 3), (int)(s & 1), lane);
             }
         }
         if (kMap) {
@@ -332,13 +338,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs &a) {
         }
     } else if (wave == 1) {
         // ---- outputs -------------------------------------------------------
-        if (kMap) {
-            // no outputs: only the barriers the other waves count on
-            if (nchunks > 0) {
-                lds_barrier();
-                for (int64_t s = 0; s < nchunks; ++s) lds_barrier();
-            }
-        } else if (nchunks > 0) {
+        if (nchunks > 0) {
             const int64_t row_stride = H * kV;
             uint16_t *out0 = a.out + (tseq * H + h) * kV + kVB * vb + 4 * g;
             auto out_at = [&](int64_t s) { return out0 + kChunk * s * row_stride; };
@@ -439,10 +439,11 @@ hipError_t kda_launch_chain(const ChainArgs &a, hipStream_t s) {
     const int64_t NH = a.N * a.H;
     if (NH <= 0) return hipSuccess;
     const int64_t groups = (NH + 7) / 8;
+    const dim3 grid((unsigned)(groups * 8 * kNVB));
     if (a.map_mode)
-        hipLaunchKernelGGL(kda_chain_map_kernel, dim3((unsigned)(groups * 8 * 2 * kNVB)), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(kda_chain_map_kernel, grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(kda_chain_kernel, dim3((unsigned)(groups * 8 * kNVB)), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(kda_chain_kernel, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -89,11 +89,10 @@ struct ChainArgs {
     void *ht;            // final state [N,H,K,V] or nullptr
     int h0_bf16, ht_bf16;
     uint16_t *out;       // [B,T,H,V] bf16
-    // Map mode (map_mode != 0): no outputs and no h0 / ht.  Each chain gets 16
-    // workgroups instead of 8: V blocks 0..7 run the chain from S = 0 and
-    // write the result to mapN, V blocks 8..15 run it from S = I with U taken
-    // as 0 and write the result to mapM, both fp32 [N,H,K,128].  These are
-    // the offset and the linear part of the chain's affine map S -> M S + N.
+    // Map mode (map_mode != 0): no outputs and no h0 / ht.  Every V-block
+    // workgroup runs its columns twice, from S = 0 (result to mapN) and from
+    // S = I with U taken as 0 (result to mapM), both fp32 [N,H,K,128]: the
+    // offset and the linear part of the chain's affine map S -> M S + N.
     int map_mode;
     float *mapM, *mapN;
 };
