@@ -54,10 +54,15 @@ __global__ __launch_bounds__(kThreads) void kda_seg_table_kernel(int64_t B, int6
 // One workgroup per (16-column block, batch row and head).  The slice S[:, cols]
 // (128 x 16 fp32) lives in LDS, transposed, double-buffered; each step is the
 // fp32 product M_s S (128 x 128 times 128 x 16) on the matrix cores plus N_s.
-// Wave w computes row tiles 2w and 2w + 1.  The 16x16x4 fp32 MFMA sums over
-// the four 16-lane groups; lane group q of product j takes k = 16 kq + 4 q + j
-// in both operands, so one 16-byte load per lane feeds four products.
-__global__ __launch_bounds__(kThreads) void kda_seg_scan_kernel(ScanArgs a) {
+// Wave w computes row tile w.  The 16x16x4 fp32 MFMA sums over the four
+// 16-lane groups; lane group q of product j takes k = 16 kq + 4 q + j in both
+// operands, so one 16-byte load per lane feeds four products.  The next
+// segment's M and N rows are loaded while the current product runs: the
+// scan is a chain of dependent steps, and each step's loads would otherwise
+// be exposed.
+constexpr int kScanThreads = 512;
+
+__global__ __launch_bounds__(kScanThreads) void kda_seg_scan_kernel(ScanArgs a) {
     __shared__ float st[2][kCols * kSP];  // [buffer][column * kSP + row]
 
     const int vb = blockIdx.x;
@@ -69,12 +74,12 @@ __global__ __launch_bounds__(kThreads) void kda_seg_scan_kernel(ScanArgs a) {
     const int64_t col0 = (int64_t)kCols * vb;
     auto seg_index = [&](int64_t s) { return (b * a.segs + s) * a.H + h; };
 
-    {   // S_0 = h0[b, h] (or zeros): thread t holds column t % 16, rows 8 (t / 16) .. + 7
-        const int c = tid & 15, r0 = 8 * (tid >> 4);
+    {   // S_0 = h0[b, h] (or zeros): thread t holds column t % 16, rows 4 (t / 16) .. + 3
+        const int c = tid & 15, r0 = 4 * (tid >> 4);
         const int64_t src = bh * KV + col0 + c;
         float *dst = a.sin + seg_index(0) * KV + col0 + c;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const int row = r0 + i;
             float v = 0.f;
             if (a.h0) v = a.h0_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t *>(a.h0)[src + row * kV])
@@ -83,36 +88,46 @@ __global__ __launch_bounds__(kThreads) void kda_seg_scan_kernel(ScanArgs a) {
             dst[row * kV] = v;
         }
     }
+
+    // this lane's operands of segment s: M[16 w + r][16 kq + 4 q .. + 3] and
+    // N[16 w + 4 q + e][col0 + r]
+    f4 am[8], an;
+    auto load = [&](int64_t s) {
+        const float *M = a.mapM + seg_index(s) * KV + (16 * w + r) * kK + 4 * q;
+#pragma unroll
+        for (int kq = 0; kq < 8; ++kq) am[kq] = *reinterpret_cast<const f4 *>(M + 16 * kq);
+        const float *N = a.mapN + seg_index(s) * KV + (16 * w + 4 * q) * kV + col0 + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) an[e] = N[e * kV];
+    };
+    load(0);
     __syncthreads();
 
     for (int64_t s = 0; s < a.segs; ++s) {
         const int p = (int)(s & 1);
-        const float *M = a.mapM + seg_index(s) * KV;
-        const float *N = a.mapN + seg_index(s) * KV + col0;
+        f4 m[8], n = an;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int it = 2 * w + t;
-            f4 acc = f4{0, 0, 0, 0};
+        for (int kq = 0; kq < 8; ++kq) m[kq] = am[kq];
+        if (s + 1 < a.segs) load(s + 1);
+        f4 acc = f4{0, 0, 0, 0};
 #pragma unroll
-            for (int kq = 0; kq < 8; ++kq) {
-                const f4 am = *reinterpret_cast<const f4 *>(M + (16 * it + r) * kK + 16 * kq + 4 * q);
-                const f4 bs = *reinterpret_cast<const f4 *>(&st[p][r * kSP + 16 * kq + 4 * q]);
+        for (int kq = 0; kq < 8; ++kq) {
+            const f4 bs = *reinterpret_cast<const f4 *>(&st[p][r * kSP + 16 * kq + 4 * q]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(am[j], bs[j], acc, 0, 0, 0);
-            }
-            // lane (r, q) holds rows 16 it + 4 q + e of column r
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[kq][j], bs[j], acc, 0, 0, 0);
+        }
+        // lane (r, q) holds rows 16 w + 4 q + e of column r
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * it + 4 * q + e;
-                const float v = acc[e] + N[row * kV + r];
-                st[p ^ 1][r * kSP + row] = v;
-                if (s + 1 < a.segs) {
-                    a.sin[seg_index(s + 1) * KV + row * kV + col0 + r] = v;
-                } else if (a.ht) {
-                    const int64_t idx = bh * KV + row * kV + col0 + r;
-                    if (a.ht_bf16) static_cast<uint16_t *>(a.ht)[idx] = f32_to_bf16_bits(v);
-                    else static_cast<float *>(a.ht)[idx] = v;
-                }
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * w + 4 * q + e;
+            const float v = acc[e] + n[e];
+            st[p ^ 1][r * kSP + row] = v;
+            if (s + 1 < a.segs) {
+                a.sin[seg_index(s + 1) * KV + row * kV + col0 + r] = v;
+            } else if (a.ht) {
+                const int64_t idx = bh * KV + row * kV + col0 + r;
+                if (a.ht_bf16) static_cast<uint16_t *>(a.ht)[idx] = f32_to_bf16_bits(v);
+                else static_cast<float *>(a.ht)[idx] = v;
             }
         }
         __syncthreads();
@@ -130,6 +145,6 @@ hipError_t kda_launch_seg_table(int64_t B, int64_t T, int64_t segs, int64_t segc
 hipError_t kda_launch_seg_scan(const ScanArgs &a, hipStream_t s) {
     const int64_t bh = a.B * a.H;
     if (bh <= 0 || a.segs <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_seg_scan_kernel, dim3((unsigned)(kV / kCols), (unsigned)bh), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(kda_seg_scan_kernel, dim3((unsigned)(kV / kCols), (unsigned)bh), dim3(kScanThreads), 0, s, a);
     return hipGetLastError();
 }
