@@ -70,3 +70,71 @@ def chunked_forward(w, C: int = 64):
                 S = np.exp(G[-1])[:, None] * S + (np.exp(G[-1][None, :] - G) * kn).T @ Ut
             fin[n, h] = S
     return out, fin
+
+
+def _chunk_wy(qq, kk, vv, gg, bb, A_log_h, dtb_h, lb):
+    """WY quantities of one chunk: (Qg, Mqk, W, U, Kbar, gn) with
+    Ut = U - W S, O = Qg S + Mqk Ut (unscaled), S_next = Diag(gn) S + Kbar^T Ut."""
+    qn = qq / np.sqrt((qq * qq).sum(-1, keepdims=True) + EPS)
+    kn = kk / np.sqrt((kk * kk).sum(-1, keepdims=True) + EPS)
+    b = 1.0 / (1.0 + np.exp(-bb))
+    a = np.maximum(lb, -np.exp(A_log_h) * _softplus(gg + dtb_h))
+    G = np.cumsum(a, axis=0)
+    n_ = len(b)
+    low = np.tril(np.ones((n_, n_), dtype=bool), -1)
+    diff = G[:, None, :] - G[None, :, :]
+    E = np.where((low | np.eye(n_, dtype=bool))[:, :, None], np.exp(np.minimum(diff, 0.0)), 0.0)
+    A = b[:, None] * np.einsum("id,jd,ijd->ij", kn, kn, E) * low
+    Mqk = np.einsum("id,jd,ijd->ij", qn, kn, E)
+    Tm = np.linalg.inv(np.eye(n_) + A)
+    W = Tm @ (b[:, None] * np.exp(G) * kn)
+    U = Tm @ (b[:, None] * vv)
+    Kbar = np.exp(G[-1][None, :] - G) * kn
+    return np.exp(G) * qn, Mqk, W, U, Kbar, np.exp(G[-1])
+
+
+def split_forward(w, segs: int, C: int = 64):
+    """fp64 forward with every sequence's chunk chain cut into ``segs`` segments of
+    ceil(chunks / segs) chunks (fixed-length batches): each segment's affine map
+    S -> M S + N (M from S = I with U = 0, N from S = 0), the maps composed in
+    order from the initial state, then every segment re-run from its entering
+    state.  In exact arithmetic this equals the unsplit forward."""
+    assert w.cu_seqlens is None
+    q, k, v, g, be = (_bf16_to_f64(t) for t in (w.q, w.k, w.v, w.g, w.beta))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    A_log = w.A_log.double().numpy()
+    dtb = w.dt_bias.double().numpy()
+    lb = float(np.float32(w.lower_bound))
+    scale = float(np.float32(w.scale))
+    nc = (T + C - 1) // C
+    segc = max(1, (nc + segs - 1) // segs)
+    out = np.zeros((B, T, H, V))
+    fin = np.zeros((B, H, K, V))
+    for bb in range(B):
+        for h in range(H):
+            chunks = []
+            for c in range(nc):
+                c0, c1 = c * C, min(c * C + C, T)
+                chunks.append((c0, c1, _chunk_wy(q[bb, c0:c1, h], k[bb, c0:c1, h], v[bb, c0:c1, h],
+                                                  g[bb, c0:c1, h], be[bb, c0:c1, h], A_log[h], dtb[h], lb)))
+            segments = [chunks[i:i + segc] for i in range(0, nc, segc)]
+            maps = []
+            for seg in segments:   # 1. the map of every segment
+                M, N = np.eye(K), np.zeros((K, V))
+                for _, _, (Qg, Mqk, Wc, Uc, Kbar, gn) in seg:
+                    M = gn[:, None] * M + Kbar.T @ (-Wc @ M)
+                    N = gn[:, None] * N + Kbar.T @ (Uc - Wc @ N)
+                maps.append((M, N))
+            S = np.zeros((K, V)) if w.initial_state is None else w.initial_state[bb, h].double().numpy().copy()
+            entering = []
+            for M, N in maps:      # 2. the scan
+                entering.append(S)
+                S = M @ S + N
+            fin[bb, h] = S
+            for seg, S in zip(segments, entering):   # 3. every segment from its entering state
+                for c0, c1, (Qg, Mqk, Wc, Uc, Kbar, gn) in seg:
+                    Ut = Uc - Wc @ S
+                    out[bb, c0:c1, h] = scale * (Qg @ S + Mqk @ Ut)
+                    S = gn[:, None] * S + Kbar.T @ Ut
+    return out, fin
