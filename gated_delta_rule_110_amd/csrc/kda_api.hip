@@ -19,10 +19,13 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // How many segments each sequence's state chain is cut into (kda.h,
 // kda_desc_t::chain_segments).  Automatic splitting aims at 8 workgroups per
 // segment and head filling the 256 CUs, keeping at least 32 chunks per segment
-// so that the extra map and scan work stays small next to the chain.
+// so that the scan stays small next to the chain.  A split runs every chunk
+// twice (the map pass and the chain pass, about 1.8 chunk steps of time
+// against 0.9 unsplit), so it pays from 3 segments on.
 constexpr int64_t kCUs = 256;
 constexpr int64_t kChainWorkgroups = 8;
 constexpr int64_t kMinSegmentChunks = 32;
+constexpr int64_t kMinAutoSegments = 3;
 
 kda_status_t choose_segments(const kda_desc_t *d, Geometry &g) {
     g.segs = 1;
@@ -35,6 +38,7 @@ kda_status_t choose_segments(const kda_desc_t *d, Geometry &g) {
     if (req == 0) {
         want = kCUs / kChainWorkgroups / (g.B * g.H);
         if (want > nc / kMinSegmentChunks) want = nc / kMinSegmentChunks;
+        if (want < kMinAutoSegments) want = 1;
     }
     if (want > nc) want = nc;
     if (want < 2) return KDA_OK;

@@ -84,9 +84,10 @@ typedef struct {
      * sequence form a serial chain; every chunk maps the state entering it
      * affinely, so a long chain can be cut into segments whose maps are
      * computed in parallel and then composed in order (see kda_fwd).
-     *   0  : automatic -- split when the chains alone cannot fill the GPU:
-     *        segments = min(32 / (B * H), chunks / 32) when that is >= 2
-     *        (sized for the 256 CUs of an MI355X, 8 workgroups per chain),
+     *   0  : automatic -- split when the chains alone leave most of the GPU
+     *        idle: segments = min(32 / (B * H), chunks / 32) when that is >= 3
+     *        (sized for the 256 CUs of an MI355X, 8 workgroups per chain; a
+     *        split runs every chunk twice, so 2 segments would gain nothing),
      *        otherwise no split;
      *   1  : never split;
      *   >= 2 : split every sequence into that many segments (at most one per

@@ -103,14 +103,18 @@ def test_workspace_size_monotone(lib):
 
 
 def test_chain_segments_rule(lib):
-    # automatic: split only when the B*H chains (8 workgroups each) leave CUs idle and the
-    # chain is long enough (at least 32 chunks per segment)
+    # automatic: split only when the B*H chains (8 workgroups each) leave most CUs idle (at
+    # least 3 segments) and the chain is long enough (at least 32 chunks per segment)
     assert kda.chain_segments_for(1, 8192, 32) == 1
     assert kda.chain_segments_for(1, 131072, 32) == 1
+    assert kda.chain_segments_for(1, 131072, 16) == 1           # 2 segments would gain nothing
+    assert kda.chain_segments_for(1, 131072, 10) == 3
+    assert kda.chain_segments_for(1, 131072, 8) == 4
     assert kda.chain_segments_for(1, 131072, 4) == 8
     assert kda.chain_segments_for(1, 131072, 1) == 32
     assert kda.chain_segments_for(2, 131072, 1) == 16
-    assert kda.chain_segments_for(1, 4096, 4) == 2
+    assert kda.chain_segments_for(1, 8192, 4) == 4              # 128 chunks: at most 4 segments
+    assert kda.chain_segments_for(1, 4096, 4) == 1              # 64 chunks: 2 segments only
     assert kda.chain_segments_for(1, 1024, 1) == 1
     # forced: equal segments of ceil(chunks / n) chunks, at most one per chunk
     assert kda.chain_segments_for(1, 64 * 40 + 17, 2, 4) == 4   # 41 chunks: 11, 11, 11, 8
