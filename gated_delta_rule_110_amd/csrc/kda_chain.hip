@@ -24,8 +24,8 @@
 //                   slot, loading the chunk's Qg and A_qk into registers just
 //                   before the barrier that hands the fragments over.
 //   wave 2 (loader) copies each chunk's ring operands straight from global
-//                   memory into the ring (global_load_lds, no registers), two
-//                   chunks ahead of the chain.
+//                   memory into the ring (global_load_lds, no registers),
+//                   kSlots - 1 chunks ahead of the chain.
 //   wave 3 (L2)     loads this workgroup's share of the head's cache lines
 //                   kAhead chunks ahead of the chain into the XCD's L2.
 //
@@ -59,23 +59,50 @@ using namespace kda;
 
 namespace {
 
-constexpr int kThreads = 256;        // wave 0: state chain, 1: outputs, 2: LDS loader, 3: L2 prefetch
 #ifndef KDA_CHAIN_AHEAD
 #define KDA_CHAIN_AHEAD 3
 #endif
 constexpr int kAhead = KDA_CHAIN_AHEAD;  // chunks the L2 prefetch runs ahead of the chain (measured: 3 beats 2 and 4-16)
-constexpr int kTouchInFlight = 32;       // L2 prefetch copies allowed in flight (two per chunk): a
-                                         // tighter bound stalls this wave, and the barrier, on HBM latency
-constexpr int kVB = 16;                  // value columns per workgroup
-constexpr int kNVB = kV / kVB;           // workgroups per (sequence, head)
-constexpr int kSlots = 4;                // LDS ring slots for -W / Kbar^T
+constexpr int kTouchInFlight = 32;       // L2 prefetch copies allowed in flight: a tighter bound
+                                         // stalls this wave, and the barrier, on HBM latency
+constexpr int kVB = 16;                  // value columns per chain wave
+constexpr int kBlocks = kV / kVB;        // 16-column blocks per head
+#ifndef KDA_CHAIN_SLOTS
+#define KDA_CHAIN_SLOTS 3
+#endif
+// Chains at which the two-block workgroup is used: when the one-block grid
+// (8 workgroups per chain) would not fit the GPU in one round.
+constexpr int64_t kOneRoundWorkgroups = 256;
 
+// Workgroup shapes; kCB = 16-column blocks of the state per workgroup.
+//   kCB = 1: waves [chain, output, loader, L2 prefetch].
+//   kCB = 2: waves [chain 0, chain 1, output 0, output 1, loader, L2 prefetch].
+// The chain waves share the operand ring, so the head's -W and Kbar^T cross
+// the CU's load path once for 32 columns instead of once per 16.  Output
+// wave o computes the row tiles [kOutTiles o, kOutTiles (o + 1)) of the
+// chunk's outputs for every block of the workgroup, loading only those rows
+// of Qg and A_qk into registers: the two output waves of a two-block
+// workgroup together load Qg and A_qk once.
+template <int kCB>
+struct Shape {
+    static constexpr int kWaves = 2 * kCB + 2;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kNVB = kBlocks / kCB;       // workgroups per (sequence, head)
+    static constexpr int kSlots = KDA_CHAIN_SLOTS;   // operand ring slots
+    static constexpr int kLead = kSlots - 1;         // chunks the ring copies run ahead of the chain
+    static constexpr int kRingFrags = 33 + 2 * kCB;  // -W 16, Kbar^T 16, U 2 per block, exp(G_n) 1
+    static constexpr int kOutTiles = 4 / kCB;        // 16-row output tiles per output wave
+};
+static_assert(KDA_CHAIN_SLOTS >= 2 && KDA_CHAIN_SLOTS <= 3,
+              "vmcnt holds at most 63 outstanding loads: 37 (slots - 2) must fit");
+
+template <int kCB>
 struct __align__(16) ChainSmem {
-    // per slot: -W frags [it*4+kb] (0..15), Kbar^T frags [16 + ct*2+kb] (16..31), this
-    // workgroup's U block (32..33, [it][lane] of 8 bytes), exp(G_n) (34, 128 floats)
-    h8 ring[kSlots][35][64];
-    h8 sS[2][4][64];           // state as fp16 B fragments [slot][k-block][lane]
-    h8 sU[2][2][64];           // pseudo-values as fp16 B fragments
+    // per slot: -W frags [it*4+kb] (0..15), Kbar^T frags [16 + ct*2+kb] (16..31), the
+    // workgroup's U blocks (32 + 2 c .. 33 + 2 c, [it][lane] of 8 bytes), exp(G_n) (32 + 2 kCB, 128 floats)
+    h8 ring[Shape<kCB>::kSlots][Shape<kCB>::kRingFrags][64];
+    h8 sS[2][kCB][4][64];      // state as fp16 B fragments [slot][block][k-block][lane]
+    h8 sU[2][kCB][2][64];      // pseudo-values as fp16 B fragments
     uint32_t dump[2][64];      // landing place of the L2 prefetch copies (never read)
 };
 
@@ -86,55 +113,57 @@ struct OutOps {        // the output wave's operands for one chunk
 
 __device__ __forceinline__ int64_t clamp_chunk(int64_t s, int64_t last) { return s < last ? s : last; }
 
+// Row tiles [kIt0, kIt0 + kNt) of one chunk's Qg and A_qk.
+template <int kIt0, int kNt>
 __device__ __forceinline__ void load_out_ops(OutOps &o, const ChainArgs &a, int64_t ws, int lane) {
     const h8 *Q = reinterpret_cast<const h8 *>(a.Qf + ws * kQfElems) + lane;
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int it = kIt0; it < kIt0 + kNt; ++it)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) o.Q[it][kb] = Q[(it * 4 + kb) * 64];
     const h8 *A = reinterpret_cast<const h8 *>(a.Af + ws * kAfElems) + lane;
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int it = kIt0; it < kIt0 + kNt; ++it)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             if (kb == 0 || it >= 2) o.A[it][kb] = A[(it * 2 + kb) * 64];  // A_qk[i][j] = 0 for j > i
 }
 
-// Copy one chunk's -W and Kbar^T fragments (32 KiB), this workgroup's U block
-// (2 KiB) and exp(G_n) (512 B) straight from global memory into ring slot
-// `slot`, 35 vector-memory instructions with no registers: each lane's 16 bytes
-// land at fragment base + lane * 16, the fragment order of the buffers.
-constexpr int kDmaPerChunk = 35;
-__device__ __forceinline__ void dma_ring(ChainSmem &sm, const ChainArgs &a, int64_t ws, int vb, int slot, int lane) {
+__device__ __forceinline__ void dma16(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+}
+
+// Copy one chunk's -W and Kbar^T fragments (32 KiB), the workgroup's U blocks
+// (2 KiB each) and exp(G_n) (512 B) straight from global memory into ring slot
+// `slot`: kRingFrags vector-memory instructions with no registers; each lane's
+// 16 bytes land at fragment base + lane * 16, the fragment order of the buffers.
+template <int kCB>
+__device__ __forceinline__ void dma_ring(ChainSmem<kCB> &sm, const ChainArgs &a, int64_t ws, int vb, int slot,
+                                         int lane) {
     const h8 *W = reinterpret_cast<const h8 *>(a.Wf + ws * kWfElems) + lane;
     const h8 *K = reinterpret_cast<const h8 *>(a.Kf + ws * kKfElems) + lane;
 #pragma unroll
-    for (int f = 0; f < 16; ++f)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(W + f * 64),
-                                         (__attribute__((address_space(3))) void *)&sm.ring[slot][f][0], 16, 0, 0);
+    for (int f = 0; f < 16; ++f) dma16(W + f * 64, &sm.ring[slot][f][0]);
 #pragma unroll
-    for (int f = 0; f < 16; ++f)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(K + f * 64),
-                                         (__attribute__((address_space(3))) void *)&sm.ring[slot][16 + f][0], 16, 0, 0);
-    const h8 *U = reinterpret_cast<const h8 *>(a.Uf + ws * kUfElems + vb * 4 * 64 * 4) + lane;
+    for (int f = 0; f < 16; ++f) dma16(K + f * 64, &sm.ring[slot][16 + f][0]);
+    const h8 *U = reinterpret_cast<const h8 *>(a.Uf + ws * kUfElems + vb * kCB * 4 * 64 * 4) + lane;
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(U + f * 64),
-                                         (__attribute__((address_space(3))) void *)&sm.ring[slot][32 + f][0], 16, 0, 0);
+    for (int f = 0; f < 2 * kCB; ++f) dma16(U + f * 64, &sm.ring[slot][32 + f][0]);
     if (lane < 32) {
         const h8 *G = reinterpret_cast<const h8 *>(a.gn + ws * kGnElems) + lane;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)G,
-                                         (__attribute__((address_space(3))) void *)&sm.ring[slot][34][0], 16, 0, 0);
+        dma16(G, &sm.ring[slot][32 + 2 * kCB][0]);
     }
 }
 
 // Load this workgroup's share of one chunk's operands so that they are in the
-// XCD's L2 when the other waves load them a few chunks later.  The eight
-// V-block workgroups of a head split the head's cache lines (one dword per
-// 128-byte line).  The loads copy into an LDS area nobody reads: no
-// destination registers, so this wave never has to wait for one except to
-// bound how many are in flight.
-__device__ __forceinline__ void touch_lines(ChainSmem &sm, const ChainArgs &a, int64_t ws, int vb, int lane) {
+// XCD's L2 when the other waves load them a few chunks later.  The V-block
+// workgroups of a head split the head's cache lines: copy j covers the share of
+// 16-column block vb kCB + j (one dword per 128-byte line).  The loads copy
+// into an LDS area nobody reads: no destination registers, so this wave never
+// has to wait for one except to bound how many are in flight.
+template <int kCB>
+__device__ __forceinline__ void touch_lines(ChainSmem<kCB> &sm, const ChainArgs &a, int64_t ws, int vb, int lane) {
     const char *wf = reinterpret_cast<const char *>(a.Wf + ws * kWfElems);
     const char *qf = reinterpret_cast<const char *>(a.Qf + ws * kQfElems);
     const char *kf = reinterpret_cast<const char *>(a.Kf + ws * kKfElems);
@@ -142,16 +171,20 @@ __device__ __forceinline__ void touch_lines(ChainSmem &sm, const ChainArgs &a, i
     const char *uf = reinterpret_cast<const char *>(a.Uf + ws * kUfElems);
     const char *gn = reinterpret_cast<const char *>(a.gn + ws * kGnElems);
     const int l = lane;
-    const char *p0;  // lines 0..63 of the share: W, Qg, Kbar, U
-    if (l < 16) p0 = wf + (16 * vb + l) * 128;
-    else if (l < 32) p0 = qf + (16 * vb + l - 16) * 128;
-    else if (l < 48) p0 = kf + (16 * vb + l - 32) * 128;
-    else p0 = uf + (16 * vb + l - 48) * 128;
-    const char *p1;  // lines 64..72: A_qk and exp(G_n) (lanes >= 8 share one line)
-    if (l < 8) p1 = af + (8 * vb + l) * 128;
-    else p1 = gn + (vb & 3) * 128;
-    lds_copy4(p0, lds_addr(&sm.dump[0][0]));
-    lds_copy4(p1, lds_addr(&sm.dump[1][0]));
+#pragma unroll
+    for (int j = 0; j < kCB; ++j) {
+        const int b = vb * kCB + j;
+        const char *p0;  // lines 0..63 of the share: W, Qg, Kbar, U
+        if (l < 16) p0 = wf + (16 * b + l) * 128;
+        else if (l < 32) p0 = qf + (16 * b + l - 16) * 128;
+        else if (l < 48) p0 = kf + (16 * b + l - 32) * 128;
+        else p0 = uf + (16 * b + l - 48) * 128;
+        const char *p1;  // lines 64..72: A_qk and exp(G_n) (lanes >= 8 share one line)
+        if (l < 8) p1 = af + (8 * b + l) * 128;
+        else p1 = gn + (b & 3) * 128;
+        lds_copy4(p0, lds_addr(&sm.dump[0][0]));
+        lds_copy4(p1, lds_addr(&sm.dump[1][0]));
+    }
 }
 
 // Two accumulator tiles (rows 4g+e of tile 2p and of tile 2p+1) -> one fp16 B
@@ -163,12 +196,13 @@ __device__ __forceinline__ h8 pack_frag(const f4 &t0, const f4 &t1) {
     return r;
 }
 
-// One chunk of the state chain.  S[ct] holds S[16 ct + 4 g + e][16 vb + r];
-// the chunk's -W and Kbar^T fragments are in ring slot `rs`.  With kNoU the
-// chunk's U is taken as zero (the linear part of the chunk map); kHandOver
-// writes the fp16 state and pseudo-values for the output wave.
-template <bool kNoU, bool kHandOver>
-__device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], int rs, int slot, int lane) {
+// One chunk of the state chain for block c of the workgroup.  S[ct] holds
+// S[16 ct + 4 g + e][16 (vb kCB + c) + r]; the chunk's -W and Kbar^T fragments
+// are in ring slot `rs`.  With kNoU the chunk's U is taken as zero (the linear
+// part of the chunk map); kHandOver writes the fp16 state and pseudo-values
+// for the output wave.
+template <int kCB, bool kNoU, bool kHandOver>
+__device__ __forceinline__ void chain_step(ChainSmem<kCB> &sm, f4 (&S)[8], int rs, int slot, int c, int lane) {
     h8 W[16];
 #pragma unroll
     for (int f = 0; f < 16; ++f) W[f] = sm.ring[rs][f][lane];
@@ -176,15 +210,15 @@ __device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], int rs, in
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         Sb[kb] = pack_frag(S[2 * kb], S[2 * kb + 1]);
-        if (kHandOver) sm.sS[slot][kb][lane] = Sb[kb];
+        if (kHandOver) sm.sS[slot][c][kb][lane] = Sb[kb];
     }
-    // Ut = U - W S: X[it] holds Ut[16 it + 4 g + e][16 vb + r]
+    // Ut = U - W S: X[it] holds Ut[16 it + 4 g + e][16 (vb kCB + c) + r]
     f4 X[4];
     if (kNoU) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) X[it] = f4{0, 0, 0, 0};
     } else {
-        const h4 *Ul = reinterpret_cast<const h4 *>(&sm.ring[rs][32][0]) + lane;
+        const h4 *Ul = reinterpret_cast<const h4 *>(&sm.ring[rs][32 + 2 * c][0]) + lane;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const h4 u = Ul[it * 64];
@@ -195,77 +229,107 @@ __device__ __forceinline__ void chain_step(ChainSmem &sm, f4 (&S)[8], int rs, in
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int it = 0; it < 4; ++it) X[it] = mfma16x16x32_f16(W[it * 4 + kb], Sb[kb], X[it]);
-    h8 K[16];   // read while the products above drain (the ring slot is stable until two barriers on)
+    h8 K[16];   // read while the products above drain
 #pragma unroll
     for (int f = 0; f < 16; ++f) K[f] = sm.ring[rs][16 + f][lane];
     h8 Ub[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         Ub[kb] = pack_frag(X[2 * kb], X[2 * kb + 1]);
-        if (kHandOver) sm.sU[slot][kb][lane] = Ub[kb];
+        if (kHandOver) sm.sU[slot][c][kb][lane] = Ub[kb];
     }
-    lds_barrier();
-    // S <- Diag(exp(G_n)) S + Kbar^T Ut;  exp(G_n)[16 ct + 4 g .. + 3] for the lane's rows
-    const f4 *Gl = reinterpret_cast<const f4 *>(&sm.ring[rs][34][0]) + (lane >> 4);
+    // exp(G_n)[16 ct + 4 g .. + 3] for the lane's rows, read before the
+    // barrier: once this wave passes it, the ring slot is free for the loader
+    f4 Gd[8];
+    const f4 *Gl = reinterpret_cast<const f4 *>(&sm.ring[rs][32 + 2 * kCB][0]) + (lane >> 4);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) S[ct] = S[ct] * Gl[4 * ct];
+    for (int ct = 0; ct < 8; ++ct) Gd[ct] = Gl[4 * ct];
+    lds_barrier();
+    // S <- Diag(exp(G_n)) S + Kbar^T Ut
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) S[ct] = S[ct] * Gd[ct];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) S[ct] = mfma16x16x32_f16(K[ct * 2 + kb], Ub[kb], S[ct]);
 }
 
-// Outputs of one chunk, computed transposed so that each lane ends up with four
-// consecutive value columns of one token: O^T = S^T Qg^T + Ut^T A_qk^T.
-__device__ __forceinline__ void out_step(ChainSmem &sm, const OutOps &op, int slot, int lane, float scale,
+// Row tiles [kIt0, kIt0 + kNt) of one chunk's outputs for every block of the
+// workgroup, computed transposed so that each lane ends up with four
+// consecutive value columns of one token: O^T = S^T Qg^T + Ut^T A_qk^T.  The
+// Qg / A_qk rows are already in `op`; the state and pseudo-value fragments of
+// each block come from hand-over slot `slot` after the barrier.
+template <int kCB, int kIt0, int kNt>
+__device__ __forceinline__ void out_step(ChainSmem<kCB> &sm, const OutOps &op, int slot, int lane, float scale,
                                          uint16_t *out_chunk, int64_t row_stride, int64_t rows) {
     lds_barrier();
-    h8 Sb[4], Ub[2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) Sb[kb] = sm.sS[slot][kb][lane];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) Ub[kb] = sm.sU[slot][kb][lane];
-    f4 O[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) O[it] = f4{0, 0, 0, 0};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int it = 0; it < 4; ++it) O[it] = mfma16x16x32_f16(Sb[kb], op.Q[it][kb], O[it]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-            if (kb == 0 || it >= 2) O[it] = mfma16x16x32_f16(Ub[kb], op.A[it][kb], O[it]);
-    // lane (r, g) holds O[16 it + r][16 vb + 4 g + e]
     const int r = lane & 15;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int row = 16 * it + r;
-        if (row < rows) {
-            uint2 pk;
-            pk.x = (uint32_t)f32_to_bf16_bits(scale * O[it][0]) | ((uint32_t)f32_to_bf16_bits(scale * O[it][1]) << 16);
-            pk.y = (uint32_t)f32_to_bf16_bits(scale * O[it][2]) | ((uint32_t)f32_to_bf16_bits(scale * O[it][3]) << 16);
-            *reinterpret_cast<uint2 *>(out_chunk + row * row_stride) = pk;
+    for (int c = 0; c < kCB; ++c) {
+        h8 Sb[4], Ub[2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) Sb[kb] = sm.sS[slot][c][kb][lane];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Ub[kb] = sm.sU[slot][c][kb][lane];
+        f4 O[kNt];
+#pragma unroll
+        for (int j = 0; j < kNt; ++j) O[j] = f4{0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int j = 0; j < kNt; ++j) O[j] = mfma16x16x32_f16(Sb[kb], op.Q[kIt0 + j][kb], O[j]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < kNt; ++j)
+                if (kb == 0 || kIt0 + j >= 2) O[j] = mfma16x16x32_f16(Ub[kb], op.A[kIt0 + j][kb], O[j]);
+        // lane (r, g) holds O[16 it + r][16 (vb kCB + c) + 4 g + e]
+#pragma unroll
+        for (int j = 0; j < kNt; ++j) {
+            const int row = 16 * (kIt0 + j) + r;
+            if (row < rows) {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16_bits(scale * O[j][0]) | ((uint32_t)f32_to_bf16_bits(scale * O[j][1]) << 16);
+                pk.y = (uint32_t)f32_to_bf16_bits(scale * O[j][2]) | ((uint32_t)f32_to_bf16_bits(scale * O[j][3]) << 16);
+                *reinterpret_cast<uint2 *>(out_chunk + row * row_stride + kVB * c) = pk;
+            }
         }
     }
 }
 
-// The chain kernel's body; kMap selects map mode (ChainArgs::map_mode), which
-// is a kernel of its own so that the ordinary chain is compiled without it.
-__shared__ ChainSmem sm;  // each of the two kernels below gets its own
+// The output wave of row tiles [kIt0, kIt0 + kNt).  Qg and A_qk of a chunk are
+// loaded into registers just before the barrier that hands over its state and
+// pseudo-value fragments: the per-CU load path is the bottleneck, and deeper
+// register prefetch (two or three chunks ahead) only adds loads in flight
+// (measured equal or slower).
+template <int kCB, int kIt0, int kNt, typename WsOf>
+__device__ __forceinline__ void out_wave(ChainSmem<kCB> &sm, const ChainArgs &a, WsOf wsof, int64_t nchunks,
+                                         uint16_t *out0, int64_t row_stride, int64_t seqlen, int lane) {
+    OutOps A;
+    lds_barrier();
+    for (int64_t s = 0; s < nchunks; ++s) {
+        load_out_ops<kIt0, kNt>(A, a, wsof(s), lane);
+        out_step<kCB, kIt0, kNt>(sm, A, (int)(s & 1), lane, a.scale, out0 + kChunk * s * row_stride, row_stride,
+                                 seqlen - kChunk * s);
+    }
+}
 
-template <bool kMap>
-__device__ __forceinline__ void chain_body(const ChainArgs &a) {
+// The chain kernel's body; kMap selects map mode (ChainArgs::map_mode, one
+// block per workgroup only), which is a kernel of its own so that the ordinary
+// chain is compiled without it.
+template <bool kMap, int kCB>
+__device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &a) {
+    using Sh = Shape<kCB>;
+    static_assert(!kMap || kCB == 1, "map mode uses one block per workgroup");
 
     const int64_t H = a.H;
     const int64_t NH = a.N * H;
-    // blockIdx -> (chain, V block) with all V blocks of a chain on one XCD
+    // blockIdx -> (chain, V-block workgroup) with all workgroups of a chain on one XCD
     const int64_t x = blockIdx.x;
     const int64_t xcd = x & 7;
     const int64_t sx = x >> 3;
-    const int vb = (int)(sx % kNVB);
-    const int64_t chain = (sx / kNVB) * 8 + xcd;
+    const int vb = (int)(sx % Sh::kNVB);
+    const int64_t chain = (sx / Sh::kNVB) * 8 + xcd;
     if (chain >= NH) return;
     const int64_t n = chain / H, h = chain - (chain / H) * H;
 
@@ -289,35 +353,34 @@ __device__ __forceinline__ void chain_body(const ChainArgs &a) {
     const int r = lane & 15;
     const int g = lane >> 4;
 
-    if (wave == 0 || (kMap && wave == 1)) {
+    if (wave < kCB || (kMap && wave == 1)) {
         // ---- state chain ---------------------------------------------------
         // (map mode: wave 0 carries N from S = 0, wave 1 carries M from S = I
         // with U = 0; both read the same ring)
         const bool linear_part = kMap && wave == 1;
+        const int c = kMap ? 0 : wave;              // block of the workgroup
+        const int col0 = kVB * (vb * kCB + c);      // first value column of the block
         f4 S[8];
-        const int64_t sbase = (n * H + h) * (int64_t)kK * kV + kVB * vb + r;
+        const int64_t sbase = (n * H + h) * (int64_t)kK * kV + col0 + r;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t idx = sbase + (int64_t)(16 * ct + 4 * g + e) * kV;
                 float v = 0.f;
-                if (kMap) v = (linear_part && 16 * ct + 4 * g + e == kVB * vb + r) ? 1.f : 0.f;
+                if (kMap) v = (linear_part && 16 * ct + 4 * g + e == col0 + r) ? 1.f : 0.f;
                 else if (a.h0) v = a.h0_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.h0)[idx])
                                              : reinterpret_cast<const float *>(a.h0)[idx];
                 S[ct][e] = v;
             }
         if (nchunks > 0) {
             lds_barrier();  // ring slot 0 written by the loader
-            if (!kMap) {
-                for (int64_t s = 0; s < nchunks; ++s)
-                    chain_step<false, true>(sm, S, (int)(s & 3), (int)(s & 1), lane);
-            } else if (linear_part) {
-                for (int64_t s = 0; s < nchunks; ++s)
-                    chain_step<true, false>(sm, S, (int)(s & 3), (int)(s & 1), lane);
-            } else {
-                for (int64_t s = 0; s < nchunks; ++s)
-                    chain_step<false, false>(sm, S, (int)(s & 3), (int)(s & 1), lane);
+            int rs = 0;     // ring slot of chunk s
+            for (int64_t s = 0; s < nchunks; ++s) {
+                if (!kMap) chain_step<kCB, false, true>(sm, S, rs, (int)(s & 1), c, lane);
+                else if (linear_part) chain_step<kCB, true, false>(sm, S, rs, (int)(s & 1), c, lane);
+                else chain_step<kCB, false, false>(sm, S, rs, (int)(s & 1), c, lane);
+                rs = rs + 1 == Sh::kSlots ? 0 : rs + 1;
             }
         }
         if (kMap) {
@@ -336,43 +399,41 @@ __device__ __forceinline__ void chain_body(const ChainArgs &a) {
                     else reinterpret_cast<float *>(a.ht)[idx] = S[ct][e];
                 }
         }
-    } else if (wave == 1) {
-        // ---- outputs -------------------------------------------------------
+    } else if (wave < 2 * kCB) {
+        // ---- outputs: row tiles of every block of the workgroup -------------
         if (nchunks > 0) {
             const int64_t row_stride = H * kV;
-            uint16_t *out0 = a.out + (tseq * H + h) * kV + kVB * vb + 4 * g;
-            auto out_at = [&](int64_t s) { return out0 + kChunk * s * row_stride; };
-            // Qg and A_qk of a chunk are loaded just before the barrier that
-            // hands over its fragments: the per-CU load path is the bottleneck, and
-            // deeper register prefetch (two or three chunks ahead) only adds
-            // loads in flight (measured equal or slower)
-            OutOps A;
-            lds_barrier();
-            for (int64_t s = 0; s < nchunks; ++s) {
-                load_out_ops(A, a, wsof(s), lane);
-                out_step(sm, A, (int)(s & 1), lane, a.scale, out_at(s), row_stride, seqlen - kChunk * s);
+            uint16_t *out0 = a.out + (tseq * H + h) * kV + kVB * (vb * kCB) + 4 * g;
+            constexpr int kNt = Sh::kOutTiles;
+            if constexpr (kCB == 1) {
+                out_wave<kCB, 0, kNt>(sm, a, wsof, nchunks, out0, row_stride, seqlen, lane);
+            } else {
+                if (wave == kCB) out_wave<kCB, 0, kNt>(sm, a, wsof, nchunks, out0, row_stride, seqlen, lane);
+                else out_wave<kCB, kNt, kNt>(sm, a, wsof, nchunks, out0, row_stride, seqlen, lane);
             }
         }
-    } else if (wave == 2) {
-        // ---- loader: W / Kbar^T into the LDS ring ---------------------------
-        // Iteration u (between barriers u - 1 and u) starts the copy of chunk
-        // u + 2 into slot (u + 2) % 4 -- the chunk that last used that slot was
-        // read before barrier u - 2 -- then waits for the copy of chunk u + 1
-        // (issued one iteration earlier) so that barrier u publishes it for
-        // chain step u + 1.  This wave issues no other vector-memory loads, and
-        // they complete in order, so "at most kDmaPerChunk outstanding" means
-        // exactly that every copy but those of chunk u + 2 has landed.
+    } else if (wave == 2 * kCB) {
+        // ---- loader: -W / Kbar^T / U / exp(G_n) into the LDS ring -----------
+        // Chunk s sits in slot s % kSlots.  Iteration u (between barriers u - 1
+        // and u) starts the copy of chunk u + kLead into slot (u - 1) % kSlots:
+        // chunk u - 1, which used it last, was read by the chain waves before
+        // barrier u - 1.  It then waits for the copy of chunk u + 1 so that
+        // barrier u publishes it for chain step u + 1.  This wave issues no
+        // other vector-memory loads, and they complete in order, so "at most
+        // kRingFrags (kLead - 1) outstanding" means exactly that every copy of
+        // chunks up to u + 1 has landed.
+        constexpr int kWait = Sh::kRingFrags * (Sh::kLead - 1);
         if (nchunks > 0) {
-            dma_ring(sm, a, wsof(0), vb, 0, lane);
-            dma_ring(sm, a, wsof(1), vb, 1, lane);
-            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaPerChunk) : "memory");
-            lds_barrier();  // ring slot 0 visible to the chain wave
-            for (int64_t s = 0; s < nchunks; s += 4) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t u = s + j;  // s is a multiple of 4
-                    dma_ring(sm, a, wsof(u + 2), vb, (j + 2) & 3, lane);
-                    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaPerChunk) : "memory");
+            for (int j = 0; j < Sh::kLead; ++j) dma_ring<kCB>(sm, a, wsof(j), vb, j, lane);
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
+            lds_barrier();  // ring slot 0 visible to the chain waves
+            for (int64_t s = 0; s < nchunks; s += Sh::kSlots) {
+#pragma unroll
+                for (int j = 0; j < Sh::kSlots; ++j) {
+                    const int64_t u = s + j;  // s is a multiple of kSlots
+                    dma_ring<kCB>(sm, a, wsof(u + Sh::kLead), vb, (j + Sh::kLead) % Sh::kSlots, lane);
+                    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWait) : "memory");
                     if (u < nchunks) lds_barrier();
                 }
             }
@@ -387,7 +448,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs &a) {
             const int64_t nu = nchunks + kAhead - 1;
             bool prologue_done = false;
             for (int64_t u = 0; u < nu; ++u) {
-                touch_lines(sm, a, wsof(u + 1), vb, lane);
+                touch_lines<kCB>(sm, a, wsof(u + 1), vb, lane);
                 asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTouchInFlight) : "memory");
                 if (u >= kAhead - 1) {
                     if (!prologue_done) { lds_barrier(); prologue_done = true; }
@@ -400,8 +461,18 @@ __device__ __forceinline__ void chain_body(const ChainArgs &a) {
     }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void kda_chain_kernel(ChainArgs a) { chain_body<false>(a); }
-__global__ __launch_bounds__(kThreads, 1) void kda_chain_map_kernel(ChainArgs a) { chain_body<true>(a); }
+__global__ __launch_bounds__(Shape<1>::kThreads, 1) void kda_chain_kernel(ChainArgs a) {
+    __shared__ ChainSmem<1> sm;
+    chain_body<false, 1>(sm, a);
+}
+__global__ __launch_bounds__(Shape<2>::kThreads, 1) void kda_chain_x2_kernel(ChainArgs a) {
+    __shared__ ChainSmem<2> sm;
+    chain_body<false, 2>(sm, a);
+}
+__global__ __launch_bounds__(Shape<1>::kThreads, 1) void kda_chain_map_kernel(ChainArgs a) {
+    __shared__ ChainSmem<1> sm;
+    chain_body<true, 1>(sm, a);
+}
 
 // Packed batches: first chunk slot of each sequence, off[n] = sum_{m<n} ceil(len_m / 64).
 __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int64_t *cu, int64_t N, int32_t *off) {
@@ -435,15 +506,25 @@ __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int64_t *cu
 
 }  // namespace
 
+#ifndef KDA_CHAIN_WIDE
+#define KDA_CHAIN_WIDE -1   // -1: by the chain count; 0: never; 1: always (measurement builds)
+#endif
+
 hipError_t kda_launch_chain(const ChainArgs &a, hipStream_t s) {
     const int64_t NH = a.N * a.H;
     if (NH <= 0) return hipSuccess;
-    const int64_t groups = (NH + 7) / 8;
-    const dim3 grid((unsigned)(groups * 8 * kNVB));
+    const int64_t groups = (NH + 7) / 8;  // chains in groups of 8, one per XCD
+    const bool wide = !a.map_mode && (KDA_CHAIN_WIDE == 1 ||
+                                      (KDA_CHAIN_WIDE == -1 && NH * kBlocks > kOneRoundWorkgroups));
     if (a.map_mode)
-        hipLaunchKernelGGL(kda_chain_map_kernel, grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(kda_chain_map_kernel, dim3((unsigned)(groups * 8 * Shape<1>::kNVB)),
+                           dim3(Shape<1>::kThreads), 0, s, a);
+    else if (wide)
+        hipLaunchKernelGGL(kda_chain_x2_kernel, dim3((unsigned)(groups * 8 * Shape<2>::kNVB)),
+                           dim3(Shape<2>::kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(kda_chain_kernel, grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(kda_chain_kernel, dim3((unsigned)(groups * 8 * Shape<1>::kNVB)),
+                           dim3(Shape<1>::kThreads), 0, s, a);
     return hipGetLastError();
 }
 
