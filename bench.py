@@ -45,6 +45,7 @@ INTER_BYTES = (4 * 64 * 128 * 2 + 6 * 1024 + 128 * 4) / 64.0
 KERNEL_BYTES = {
     "kda_intra_kernel": 4 * 256 + 2 + INTER_BYTES,
     "kda_chain_kernel": INTER_BYTES + 256,
+    "kda_chain_x2_kernel": INTER_BYTES + 256,
     # split chains (the map pass, the scan over segments and the chain with outputs, timed
     # together): the intermediates are read twice, once per chain pass
     "split_chain": 2 * INTER_BYTES + 256,
@@ -135,7 +136,8 @@ def write_traffic(pmc_dir: str, workload_name: str) -> dict:
             for r in csv.DictReader(open(f)):
                 name = r["Kernel_Name"]
                 key = None
-                for kn in ("kda_intra_kernel", "kda_chain_kernel", "kda_chunk_table_kernel", "copyBuffer"):
+                for kn in ("kda_intra_kernel", "kda_chain_kernel", "kda_chain_x2_kernel", "kda_chunk_table_kernel",
+                           "copyBuffer"):
                     if kn in name:
                         key = kn
                 if key is None:
@@ -314,7 +316,15 @@ def main(argv=None) -> int:
     path_bytes = BYTES_ALG * tok_heads + state_bytes(w)
     gbs = path_bytes / (ms / 1e3) / 1e9
 
-    chain_key = "split_chain" if segs > 1 else "kda_chain_kernel"
+    # the library runs the chain with two 16-column blocks per workgroup
+    # (kda_chain_x2_kernel) when one block per workgroup would need more than
+    # 256 workgroups (8 per sequence and head)
+    if segs > 1:
+        chain_key = "split_chain"
+    elif w.N * w.H * 8 > 256:
+        chain_key = "kda_chain_x2_kernel"
+    else:
+        chain_key = "kda_chain_kernel"
     kernels = {"kda_intra_kernel": intra_ms, chain_key: chain_ms}
     dom = max(kernels, key=kernels.get)
     dom_bytes = KERNEL_BYTES[dom] * tok_heads

@@ -36,17 +36,21 @@
 // compiler's wait counts never cover a path without it.
 //
 // What bounds a chunk step is the CU's vector-memory path: each workgroup
-// moves about 61 KiB per chunk through it (every V block needs the head's
-// whole W, Kbar, Qg and A_qk), which takes about 1.2 us at the rate one CU
+// moves about 59 KiB per chunk through it (every V block needs the head's
+// whole W, Kbar, Qg and A_qk), which takes about 1.07 us at the rate one CU
 // sustains, longer than the chain wave's own arithmetic.
 //
-// The eight V-block workgroups of a head are placed on one XCD (same
-// blockIdx % 8), so the head's per-chunk operands come from HBM once into that
-// XCD's L2.  The optional initial state seeds S and the final state is
-// written after the last chunk; passing one call's final state as the next
-// call's initial state continues a sequence, which is the multi-turn state
-// carry the forward call exposes ("¿Qué es la atención Kimi Delta…",
-// 7minutos.es).
+// With more than 32 chains, kda_chain_x2_kernel gives each workgroup two
+// 16-column blocks (two chain waves on one operand ring, two output waves with
+// half of the output rows each), so the head's operands cross each CU's load
+// path once per 32 columns; with fewer chains that would leave CUs idle.
+//
+// The V-block workgroups of a head are placed on one XCD (same blockIdx % 8),
+// so the head's per-chunk operands come from HBM once into that XCD's L2.
+// The optional initial state seeds S and the final state is written after
+// the last chunk; passing one call's final state as the next call's initial
+// state continues a sequence, which is the multi-turn state carry the forward
+// call exposes ("¿Qué es la atención Kimi Delta…", 7minutos.es).
 //
 // kda_chain_map_kernel is the same chain without outputs, used to split long
 // chains (kda_segment.hip): it gives every chain its affine map S -> M S + N.
