@@ -70,3 +70,25 @@ def test_prefill_then_decode(state_dtype):
         w.initial_state = w.initial_state.to(torch.bfloat16)  # the oracle sees the same rounded start
     ro, rf = run_oracle(w)
     compare(to_np(out), ro, to_np(st), rf, state_dtype, "prefill+decode %s" % state_dtype)
+
+
+def test_decode_streamed_state_matches_cached():
+    # 128 sequences x 32 heads of fp32 state is 256 MiB: the step streams the state past the
+    # Infinity Cache (non-temporal loads and stores); the same step on a bf16 state of the same
+    # shape (128 MiB) is cached.  Both must match the oracle; in place, the streamed step must
+    # equal the out-of-place one bit for bit.
+    N, H = 128, 32
+    w = W.make("decode_stream", N, 1, H, 5301, lower_bound=-5.0, init="fp32", final="fp32")
+    say("case decode streamed N=%d H=%d (fp32 state %d MiB)" % (N, H, N * H * 64 // 1024))
+    h0 = w.initial_state.to("cuda")
+    out, fin = _decode(w, h0, torch.empty_like(h0))
+    ro, rf = run_oracle(w)
+    compare(to_np(out), ro, to_np(fin), rf, torch.float32, "decode streamed")
+    st = h0.clone()
+    out2, _ = _decode(w, st, st)
+    assert torch.equal(out2, out) and torch.equal(st, fin)
+    wb = W.make("decode_stream", N, 1, H, 5301, lower_bound=-5.0, init="bf16", final="bf16")
+    hb = wb.initial_state.to("cuda")
+    outb, finb = _decode(wb, hb, torch.empty_like(hb))
+    rob, rfb = run_oracle(wb)
+    compare(to_np(outb), rob, to_np(finb), rfb, torch.bfloat16, "decode cached bf16")
