@@ -102,12 +102,28 @@ def cpu_baseline(w, target_s: float = 10.0):
                       "%d repetitions, %d OpenMP threads, %.1f s" % (T_s, w.T, w.H, reps, threads, total)}
 
 
-def source_digest() -> str:
-    """sha256 over the HIP sources, headers and build flags the library is built from."""
+# The files each kernel's code and launch depend on: its own source, the
+# shared header, the host code that sizes and launches it, the public header
+# and the build flags.
+_COMMON_SOURCES = ["kda_common.h", "kda_api.hip", "../../include/kda.h", "../_build.py"]
+KERNEL_SOURCES = {
+    "kda_intra_kernel": ["kda_intra.hip"],
+    "kda_chain_kernel": ["kda_chain.hip"],
+    "kda_chain_x2_kernel": ["kda_chain.hip"],
+    "kda_chunk_table_kernel": ["kda_chain.hip"],
+    "split_chain": ["kda_chain.hip", "kda_segment.hip"],
+}
+
+
+def source_digest(kernel=None) -> str:
+    """sha256 over the HIP sources, headers and build flags the library is built
+    from: all of them, or those ``kernel`` is built and launched from."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_110_amd", "csrc")
-    for name in sorted(os.listdir(csrc)) + ["../../include/kda.h", "../_build.py"]:
+    names = (sorted(os.listdir(csrc)) + ["../../include/kda.h", "../_build.py"] if kernel is None
+             else sorted(KERNEL_SOURCES[kernel]) + _COMMON_SOURCES)
+    for name in names:
         path = os.path.normpath(os.path.join(csrc, name))
         if os.path.isfile(path):
             h.update(name.encode())
@@ -161,6 +177,8 @@ def write_traffic(pmc_dir: str, workload_name: str) -> dict:
         rb = fe[k] * 1024.0 * scale_f
         wb = wr.get(k, 0.0) * 1024.0 * scale_w
         res["kernels"][k] = {"read_bytes": round(rb), "write_bytes": round(wb), "bytes": round(rb + wb)}
+        if k in KERNEL_SOURCES:
+            res["kernels"][k]["source_sha256"] = source_digest(k)
     with open(traffic_path(workload_name), "w") as f:
         json.dump(res, f, indent=1)
     return res
@@ -168,16 +186,16 @@ def write_traffic(pmc_dir: str, workload_name: str) -> dict:
 
 def load_traffic(workload_name: str, kernel: str):
     """HBM bytes per launch of ``kernel`` from the committed counter summary, or
-    None when there is none or the kernel sources changed since it was taken."""
+    None when there is none or the kernel's sources changed since it was taken."""
     path = traffic_path(workload_name)
-    if not os.path.exists(path):
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
         return None
     with open(path) as f:
         tr = json.load(f)
-    if tr.get("source_sha256") != source_digest():
-        return None
     k = tr.get("kernels", {}).get(kernel)
-    return None if k is None else k["bytes"]
+    if k is None or k.get("source_sha256") != source_digest(kernel):
+        return None
+    return k["bytes"]
 
 
 def bench_decode(kda, args, dev, H) -> int:

@@ -66,11 +66,26 @@ def test_traffic_summary_scaling_and_staleness(tmp_path, monkeypatch):
     res = bench.write_traffic(str(pmc), "wl")
     assert res["fetch_scale"] == 2.0 and res["write_scale"] == 1.0
     assert res["kernels"]["kda_intra_kernel"] == {"read_bytes": 200 * 2 * 1024, "write_bytes": 20 * 1024,
-                                                  "bytes": 420 * 1024}
+                                                  "bytes": 420 * 1024,
+                                                  "source_sha256": bench.source_digest("kda_intra_kernel")}
     assert res["kernels"]["kda_chain_kernel"]["bytes"] == (100 + 5) * 1024
-    assert json.loads(out.read_text())["source_sha256"] == bench.source_digest()
+    saved = json.loads(out.read_text())
+    assert saved["source_sha256"] == bench.source_digest()
+    assert saved["kernels"]["kda_chain_kernel"]["source_sha256"] == bench.source_digest("kda_chain_kernel")
     assert bench.load_traffic("wl", "kda_chain_kernel") == 105 * 1024
     assert bench.load_traffic("wl", "kda_chunk_table_kernel") is None
-    # a summary taken from other kernel sources is not used
-    monkeypatch.setattr(bench, "source_digest", lambda: "0" * 64)
+    # a kernel's summary is not used once that kernel's sources change; the others' still are
+    real = bench.source_digest
+    monkeypatch.setattr(bench, "source_digest",
+                        lambda kernel=None: "0" * 64 if kernel == "kda_chain_kernel" else real(kernel))
     assert bench.load_traffic("wl", "kda_chain_kernel") is None
+    assert bench.load_traffic("wl", "kda_intra_kernel") == 420 * 1024
+
+
+def test_kernel_digests_cover_their_sources():
+    # each kernel's digest changes with its own source and the shared files, and only with those
+    for k, files in bench.KERNEL_SOURCES.items():
+        assert "kda_common.h" in bench._COMMON_SOURCES and files
+    assert bench.source_digest("kda_intra_kernel") != bench.source_digest("kda_chain_kernel")
+    assert bench.source_digest("kda_chain_kernel") == bench.source_digest("kda_chain_x2_kernel")
+    assert bench.source_digest("split_chain") != bench.source_digest("kda_chain_kernel")
