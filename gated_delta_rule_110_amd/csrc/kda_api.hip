@@ -74,6 +74,7 @@ WorkspaceLayout make_layout(const Geometry &g) {
     const size_t per = (size_t)g.slots * (size_t)g.H;
     size_t o = 0;
     L.off_chunk_off = o; o = align_up(o + (g.varlen ? sizeof(int32_t) * (size_t)(g.N + 1) : 0), 256);
+    L.off_seq_order = o; o = align_up(o + (g.varlen ? sizeof(int32_t) * (size_t)g.N : 0), 256);
     L.off_Wf = o; o = align_up(o + per * kWfElems * 2, 256);
     L.off_Qf = o; o = align_up(o + per * kQfElems * 2, 256);
     L.off_Kf = o; o = align_up(o + per * kKfElems * 2, 256);
@@ -171,9 +172,10 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
 
     hipEvent_t *ev = desc->phase_events;
     int32_t *chunk_off = geo.varlen ? reinterpret_cast<int32_t *>(ws + lay.off_chunk_off) : nullptr;
+    int32_t *seq_order = geo.varlen ? reinterpret_cast<int32_t *>(ws + lay.off_seq_order) : nullptr;
     hipError_t err = hipSuccess;
     if (ev) err = hipEventRecord(ev[0], stream);
-    if (err == hipSuccess && geo.varlen) err = kda_launch_chunk_table(cu_seqlens, geo.N, chunk_off, stream);
+    if (err == hipSuccess && geo.varlen) err = kda_launch_chunk_table(cu_seqlens, geo.N, chunk_off, seq_order, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[1], stream);
 
     IntraArgs ia{};
@@ -194,7 +196,7 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
 
     ChainArgs ca{};
     ca.Wf = ia.Wf; ca.Qf = ia.Qf; ca.Kf = ia.Kf; ca.Af = ia.Af; ca.Uf = ia.Uf; ca.gn = ia.gn;
-    ca.cu = cu_seqlens; ca.chunk_off = chunk_off;
+    ca.cu = cu_seqlens; ca.chunk_off = chunk_off; ca.seq_order = seq_order;
     ca.T = geo.T; ca.H = geo.H; ca.N = geo.N; ca.nc_fixed = geo.nc_fixed;
     ca.scale = scale;
     ca.h0 = initial_state; ca.ht = final_state;
@@ -209,7 +211,7 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
         float *mapN = reinterpret_cast<float *>(ws + lay.off_mapN);
         float *sin = reinterpret_cast<float *>(ws + lay.off_sin);
         ChainArgs seg = ca;
-        seg.cu = seg_cu; seg.chunk_off = seg_off;
+        seg.cu = seg_cu; seg.chunk_off = seg_off; seg.seq_order = nullptr;
         seg.N = geo.B * geo.segs; seg.nc_fixed = 0;
         if (err == hipSuccess) err = kda_launch_seg_table(geo.B, geo.T, geo.segs, geo.segc, seg_cu, seg_off, stream);
         ChainArgs maps = seg;  // 1. the map of every segment

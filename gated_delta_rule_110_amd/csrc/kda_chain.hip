@@ -335,7 +335,11 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
     const int vb = (int)(sx % Sh::kNVB);
     const int64_t chain = (sx / Sh::kNVB) * 8 + xcd;
     if (chain >= NH) return;
-    const int64_t n = chain / H, h = chain - (chain / H) * H;
+    // packed batches: the i-th sequence in dispatch order (longest first), so
+    // that short chains fill the GPU around the long ones instead of a long
+    // one starting last
+    const int64_t i_seq = chain / H, h = chain - i_seq * H;
+    const int64_t n = a.seq_order ? (int64_t)a.seq_order[i_seq] : i_seq;
 
     int64_t c0, nchunks, tseq, seqlen;
     if (a.cu) {
@@ -478,12 +482,23 @@ __global__ __launch_bounds__(Shape<1>::kThreads, 1) void kda_chain_map_kernel(Ch
     chain_body<true, 1>(sm, a);
 }
 
-// Packed batches: first chunk slot of each sequence, off[n] = sum_{m<n} ceil(len_m / 64).
-__global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int64_t *cu, int64_t N, int32_t *off) {
+// Packed batches: first chunk slot of each sequence, off[n] = sum_{m<n} ceil(len_m / 64),
+// and the order the chain kernel dispatches the sequences in: by chunk count,
+// longest first, to within a factor of two (buckets of floor(log2(chunks)),
+// empty sequences last; the order inside a bucket is arbitrary).  Every chain
+// is computed independently, so the order changes only the schedule.
+__device__ __forceinline__ int chunk_bucket(int64_t cnt) {  // 31 - floor(log2(cnt)); 32 when empty
+    return cnt > 0 ? __clz((int)cnt) : 32;
+}
+
+__global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int64_t *cu, int64_t N, int32_t *off,
+                                                               int32_t *order) {
     __shared__ int64_t part[1024];
     __shared__ int64_t carry;
+    __shared__ int32_t bcount[33];  // sequences per bucket, then the next free position of each
     const int tid = threadIdx.x;
     if (tid == 0) carry = 0;
+    if (tid < 33) bcount[tid] = 0;
     __syncthreads();
     for (int64_t base = 0; base < N; base += 1024) {
         const int64_t n = base + tid;
@@ -500,12 +515,32 @@ __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int64_t *cu
             part[tid] += t;
             __syncthreads();
         }
-        if (n < N) off[n] = (int32_t)(carry + part[tid] - cnt);
+        if (n < N) {
+            off[n] = (int32_t)(carry + part[tid] - cnt);
+            atomicAdd(&bcount[chunk_bucket(cnt)], 1);
+        }
         __syncthreads();
         if (tid == 1023) carry += part[1023];
         __syncthreads();
     }
-    if (tid == 0) off[N] = (int32_t)carry;
+    if (tid == 0) {
+        off[N] = (int32_t)carry;
+        int32_t start = 0;  // buckets in ascending order of 31 - log2: the longest first
+        for (int b = 0; b <= 32; ++b) {
+            const int32_t c = bcount[b];
+            bcount[b] = start;
+            start += c;
+        }
+    }
+    __syncthreads();
+    for (int64_t base = 0; base < N; base += 1024) {
+        const int64_t n = base + tid;
+        if (n < N) {
+            const int64_t len = cu[n + 1] - cu[n];
+            const int64_t cnt = len > 0 ? (len + kChunk - 1) / kChunk : 0;
+            order[atomicAdd(&bcount[chunk_bucket(cnt)], 1)] = (int32_t)n;
+        }
+    }
 }
 
 }  // namespace
@@ -532,7 +567,8 @@ hipError_t kda_launch_chain(const ChainArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t kda_launch_chunk_table(const int64_t *cu, int64_t N, int32_t *chunk_off, hipStream_t s) {
-    hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, s, cu, N, chunk_off);
+hipError_t kda_launch_chunk_table(const int64_t *cu, int64_t N, int32_t *chunk_off, int32_t *seq_order,
+                                  hipStream_t s) {
+    hipLaunchKernelGGL(kda_chunk_table_kernel, dim3(1), dim3(1024), 0, s, cu, N, chunk_off, seq_order);
     return hipGetLastError();
 }

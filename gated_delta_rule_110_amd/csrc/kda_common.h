@@ -57,6 +57,7 @@ struct Geometry {
 
 struct WorkspaceLayout {
     size_t off_chunk_off;  // int32 [N + 1] per-sequence first chunk slot (packed only)
+    size_t off_seq_order;  // int32 [N] sequences in chain dispatch order, longest first (packed only)
     size_t off_Wf, off_Qf, off_Kf, off_Af, off_Uf, off_gn;
     // split chains only: the segments as packed sequences (int64 [B segs + 1]
     // token offsets, int32 [B segs + 1] first chunk slots), the affine map of
@@ -83,6 +84,7 @@ struct ChainArgs {
     const float *gn;
     const int64_t *cu;
     const int32_t *chunk_off;
+    const int32_t *seq_order;  // packed: the order chains are dispatched in (longest first), or nullptr
     int64_t T, H, N, nc_fixed;
     float scale;
     const void *h0;      // initial state [N,H,K,V] or nullptr
@@ -228,7 +230,8 @@ __device__ __forceinline__ int64_t seq_of_slot(const int32_t *off, int64_t N, in
 }  // namespace kda
 
 // Kernel launchers (defined in the .hip files).
-hipError_t kda_launch_chunk_table(const int64_t *cu, int64_t N, int32_t *chunk_off, hipStream_t s);
+hipError_t kda_launch_chunk_table(const int64_t *cu, int64_t N, int32_t *chunk_off, int32_t *seq_order,
+                                  hipStream_t s);
 hipError_t kda_launch_intra(const kda::IntraArgs &a, int64_t slots, hipStream_t s);
 hipError_t kda_launch_chain(const kda::ChainArgs &a, hipStream_t s);
 hipError_t kda_launch_seg_table(int64_t B, int64_t T, int64_t segs, int64_t segc, int64_t *cu, int32_t *off,
