@@ -43,6 +43,7 @@ def _check_split(w, segs, label, expect_segs=None):
     (1, 64 * 7, 1, 7, None, "fp32", 7),              # one chunk per segment, no initial state
     (1, 64 * 5 + 1, 2, 100, "fp32", "fp32", 6),      # more segments asked for than chunks
     (1, 64 * 9, 2, 4, "fp32", None, 3),              # no final state: the scan writes only entering states
+    (2, 64 * 12 + 9, 5, 4, "fp32", "fp32", 4),       # 2 x 5 x 4 = 40 segment chains: the two-block chain pass
 ])
 def test_split_matches_oracle(B, T, H, segs, init, final, expect):
     w = W.make("split", B, T, H, 5000 + T + segs, lower_bound=-5.0, init=init, final=final)
