@@ -115,6 +115,27 @@ KERNEL_SOURCES = {
 }
 
 
+def copy_bandwidth(dev, mib: int = 1024, reps: int = 5) -> float:
+    """Achievable HBM bandwidth: bytes read plus written per second of a plain
+    device-to-device copy of ``mib`` MiB (the median of ``reps`` copies), a
+    second denominator beside the vendor peak."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        dst.copy_(src)
+        t1.record()
+        torch.cuda.synchronize(dev)
+        times.append(t0.elapsed_time(t1))
+    ms = sorted(times)[len(times) // 2]
+    del src, dst
+    return 2 * n / (ms / 1e3) / 1e9
+
+
 def source_digest(kernel=None) -> str:
     """sha256 over the HIP sources, headers and build flags the library is built
     from: all of them, or those ``kernel`` is built and launched from."""
@@ -375,6 +396,7 @@ def main(argv=None) -> int:
         dom_bytes += SPLIT_BYTES_PER_SEGMENT_HEAD * w.B * segs * w.H
     achieved = dom_bytes / (kernels[dom] / 1e3) / 1e9
     traffic = load_traffic(wname, dom)
+    copy_gbs = copy_bandwidth(dev)
 
     result = {
         "metric": "KDA prefill tokens/s and MFMA TFLOP/s (% bf16 peak) at T=8K,H=32,K=V=128",
@@ -403,7 +425,8 @@ def main(argv=None) -> int:
         "kernel_ms_samples": len(evs),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic, "copy_gbs": round(copy_gbs, 1),
+                     "frac_of_copy": round(achieved / copy_gbs, 4)},
         "wall_s": round(wall, 4),
     }
     if not args.no_cpu_baseline:
