@@ -136,9 +136,22 @@ def copy_bandwidth(dev, mib: int = 1024, reps: int = 5) -> float:
     return 2 * n / (ms / 1e3) / 1e9
 
 
+def _code_only(name: str, text: str) -> str:
+    """The code of a source file without its comments and with runs of white
+    space collapsed, so that editing a comment does not change a digest."""
+    import re
+    if name.endswith(".py"):
+        text = re.sub(r"(?m)^\s*#.*$", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
+
+
 def source_digest(kernel=None) -> str:
-    """sha256 over the HIP sources, headers and build flags the library is built
-    from: all of them, or those ``kernel`` is built and launched from."""
+    """sha256 over the code (comments aside) of the HIP sources, headers and
+    build flags the library is built from: all of them, or those ``kernel`` is
+    built and launched from."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_110_amd", "csrc")
@@ -148,8 +161,8 @@ def source_digest(kernel=None) -> str:
         path = os.path.normpath(os.path.join(csrc, name))
         if os.path.isfile(path):
             h.update(name.encode())
-            with open(path, "rb") as f:
-                h.update(f.read())
+            with open(path, encoding="utf-8") as f:
+                h.update(_code_only(name, f.read()).encode())
     return h.hexdigest()
 
 

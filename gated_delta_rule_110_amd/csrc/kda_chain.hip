@@ -18,7 +18,7 @@
 //                   accumulator layout, so two accumulator tiles converted to
 //                   fp16 are directly the B operand of the next product -- no
 //                   LDS round trip sits on the serial path.  It reads -W,
-//                   Kbar^T, its U block and exp(G_n) from a four-slot LDS ring.
+//                   Kbar^T, its U block and exp(G_n) from a three-slot LDS ring.
 //   wave 1 (output) computes O from the fp16 state and pseudo-value fragments
 //                   the chain wave hands over through a double-buffered LDS
 //                   slot, loading the chunk's Qg and A_qk into registers just

@@ -89,3 +89,12 @@ def test_kernel_digests_cover_their_sources():
     assert bench.source_digest("kda_intra_kernel") != bench.source_digest("kda_chain_kernel")
     assert bench.source_digest("kda_chain_kernel") == bench.source_digest("kda_chain_x2_kernel")
     assert bench.source_digest("split_chain") != bench.source_digest("kda_chain_kernel")
+
+
+def test_digest_ignores_comments_only():
+    code = "int f(int x) {  // add one\n  return x + 1; /* done */ }\n"
+    assert bench._code_only("a.hip", code) == bench._code_only("a.hip", code.replace("add one", "increment"))
+    assert bench._code_only("a.hip", code) != bench._code_only("a.hip", code.replace("x + 1", "x + 2"))
+    py = "# flags\nFLAGS = ['-O3']  \n"
+    assert bench._code_only("b.py", py) == bench._code_only("b.py", "# other words\nFLAGS = ['-O3']\n")
+    assert bench._code_only("b.py", py) != bench._code_only("b.py", "FLAGS = ['-O2']\n")
