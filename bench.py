@@ -112,7 +112,12 @@ KERNEL_SOURCES = {
     "kda_chain_x2_kernel": ["kda_chain.hip"],
     "kda_chunk_table_kernel": ["kda_chain.hip"],
     "split_chain": ["kda_chain.hip", "kda_segment.hip"],
+    "kda_decode_kernel": ["kda_decode.hip"],
+    "kda_decode_stream_kernel": ["kda_decode.hip"],
 }
+# States of this many bytes or more are streamed past the Infinity Cache by
+# kda_decode_stream_kernel (the library's rule, mirrored to name the kernel).
+DECODE_STREAM_STATE_BYTES = 256 << 20
 
 
 def copy_bandwidth(dev, mib: int = 1024, reps: int = 5) -> float:
@@ -188,7 +193,7 @@ def write_traffic(pmc_dir: str, workload_name: str) -> dict:
                 name = r["Kernel_Name"]
                 key = None
                 for kn in ("kda_intra_kernel", "kda_chain_kernel", "kda_chain_x2_kernel", "kda_chunk_table_kernel",
-                           "copyBuffer"):
+                           "kda_decode_kernel", "kda_decode_stream_kernel", "copyBuffer"):
                     if kn in name:
                         key = kn
                 if key is None:
@@ -232,13 +237,17 @@ def load_traffic(workload_name: str, kernel: str):
     return k["bytes"]
 
 
+def decode_name(N: int, H: int) -> str:
+    return "decode_N%d_H%d" % (N, H)
+
+
 def bench_decode(kda, args, dev, H) -> int:
     """Decode step: N sequences x H heads, one token each, fp32 state in place,
     timed as K steps replayed from a HIP graph (eager launches reported beside).
     Algorithmic HBM bytes per step: the state read and written (2 x 64 KiB per
     head) plus q, k, v, g (4 x 256 B), beta (2 B) and out (256 B) per head."""
     N = args.decode
-    w = W.make("decode_N%d_H%d" % (N, H), N, 1, H, 6000 + N, lower_bound=-5.0, init="fp32", final="fp32").to(dev)
+    w = W.make(decode_name(N, H), N, 1, H, 6000 + N, lower_bound=-5.0, init="fp32", final="fp32").to(dev)
     st = w.initial_state.clone()
     out = torch.empty((N, 1, H, 128), dtype=torch.bfloat16, device=dev)
 
@@ -271,6 +280,8 @@ def bench_decode(kda, args, dev, H) -> int:
     ms = t0.elapsed_time(t1) / args.steps
     nbytes = N * H * (2 * 128 * 128 * 4 + 4 * 256 + 2 + 256)
     gbs = nbytes / (ms / 1e3) / 1e9
+    kernel = ("kda_decode_stream_kernel" if N * H * 128 * 128 * 4 >= DECODE_STREAM_STATE_BYTES
+              else "kda_decode_kernel")
     print(json.dumps({"metric": "KDA decode tokens/s (one token per sequence, fp32 state in place)",
                       "value": round(N / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
                       "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
@@ -278,9 +289,9 @@ def bench_decode(kda, args, dev, H) -> int:
                       "config": {"workload": "decode", "N": N, "H": H, "K": 128, "V": 128,
                                  "launch": "hip_graph of the timed steps"},
                       "eager_us_per_step": round(eager_ms * 1e3, 2),
-                      "roofline": {"kernel": "kda_decode_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                      "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1),
                                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                   "traffic": None}}), flush=True)
+                                   "traffic": load_traffic(decode_name(N, H), kernel)}}), flush=True)
     return 0
 
 
@@ -312,6 +323,9 @@ def main(argv=None) -> int:
         return 2
 
     wname = W.CONFIG_NAMES[int(args.workload)] if args.workload.isdigit() else args.workload
+    decode_H = W.by_name(wname).H if args.decode else 0
+    if args.decode:
+        wname = decode_name(args.decode, decode_H)
     if args.traffic_from:
         print(json.dumps(write_traffic(args.traffic_from, wname)))
         return 0
@@ -332,7 +346,7 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.decode:
-        return bench_decode(kda, args, dev, W.by_name(wname).H)
+        return bench_decode(kda, args, dev, decode_H)
     w_host = W.by_name(wname)
     w = w_host.to(dev)
     out = torch.empty((w.B, w.T, w.H, w.V), dtype=torch.bfloat16, device=dev)
