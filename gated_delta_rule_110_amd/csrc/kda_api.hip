@@ -5,6 +5,8 @@
 // contiguity / same-device requirements follow "性能与注意事项"
 // (zuobiaodaohang.com FlashKDA page).
 #include <math.h>
+#include <stdlib.h>
+#include <vector>
 #include "kda_common.h"
 #include "kda.h"
 
@@ -94,6 +96,26 @@ WorkspaceLayout make_layout(const Geometry &g) {
     return L;
 }
 
+// With KDA_VALIDATE=1 in the environment, kda_fwd reads cu_seqlens back to the
+// host (synchronising `stream`) and refuses contents that would send the
+// kernels outside the token tensors.  Off by default: it costs a device
+// round trip and cannot be captured in a graph.
+bool validate_requested() {
+    const char *e = getenv("KDA_VALIDATE");
+    return e && e[0] == '1' && e[1] == 0;
+}
+
+kda_status_t validate_cu_seqlens(const int64_t *cu, int64_t N, int64_t T, hipStream_t stream) {
+    std::vector<int64_t> h((size_t)N + 1);
+    if (hipMemcpyAsync(h.data(), cu, sizeof(int64_t) * (size_t)(N + 1), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (h[0] != 0 || h[(size_t)N] != T) return KDA_ERR_SHAPE;
+    for (int64_t n = 0; n < N; ++n)
+        if (h[(size_t)n + 1] < h[(size_t)n]) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc) {
@@ -157,6 +179,10 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
         (cu_seqlens && !aligned(cu_seqlens, 8)) ||
         (initial_state && !aligned(initial_state, 4)) || (final_state && !aligned(final_state, 4)))
         return KDA_ERR_ALIGN;
+    if (cu_seqlens && validate_requested()) {
+        st = validate_cu_seqlens(cu_seqlens, geo.N, geo.T, stream);
+        if (st != KDA_OK) return st;
+    }
     const WorkspaceLayout lay = make_layout(geo);
     char *ws = static_cast<char *>(desc->workspace);
     bool owned = false;

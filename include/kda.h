@@ -125,7 +125,12 @@ int64_t kda_fwd_chain_segments(const kda_desc_t *desc);
  *                      It may alias initial_state when both dtypes match.
  *   cu_seqlens       : device int64 [N + 1] cumulative lengths, or NULL.  Its
  *                      contents must satisfy cu[0] = 0, cu[n] <= cu[n+1],
- *                      cu[N] = T; they are not validated (no host sync).
+ *                      cu[N] = T.  They are trusted (no host sync) unless the
+ *                      environment has KDA_VALIDATE=1: then kda_fwd copies them
+ *                      to the host, synchronising `stream`, and returns
+ *                      KDA_ERR_SHAPE for contents that break these rules,
+ *                      before anything is allocated or launched (a debugging
+ *                      aid; such a call cannot be captured in a graph).
  *                      Empty sequences are allowed: their final state is their
  *                      initial state.
  *   out              : bf16 [B, T, H, V], caller-allocated, must not alias inputs.
