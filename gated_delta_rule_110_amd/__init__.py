@@ -24,7 +24,7 @@ import torch
 from ._build import LIB as LIB_PATH
 from ._build import build
 
-__all__ = ["fwd", "decode", "workspace_size", "chain_segments_for", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
+__all__ = ["fwd", "decode", "workspace_size", "chain_segments_for", "KdaArgumentError", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
            "KDA_FP32"]
 
 KDA_BF16 = 1
@@ -37,9 +37,24 @@ _STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR
 
 
 class KdaError(RuntimeError):
+    """A non-OK status from libkda; ``status`` holds the kda_status_t code."""
+
     def __init__(self, status: int, message: str):
         super().__init__("%s (%d): %s" % (_STATUS_NAMES.get(status, "?"), status, message))
         self.status = status
+
+
+class KdaArgumentError(KdaError, ValueError):
+    """A status the library returns for its arguments before launching anything
+    (every status but KDA_ERR_HIP); also a ValueError."""
+
+
+KDA_ERR_HIP = 8
+
+
+def _raise_status(lib, st: int):
+    msg = lib.kda_status_string(st).decode()
+    raise (KdaError if st == KDA_ERR_HIP else KdaArgumentError)(st, msg)
 
 
 class KdaDesc(ctypes.Structure):
@@ -190,7 +205,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
                          _ptr(final_state), _ptr(cu_seqlens), _ptr(out), ctypes.byref(d),
                          ctypes.c_void_p(stream))
     if st != 0:
-        raise KdaError(st, lib.kda_status_string(st).decode())
+        _raise_status(lib, st)
     return out, final_state
 
 
@@ -246,5 +261,5 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
                             _ptr(dt_bias), float(lower_bound), _ptr(initial_state), _ptr(final_state),
                             _ptr(out), ctypes.byref(d), ctypes.c_void_p(stream))
     if st != 0:
-        raise KdaError(st, lib.kda_status_string(st).decode())
+        _raise_status(lib, st)
     return out, final_state

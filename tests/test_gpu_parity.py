@@ -190,6 +190,7 @@ def test_abi_errors_on_device():
     with pytest.raises(kda.KdaError) as e:
         kda.fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, None, w.A_log, w.dt_bias, -6.0)
     assert e.value.status == 4
+    assert isinstance(e.value, ValueError) and isinstance(e.value, kda.KdaArgumentError)
     with pytest.raises(kda.KdaError) as e:
         kda.fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, None, w.A_log, w.dt_bias, 0.5)
     assert e.value.status == 4

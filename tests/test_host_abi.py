@@ -173,3 +173,14 @@ def test_python_decode_rejects_bad_shapes():
     with pytest.raises(ValueError):
         kda.decode(x, x, x, x, torch.zeros((2, 2, 3), dtype=torch.bfloat16), 0.1, None,
                    torch.zeros(3), torch.zeros(3, 128), -5.0)
+
+
+def test_python_status_errors():
+    # argument statuses are ValueErrors (and KdaErrors); a HIP launch error is a RuntimeError only
+    lib = kda.library()
+    with pytest.raises(ValueError) as e:
+        kda._raise_status(lib, 4)
+    assert isinstance(e.value, kda.KdaArgumentError) and e.value.status == 4
+    with pytest.raises(kda.KdaError) as e:
+        kda._raise_status(lib, kda.KDA_ERR_HIP)
+    assert not isinstance(e.value, ValueError) and isinstance(e.value, RuntimeError)
