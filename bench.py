@@ -102,16 +102,16 @@ def cpu_baseline(w, target_s: float = 10.0):
                       "%d repetitions, %d OpenMP threads, %.1f s" % (T_s, w.T, w.H, reps, threads, total)}
 
 
-# The files each kernel's code and launch depend on: its own source, the
-# shared header, the host code that sizes and launches it, the public header
-# and the build flags.
-_COMMON_SOURCES = ["kda_common.h", "kda_api.hip", "../../include/kda.h", "../_build.py"]
+# The files each kernel's code and launch depend on: its own source (which
+# holds its launcher and grid), the shared header, the public header and the
+# build flags; for split chains also kda_api.hip, which chooses the segments.
+_COMMON_SOURCES = ["kda_common.h", "../../include/kda.h", "../_build.py"]
 KERNEL_SOURCES = {
     "kda_intra_kernel": ["kda_intra.hip"],
     "kda_chain_kernel": ["kda_chain.hip"],
     "kda_chain_x2_kernel": ["kda_chain.hip"],
     "kda_chunk_table_kernel": ["kda_chain.hip"],
-    "split_chain": ["kda_chain.hip", "kda_segment.hip"],
+    "split_chain": ["kda_chain.hip", "kda_segment.hip", "kda_api.hip"],
     "kda_decode_kernel": ["kda_decode.hip"],
     "kda_decode_stream_kernel": ["kda_decode.hip"],
 }
