@@ -60,3 +60,39 @@ def test_graph_replays_match_eager(case):
         assert torch.equal(out, out_e), (case, rep)
         assert torch.equal(fin, fin_e), (case, rep)
         say("  replay %d equals eager" % rep)
+
+
+@pytest.mark.parametrize("N", [4, 128])   # 128 x 32 heads of fp32 state: the streamed decode kernel
+def test_decode_graph_replays_match_eager(N):
+    # three in-place decode steps captured once; each replay continues the state, and must equal
+    # three more eager steps from the same state, bit for bit
+    H, steps = (3, 3) if N == 4 else (32, 3)
+    w = W.make("graph-decode", N, steps, H, 6100 + N, lower_bound=-5.0, init="fp32", final="fp32")
+    say("case graph decode: N=%d H=%d, %d steps per replay" % (N, H, steps))
+    wd = w.to("cuda")
+    toks = [[t[:, s:s + 1].contiguous() for t in (wd.q, wd.k, wd.v, wd.g, wd.beta)] for s in range(steps)]
+    outs_g = [torch.empty((N, 1, H, 128), dtype=torch.bfloat16, device="cuda") for _ in range(steps)]
+
+    def run(st, outs):
+        for s in range(steps):
+            kda.decode(*toks[s], w.scale, outs[s], wd.A_log, wd.dt_bias, w.lower_bound, st, st)
+
+    st_g = wd.initial_state.clone()
+    graph = torch.cuda.CUDAGraph()
+    warm = st_g.clone()
+    run(warm, [torch.empty_like(o) for o in outs_g])  # warm-up outside the capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run(st_g, outs_g)
+    st_e = wd.initial_state.clone()
+    st_g.copy_(wd.initial_state)
+    for rep in range(3):
+        outs_e = [torch.empty_like(o) for o in outs_g]
+        run(st_e, outs_e)          # eager: the next three steps
+        torch.cuda.synchronize()
+        graph.replay()             # the same three steps from the graph's own state
+        torch.cuda.synchronize()
+        same = torch.equal(st_g, st_e) and all(torch.equal(a.view(torch.int16), b.view(torch.int16))
+                                               for a, b in zip(outs_g, outs_e))
+        say("  replay %d equal to eager: %s" % (rep, same))
+        assert same
