@@ -122,17 +122,19 @@ DECODE_STREAM_STATE_BYTES = 256 << 20
 
 def copy_bandwidth(dev, mib: int = 1024, reps: int = 5) -> float:
     """Achievable HBM bandwidth: bytes read plus written per second of a plain
-    device-to-device copy of ``mib`` MiB (the median of ``reps`` copies), a
-    second denominator beside the vendor peak."""
+    streaming copy of ``mib`` MiB (the median of ``reps``), a second
+    denominator beside the vendor peak.  The copy is torch's elementwise
+    kernel (dst = src * 1 in fp32), which streams faster than the runtime's
+    blit behind ``copy_`` (about 6.1 against 5.1 TB/s)."""
     n = mib << 20
-    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    dst.copy_(src)
+    torch.mul(src, 1.0, out=dst)
     times = []
     for _ in range(reps):
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         t1.record()
         torch.cuda.synchronize(dev)
         times.append(t0.elapsed_time(t1))
