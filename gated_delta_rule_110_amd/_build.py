@@ -31,7 +31,11 @@ def hipcc() -> str:
 # Per-source additions.  The state chain keeps its MFMA accumulators in
 # ordinary VGPRs: the state update multiplies them by the decay every chunk, and
 # accumulator-register copies around that multiply would sit on the serial path.
-EXTRA_FLAGS = {"kda_chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# The intra-chunk kernel is scheduled for instruction-level parallelism (it
+# runs two workgroups per CU and spends much of each one's life on dependent
+# chains): 1.2% faster than the default scheduler over 10 paired runs.
+EXTRA_FLAGS = {"kda_chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "kda_intra.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _run(cmd, verbose):
