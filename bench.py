@@ -114,10 +114,26 @@ KERNEL_SOURCES = {
     "split_chain": ["kda_chain.hip", "kda_segment.hip", "kda_api.hip"],
     "kda_decode_kernel": ["kda_decode.hip"],
     "kda_decode_stream_kernel": ["kda_decode.hip"],
+    "kda_decode_split2_kernel": ["kda_decode.hip"],
+    "kda_decode_split4_kernel": ["kda_decode.hip"],
 }
-# States of this many bytes or more are streamed past the Infinity Cache by
-# kda_decode_stream_kernel (the library's rule, mirrored to name the kernel).
+# The library's choice of decode kernel, mirrored to name it: states of this
+# many bytes or more are streamed past the Infinity Cache; otherwise each head
+# is spread over 4 column slices while that makes at most 512 workgroups, over
+# 2 slices up to 1024, else one workgroup per (sequence, head).
 DECODE_STREAM_STATE_BYTES = 256 << 20
+DECODE_SPLIT_WORKGROUPS = 512
+
+
+def decode_kernel_name(N: int, H: int) -> str:
+    units = N * H
+    if units * 128 * 128 * 4 >= DECODE_STREAM_STATE_BYTES:
+        return "kda_decode_stream_kernel"
+    if units * 4 <= DECODE_SPLIT_WORKGROUPS:
+        return "kda_decode_split4_kernel"
+    if units * 2 <= 2 * DECODE_SPLIT_WORKGROUPS:
+        return "kda_decode_split2_kernel"
+    return "kda_decode_kernel"
 
 
 def copy_bandwidth(dev, mib: int = 1024, reps: int = 5) -> float:
@@ -195,7 +211,8 @@ def write_traffic(pmc_dir: str, workload_name: str) -> dict:
                 name = r["Kernel_Name"]
                 key = None
                 for kn in ("kda_intra_kernel", "kda_chain_kernel", "kda_chain_x2_kernel", "kda_chunk_table_kernel",
-                           "kda_decode_kernel", "kda_decode_stream_kernel", "copyBuffer"):
+                           "kda_decode_kernel", "kda_decode_stream_kernel", "kda_decode_split2_kernel",
+                           "kda_decode_split4_kernel", "copyBuffer"):
                     if kn in name:
                         key = kn
                 if key is None:
@@ -282,8 +299,7 @@ def bench_decode(kda, args, dev, H) -> int:
     ms = t0.elapsed_time(t1) / args.steps
     nbytes = N * H * (2 * 128 * 128 * 4 + 4 * 256 + 2 + 256)
     gbs = nbytes / (ms / 1e3) / 1e9
-    kernel = ("kda_decode_stream_kernel" if N * H * 128 * 128 * 4 >= DECODE_STREAM_STATE_BYTES
-              else "kda_decode_kernel")
+    kernel = decode_kernel_name(N, H)
     print(json.dumps({"metric": "KDA decode tokens/s (one token per sequence, fp32 state in place)",
                       "value": round(N / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
                       "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,

@@ -98,3 +98,12 @@ def test_digest_ignores_comments_only():
     py = "# flags\nFLAGS = ['-O3']  \n"
     assert bench._code_only("b.py", py) == bench._code_only("b.py", "# other words\nFLAGS = ['-O3']\n")
     assert bench._code_only("b.py", py) != bench._code_only("b.py", "FLAGS = ['-O2']\n")
+
+
+def test_decode_kernel_names():
+    # mirrors the library's rule: streamed from 256 MiB of fp32 state, then 4, 2 or 1 column slices
+    assert bench.decode_kernel_name(1, 32) == "kda_decode_split4_kernel"
+    assert bench.decode_kernel_name(4, 32) == "kda_decode_split4_kernel"
+    assert bench.decode_kernel_name(16, 32) == "kda_decode_split2_kernel"
+    assert bench.decode_kernel_name(32, 32) == "kda_decode_kernel"
+    assert bench.decode_kernel_name(128, 32) == "kda_decode_stream_kernel"

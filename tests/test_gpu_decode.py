@@ -19,8 +19,10 @@ def _decode(w, initial, final, dev="cuda"):
     return out, fin
 
 
+# (sequence, head) counts: up to 128 -> 4 column slices per head, up to 512 -> 2, above -> 1
 @pytest.mark.parametrize("N,H,init,final", [(5, 6, "fp32", "fp32"), (3, 4, "bf16", "bf16"),
-                                            (4, 2, None, "fp32"), (64, 32, "fp32", "fp32")])
+                                            (4, 2, None, "fp32"), (16, 16, "fp32", "bf16"),
+                                            (64, 32, "fp32", "fp32")])
 def test_decode_vs_oracle(N, H, init, final):
     w = W.make("decode", N, 1, H, 5000 + N * H, lower_bound=-4.0, init=init, final=final)
     say("case decode N=%d H=%d init=%s final=%s" % (N, H, init, final))
