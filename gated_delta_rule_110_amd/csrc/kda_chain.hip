@@ -333,7 +333,7 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
     const int64_t xcd = x & 7;
     const int64_t sx = x >> 3;
     const int vb = (int)(sx % Sh::kNVB);
-    const int64_t chain = (sx / Sh::kNVB) * 8 + xcd;
+    const int64_t chain = a.chain_base + (sx / Sh::kNVB) * 8 + xcd;
     if (chain >= NH) return;
     // packed batches: the i-th sequence in dispatch order (longest first), so
     // that short chains fill the GPU around the long ones instead of a long
@@ -549,22 +549,36 @@ __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int64_t *cu
 #define KDA_CHAIN_WIDE -1   // -1: by the chain count; 0: never; 1: always (measurement builds)
 #endif
 
+// Chains per launch are capped so that a launch stays within 2^30 work-items
+// (a dispatch's grid is counted in 32-bit work-items per dimension): 65536
+// groups of 8 chains, at 8 x 256 or 4 x 384 threads per chain.  Bigger
+// batches (over half a million (sequence, head) chains) take several launches.
+constexpr int64_t kMaxGroupsPerLaunch = 65536;
+
 hipError_t kda_launch_chain(const ChainArgs &a, hipStream_t s) {
     const int64_t NH = a.N * a.H;
     if (NH <= 0) return hipSuccess;
     const int64_t groups = (NH + 7) / 8;  // chains in groups of 8, one per XCD
     const bool wide = !a.map_mode && (KDA_CHAIN_WIDE == 1 ||
                                       (KDA_CHAIN_WIDE == -1 && NH * kBlocks > kOneRoundWorkgroups));
-    if (a.map_mode)
-        hipLaunchKernelGGL(kda_chain_map_kernel, dim3((unsigned)(groups * 8 * Shape<1>::kNVB)),
-                           dim3(Shape<1>::kThreads), 0, s, a);
-    else if (wide)
-        hipLaunchKernelGGL(kda_chain_x2_kernel, dim3((unsigned)(groups * 8 * Shape<2>::kNVB)),
-                           dim3(Shape<2>::kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(kda_chain_kernel, dim3((unsigned)(groups * 8 * Shape<1>::kNVB)),
-                           dim3(Shape<1>::kThreads), 0, s, a);
-    return hipGetLastError();
+    const int64_t piece = launch_piece(kMaxGroupsPerLaunch);
+    for (int64_t g0 = 0; g0 < groups; g0 += piece) {
+        const int64_t ng = groups - g0 < piece ? groups - g0 : piece;
+        ChainArgs b = a;
+        b.chain_base = 8 * g0;
+        if (a.map_mode)
+            hipLaunchKernelGGL(kda_chain_map_kernel, dim3((unsigned)(ng * 8 * Shape<1>::kNVB)),
+                               dim3(Shape<1>::kThreads), 0, s, b);
+        else if (wide)
+            hipLaunchKernelGGL(kda_chain_x2_kernel, dim3((unsigned)(ng * 8 * Shape<2>::kNVB)),
+                               dim3(Shape<2>::kThreads), 0, s, b);
+        else
+            hipLaunchKernelGGL(kda_chain_kernel, dim3((unsigned)(ng * 8 * Shape<1>::kNVB)),
+                               dim3(Shape<1>::kThreads), 0, s, b);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t kda_launch_chunk_table(const int64_t *cu, int64_t N, int32_t *chunk_off, int32_t *seq_order,

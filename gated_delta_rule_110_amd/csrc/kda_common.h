@@ -3,6 +3,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace kda {
 
@@ -77,6 +78,7 @@ struct IntraArgs {
     _Float16 *Wf, *Qf, *Kf, *Af, *Uf;
     float *gn;
     int heads_fast;             // grid (H, slots) rather than (slots, H); set by the launcher
+    int64_t slot_base;          // first chunk slot of this launch; set by the launcher
 };
 
 struct ChainArgs {
@@ -97,6 +99,7 @@ struct ChainArgs {
     // offset and the linear part of the chain's affine map S -> M S + N.
     int map_mode;
     float *mapM, *mapN;
+    int64_t chain_base;  // first chain (in dispatch order) of this launch; set by the launcher
 };
 
 // The sequential pass over the segments of split chains: for batch row b and
@@ -121,6 +124,7 @@ struct DecodeArgs {
     void *ht;            // state out [N,H,K,V] or nullptr; may alias h0
     int h0_bf16, ht_bf16;
     uint16_t *out;       // [N,H,V] bf16
+    int64_t unit_base;   // first (sequence, head) of this launch; set by the launcher
 };
 
 // ---- small numeric helpers --------------------------------------------------
@@ -225,6 +229,18 @@ __device__ __forceinline__ int64_t seq_of_slot(const int32_t *off, int64_t N, in
         if (off[mid] <= slot) lo = mid; else hi = mid;
     }
     return lo;
+}
+
+// Largest grid piece (chains, chunk slots or decode units) one launch may
+// cover: `dflt`, or the positive value of the environment variable
+// KDA_LAUNCH_PIECE when it is set.  The defaults keep every launch within
+// 2^30 work-items, so only very large batches take several launches; the
+// variable makes small inputs take that path too, so that it can be tested.
+inline int64_t launch_piece(int64_t dflt, bool *forced = nullptr) {
+    const char *e = getenv("KDA_LAUNCH_PIECE");
+    const long long v = e ? atoll(e) : 0;
+    if (forced) *forced = v > 0;
+    return v > 0 && v < dflt ? (int64_t)v : dflt;
 }
 
 }  // namespace kda

@@ -83,8 +83,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a) {
     constexpr int kRows = kK / kGroups;         // rows per thread
     static_assert(kGroups * kCols * 2 <= 8 * kV, "partial sums must fit");
     __shared__ DecodeSmem sm;
-    const int64_t unit = blockIdx.x / kS;
-    const int slice = (int)(blockIdx.x - unit * kS);
+    const int64_t local = blockIdx.x / kS;
+    const int slice = (int)(blockIdx.x - local * kS);
+    const int64_t unit = a.unit_base + local;
     const int64_t n = unit / a.H, h = unit - (unit / a.H) * a.H;
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63;
@@ -199,17 +200,38 @@ __global__ __launch_bounds__(kThreads) void kda_decode_split4_kernel(DecodeArgs 
 
 }  // namespace
 
+// (sequence, head) units per launch of the one-slice kernels: at most 2^22
+// workgroups of 256 threads, i.e. 2^30 work-items (a dispatch's grid is
+// counted in 32-bit work-items per dimension).  The sliced kernels are only
+// used for at most 1024 workgroups.
+constexpr int64_t kMaxUnitsPerLaunch = int64_t(1) << 22;
+
 hipError_t kda_launch_decode(const DecodeArgs &a, hipStream_t s) {
     const int64_t units = a.N * a.H;
     if (units <= 0) return hipSuccess;
+    DecodeArgs b = a;
+    b.unit_base = 0;
     const int64_t elt = (a.h0 && !a.h0_bf16) || (a.ht && !a.ht_bf16) ? 4 : 2;
-    if (units * kK * kV * elt >= kStreamStateBytes)
-        hipLaunchKernelGGL(kda_decode_stream_kernel, dim3((unsigned)units), dim3(kThreads), 0, s, a);
-    else if (units * 4 <= kSplitWorkgroups)
-        hipLaunchKernelGGL(kda_decode_split4_kernel, dim3((unsigned)(units * 4)), dim3(kThreads), 0, s, a);
-    else if (units * 2 <= 2 * kSplitWorkgroups)
-        hipLaunchKernelGGL(kda_decode_split2_kernel, dim3((unsigned)(units * 2)), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(kda_decode_kernel, dim3((unsigned)units), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    const bool stream = units * kK * kV * elt >= kStreamStateBytes;
+    bool forced = false;
+    const int64_t piece = launch_piece(kMaxUnitsPerLaunch, &forced);
+    if (!stream && !forced && units * 4 <= kSplitWorkgroups) {
+        hipLaunchKernelGGL(kda_decode_split4_kernel, dim3((unsigned)(units * 4)), dim3(kThreads), 0, s, b);
+        return hipGetLastError();
+    }
+    if (!stream && !forced && units * 2 <= 2 * kSplitWorkgroups) {
+        hipLaunchKernelGGL(kda_decode_split2_kernel, dim3((unsigned)(units * 2)), dim3(kThreads), 0, s, b);
+        return hipGetLastError();
+    }
+    for (int64_t u0 = 0; u0 < units; u0 += piece) {
+        const int64_t nu = units - u0 < piece ? units - u0 : piece;
+        b.unit_base = u0;
+        if (stream)
+            hipLaunchKernelGGL(kda_decode_stream_kernel, dim3((unsigned)nu), dim3(kThreads), 0, s, b);
+        else
+            hipLaunchKernelGGL(kda_decode_kernel, dim3((unsigned)nu), dim3(kThreads), 0, s, b);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }

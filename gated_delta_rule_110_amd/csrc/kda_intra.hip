@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     // Heads fastest where the grid allows (gridDim.y <= 65535 chunk slots): the
     // workgroups in flight together then cover whole token rows, and the chain
     // kernel that runs next reads the intermediates measurably faster.
-    const int64_t slot = a.heads_fast ? blockIdx.y : blockIdx.x;
+    const int64_t slot = a.slot_base + (a.heads_fast ? blockIdx.y : blockIdx.x);
     const int64_t h = a.heads_fast ? blockIdx.x : blockIdx.y;
     const int64_t H = a.H;
 
@@ -510,11 +510,28 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
 
 }  // namespace
 
+// Above 65535 chunk slots the grid is (slots, H), launched in pieces of at
+// most 2^22 slots so that a launch stays within 2^30 work-items in x (a
+// dispatch's grid is counted in 32-bit work-items per dimension).
+constexpr int64_t kMaxSlotsPerLaunch = int64_t(1) << 22;
+
 hipError_t kda_launch_intra(const IntraArgs &a, int64_t slots, hipStream_t s) {
     if (slots <= 0) return hipSuccess;
     IntraArgs b = a;
-    b.heads_fast = slots <= 65535 && a.H <= 65535;
-    const dim3 grid = b.heads_fast ? dim3((unsigned)a.H, (unsigned)slots) : dim3((unsigned)slots, (unsigned)a.H);
-    hipLaunchKernelGGL(kda_intra_kernel, grid, dim3(kThreads), 0, s, b);
-    return hipGetLastError();
+    bool forced = false;
+    const int64_t piece = launch_piece(kMaxSlotsPerLaunch, &forced);
+    b.heads_fast = slots <= 65535 && a.H <= 65535 && !forced;
+    if (b.heads_fast) {
+        b.slot_base = 0;
+        hipLaunchKernelGGL(kda_intra_kernel, dim3((unsigned)a.H, (unsigned)slots), dim3(kThreads), 0, s, b);
+        return hipGetLastError();
+    }
+    for (int64_t s0 = 0; s0 < slots; s0 += piece) {
+        const int64_t ns = slots - s0 < piece ? slots - s0 : piece;
+        b.slot_base = s0;
+        hipLaunchKernelGGL(kda_intra_kernel, dim3((unsigned)ns, (unsigned)a.H), dim3(kThreads), 0, s, b);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }

@@ -65,8 +65,8 @@ constexpr int kScanThreads = 512;
 __global__ __launch_bounds__(kScanThreads) void kda_seg_scan_kernel(ScanArgs a) {
     __shared__ float st[2][kCols * kSP];  // [buffer][column * kSP + row]
 
-    const int vb = blockIdx.x;
-    const int64_t bh = blockIdx.y;
+    const int64_t bh = blockIdx.x;  // on x: a grid's y extent is small
+    const int vb = blockIdx.y;
     const int64_t b = bh / a.H, h = bh - b * a.H;
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
@@ -145,6 +145,6 @@ hipError_t kda_launch_seg_table(int64_t B, int64_t T, int64_t segs, int64_t segc
 hipError_t kda_launch_seg_scan(const ScanArgs &a, hipStream_t s) {
     const int64_t bh = a.B * a.H;
     if (bh <= 0 || a.segs <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_seg_scan_kernel, dim3((unsigned)(kV / kCols), (unsigned)bh), dim3(kScanThreads), 0, s, a);
+    hipLaunchKernelGGL(kda_seg_scan_kernel, dim3((unsigned)bh, (unsigned)(kV / kCols)), dim3(kScanThreads), 0, s, a);
     return hipGetLastError();
 }

@@ -139,6 +139,15 @@ int64_t kda_fwd_chain_segments(const kda_desc_t *desc);
  * Returns KDA_OK when the work was enqueued; device faults surface at the
  * caller's next synchronisation.
  *
+ * Launch size.  A kernel launch covers at most 2^30 work-items.  Bigger
+ * batches (from about half a million (sequence, head) pairs) are enqueued as
+ * several launches of the same kernel, with identical results.  The
+ * environment variable KDA_LAUNCH_PIECE=n (n > 0), read at every call of
+ * kda_fwd and kda_decode, caps each launch at n chain groups of 8 (sequence,
+ * head) pairs, n 64-token chunk rows or n decode (sequence, head) pairs, so
+ * that small inputs take the same several-launch path (a testing aid; it
+ * slows the call).
+ *
  * With split chains (desc->chain_segments) the state chain of every sequence
  * runs in three launches instead of one: the map of every segment, an fp32
  * scan over the segments (the entering states and the final state), and the
