@@ -77,6 +77,14 @@ __device__ __forceinline__ h8 to_h8(const f4 &a, const f4 &b) {
     return r;
 }
 
+// A 16-byte intermediate store, with the non-temporal hint when kStream: the
+// state chain reads the line once, from HBM, much later.
+template <bool kStream>
+__device__ __forceinline__ void store_h8(_Float16 *p, const h8 &v) {
+    if constexpr (kStream) __builtin_nontemporal_store(v, reinterpret_cast<h8 *>(p));
+    else *reinterpret_cast<h8 *>(p) = v;
+}
+
 // fp16 hi + lo split of four floats.
 __device__ __forceinline__ void split_h4(const f4 &x, h4 &hi, h4 &lo) {
 #pragma unroll
@@ -122,6 +130,7 @@ __device__ __forceinline__ void offdiag_column(IntraSmem &sm, int r16, int cg) {
     }
 }
 
+template <bool kStream>
 __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     __shared__ IntraSmem sm;
 
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
         {
             const f4 lo = mfma16x16x32_f16(sel[0], qg8, f4{0, 0, 0, 0});
             const f4 hi = mfma16x16x32_f16(sel[1], qg8, f4{0, 0, 0, 0});
-            *reinterpret_cast<h8 *>(Qf + ((w * 4 + kk) * 64 + lane) * 8) = to_h8(lo, hi);
+            store_h8<kStream>(Qf + ((w * 4 + kk) * 64 + lane) * 8, to_h8(lo, hi));
         }
         // Kf[2 kk + half][w / 2]: lane (r, g) <- Kbar[16 w + 4 g + e][32 kk + 16 half + r]   (Kbar x Sel)
 #pragma unroll
@@ -415,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             if (kb == 0 || w >= 2)  // rows 0..31 have no A_qk entries in columns 32..63 (never read)
-                *reinterpret_cast<h8 *>(Af + ((w * 2 + kb) * 64 + lane) * 8) = to_h8(dq[2 * kb], dq[2 * kb + 1]);
+                store_h8<kStream>(Af + ((w * 2 + kb) * 64 + lane) * 8, to_h8(dq[2 * kb], dq[2 * kb + 1]));
     }
     // ---- P2: invert the diagonal 16x16 blocks of (I + A_kk) -----------------
     // Each wave inverts its own block from the rows it has just written (one
@@ -499,7 +508,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
         _Float16 *Wf = a.Wf + ws * kWfElems;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-            *reinterpret_cast<h8 *>(Wf + ((w * 4 + kb) * 64 + lane) * 8) = to_h8(-accW[2 * kb], -accW[2 * kb + 1]);
+            store_h8<kStream>(Wf + ((w * 4 + kb) * 64 + lane) * 8, to_h8(-accW[2 * kb], -accW[2 * kb + 1]));
         // accU[vt]: U[16 w + 4 cg + e][16 vt + r] -> Uf[vt][w]
         _Float16 *Uf = a.Uf + ws * kUfElems;
 #pragma unroll
@@ -508,30 +517,49 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     }
 }
 
-}  // namespace
+// Intermediates of at least this many bytes are written with the
+// non-temporal hint on their 16-byte stores (W, Q_gamma, A_qk).  From this
+// size on, the kernel's inputs and intermediates together outgrow the 256 MB
+// Infinity Cache, so the intermediates cannot wait there for the chain kernel
+// anyway.  Written past it, they leave no dirty lines in the cache for the
+// chain's reads to evict (the likely reason), and the chain runs 2-5% faster
+// (one 8K-token sequence at H = 32: 135 -> 129 us).  Below it they are read back from the cache, and the
+// hint would cost 5-13% of the forward.  (The hint on the 8-byte stores, K and
+// U, slowed this kernel by 2% and is not used.)
+constexpr int64_t kStreamStoreBytes = int64_t(128) << 20;
+constexpr int64_t kInterBytesPerChunkHead =
+    2 * (kWfElems + kQfElems + kKfElems + kAfElems + kUfElems) + 4 * kGnElems;
 
 // Above 65535 chunk slots the grid is (slots, H), launched in pieces of at
 // most 2^22 slots so that a launch stays within 2^30 work-items in x (a
 // dispatch's grid is counted in 32-bit work-items per dimension).
 constexpr int64_t kMaxSlotsPerLaunch = int64_t(1) << 22;
 
-hipError_t kda_launch_intra(const IntraArgs &a, int64_t slots, hipStream_t s) {
-    if (slots <= 0) return hipSuccess;
+template <bool kStream>
+hipError_t launch_intra(const IntraArgs &a, int64_t slots, hipStream_t s) {
     IntraArgs b = a;
     bool forced = false;
     const int64_t piece = launch_piece(kMaxSlotsPerLaunch, &forced);
     b.heads_fast = slots <= 65535 && a.H <= 65535 && !forced;
     if (b.heads_fast) {
         b.slot_base = 0;
-        hipLaunchKernelGGL(kda_intra_kernel, dim3((unsigned)a.H, (unsigned)slots), dim3(kThreads), 0, s, b);
+        hipLaunchKernelGGL(kda_intra_kernel<kStream>, dim3((unsigned)a.H, (unsigned)slots), dim3(kThreads), 0, s, b);
         return hipGetLastError();
     }
     for (int64_t s0 = 0; s0 < slots; s0 += piece) {
         const int64_t ns = slots - s0 < piece ? slots - s0 : piece;
         b.slot_base = s0;
-        hipLaunchKernelGGL(kda_intra_kernel, dim3((unsigned)ns, (unsigned)a.H), dim3(kThreads), 0, s, b);
+        hipLaunchKernelGGL(kda_intra_kernel<kStream>, dim3((unsigned)ns, (unsigned)a.H), dim3(kThreads), 0, s, b);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t kda_launch_intra(const IntraArgs &a, int64_t slots, hipStream_t s) {
+    if (slots <= 0) return hipSuccess;
+    if (slots * a.H * kInterBytesPerChunkHead >= kStreamStoreBytes) return launch_intra<true>(a, slots, s);
+    return launch_intra<false>(a, slots, s);
 }
