@@ -517,18 +517,19 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
     }
 }
 
-// Intermediates of at least this many bytes are written with the
-// non-temporal hint on their 16-byte stores (W, Q_gamma, A_qk).  From this
+// Intermediates of at least 128 MiB (this many chunk-heads) are written with
+// the non-temporal hint on their 16-byte stores (W, Q_gamma, A_qk).  From this
 // size on, the kernel's inputs and intermediates together outgrow the 256 MB
 // Infinity Cache, so the intermediates cannot wait there for the chain kernel
 // anyway.  Written past it, they leave no dirty lines in the cache for the
 // chain's reads to evict (the likely reason), and the chain runs 2-5% faster
-// (one 8K-token sequence at H = 32: 135 -> 129 us).  Below it they are read back from the cache, and the
-// hint would cost 5-13% of the forward.  (The hint on the 8-byte stores, K and
-// U, slowed this kernel by 2% and is not used.)
-constexpr int64_t kStreamStoreBytes = int64_t(128) << 20;
+// (one 8K-token sequence at H = 32: 135 -> 129 us).  Below it they are read
+// back from the cache, and the hint would cost 5-13% of the forward.  (On the
+// 8-byte K-bar stores, whose halves come from two waves, the hint slowed this
+// kernel by 2%; on the U stores it changed nothing.)
 constexpr int64_t kInterBytesPerChunkHead =
     2 * (kWfElems + kQfElems + kKfElems + kAfElems + kUfElems) + 4 * kGnElems;
+constexpr int64_t kStreamChunkHeads = ((int64_t(128) << 20) + kInterBytesPerChunkHead - 1) / kInterBytesPerChunkHead;
 
 // Above 65535 chunk slots the grid is (slots, H), launched in pieces of at
 // most 2^22 slots so that a launch stays within 2^30 work-items in x (a
@@ -560,6 +561,6 @@ hipError_t launch_intra(const IntraArgs &a, int64_t slots, hipStream_t s) {
 
 hipError_t kda_launch_intra(const IntraArgs &a, int64_t slots, hipStream_t s) {
     if (slots <= 0) return hipSuccess;
-    if (slots * a.H * kInterBytesPerChunkHead >= kStreamStoreBytes) return launch_intra<true>(a, slots, s);
+    if (slots * a.H >= kStreamChunkHeads) return launch_intra<true>(a, slots, s);
     return launch_intra<false>(a, slots, s);
 }
