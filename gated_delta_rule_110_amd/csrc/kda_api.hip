@@ -19,11 +19,17 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // How many segments each sequence's state chain is cut into (kda.h,
-// kda_desc_t::chain_segments).  Automatic splitting aims at 8 workgroups per
-// segment and head filling the 256 CUs, keeping at least 32 chunks per segment
-// so that the scan stays small next to the chain.  A split runs every chunk
-// twice (the map pass and the chain pass, about 1.8 chunk steps of time
-// against 0.9 unsplit), so it pays from 3 segments on.
+// kda_desc_t::chain_segments).  Automatic splitting gives every (segment,
+// head) 8 workgroups and takes the larger of two counts: one round of
+// workgroups over the 256 CUs with at least 32 chunks per segment, or two
+// rounds with at least 64 chunks per segment.  Two rounds measured faster
+// wherever their segments stay that long (one 128K-token sequence: H = 4
+// 722 -> 682 us, H = 8 1351 -> 1237 us, H = 12 2607 -> 1886 us unsplit before,
+// H = 16 2801 -> 2389 us unsplit before), one round where they would not
+// (H = 1: 32 segments 252 us, 64 segments 318 us).  A split runs every chunk
+// twice (the map pass and the chain pass), so it pays from 3 segments on
+// (H = 20: 3 segments 3118 us against 3176 unsplit; H = 24 and 32: 2 segments
+// 22% slower than none).
 constexpr int64_t kCUs = 256;
 constexpr int64_t kChainWorkgroups = 8;
 constexpr int64_t kMinSegmentChunks = 32;
@@ -38,8 +44,12 @@ kda_status_t choose_segments(const kda_desc_t *d, Geometry &g) {
     const int64_t nc = g.nc_fixed;
     int64_t want = req;
     if (req == 0) {
-        want = kCUs / kChainWorkgroups / (g.B * g.H);
-        if (want > nc / kMinSegmentChunks) want = nc / kMinSegmentChunks;
+        const int64_t bh = g.B * g.H;
+        int64_t one = kCUs / kChainWorkgroups / bh;
+        if (one > nc / kMinSegmentChunks) one = nc / kMinSegmentChunks;
+        int64_t two = 2 * kCUs / kChainWorkgroups / bh;
+        if (two > nc / (2 * kMinSegmentChunks)) two = nc / (2 * kMinSegmentChunks);
+        want = one > two ? one : two;
         if (want < kMinAutoSegments) want = 1;
     }
     if (want > nc) want = nc;

@@ -85,10 +85,12 @@ typedef struct {
      * affinely, so a long chain can be cut into segments whose maps are
      * computed in parallel and then composed in order (see kda_fwd).
      *   0  : automatic -- split when the chains alone leave most of the GPU
-     *        idle: segments = min(32 / (B * H), chunks / 32) when that is >= 3
-     *        (sized for the 256 CUs of an MI355X, 8 workgroups per chain; a
-     *        split runs every chunk twice, so 2 segments would gain nothing),
-     *        otherwise no split;
+     *        idle: segments = max(min(32 / (B * H), chunks / 32),
+     *        min(64 / (B * H), chunks / 64)) when that is >= 3, otherwise no
+     *        split (sized for the 256 CUs of an MI355X at 8 workgroups per
+     *        segment and head: one round of workgroups with segments of at
+     *        least 32 chunks, or two rounds with segments of at least 64; a
+     *        split runs every chunk twice, so 2 segments would gain nothing);
      *   1  : never split;
      *   >= 2 : split every sequence into that many segments (at most one per
      *        64-token chunk; fewer when the chunks do not divide evenly).

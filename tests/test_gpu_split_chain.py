@@ -81,10 +81,11 @@ def test_split_in_place_state_and_poisoned_workspace():
 
 
 def test_split_long_few_heads_auto():
-    # the bench workload for split chains at its full size: T = 131072, H = 4 (automatic split)
+    # the bench workload for split chains at its full size: T = 131072, H = 4 (automatic split:
+    # two rounds of 8 workgroups per segment and head over the 256 CUs)
     w = W.by_name("long_T131072_H4")
     segs = kda.chain_segments_for(w.B, w.T, w.H)
-    assert segs == 8
+    assert segs == 16
     say("case %s: automatic split into %d segments" % (w.name, segs))
     out, fin = run_gpu(w)
     ro, rf = run_oracle(w)

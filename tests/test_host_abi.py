@@ -104,15 +104,22 @@ def test_workspace_size_monotone(lib):
 
 def test_chain_segments_rule(lib):
     # automatic: split only when the B*H chains (8 workgroups each) leave most CUs idle (at
-    # least 3 segments) and the chain is long enough (at least 32 chunks per segment)
+    # least 3 segments); the larger of one round of segment workgroups over the 256 CUs with
+    # at least 32 chunks per segment, and two rounds with at least 64 chunks per segment
     assert kda.chain_segments_for(1, 8192, 32) == 1
-    assert kda.chain_segments_for(1, 131072, 32) == 1
-    assert kda.chain_segments_for(1, 131072, 16) == 1           # 2 segments would gain nothing
-    assert kda.chain_segments_for(1, 131072, 10) == 3
-    assert kda.chain_segments_for(1, 131072, 8) == 4
-    assert kda.chain_segments_for(1, 131072, 4) == 8
-    assert kda.chain_segments_for(1, 131072, 1) == 32
-    assert kda.chain_segments_for(2, 131072, 1) == 16
+    assert kda.chain_segments_for(1, 131072, 32) == 1           # two rounds: 2 segments, too few
+    assert kda.chain_segments_for(1, 131072, 24) == 1
+    assert kda.chain_segments_for(1, 131072, 20) == 3           # two rounds
+    assert kda.chain_segments_for(1, 131072, 16) == 4
+    assert kda.chain_segments_for(1, 131072, 12) == 5
+    assert kda.chain_segments_for(1, 131072, 10) == 6
+    assert kda.chain_segments_for(1, 131072, 8) == 8
+    assert kda.chain_segments_for(1, 131072, 4) == 16
+    assert kda.chain_segments_for(1, 131072, 2) == 32
+    assert kda.chain_segments_for(1, 131072, 1) == 32           # one round: 64 chunks per segment
+    assert kda.chain_segments_for(2, 131072, 1) == 32
+    assert kda.chain_segments_for(1, 65536, 4) == 16
+    assert kda.chain_segments_for(1, 16384, 4) == 8             # one round: two would need 64 chunks
     assert kda.chain_segments_for(1, 8192, 4) == 4              # 128 chunks: at most 4 segments
     assert kda.chain_segments_for(1, 4096, 4) == 1              # 64 chunks: 2 segments only
     assert kda.chain_segments_for(1, 1024, 1) == 1
