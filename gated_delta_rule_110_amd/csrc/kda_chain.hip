@@ -54,9 +54,11 @@
 //
 // kda_chain_map_kernel is the same chain without outputs, used to split long
 // chains (kda_segment.hip): it gives every chain its affine map S -> M S + N.
-// Its wave 1 is a second chain wave: in each V-block workgroup wave 0 carries
-// the block's columns of N (from S = 0) and wave 1 those of M (from S = I with
-// the chunks' U taken as zero), both reading the same operand ring.
+// Its output waves are chain waves too: in each V-block workgroup, chain wave c
+// carries block c's columns of N (from S = 0) and wave kCB + c those of M (from
+// S = I with the chunks' U taken as zero), all reading the same operand ring.
+// kda_chain_map_x2_kernel does so with two blocks per workgroup, under the
+// same rule as the two-block chain kernel.
 #include "kda_common.h"
 
 using namespace kda;
@@ -318,13 +320,11 @@ __device__ __forceinline__ void out_wave(ChainSmem<kCB> &sm, const ChainArgs &a,
     }
 }
 
-// The chain kernel's body; kMap selects map mode (ChainArgs::map_mode, one
-// block per workgroup only), which is a kernel of its own so that the ordinary
-// chain is compiled without it.
+// The chain kernel's body; kMap selects map mode (ChainArgs::map_mode), which
+// is a kernel of its own so that the ordinary chain is compiled without it.
 template <bool kMap, int kCB>
 __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &a) {
     using Sh = Shape<kCB>;
-    static_assert(!kMap || kCB == 1, "map mode uses one block per workgroup");
 
     const int64_t H = a.H;
     const int64_t NH = a.N * H;
@@ -361,12 +361,12 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
     const int r = lane & 15;
     const int g = lane >> 4;
 
-    if (wave < kCB || (kMap && wave == 1)) {
+    if (wave < kCB || (kMap && wave < 2 * kCB)) {
         // ---- state chain ---------------------------------------------------
-        // (map mode: wave 0 carries N from S = 0, wave 1 carries M from S = I
-        // with U = 0; both read the same ring)
-        const bool linear_part = kMap && wave == 1;
-        const int c = kMap ? 0 : wave;              // block of the workgroup
+        // (map mode: wave c carries block c's N from S = 0, wave kCB + c its M
+        // from S = I with U = 0; all read the same ring)
+        const bool linear_part = kMap && wave >= kCB;
+        const int c = linear_part ? wave - kCB : wave;  // block of the workgroup
         const int col0 = kVB * (vb * kCB + c);      // first value column of the block
         f4 S[8];
         const int64_t sbase = (n * H + h) * (int64_t)kK * kV + col0 + r;
@@ -481,6 +481,10 @@ __global__ __launch_bounds__(Shape<1>::kThreads, 1) void kda_chain_map_kernel(Ch
     __shared__ ChainSmem<1> sm;
     chain_body<true, 1>(sm, a);
 }
+__global__ __launch_bounds__(Shape<2>::kThreads, 1) void kda_chain_map_x2_kernel(ChainArgs a) {
+    __shared__ ChainSmem<2> sm;
+    chain_body<true, 2>(sm, a);
+}
 
 // Packed batches: first chunk slot of each sequence, off[n] = sum_{m<n} ceil(len_m / 64),
 // and the order the chain kernel dispatches the sequences in: by chunk count,
@@ -548,6 +552,9 @@ __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int64_t *cu
 #ifndef KDA_CHAIN_WIDE
 #define KDA_CHAIN_WIDE -1   // -1: by the chain count; 0: never; 1: always (measurement builds)
 #endif
+#ifndef KDA_MAP_WIDE
+#define KDA_MAP_WIDE -1     // the same for the map pass of split chains
+#endif
 
 // Chains per launch are capped so that a launch stays within 2^30 work-items
 // (a dispatch's grid is counted in 32-bit work-items per dimension): 65536
@@ -559,14 +566,18 @@ hipError_t kda_launch_chain(const ChainArgs &a, hipStream_t s) {
     const int64_t NH = a.N * a.H;
     if (NH <= 0) return hipSuccess;
     const int64_t groups = (NH + 7) / 8;  // chains in groups of 8, one per XCD
-    const bool wide = !a.map_mode && (KDA_CHAIN_WIDE == 1 ||
-                                      (KDA_CHAIN_WIDE == -1 && NH * kBlocks > kOneRoundWorkgroups));
+    const bool wide = a.map_mode ? (KDA_MAP_WIDE == 1 || (KDA_MAP_WIDE == -1 && NH * kBlocks > kOneRoundWorkgroups))
+                                 : (KDA_CHAIN_WIDE == 1 ||
+                                    (KDA_CHAIN_WIDE == -1 && NH * kBlocks > kOneRoundWorkgroups));
     const int64_t piece = launch_piece(kMaxGroupsPerLaunch);
     for (int64_t g0 = 0; g0 < groups; g0 += piece) {
         const int64_t ng = groups - g0 < piece ? groups - g0 : piece;
         ChainArgs b = a;
         b.chain_base = 8 * g0;
-        if (a.map_mode)
+        if (a.map_mode && wide)
+            hipLaunchKernelGGL(kda_chain_map_x2_kernel, dim3((unsigned)(ng * 8 * Shape<2>::kNVB)),
+                               dim3(Shape<2>::kThreads), 0, s, b);
+        else if (a.map_mode)
             hipLaunchKernelGGL(kda_chain_map_kernel, dim3((unsigned)(ng * 8 * Shape<1>::kNVB)),
                                dim3(Shape<1>::kThreads), 0, s, b);
         else if (wide)

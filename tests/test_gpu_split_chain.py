@@ -91,3 +91,18 @@ def test_split_long_few_heads_auto():
     ro, rf = run_oracle(w)
     res = compare(to_np(out), ro, to_np(fin), rf, torch.float32, w.name)
     say("  vs oracle %s" % res)
+
+
+def test_two_block_map_equals_one_block():
+    # 8 segments x 8 heads = 64 (segment, head) chains: the map pass and the chain pass both
+    # take two state blocks per workgroup; each 4-head half (32 chains) takes one block per
+    # workgroup in both passes.  Heads are independent, so the results are equal bit for bit.
+    w = W.make("map_x2", 1, 64 * 64 + 29, 8, 7801, lower_bound=-5.0, init="fp32", final="fp32")
+    assert kda.chain_segments_for(w.B, w.T, w.H, 8) == 8
+    say("case two-block map: T=%d H=8, 8 segments, against two 4-head halves" % w.T)
+    out, fin = run_gpu(w, chain_segments=8)
+    for lo in (0, 4):
+        o, f = run_gpu(w.head_slice(range(lo, lo + 4)), chain_segments=8)
+        assert torch.equal(out[:, :, lo:lo + 4], o) and torch.equal(fin[:, lo:lo + 4], f), lo
+    ro, rf = run_oracle(w)
+    compare(to_np(out), ro, to_np(fin), rf, torch.float32, "two-block map")
