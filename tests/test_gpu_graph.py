@@ -20,14 +20,16 @@ def _buffers(w, chain_segments):
     return ws, out, fin
 
 
-@pytest.mark.parametrize("case", ["fixed", "packed", "split"])
+@pytest.mark.parametrize("case", ["fixed", "packed", "split", "split_wide"])
 def test_graph_replays_match_eager(case):
     if case == "fixed":
         w, segs = W.make("graph-fixed", 2, 300, 3, 6001, init="fp32", final="fp32"), 0
     elif case == "packed":
         w, segs = W.make("graph-packed", 1, 260, 3, 6002, init="bf16", final="fp32", seqlens=[100, 0, 97, 63]), 0
-    else:
+    elif case == "split":
         w, segs = W.make("graph-split", 1, 64 * 12 + 9, 2, 6003, init="fp32", final="fp32"), 4
+    else:  # 4 segments x 9 heads = 36 chains: two-block map and chain passes
+        w, segs = W.make("graph-split-wide", 1, 64 * 12 + 9, 9, 6004, init="fp32", final="fp32"), 4
     say("case graph %s: B=%d T=%d H=%d N=%d chain_segments=%d" % (case, w.B, w.T, w.H, w.N, segs))
     wd = w.to("cuda")
 

@@ -62,11 +62,13 @@ def test_fixed_batch_in_pieces():
     _check_fwd(w, [1, 2], "fixed")
 
 
-def test_split_chains_in_pieces():
-    # 4 segments x 5 heads = 20 map chains in 3 groups, then the chains from the entering states
-    w = W.make("pieces_split", 1, 64 * 13 + 7, 5, 6102, lower_bound=-5.0, init="fp32", final="fp32")
+@pytest.mark.parametrize("H", [5, 9])
+def test_split_chains_in_pieces(H):
+    # 4 segments x H heads: 20 map chains in 3 groups (one-block passes), or 36 in 5 groups
+    # (two-block passes), then the chains from the entering states
+    w = W.make("pieces_split", 1, 64 * 13 + 7, H, 6102, lower_bound=-5.0, init="fp32", final="fp32")
     assert kda.chain_segments_for(w.B, w.T, w.H, 4) == 4
-    _check_fwd(w, [1], "split", chain_segments=4)
+    _check_fwd(w, [1], "split H=%d" % H, chain_segments=4)
 
 
 @pytest.mark.parametrize("init,final", [("fp32", "fp32"), ("bf16", "bf16")])
