@@ -34,14 +34,19 @@ import workloads as W  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA, vendor figure
 # Algorithmic work per token-head (C = 64, K = V = 128):
-#   FLOPs 6KV + C(3K + 2V) = 139,264; bytes: q, k, v, g in (4 x 256) + beta (2) + out (256) = 1282
+#   FLOPs 6KV + C(3K + 2V) = 139,264; bytes: q, k, v, g in (4 x 256) + beta (2) + out (256) = 1282,
+#   plus the optional states (K V x 2 or 4 bytes per (sequence, head) each).
 F_ALG = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
 BYTES_ALG = 4 * 256 + 2 + 256
+# The part of those bytes each kernel moves: the intra-chunk kernel reads the
+# inputs, the state chain writes the outputs and reads / writes the states.
+ALG_SHARE_BYTES = {"kda_intra_kernel": 4 * 256 + 2, "chain": 256}
 # Interface bytes per token-head of each kernel, reading its inputs and writing
-# its outputs once.  The chunk intermediates are W, Qg, Kbar^T, U (64 x 128
-# fp16 each), the 6 of 8 A_qk fragments that are not identically zero (rows
-# 0..31 have no entries in columns 32..63) and exp(G_n) (128 fp32): 70.5 KiB per
-# 64-token chunk and head = 1128 B per token-head.
+# its outputs once, the library's own intermediates included.  These are W, Qg,
+# Kbar^T, U (64 x 128 fp16 each), the 6 of 8 A_qk fragments that are not
+# identically zero (rows 0..31 have no entries in columns 32..63) and exp(G_n)
+# (128 fp32): 70.5 KiB per 64-token chunk and head = 1128 B per token-head.
+# They are reported beside the algorithmic figures (frac_interface), never as them.
 INTER_BYTES = (4 * 64 * 128 * 2 + 6 * 1024 + 128 * 4) / 64.0
 KERNEL_BYTES = {
     "kda_intra_kernel": 4 * 256 + 2 + INTER_BYTES,
@@ -54,6 +59,9 @@ KERNEL_BYTES = {
 # Split chains also move, per (batch row, segment, head), the two fp32 maps (written by the
 # map pass, read by the scan) and the entering state (written by the scan, read by the chain).
 SPLIT_BYTES_PER_SEGMENT_HEAD = 2 * (2 * 128 * 128 * 4) + 2 * (128 * 128 * 4)
+# The matrix-core operand types the kernels use (the I/O type is "dtype").
+MFMA_OPERANDS = ("fp16 (state path and output path), bf16 hi+lo splits on the diagonal Gram blocks, "
+                 "split-fp16 off-diagonal inverse blocks; fp32 accumulation")
 
 
 def state_bytes(w) -> int:
@@ -256,6 +264,19 @@ def load_traffic(workload_name: str, kernel: str):
     return k["bytes"]
 
 
+def load_limiter(kernel: str):
+    """What the committed counters say bounds ``kernel`` (profiles/limiters.json),
+    or None when there is no entry or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", "limiters.json")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    with open(path) as f:
+        lim = json.load(f).get(kernel)
+    if lim is None or lim.get("source_sha256") != source_digest(kernel):
+        return None
+    return lim.get("limiter")
+
+
 def decode_name(N: int, H: int) -> str:
     return "decode_N%d_H%d" % (N, H)
 
@@ -442,16 +463,36 @@ def main(argv=None) -> int:
         return b
 
     dom = max(kernels, key=kernels.get)
-    achieved = kernel_bytes(dom) / (kernels[dom] / 1e3) / 1e9
-    traffic = load_traffic(wname, dom)
+    # The roofline of the path: the algorithmic bytes of the whole forward
+    # (1282 B per token-head plus the states), credited to the dominant kernel's
+    # time, against the HBM peak.  Each kernel's own share of those bytes (the
+    # inputs it reads, the outputs and states it writes) gives its share rate;
+    # the interface rate (its reads and writes including the intermediates) is
+    # reported beside them.
+    alg_bytes = path_bytes
+
+    def share_bytes(name):
+        if name == "kda_intra_kernel":
+            return ALG_SHARE_BYTES[name] * tok_heads
+        return ALG_SHARE_BYTES["chain"] * tok_heads + state_bytes(w)
+
+    achieved = alg_bytes / (kernels[dom] / 1e3) / 1e9
     copy_gbs = copy_bandwidth(dev)
-    # every kernel's algorithmic rate, since the two kernels can take about
-    # the same time and the dominant one then flips between runs
     per_kernel = {}
+    counter_total = 0
     for name, t in kernels.items():
-        gb = kernel_bytes(name) / (t / 1e3) / 1e9
-        per_kernel[name] = {"achieved": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4),
-                            "traffic": load_traffic(wname, name)}
+        sh = share_bytes(name) / (t / 1e3) / 1e9
+        gi = kernel_bytes(name) / (t / 1e3) / 1e9
+        tr = load_traffic(wname, name)
+        counter_total = None if (tr is None or counter_total is None) else counter_total + tr
+        per_kernel[name] = {"alg_share_bytes": share_bytes(name), "share_achieved": round(sh, 1),
+                            "share_frac": round(sh / HBM_PEAK_GBS, 4),
+                            "interface_bytes": round(kernel_bytes(name)), "interface_achieved": round(gi, 1),
+                            "frac_interface": round(gi / HBM_PEAK_GBS, 4), "traffic": tr,
+                            "traffic_ratio": None if tr is None else round(tr / share_bytes(name), 3),
+                            "limiter": load_limiter(name)}
+    traffic = load_traffic(wname, dom)
+    dom_iface = kernel_bytes(dom) / (kernels[dom] / 1e3) / 1e9
 
     result = {
         "metric": "KDA prefill tokens/s and MFMA TFLOP/s (% bf16 peak) at T=8K,H=32,K=V=128",
@@ -480,8 +521,13 @@ def main(argv=None) -> int:
         "kernel_ms_samples": len(evs),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "copy_gbs": round(copy_gbs, 1),
-                     "frac_of_copy": round(achieved / copy_gbs, 4), "kernels": per_kernel},
+                     "alg_bytes": alg_bytes, "traffic": traffic,
+                     "traffic_ratio": None if counter_total is None else round(counter_total / alg_bytes, 3),
+                     "frac_interface": round(dom_iface / HBM_PEAK_GBS, 4),
+                     "limiter": load_limiter(dom),
+                     "copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4),
+                     "kernels": per_kernel},
+        "mfma_operands": MFMA_OPERANDS,
         "wall_s": round(wall, 4),
     }
     if not args.no_cpu_baseline:

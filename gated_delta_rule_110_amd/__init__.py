@@ -62,7 +62,8 @@ class KdaDesc(ctypes.Structure):
                 ("K", ctypes.c_int64), ("V", ctypes.c_int64), ("num_seqs", ctypes.c_int64),
                 ("initial_state_dtype", ctypes.c_int32), ("final_state_dtype", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("phase_events", ctypes.c_void_p), ("chain_segments", ctypes.c_int64)]
+                ("phase_events", ctypes.c_void_p), ("chain_segments", ctypes.c_int64),
+                ("launch_piece", ctypes.c_int64)]
 
 
 _lock = threading.Lock()
@@ -95,9 +96,10 @@ def library() -> ctypes.CDLL:
     return _lib
 
 
-def _desc(B, T, H, N, h0_dtype=0, ht_dtype=0, workspace=None, nbytes=0, chain_segments=0) -> KdaDesc:
+def _desc(B, T, H, N, h0_dtype=0, ht_dtype=0, workspace=None, nbytes=0, chain_segments=0,
+          launch_piece=0) -> KdaDesc:
     return KdaDesc(B, T, H, HEAD_DIM, HEAD_DIM, N, h0_dtype, ht_dtype,
-                   ctypes.c_void_p(workspace), nbytes, None, chain_segments)
+                   ctypes.c_void_p(workspace), nbytes, None, chain_segments, launch_piece)
 
 
 def workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None, chain_segments: int = 0) -> int:
@@ -131,7 +133,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         lower_bound: float, initial_state: Optional[torch.Tensor] = None,
         final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None,
-        phase_events=None, chain_segments: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        phase_events=None, chain_segments: int = 0,
+        launch_piece: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KDA forward on the current HIP stream.  Returns ``(out, final_state)``.
 
     q, k, g: bf16 [B,T,H,128]; v: bf16 [B,T,H,128]; beta: bf16 logits [B,T,H];
@@ -142,7 +145,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     of at least ``workspace_size`` bytes or None (allocated); phase_events:
     None or the address of a caller-owned array of 4 hipEvent_t (instrumentation);
     chain_segments: 0 (automatic), 1 (never) or the number of segments each
-    sequence's state chain is split into (batches without cu_seqlens).
+    sequence's state chain is split into (batches without cu_seqlens);
+    launch_piece: kda_desc_t::launch_piece (0: the library's launch size).
     """
     lib = library()
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -188,7 +192,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
             raise ValueError("%s must be [N,H,K,V] = %s" % (name, (N, H, K, V)))
     h0d = _state_dtype(initial_state, "initial_state")
     htd = _state_dtype(final_state, "final_state")
-    d = _desc(B, T, H, N, h0d, htd, chain_segments=int(chain_segments))
+    d = _desc(B, T, H, N, h0d, htd, chain_segments=int(chain_segments), launch_piece=int(launch_piece))
     d.K, d.V = K, V
     need = int(lib.kda_fwd_workspace_size(ctypes.byref(d)))
     with torch.cuda.device(dev):
@@ -212,12 +216,14 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
            scale: float, out: Optional[torch.Tensor], A_log: torch.Tensor, dt_bias: torch.Tensor,
            lower_bound: float, initial_state: Optional[torch.Tensor] = None,
-           final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+           final_state: Optional[torch.Tensor] = None,
+           launch_piece: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """One recurrent KDA step per sequence on the current HIP stream.
 
     q, k, g, v: bf16 [N,1,H,128]; beta: bf16 [N,1,H]; states: bf16 or fp32
     [N,H,128,128] or None (final_state may be the same tensor as
-    initial_state for an in-place update); out: bf16 [N,1,H,128] or None.
+    initial_state for an in-place update); out: bf16 [N,1,H,128] or None;
+    launch_piece: kda_desc_t::launch_piece (0: the library's launch size).
     Returns ``(out, final_state)``."""
     lib = library()
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -253,7 +259,8 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
     for name, t in (("initial_state", initial_state), ("final_state", final_state)):
         if t is not None and tuple(t.shape) != (N, H, K, V):
             raise ValueError("%s must be [N,H,K,V] = %s" % (name, (N, H, K, V)))
-    d = _desc(N, 1, H, N, _state_dtype(initial_state, "initial_state"), _state_dtype(final_state, "final_state"))
+    d = _desc(N, 1, H, N, _state_dtype(initial_state, "initial_state"), _state_dtype(final_state, "final_state"),
+              launch_piece=int(launch_piece))
     d.K, d.V = K, V
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream

@@ -176,6 +176,7 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
     Geometry geo;
     kda_status_t st = make_geometry(desc, cu_seqlens != nullptr, geo);
     if (st != KDA_OK) return st;
+    if (desc->launch_piece < 0) return KDA_ERR_PARAM;
     // token tensors hold B*T rows; with no tokens they may be empty (NULL)
     if (geo.T > 0 && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_NULL;
     if (!(lower_bound >= -5.0f && lower_bound <= 0.0f)) return KDA_ERR_PARAM;  // also rejects NaN
@@ -227,6 +228,7 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
     ia.Af = reinterpret_cast<_Float16 *>(ws + lay.off_Af);
     ia.Uf = reinterpret_cast<_Float16 *>(ws + lay.off_Uf);
     ia.gn = reinterpret_cast<float *>(ws + lay.off_gn);
+    ia.piece_cap = desc->launch_piece;
     if (err == hipSuccess && geo.T > 0) err = kda_launch_intra(ia, geo.slots, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[2], stream);
 
@@ -239,6 +241,7 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
     ca.h0_bf16 = desc->initial_state_dtype == KDA_BF16;
     ca.ht_bf16 = desc->final_state_dtype == KDA_BF16;
     ca.out = static_cast<uint16_t *>(out);
+    ca.piece_cap = desc->launch_piece;
     if (geo.segs > 1) {
         // split chains: every segment is a packed sequence of the chain kernel
         int64_t *seg_cu = reinterpret_cast<int64_t *>(ws + lay.off_seg_cu);
@@ -283,6 +286,7 @@ extern "C" kda_status_t kda_decode(const void *q, const void *k, const void *v, 
     if (desc->B < 1 || desc->H < 1 || desc->T != 1 || desc->num_seqs != desc->B) return KDA_ERR_SHAPE;
     if (desc->K != kK || desc->V != kV) return KDA_ERR_UNSUPPORTED;
     if (desc->B * desc->H > 0xffffffffLL) return KDA_ERR_SHAPE;
+    if (desc->launch_piece < 0) return KDA_ERR_PARAM;
     if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_NULL;
     if (!(lower_bound >= -5.0f && lower_bound <= 0.0f)) return KDA_ERR_PARAM;
     if (!isfinite(scale)) return KDA_ERR_PARAM;
@@ -304,5 +308,6 @@ extern "C" kda_status_t kda_decode(const void *q, const void *k, const void *v, 
     da.h0_bf16 = desc->initial_state_dtype == KDA_BF16;
     da.ht_bf16 = desc->final_state_dtype == KDA_BF16;
     da.out = static_cast<uint16_t *>(out);
+    da.piece_cap = desc->launch_piece;
     return kda_launch_decode(da, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

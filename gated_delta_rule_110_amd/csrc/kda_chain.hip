@@ -65,17 +65,11 @@ using namespace kda;
 
 namespace {
 
-#ifndef KDA_CHAIN_AHEAD
-#define KDA_CHAIN_AHEAD 3
-#endif
-constexpr int kAhead = KDA_CHAIN_AHEAD;  // chunks the L2 prefetch runs ahead of the chain (measured: 3 beats 2 and 4-16)
+constexpr int kAhead = 3;                // chunks the L2 prefetch runs ahead of the chain (measured: 3 beats 2 and 4-16)
 constexpr int kTouchInFlight = 32;       // L2 prefetch copies allowed in flight: a tighter bound
                                          // stalls this wave, and the barrier, on HBM latency
 constexpr int kVB = 16;                  // value columns per chain wave
 constexpr int kBlocks = kV / kVB;        // 16-column blocks per head
-#ifndef KDA_CHAIN_SLOTS
-#define KDA_CHAIN_SLOTS 3
-#endif
 // Chains at which the two-block workgroup is used: when the one-block grid
 // (8 workgroups per chain) would not fit the GPU in one round.
 constexpr int64_t kOneRoundWorkgroups = 256;
@@ -94,13 +88,13 @@ struct Shape {
     static constexpr int kWaves = 2 * kCB + 2;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kNVB = kBlocks / kCB;       // workgroups per (sequence, head)
-    static constexpr int kSlots = KDA_CHAIN_SLOTS;   // operand ring slots
+    static constexpr int kSlots = 3;                 // operand ring slots (2 measured 4% slower)
     static constexpr int kLead = kSlots - 1;         // chunks the ring copies run ahead of the chain
     static constexpr int kRingFrags = 33 + 2 * kCB;  // -W 16, Kbar^T 16, U 2 per block, exp(G_n) 1
     static constexpr int kOutTiles = 4 / kCB;        // 16-row output tiles per output wave
 };
-static_assert(KDA_CHAIN_SLOTS >= 2 && KDA_CHAIN_SLOTS <= 3,
-              "vmcnt holds at most 63 outstanding loads: 37 (slots - 2) must fit");
+static_assert(Shape<1>::kSlots >= 2 && Shape<2>::kRingFrags * (Shape<2>::kSlots - 2) <= 63,
+              "vmcnt holds at most 63 outstanding loads: kRingFrags (slots - 2) must fit");
 
 template <int kCB>
 struct __align__(16) ChainSmem {
@@ -167,8 +161,10 @@ __device__ __forceinline__ void dma_ring(ChainSmem<kCB> &sm, const ChainArgs &a,
 // workgroups of a head split the head's cache lines: copy j covers the share of
 // 16-column block vb kCB + j (one dword per 128-byte line).  The loads copy
 // into an LDS area nobody reads: no destination registers, so this wave never
-// has to wait for one except to bound how many are in flight.
-template <int kCB>
+// has to wait for one except to bound how many are in flight.  Map mode reads
+// no Qg and no A_qk, so those lanes repeat a line the wave already touches
+// (one request per line and instruction).
+template <int kCB, bool kMap>
 __device__ __forceinline__ void touch_lines(ChainSmem<kCB> &sm, const ChainArgs &a, int64_t ws, int vb, int lane) {
     const char *wf = reinterpret_cast<const char *>(a.Wf + ws * kWfElems);
     const char *qf = reinterpret_cast<const char *>(a.Qf + ws * kQfElems);
@@ -182,11 +178,11 @@ __device__ __forceinline__ void touch_lines(ChainSmem<kCB> &sm, const ChainArgs 
         const int b = vb * kCB + j;
         const char *p0;  // lines 0..63 of the share: W, Qg, Kbar, U
         if (l < 16) p0 = wf + (16 * b + l) * 128;
-        else if (l < 32) p0 = qf + (16 * b + l - 16) * 128;
+        else if (l < 32) p0 = kMap ? wf + (16 * b + l - 16) * 128 : qf + (16 * b + l - 16) * 128;
         else if (l < 48) p0 = kf + (16 * b + l - 32) * 128;
         else p0 = uf + (16 * b + l - 48) * 128;
         const char *p1;  // lines 64..72: A_qk and exp(G_n) (lanes >= 8 share one line)
-        if (l < 8) p1 = af + (8 * b + l) * 128;
+        if (l < 8 && !kMap) p1 = af + (8 * b + l) * 128;
         else p1 = gn + (b & 3) * 128;
         lds_copy4(p0, lds_addr(&sm.dump[0][0]));
         lds_copy4(p1, lds_addr(&sm.dump[1][0]));
@@ -456,7 +452,7 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
             const int64_t nu = nchunks + kAhead - 1;
             bool prologue_done = false;
             for (int64_t u = 0; u < nu; ++u) {
-                touch_lines<kCB>(sm, a, wsof(u + 1), vb, lane);
+                touch_lines<kCB, kMap>(sm, a, wsof(u + 1), vb, lane);
                 asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTouchInFlight) : "memory");
                 if (u >= kAhead - 1) {
                     if (!prologue_done) { lds_barrier(); prologue_done = true; }
@@ -549,12 +545,6 @@ __global__ __launch_bounds__(1024) void kda_chunk_table_kernel(const int64_t *cu
 
 }  // namespace
 
-#ifndef KDA_CHAIN_WIDE
-#define KDA_CHAIN_WIDE -1   // -1: by the chain count; 0: never; 1: always (measurement builds)
-#endif
-#ifndef KDA_MAP_WIDE
-#define KDA_MAP_WIDE -1     // the same for the map pass of split chains
-#endif
 
 // Chains per launch are capped so that a launch stays within 2^30 work-items
 // (a dispatch's grid is counted in 32-bit work-items per dimension): 65536
@@ -566,10 +556,9 @@ hipError_t kda_launch_chain(const ChainArgs &a, hipStream_t s) {
     const int64_t NH = a.N * a.H;
     if (NH <= 0) return hipSuccess;
     const int64_t groups = (NH + 7) / 8;  // chains in groups of 8, one per XCD
-    const bool wide = a.map_mode ? (KDA_MAP_WIDE == 1 || (KDA_MAP_WIDE == -1 && NH * kBlocks > kOneRoundWorkgroups))
-                                 : (KDA_CHAIN_WIDE == 1 ||
-                                    (KDA_CHAIN_WIDE == -1 && NH * kBlocks > kOneRoundWorkgroups));
-    const int64_t piece = launch_piece(kMaxGroupsPerLaunch);
+    // two blocks per workgroup when one block per workgroup would not fit the GPU in one round
+    const bool wide = NH * kBlocks > kOneRoundWorkgroups;
+    const int64_t piece = launch_piece(kMaxGroupsPerLaunch, a.piece_cap);
     for (int64_t g0 = 0; g0 < groups; g0 += piece) {
         const int64_t ng = groups - g0 < piece ? groups - g0 : piece;
         ChainArgs b = a;

@@ -79,6 +79,7 @@ struct IntraArgs {
     float *gn;
     int heads_fast;             // grid (H, slots) rather than (slots, H); set by the launcher
     int64_t slot_base;          // first chunk slot of this launch; set by the launcher
+    int64_t piece_cap;          // kda_desc_t::launch_piece (0: launch size by the default rule)
 };
 
 struct ChainArgs {
@@ -100,6 +101,7 @@ struct ChainArgs {
     int map_mode;
     float *mapM, *mapN;
     int64_t chain_base;  // first chain (in dispatch order) of this launch; set by the launcher
+    int64_t piece_cap;   // kda_desc_t::launch_piece (0: launch size by the default rule)
 };
 
 // The sequential pass over the segments of split chains: for batch row b and
@@ -125,6 +127,7 @@ struct DecodeArgs {
     int h0_bf16, ht_bf16;
     uint16_t *out;       // [N,H,V] bf16
     int64_t unit_base;   // first (sequence, head) of this launch; set by the launcher
+    int64_t piece_cap;   // kda_desc_t::launch_piece (0: launch size by the default rule)
 };
 
 // ---- small numeric helpers --------------------------------------------------
@@ -162,6 +165,26 @@ __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp
 __device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_logf(x) * 0.6931471805599453f; }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// log2 of the per-channel decay, log2e * max(lb, -exp(A_log) softplus(x)) with
+// x = g + dt_bias, nA = -exp(A_log) and lb2 = lb log2e.  softplus(x) = log(1 + e^x)
+// is taken in three ranges so that it keeps its relative precision everywhere:
+//   e^x < 2^-6 : the series t - t^2/2 + t^3/3 (relative error below 1e-6; the
+//                plain log(1 + t) would lose the low bits of t once 1 + t
+//                rounds, and return 0 below x = -16.6);
+//   x > 15     : x itself (the remainder log1p(e^-x) < 4e-7 is below fp32
+//                resolution, and e^x would overflow above x = 88.7);
+//   otherwise  : log2(1 + e^x) on the hardware log.
+// x = +inf gives the clamp lb, x = -inf gives 0.
+__device__ __forceinline__ float gate_log2(float x, float nA, float lb2) {
+    constexpr float kL2e = 1.4426950408889634f;
+    const float t = __builtin_amdgcn_exp2f(x * kL2e);
+    const float series = t * (kL2e - t * (0.5f * kL2e - t * (kL2e / 3.0f)));
+    float sp2 = __builtin_amdgcn_logf(1.0f + t);  // log2(1 + t)
+    sp2 = t < 0.015625f ? series : sp2;
+    sp2 = x > 15.0f ? x * kL2e : sp2;
+    return fmaxf(lb2, nA * sp2);
+}
 
 // DPP lane moves within 16-lane rows.
 __device__ __forceinline__ float dpp_row_shr(float x, float fill, int s) {
@@ -232,15 +255,12 @@ __device__ __forceinline__ int64_t seq_of_slot(const int32_t *off, int64_t N, in
 }
 
 // Largest grid piece (chains, chunk slots or decode units) one launch may
-// cover: `dflt`, or the positive value of the environment variable
-// KDA_LAUNCH_PIECE when it is set.  The defaults keep every launch within
-// 2^30 work-items, so only very large batches take several launches; the
-// variable makes small inputs take that path too, so that it can be tested.
-inline int64_t launch_piece(int64_t dflt, bool *forced = nullptr) {
-    const char *e = getenv("KDA_LAUNCH_PIECE");
-    const long long v = e ? atoll(e) : 0;
-    if (forced) *forced = v > 0;
-    return v > 0 && v < dflt ? (int64_t)v : dflt;
+// cover: `dflt`, or `cap` when the caller asked for a smaller one
+// (kda_desc_t::launch_piece > 0).  The defaults keep every launch within 2^30
+// work-items, so only very large batches take several launches; a cap makes
+// small inputs take that path too, so that it can be tested.
+inline int64_t launch_piece(int64_t dflt, int64_t cap) {
+    return cap > 0 && cap < dflt ? cap : dflt;
 }
 
 }  // namespace kda

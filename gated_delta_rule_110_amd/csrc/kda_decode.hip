@@ -129,7 +129,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a) {
         const int c = 64 * (w - 2) + lane;
         const float x = bf16_bits_to_f32(a.g[row * kK + c]) + a.dt_bias[h * kK + c];
         const float nA = -fast_exp(a.A_log[h]);
-        const float l2 = fmaxf(a.lower_bound * kLog2e, nA * __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(x * kLog2e)));
+        const float l2 = gate_log2(x, nA, a.lower_bound * kLog2e);
         sm.dec[c] = __builtin_amdgcn_exp2f(l2);
         if (w == 2 && lane == 0) sm.scal[0] = fast_rcp(1.0f + fast_exp(-bf16_bits_to_f32(a.beta[row])));
     }
@@ -213,8 +213,8 @@ hipError_t kda_launch_decode(const DecodeArgs &a, hipStream_t s) {
     b.unit_base = 0;
     const int64_t elt = (a.h0 && !a.h0_bf16) || (a.ht && !a.ht_bf16) ? 4 : 2;
     const bool stream = units * kK * kV * elt >= kStreamStateBytes;
-    bool forced = false;
-    const int64_t piece = launch_piece(kMaxUnitsPerLaunch, &forced);
+    const bool forced = a.piece_cap > 0;
+    const int64_t piece = launch_piece(kMaxUnitsPerLaunch, a.piece_cap);
     if (!stream && !forced && units * 4 <= kSplitWorkgroups) {
         hipLaunchKernelGGL(kda_decode_split4_kernel, dim3((unsigned)(units * 4)), dim3(kThreads), 0, s, b);
         return hipGetLastError();

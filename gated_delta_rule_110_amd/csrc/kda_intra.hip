@@ -201,8 +201,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // gate in base 2: log2 d = max(lb log2e, -exp(A_log) log2(1 + 2^(x log2e))), x = g + dt_bias,
-    // i.e. d = exp(max(lb, -exp(A_log) softplus(x))); then the inclusive product
+    // gate in base 2: log2 d = log2e max(lb, -exp(A_log) softplus(x)), x = g + dt_bias
+    // (gate_log2), i.e. d = exp(max(lb, -exp(A_log) softplus(x))); then the inclusive product
     // over the block's rows: P_i = exp(G_i - G_{r-1}).
     float P[32];
     {
@@ -216,8 +216,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraArgs a) {
             unpack_bf16x8(graw[kk], gf);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float t = __builtin_amdgcn_exp2f((gf[e] + db[e]) * kLog2e);
-                const float l2 = fmaxf(lb2, nA * __builtin_amdgcn_logf(1.0f + t));
+                const float l2 = gate_log2(gf[e] + db[e], nA, lb2);
                 P[8 * kk + e] = valid ? l2 : 0.0f;  // log2 of the decay
             }
         }
@@ -539,8 +538,8 @@ constexpr int64_t kMaxSlotsPerLaunch = int64_t(1) << 22;
 template <bool kStream>
 hipError_t launch_intra(const IntraArgs &a, int64_t slots, hipStream_t s) {
     IntraArgs b = a;
-    bool forced = false;
-    const int64_t piece = launch_piece(kMaxSlotsPerLaunch, &forced);
+    const bool forced = a.piece_cap > 0;
+    const int64_t piece = launch_piece(kMaxSlotsPerLaunch, a.piece_cap);
     b.heads_fast = slots <= 65535 && a.H <= 65535 && !forced;
     if (b.heads_fast) {
         b.slot_base = 0;

@@ -98,6 +98,13 @@ typedef struct {
      * KDA_ERR_UNSUPPORTED.  The result is the same function of the inputs
      * either way, up to rounding. */
     int64_t chain_segments;
+    /* Largest piece of a kernel grid one launch may cover (a testing aid):
+     * 0 for the library's rule (see "Launch size" at kda_fwd); n > 0 caps each
+     * launch at n chain groups of 8 (sequence, head) pairs, n 64-token chunk
+     * rows or n decode (sequence, head) pairs, so that small inputs take the
+     * several-launch path of very large ones.  Results are identical either
+     * way.  Negative values are KDA_ERR_PARAM. */
+    int64_t launch_piece;
 } kda_desc_t;
 
 /* Bytes of workspace kda_fwd needs for these shapes (0 if the shapes are
@@ -143,12 +150,27 @@ int64_t kda_fwd_chain_segments(const kda_desc_t *desc);
  *
  * Launch size.  A kernel launch covers at most 2^30 work-items.  Bigger
  * batches (from about half a million (sequence, head) pairs) are enqueued as
- * several launches of the same kernel, with identical results.  The
- * environment variable KDA_LAUNCH_PIECE=n (n > 0), read at every call of
- * kda_fwd and kda_decode, caps each launch at n chain groups of 8 (sequence,
- * head) pairs, n 64-token chunk rows or n decode (sequence, head) pairs, so
- * that small inputs take the same several-launch path (a testing aid; it
- * slows the call).
+ * several launches of the same kernel, with identical results
+ * (desc->launch_piece forces that path for small inputs).
+ *
+ * Value range.  The matrix-core operands of the state path are fp16 (11-bit
+ * significand, largest finite value 65504), with fp32 accumulation.  Every
+ * factor built from q, k and the gate is bounded by 1 in magnitude (unit-norm
+ * q and k, decays <= 1), so the limit falls on the terms that scale with v and
+ * the state.  Writing s_j for column j of the state (a K-vector), the delta
+ * rule only replaces the component of s_j along the written key, so
+ *   |S[i, j]| <= |s_j|_2 <= sqrt(|s_j(0)|_2^2 + sum_t v_t[j]^2)
+ * over the tokens t seen so far, and each pseudo-value
+ *   |u_t[j]| <= |v_t[j]| + |s_j|_2.
+ * The result is exact up to rounding while these stay below 65504: for
+ * example |v| <= 160 and |initial_state| <= 100 for sequences of up to 131072
+ * tokens (sqrt(128 * 100^2 + 131072 * 160^2) + 160 < 59000), or |v| <= 1500
+ * and |initial_state| <= 1000 up to 1024 tokens (< 51000).  These are worst-case bounds
+ * (keys chosen against the state); unit-scale activations stay orders of
+ * magnitude below them.  Larger magnitudes overflow fp16 silently and give
+ * inf or NaN outputs; no error is returned.  At the small end, values below
+ * 2^-14 (6.1e-5) lose significand bits in fp16 subnormals: v and the state
+ * should not be scaled below about 2^-12 of unit scale.
  *
  * With split chains (desc->chain_segments) the state chain of every sequence
  * runs in three launches instead of one: the map of every segment, an fp32
@@ -179,7 +201,9 @@ kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
  *   out              : [N, 1, H, 128] bf16.
  * Feeding kda_fwd's final_state in as initial_state continues a prefilled
  * sequence.  Errors as for kda_fwd (KDA_ERR_SHAPE when T != 1).  One kernel,
- * no workspace, no allocation; enqueued on `stream`. */
+ * no workspace, no allocation; enqueued on `stream`.  The step itself runs in
+ * fp32, but a state carried from kda_fwd is subject to kda_fwd's value range
+ * ("Value range" above). */
 kda_status_t kda_decode(const void *q, const void *k, const void *v, const void *g,
                         const void *beta, float scale, const float *A_log,
                         const float *dt_bias, float lower_bound,

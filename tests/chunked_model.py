@@ -72,9 +72,10 @@ def chunked_forward(w, C: int = 64):
     return out, fin
 
 
-def _chunk_wy(qq, kk, vv, gg, bb, A_log_h, dtb_h, lb):
+def _chunk_wy(qq, kk, vv, gg, bb, A_log_h, dtb_h, lb, with_inverse=False):
     """WY quantities of one chunk: (Qg, Mqk, W, U, Kbar, gn) with
-    Ut = U - W S, O = Qg S + Mqk Ut (unscaled), S_next = Diag(gn) S + Kbar^T Ut."""
+    Ut = U - W S, O = Qg S + Mqk Ut (unscaled), S_next = Diag(gn) S + Kbar^T Ut;
+    with_inverse also returns T = (I + A)^-1 last."""
     qn = qq / np.sqrt((qq * qq).sum(-1, keepdims=True) + EPS)
     kn = kk / np.sqrt((kk * kk).sum(-1, keepdims=True) + EPS)
     b = 1.0 / (1.0 + np.exp(-bb))
@@ -90,6 +91,8 @@ def _chunk_wy(qq, kk, vv, gg, bb, A_log_h, dtb_h, lb):
     W = Tm @ (b[:, None] * np.exp(G) * kn)
     U = Tm @ (b[:, None] * vv)
     Kbar = np.exp(G[-1][None, :] - G) * kn
+    if with_inverse:
+        return np.exp(G) * qn, Mqk, W, U, Kbar, np.exp(G[-1]), Tm
     return np.exp(G) * qn, Mqk, W, U, Kbar, np.exp(G[-1])
 
 

@@ -11,9 +11,11 @@ import oracle
 import gated_delta_rule_110_amd as kda
 
 # Tolerances: bf16 outputs within max-abs 2e-2 and relative RMS 5e-3 of the
-# fp64 oracle; an fp32 final state within relative 1e-3 (Frobenius, over the
-# whole tensor); a bf16 final state within relative 5e-3, since rounding the
-# exact state to bf16 alone costs about 1.7e-3.
+# fp64 oracle; an fp32 final state within relative 1e-3 (Frobenius), over the
+# whole tensor and for every (sequence, head) on its own, so that one bad short
+# sequence of a packed batch is not diluted by the long ones; a bf16 final state
+# within relative 5e-3 the same way, since rounding the exact state to bf16
+# alone costs about 1.7e-3.
 OUT_MAX_ABS = 2e-2
 OUT_REL_RMS = 5e-3
 STATE_REL_FP32 = 1e-3
@@ -25,13 +27,13 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_gpu(w, device="cuda", workspace=None, out=None, final=None, chain_segments=0):
+def run_gpu(w, device="cuda", workspace=None, out=None, final=None, chain_segments=0, launch_piece=0):
     wd = w.to(device)
     if final is None and w.final_state_dtype is not None:
         final = torch.empty((w.N, w.H, w.K, w.V), dtype=w.final_state_dtype, device=device)
     out, fin = kda.fwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, out, wd.A_log, wd.dt_bias,
                        w.lower_bound, wd.initial_state, final, wd.cu_seqlens, workspace=workspace,
-                       chain_segments=chain_segments)
+                       chain_segments=chain_segments, launch_piece=launch_piece)
     torch.cuda.synchronize()
     return out, fin
 
@@ -69,5 +71,6 @@ def compare(out_gpu, out_ref, fin_gpu=None, fin_ref=None, fin_dtype=None, label=
         res["state_rel_worst"] = worst
         assert np.isfinite(fin_gpu).all(), label + ": non-finite state"
         assert res["state_rel"] <= tol, (label, res)
+        assert res["state_rel_worst"] <= tol, (label, res)
     say("  %s %s" % (label, {k: "%.3e" % v for k, v in res.items()}))
     return res

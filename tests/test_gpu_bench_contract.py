@@ -33,8 +33,16 @@ def test_prefill_line(capsys):
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert r["kernel"] in d["kernel_ms"] and 0 < r["frac"] <= 1 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    # achieved = the path's algorithmic bytes (1282 B per token-head, plus the bf16 final state)
+    # over the dominant kernel's time; never the library's own intermediates
+    assert r["alg_bytes"] == 1282 * 8192 * 32 + 32 * 128 * 128 * 2
+    assert abs(r["achieved"] - r["alg_bytes"] / (d["kernel_ms"][r["kernel"]] * 1e-3) / 1e9) <= 1e-3 * r["achieved"]
+    assert r["frac_interface"] > r["frac"]
     assert r["traffic"] is None or r["traffic"] > 0
     assert r["copy_gbs"] > 1000 and set(r["kernels"]) == set(d["kernel_ms"])
+    shares = sum(k["alg_share_bytes"] for k in r["kernels"].values())
+    assert shares == r["alg_bytes"]  # the kernels' shares add up to the path's bytes
+    assert d["dtype"] == "bf16" and "fp16" in d["mfma_operands"]
 
 
 def test_decode_line(capsys):

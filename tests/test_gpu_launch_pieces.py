@@ -2,13 +2,11 @@
 
 A batch too big for one launch of 2^30 work-items is enqueued as several
 launches of the same kernel, each covering a range of chain groups, chunk rows
-or decode units.  KDA_LAUNCH_PIECE makes small inputs take that path.  Every
-(sequence, head) is computed by the same code either way, so the results must
-be bit-identical to one launch, and within the usual tolerances of the oracle.
+or decode units.  The descriptor's launch_piece cap makes small inputs take
+that path.  Every (sequence, head) is computed by the same code either way, so
+the results must be bit-identical to one launch, and within the usual
+tolerances of the oracle.
 """
-import contextlib
-import os
-
 import pytest
 import torch
 
@@ -19,19 +17,6 @@ from tests.parity import compare, run_gpu, run_oracle, say, to_np
 pytestmark = pytest.mark.gpu
 
 
-@contextlib.contextmanager
-def launch_piece(n):
-    old = os.environ.get("KDA_LAUNCH_PIECE")
-    os.environ["KDA_LAUNCH_PIECE"] = str(n)
-    try:
-        yield
-    finally:
-        if old is None:
-            del os.environ["KDA_LAUNCH_PIECE"]
-        else:
-            os.environ["KDA_LAUNCH_PIECE"] = old
-
-
 def _same(a, b):
     return (a is None and b is None) or torch.equal(a, b)
 
@@ -40,9 +25,8 @@ def _check_fwd(w, pieces, label, chain_segments=0):
     ref_out, ref_fin = run_gpu(w, chain_segments=chain_segments)
     ro, rf = run_oracle(w)
     for p in pieces:
-        say("case %s: KDA_LAUNCH_PIECE=%d" % (label, p))
-        with launch_piece(p):
-            out, fin = run_gpu(w, chain_segments=chain_segments)
+        say("case %s: launch_piece=%d" % (label, p))
+        out, fin = run_gpu(w, chain_segments=chain_segments, launch_piece=p)
         assert _same(out, ref_out) and _same(fin, ref_fin), (label, p)
         compare(to_np(out), ro, to_np(fin), rf, w.final_state_dtype, "%s piece %d" % (label, p))
 
@@ -80,11 +64,10 @@ def test_decode_in_pieces(init, final):
     wd = w.to("cuda")
     res = {}
     for p in (1000000, 4, 1):
-        say("case decode N=%d H=%d %s/%s: KDA_LAUNCH_PIECE=%d" % (N, H, init, final, p))
+        say("case decode N=%d H=%d %s/%s: launch_piece=%d" % (N, H, init, final, p))
         ht = torch.empty((N, H, 128, 128), dtype=w.final_state_dtype, device="cuda")
-        with launch_piece(p):
-            out, fin = kda.decode(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, None, wd.A_log, wd.dt_bias,
-                                  w.lower_bound, wd.initial_state, ht)
+        out, fin = kda.decode(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, None, wd.A_log, wd.dt_bias,
+                              w.lower_bound, wd.initial_state, ht, launch_piece=p)
         torch.cuda.synchronize()
         res[p] = (out, fin)
     for p in (4, 1):

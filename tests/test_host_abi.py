@@ -133,6 +133,7 @@ def test_chain_segments_rule(lib):
     assert kda.chain_segments_for(1, 8192, 4, -1) == -1
     # errors: a negative count; a split asked for together with cu_seqlens
     assert _call(lib, _desc(chain_segments=-2)) == 4
+    assert _call(lib, _desc(launch_piece=-1)) == 4              # negative launch cap
     assert _call(lib, _desc(chain_segments=2), cu=ctypes.c_void_p(FAKE)) == 3
     # 192 KiB of workspace per (batch row, segment, head): two maps and the entering state,
     # fp32 128 x 128 each (B = 2: only the unpacked layout counts)
