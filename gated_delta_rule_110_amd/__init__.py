@@ -24,7 +24,7 @@ import torch
 from ._build import LIB as LIB_PATH
 from ._build import build
 
-__all__ = ["fwd", "decode", "workspace_size", "chain_segments_for", "KdaArgumentError", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
+__all__ = ["fwd", "fwd_noalloc", "noalloc_max_workspace", "decode", "workspace_size", "chain_segments_for", "KdaArgumentError", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
            "KDA_FP32"]
 
 KDA_BF16 = 1
@@ -33,7 +33,7 @@ HEAD_DIM = 128
 
 _STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
                  4: "KDA_ERR_PARAM", 5: "KDA_ERR_DTYPE", 6: "KDA_ERR_ALIGN",
-                 7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP"}
+                 7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP", 9: "KDA_ERR_SCRATCH"}
 
 
 class KdaError(RuntimeError):
@@ -83,6 +83,10 @@ def library() -> ctypes.CDLL:
             lib.kda_fwd.restype = ctypes.c_int
             lib.kda_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_float,
                                     P, P, P, P, ctypes.POINTER(KdaDesc), P]
+            lib.kda_fwd_noalloc.restype = ctypes.c_int
+            lib.kda_fwd_noalloc.argtypes = lib.kda_fwd.argtypes
+            lib.kda_fwd_noalloc_max_workspace.restype = ctypes.c_size_t
+            lib.kda_fwd_noalloc_max_workspace.argtypes = []
             lib.kda_decode.restype = ctypes.c_int
             lib.kda_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_float,
                                        P, P, P, ctypes.POINTER(KdaDesc), P]
@@ -128,27 +132,10 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
-        scale: float, out: Optional[torch.Tensor], A_log: torch.Tensor, dt_bias: torch.Tensor,
-        lower_bound: float, initial_state: Optional[torch.Tensor] = None,
-        final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
-        workspace: Optional[torch.Tensor] = None,
-        phase_events=None, chain_segments: int = 0,
-        launch_piece: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """KDA forward on the current HIP stream.  Returns ``(out, final_state)``.
-
-    q, k, g: bf16 [B,T,H,128]; v: bf16 [B,T,H,128]; beta: bf16 logits [B,T,H];
-    A_log: fp32 [H]; dt_bias: fp32 [H,128]; lower_bound in [-5, 0];
-    initial_state / final_state: bf16 or fp32 [N,H,128,128] or None;
-    cu_seqlens: int64 [N+1] on the device (then B == 1) or None;
-    out: bf16 [B,T,H,128] or None (allocated); workspace: uint8 device tensor
-    of at least ``workspace_size`` bytes or None (allocated); phase_events:
-    None or the address of a caller-owned array of 4 hipEvent_t (instrumentation);
-    chain_segments: 0 (automatic), 1 (never) or the number of segments each
-    sequence's state chain is split into (batches without cu_seqlens);
-    launch_piece: kda_desc_t::launch_piece (0: the library's launch size).
-    """
-    lib = library()
+def _check_fwd_args(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens,
+                    chain_segments, launch_piece, allocate_out):
+    """Validate the forward's tensors and build its descriptor (no workspace yet).
+    Returns ``(descriptor, device, out)``."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         if t.dtype != torch.bfloat16:
             raise ValueError("%s must be bfloat16, got %s" % (name, t.dtype))
@@ -171,6 +158,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     else:
         N = B
     if out is None:
+        if not allocate_out:
+            raise ValueError("out must be given")
         out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=q.device)
     tensors = [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out),
                ("A_log", A_log), ("dt_bias", dt_bias), ("initial_state", initial_state),
@@ -194,6 +183,32 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     htd = _state_dtype(final_state, "final_state")
     d = _desc(B, T, H, N, h0d, htd, chain_segments=int(chain_segments), launch_piece=int(launch_piece))
     d.K, d.V = K, V
+    return d, dev, out
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+        scale: float, out: Optional[torch.Tensor], A_log: torch.Tensor, dt_bias: torch.Tensor,
+        lower_bound: float, initial_state: Optional[torch.Tensor] = None,
+        final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None,
+        phase_events=None, chain_segments: int = 0,
+        launch_piece: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """KDA forward on the current HIP stream.  Returns ``(out, final_state)``.
+
+    q, k, g: bf16 [B,T,H,128]; v: bf16 [B,T,H,128]; beta: bf16 logits [B,T,H];
+    A_log: fp32 [H]; dt_bias: fp32 [H,128]; lower_bound in [-5, 0];
+    initial_state / final_state: bf16 or fp32 [N,H,128,128] or None;
+    cu_seqlens: int64 [N+1] on the device (then B == 1) or None;
+    out: bf16 [B,T,H,128] or None (allocated); workspace: uint8 device tensor
+    of at least ``workspace_size`` bytes or None (allocated); phase_events:
+    None or the address of a caller-owned array of 4 hipEvent_t (instrumentation);
+    chain_segments: 0 (automatic), 1 (never) or the number of segments each
+    sequence's state chain is split into (batches without cu_seqlens);
+    launch_piece: kda_desc_t::launch_piece (0: the library's launch size).
+    """
+    lib = library()
+    d, dev, out = _check_fwd_args(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state,
+                                  cu_seqlens, chain_segments, launch_piece, allocate_out=True)
     need = int(lib.kda_fwd_workspace_size(ctypes.byref(d)))
     with torch.cuda.device(dev):
         if workspace is None:
@@ -211,6 +226,33 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     if st != 0:
         _raise_status(lib, st)
     return out, final_state
+
+
+def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                scale: float, out: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor,
+                lower_bound: float, initial_state: Optional[torch.Tensor] = None,
+                final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                chain_segments: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``kda_fwd_noalloc``: the forward of ``fwd`` in the library's static
+    scratch, allocating nothing (``out`` must be given).  Calls that can
+    overlap on one GPU share the scratch and race.  Returns ``(out, final_state)``."""
+    lib = library()
+    d, dev, out = _check_fwd_args(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state,
+                                  cu_seqlens, chain_segments, 0, allocate_out=False)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.kda_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                                 _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                                 _ptr(final_state), _ptr(cu_seqlens), _ptr(out), ctypes.byref(d),
+                                 ctypes.c_void_p(stream))
+    if st != 0:
+        _raise_status(lib, st)
+    return out, final_state
+
+
+def noalloc_max_workspace() -> int:
+    """Bytes of the static scratch ``fwd_noalloc`` runs in."""
+    return int(library().kda_fwd_noalloc_max_workspace())
 
 
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

@@ -6,6 +6,7 @@
 // (zuobiaodaohang.com FlashKDA page).
 #include <math.h>
 #include <stdlib.h>
+#include <mutex>
 #include <vector>
 #include "kda_common.h"
 #include "kda.h"
@@ -162,16 +163,32 @@ extern "C" const char *kda_status_string(kda_status_t s) {
         case KDA_ERR_ALIGN: return "misaligned pointer (tensors 16 bytes, workspace 256 bytes)";
         case KDA_ERR_WORKSPACE: return "workspace smaller than kda_fwd_workspace_size()";
         case KDA_ERR_HIP: return "HIP launch error";
+        case KDA_ERR_SCRATCH: return "workspace need exceeds the static scratch of kda_fwd_noalloc (kda_fwd_noalloc_max_workspace() bytes)";
     }
     return "unknown status";
 }
 
-extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
-                                const void *beta, float scale, const float *A_log,
-                                const float *dt_bias, float lower_bound,
-                                const void *initial_state, void *final_state,
-                                const int64_t *cu_seqlens, void *out,
-                                const kda_desc_t *desc, hipStream_t stream) {
+// Static scratch of kda_fwd_noalloc: the workspace of its calls, in the code
+// object's own device memory, so that the call needs no allocation.  Host code
+// must never pass `scratch` itself to a kernel or a copy: in host code the name
+// stands for a host-side shadow, not for the device array.  Its device address
+// is looked up once per device with hipGetSymbolAddress (scratch_on_device) and
+// only that address is used.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+void *scratch_on_device(int dev);
+
+// The forward pass behind kda_fwd and kda_fwd_noalloc.  With `noalloc` the
+// call runs in the library's static scratch (the descriptor's workspace is
+// ignored) and allocates nothing, on the device or the host; otherwise it runs
+// in the caller's workspace or one taken with hipMallocAsync.
+kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                      float scale, const float *A_log, const float *dt_bias, float lower_bound,
+                      const void *initial_state, void *final_state, const int64_t *cu_seqlens, void *out,
+                      const kda_desc_t *desc, bool noalloc, hipStream_t stream) {
     if (!desc || !A_log || !dt_bias) return KDA_ERR_NULL;
     Geometry geo;
     kda_status_t st = make_geometry(desc, cu_seqlens != nullptr, geo);
@@ -190,14 +207,20 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
         (cu_seqlens && !aligned(cu_seqlens, 8)) ||
         (initial_state && !aligned(initial_state, 4)) || (final_state && !aligned(final_state, 4)))
         return KDA_ERR_ALIGN;
-    if (cu_seqlens && validate_requested()) {
+    if (cu_seqlens && !noalloc && validate_requested()) {
         st = validate_cu_seqlens(cu_seqlens, geo.N, geo.T, stream);
         if (st != KDA_OK) return st;
     }
     const WorkspaceLayout lay = make_layout(geo);
-    char *ws = static_cast<char *>(desc->workspace);
+    char *ws = noalloc ? nullptr : static_cast<char *>(desc->workspace);
     bool owned = false;
-    if (ws) {
+    if (noalloc) {
+        if (lay.total > kScratchBytes) return KDA_ERR_SCRATCH;
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+        ws = static_cast<char *>(scratch_on_device(dev));
+        if (!ws) return KDA_ERR_HIP;
+    } else if (ws) {
         if (!aligned(ws, 256)) return KDA_ERR_ALIGN;
         if (desc->workspace_bytes < lay.total) return KDA_ERR_WORKSPACE;
     } else if (lay.total > 0) {
@@ -275,6 +298,47 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
         if (err == hipSuccess) err = e2;
     }
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of this device's `scratch`, looked up on the first call
+// with that device current; nullptr if the lookup fails.
+void *scratch_on_device(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
+                                const void *beta, float scale, const float *A_log,
+                                const float *dt_bias, float lower_bound,
+                                const void *initial_state, void *final_state,
+                                const int64_t *cu_seqlens, void *out,
+                                const kda_desc_t *desc, hipStream_t stream) {
+    return fwd_impl(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state, final_state, cu_seqlens,
+                    out, desc, false, stream);
+}
+
+extern "C" size_t kda_fwd_noalloc_max_workspace(void) { return kScratchBytes; }
+
+extern "C" kda_status_t kda_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                                        const void *beta, float scale, const float *A_log,
+                                        const float *dt_bias, float lower_bound,
+                                        const void *initial_state, void *final_state,
+                                        const int64_t *cu_seqlens, void *out,
+                                        const kda_desc_t *desc, hipStream_t stream) {
+    return fwd_impl(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state, final_state, cu_seqlens,
+                    out, desc, true, stream);
 }
 
 extern "C" kda_status_t kda_decode(const void *q, const void *k, const void *v, const void *g,

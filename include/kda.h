@@ -54,7 +54,8 @@ typedef enum {
     KDA_ERR_DTYPE = 5,       /* a state dtype other than KDA_BF16 / KDA_FP32      */
     KDA_ERR_ALIGN = 6,       /* a tensor pointer not 16-byte aligned (workspace: 256) */
     KDA_ERR_WORKSPACE = 7,   /* workspace_bytes smaller than kda_fwd_workspace_size() */
-    KDA_ERR_HIP = 8          /* a HIP launch error                                 */
+    KDA_ERR_HIP = 8,         /* a HIP launch error                                 */
+    KDA_ERR_SCRATCH = 9      /* kda_fwd_noalloc: the call needs more workspace than its static scratch */
 } kda_status_t;
 
 /* Shapes and the caller-owned workspace of one call.
@@ -182,6 +183,32 @@ kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g,
                      const void *initial_state, void *final_state,
                      const int64_t *cu_seqlens, void *out,
                      const kda_desc_t *desc, hipStream_t stream);
+
+/* kda_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation, arguments and errors as kda_fwd, except that the workspace
+ * is the library's own static scratch -- a device array of
+ * kda_fwd_noalloc_max_workspace() bytes (128 MiB) in the library's code
+ * object, which every GPU the library runs on holds until the process ends --
+ * and desc->workspace / workspace_bytes are ignored.  The call allocates
+ * nothing (no hipMalloc, hipMallocAsync or host allocation; KDA_VALIDATE is
+ * not honoured, since reading cu_seqlens back needs a host buffer).  A call
+ * whose kda_fwd_workspace_size() exceeds the scratch returns KDA_ERR_SCRATCH
+ * before anything is enqueued: 128 MiB covers about 1800 (64-token chunk,
+ * head) pairs, e.g. 2048 tokens at 32 heads, or 4096 tokens at 16 heads.
+ * The scratch holds no state between calls (every byte is written before it
+ * is read), but all calls on one GPU share it: calls that can overlap on one
+ * GPU (different streams, or different host threads) race and must be
+ * serialised by the caller. */
+kda_status_t kda_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, float scale, const float *A_log,
+                             const float *dt_bias, float lower_bound,
+                             const void *initial_state, void *final_state,
+                             const int64_t *cu_seqlens, void *out,
+                             const kda_desc_t *desc, hipStream_t stream);
+
+/* Bytes of the static scratch kda_fwd_noalloc runs in (128 MiB). */
+size_t kda_fwd_noalloc_max_workspace(void);
 
 /* One recurrent step per sequence -- the token-by-token form used during
  * generation ("¿Qué es la atención Kimi Delta y por qué es importante?",

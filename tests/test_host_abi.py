@@ -192,3 +192,25 @@ def test_python_status_errors():
     with pytest.raises(kda.KdaError) as e:
         kda._raise_status(lib, kda.KDA_ERR_HIP)
     assert not isinstance(e.value, ValueError) and isinstance(e.value, RuntimeError)
+
+
+def test_noalloc_validation_and_limit(lib):
+    # kda_fwd_noalloc validates exactly like kda_fwd, and refuses a call whose workspace
+    # would exceed its static scratch before touching the device (no GPU needed here)
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_fwd_noalloc_max_workspace.restype = ctypes.c_size_t
+    cap = lib.kda_fwd_noalloc_max_workspace()
+    assert cap == 128 << 20
+
+    def call(d, lb=-5.0):
+        ptrs = [ctypes.c_void_p(FAKE)] * 5
+        return lib.kda_fwd_noalloc(*ptrs, ctypes.c_float(0.1), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                                   ctypes.c_float(lb), None, None, None, ctypes.c_void_p(FAKE), ctypes.byref(d),
+                                   None)
+    assert call(_desc(K=64)) == 3
+    assert call(_desc(), lb=0.5) == 4
+    assert call(_desc(launch_piece=-1)) == 4
+    big = _desc(T=8192, H=32)  # 4096 (chunk, head) pairs: about 290 MiB of workspace
+    assert kda.workspace_size(1, 8192, 32) > cap
+    assert call(big) == 9
+    assert lib.kda_status_string(9).startswith(b"workspace need exceeds the static scratch")
