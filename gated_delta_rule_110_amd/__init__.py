@@ -24,7 +24,8 @@ import torch
 from ._build import LIB as LIB_PATH
 from ._build import build
 
-__all__ = ["fwd", "fwd_noalloc", "noalloc_max_workspace", "decode", "workspace_size", "chain_segments_for", "KdaArgumentError", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
+__all__ = ["fwd", "fwd_noalloc", "noalloc_max_workspace", "decode", "workspace_size", "chain_segments_for",
+           "pipelined_for", "KdaArgumentError", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
            "KDA_FP32"]
 
 KDA_BF16 = 1
@@ -63,7 +64,7 @@ class KdaDesc(ctypes.Structure):
                 ("initial_state_dtype", ctypes.c_int32), ("final_state_dtype", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("phase_events", ctypes.c_void_p), ("chain_segments", ctypes.c_int64),
-                ("launch_piece", ctypes.c_int64)]
+                ("launch_piece", ctypes.c_int64), ("pipeline", ctypes.c_int64)]
 
 
 _lock = threading.Lock()
@@ -92,6 +93,8 @@ def library() -> ctypes.CDLL:
                                        P, P, P, ctypes.POINTER(KdaDesc), P]
             lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
             lib.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(KdaDesc)]
+            lib.kda_fwd_pipelined.restype = ctypes.c_int
+            lib.kda_fwd_pipelined.argtypes = [ctypes.POINTER(KdaDesc)]
             lib.kda_fwd_chain_segments.restype = ctypes.c_int64
             lib.kda_fwd_chain_segments.argtypes = [ctypes.POINTER(KdaDesc)]
             lib.kda_status_string.restype = ctypes.c_char_p
@@ -101,15 +104,25 @@ def library() -> ctypes.CDLL:
 
 
 def _desc(B, T, H, N, h0_dtype=0, ht_dtype=0, workspace=None, nbytes=0, chain_segments=0,
-          launch_piece=0) -> KdaDesc:
+          launch_piece=0, pipeline=0) -> KdaDesc:
     return KdaDesc(B, T, H, HEAD_DIM, HEAD_DIM, N, h0_dtype, ht_dtype,
-                   ctypes.c_void_p(workspace), nbytes, None, chain_segments, launch_piece)
+                   ctypes.c_void_p(workspace), nbytes, None, chain_segments, launch_piece, pipeline)
 
 
-def workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None, chain_segments: int = 0) -> int:
+def workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None, chain_segments: int = 0,
+                   pipeline: int = 0) -> int:
     """Workspace bytes ``fwd`` needs for these shapes (and chain split)."""
-    d = _desc(B, T, H, B if num_seqs is None else num_seqs, chain_segments=chain_segments)
+    d = _desc(B, T, H, B if num_seqs is None else num_seqs, chain_segments=chain_segments, pipeline=pipeline)
     return int(library().kda_fwd_workspace_size(ctypes.byref(d)))
+
+
+def pipelined_for(B: int, T: int, H: int, chain_segments: int = 0, pipeline: int = 0) -> bool:
+    """Whether ``fwd`` runs these shapes (without cu_seqlens) on the pipelined forward."""
+    d = _desc(B, T, H, B, chain_segments=chain_segments, pipeline=pipeline)
+    r = int(library().kda_fwd_pipelined(ctypes.byref(d)))
+    if r < 0:
+        raise ValueError("invalid shapes")
+    return r == 1
 
 
 def chain_segments_for(B: int, T: int, H: int, chain_segments: int = 0) -> int:
@@ -133,7 +146,7 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _check_fwd_args(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens,
-                    chain_segments, launch_piece, allocate_out):
+                    chain_segments, launch_piece, allocate_out, pipeline=0):
     """Validate the forward's tensors and build its descriptor (no workspace yet).
     Returns ``(descriptor, device, out)``."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -181,7 +194,8 @@ def _check_fwd_args(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_
             raise ValueError("%s must be [N,H,K,V] = %s" % (name, (N, H, K, V)))
     h0d = _state_dtype(initial_state, "initial_state")
     htd = _state_dtype(final_state, "final_state")
-    d = _desc(B, T, H, N, h0d, htd, chain_segments=int(chain_segments), launch_piece=int(launch_piece))
+    d = _desc(B, T, H, N, h0d, htd, chain_segments=int(chain_segments), launch_piece=int(launch_piece),
+              pipeline=int(pipeline))
     d.K, d.V = K, V
     return d, dev, out
 
@@ -192,7 +206,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None,
         phase_events=None, chain_segments: int = 0,
-        launch_piece: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        launch_piece: int = 0, pipeline: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KDA forward on the current HIP stream.  Returns ``(out, final_state)``.
 
     q, k, g: bf16 [B,T,H,128]; v: bf16 [B,T,H,128]; beta: bf16 logits [B,T,H];
@@ -204,11 +218,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     None or the address of a caller-owned array of 4 hipEvent_t (instrumentation);
     chain_segments: 0 (automatic), 1 (never) or the number of segments each
     sequence's state chain is split into (batches without cu_seqlens);
-    launch_piece: kda_desc_t::launch_piece (0: the library's launch size).
+    launch_piece: kda_desc_t::launch_piece (0: the library's launch size);
+    pipeline: kda_desc_t::pipeline (0: the two-kernel forward, 1: the pipelined one where it applies).
     """
     lib = library()
     d, dev, out = _check_fwd_args(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state,
-                                  cu_seqlens, chain_segments, launch_piece, allocate_out=True)
+                                  cu_seqlens, chain_segments, launch_piece, allocate_out=True,
+                                  pipeline=pipeline)
     need = int(lib.kda_fwd_workspace_size(ctypes.byref(d)))
     with torch.cuda.device(dev):
         if workspace is None:

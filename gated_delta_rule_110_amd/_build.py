@@ -10,8 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_intra.hip", "kda_chain.hip", "kda_segment.hip", "kda_decode.hip", "kda_api.hip"]
-HEADERS = [os.path.join(CSRC, "kda_common.h"), os.path.join(INCLUDE, "kda.h")]
+SOURCES = ["kda_intra.hip", "kda_chain.hip", "kda_fused.hip", "kda_segment.hip", "kda_decode.hip", "kda_api.hip"]
+HEADERS = [os.path.join(CSRC, "kda_common.h"), os.path.join(CSRC, "kda_intra_body.h"), os.path.join(INCLUDE, "kda.h")]
 
 # -packed-fp32-ops off: hipcc must not emit packed fp32 VALU instructions.
 HIPCC_FLAGS = [
@@ -35,6 +35,7 @@ def hipcc() -> str:
 # runs two workgroups per CU and spends much of each one's life on dependent
 # chains): 1.2% faster than the default scheduler over 10 paired runs.
 EXTRA_FLAGS = {"kda_chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "kda_fused.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
                "kda_intra.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 

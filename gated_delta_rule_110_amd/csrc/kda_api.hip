@@ -79,7 +79,10 @@ kda_status_t make_geometry(const kda_desc_t *d, bool varlen, Geometry &g) {
         g.slots = g.N * nc;
     }
     if (g.slots > 0x7fffffffLL || g.N > 0x7fffffffLL) return KDA_ERR_SHAPE;
-    return choose_segments(d, g);
+    if (d->pipeline < 0 || d->pipeline > 1) return KDA_ERR_PARAM;
+    const kda_status_t st = choose_segments(d, g);
+    g.fused = st == KDA_OK && g.segs == 1 && d->pipeline == 1 && kda_fused_applies(g.N, g.H, g.varlen);
+    return st;
 }
 
 WorkspaceLayout make_layout(const Geometry &g) {
@@ -102,6 +105,11 @@ WorkspaceLayout make_layout(const Geometry &g) {
         L.off_mapM = o;    o = align_up(o + maps, 256);
         L.off_mapN = o;    o = align_up(o + maps, 256);
         L.off_sin = o;     o = align_up(o + maps, 256);
+    }
+    if (g.fused) {
+        L.off_flags = o; o = align_up(o + per * sizeof(int32_t), 256);
+        L.off_error = o; o = align_up(o + sizeof(int32_t), 256);
+        L.off_counters = o; o = align_up(o + 8 * sizeof(unsigned long long), 256);
     }
     L.total = o;
     return L;
@@ -150,6 +158,13 @@ extern "C" int64_t kda_fwd_chain_segments(const kda_desc_t *desc) {
     Geometry g;
     if (make_geometry(desc, false, g) != KDA_OK) return -1;
     return g.segs;
+}
+
+extern "C" int kda_fwd_pipelined(const kda_desc_t *desc) {
+    if (!desc) return -1;
+    Geometry g;
+    if (make_geometry(desc, false, g) != KDA_OK) return -1;
+    return g.fused ? 1 : 0;
 }
 
 extern "C" const char *kda_status_string(kda_status_t s) {
@@ -252,6 +267,29 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
     ia.Uf = reinterpret_cast<_Float16 *>(ws + lay.off_Uf);
     ia.gn = reinterpret_cast<float *>(ws + lay.off_gn);
     ia.piece_cap = desc->launch_piece;
+    if (geo.fused) {
+        // the pipelined forward: one grid for both sides (event 2 after it, event 3 right behind)
+        ChainArgs ca{};
+        ca.Wf = ia.Wf; ca.Qf = ia.Qf; ca.Kf = ia.Kf; ca.Af = ia.Af; ca.Uf = ia.Uf; ca.gn = ia.gn;
+        ca.T = geo.T; ca.H = geo.H; ca.N = geo.N; ca.nc_fixed = geo.nc_fixed;
+        ca.scale = scale;
+        ca.h0 = initial_state; ca.ht = final_state;
+        ca.h0_bf16 = desc->initial_state_dtype == KDA_BF16;
+        ca.ht_bf16 = desc->final_state_dtype == KDA_BF16;
+        ca.out = static_cast<uint16_t *>(out);
+        if (err == hipSuccess && geo.T > 0)
+            err = kda_launch_fused(ia, ca, reinterpret_cast<int32_t *>(ws + lay.off_flags),
+                                   reinterpret_cast<int32_t *>(ws + lay.off_error),
+                                   reinterpret_cast<unsigned long long *>(ws + lay.off_counters), geo.slots, stream);
+        else if (err == hipSuccess) err = kda_launch_chain(ca, stream);  // T = 0: the states only
+        if (ev && err == hipSuccess) err = hipEventRecord(ev[2], stream);
+        if (ev && err == hipSuccess) err = hipEventRecord(ev[3], stream);
+        if (owned) {
+            hipError_t e2 = hipFreeAsync(ws, stream);
+            if (err == hipSuccess) err = e2;
+        }
+        return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
     if (err == hipSuccess && geo.T > 0) err = kda_launch_intra(ia, geo.slots, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[2], stream);
 

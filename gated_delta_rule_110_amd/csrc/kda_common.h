@@ -54,6 +54,7 @@ struct Geometry {
     bool varlen;
     int64_t segs;         // segments each sequence's chunk chain is split into (1 = not split)
     int64_t segc;         // chunks per segment (the last one may hold fewer)
+    bool fused;           // the pipelined forward (kda_fused.hip) runs the call
 };
 
 struct WorkspaceLayout {
@@ -65,6 +66,9 @@ struct WorkspaceLayout {
     // every segment (fp32 [B segs, H, K, K] linear part, [B segs, H, K, V]
     // offset) and the state entering every segment (fp32 [B segs, H, K, V])
     size_t off_seg_cu, off_seg_off, off_mapM, off_mapN, off_sin;
+    // pipelined forward only: int32 [slots * H] chunk ready flags, an int32 error
+    // word and uint64 [8] producer item counters
+    size_t off_flags, off_error, off_counters;
     size_t total;
 };
 
@@ -274,3 +278,8 @@ hipError_t kda_launch_seg_table(int64_t B, int64_t T, int64_t segs, int64_t segc
                                 hipStream_t s);
 hipError_t kda_launch_seg_scan(const kda::ScanArgs &a, hipStream_t s);
 hipError_t kda_launch_decode(const kda::DecodeArgs &a, hipStream_t s);
+// The pipelined forward (kda_fused.hip): whether it handles these shapes, and
+// its launch (the flag clear and the fused producer / consumer grid).
+bool kda_fused_applies(int64_t N, int64_t H, bool varlen);
+hipError_t kda_launch_fused(const kda::IntraArgs &in, const kda::ChainArgs &ch, int32_t *flags, int32_t *error,
+                            unsigned long long *counters, int64_t slots, hipStream_t s);

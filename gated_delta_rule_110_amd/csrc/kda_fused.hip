@@ -1,0 +1,480 @@
+// kda_fused.hip -- the pipelined forward: intra-chunk producers and state-chain
+// consumers in one grid (gfx950).
+//
+// The two-kernel forward writes every chunk's intermediates (W, Q_gamma,
+// Kbar, A_qk, U, exp(G_n): 72.5 KiB per chunk and head) to HBM in one kernel
+// and reads them back in the next, and the serial chain of each (sequence,
+// head) starts only once the last chunk of the batch is done.  Here the two
+// run at the same time on different CUs, and the intermediates pass through
+// the L2 of the XCD both sides run on:
+//
+//   producers  (most workgroups)  two independent 4-wave halves each; a half
+//              runs the intra-chunk computation (kda_intra_body.h) for one
+//              (chunk, head) after another, stores the intermediates, waits
+//              until the stores have reached L2 and then sets the chunk's
+//              ready flag.  Producers never wait on anything else.
+//   consumers  (4 workgroups per XCD) carry whole (sequence, head) chains,
+//              all 128 value columns per workgroup: two loader waves poll the
+//              ready flag of the next chunk and copy its intermediates from L2
+//              into a two-slot LDS ring; four chain waves, each with 32
+//              columns of the fp32 state in MFMA accumulators, compute the
+//              pseudo-values Ut = U - W S, the chunk's outputs
+//              O = scale (Q_gamma S + A_qk Ut) and the next state
+//              S <- Diag(exp(G_n)) S + Kbar^T Ut.
+//
+// Workgroup b runs on XCD b % 8 (the hardware dispatches workgroups to the
+// XCDs round-robin).  Consumer workgroups take the heads h with h % 8 equal to
+// their XCD, and so do the producers, so every intermediate is read by the XCD
+// that wrote it, from its own L2: no HBM round trip and no prefetch.  Producers
+// walk their XCD's (chunk, head) pairs in the order the consumers need them:
+// rounds of as many chains as the XCD has consumers, chunk by chunk.
+//
+// Every wait is bounded (a consumer that runs out of patience marks the
+// workspace's error word and carries on), and the producers never wait, so
+// the grid always drains.  Used for batches without cu_seqlens when H is a
+// multiple of 8; the flags are cleared by kda_fused_clear_kernel first.
+#include "kda_intra_body.h"
+
+using namespace kda;
+
+namespace {
+
+constexpr int kFusedThreads = 512;        // 8 waves
+constexpr int kChainWaves = 4;            // consumer: 32 value columns each
+constexpr int kRingSlots = 2;
+// Consumer ring slot: -W 16 frags, Kbar^T 16, U (all 8 column blocks) 16, exp(G_n) 1, Q_gamma 16, A_qk 8
+constexpr int kFW = 0, kFK = 16, kFU = 32, kFG = 48, kFQ = 49, kFA = 65, kFrags = 73;
+#ifndef FUSED_NT_LOADS
+#define FUSED_NT_LOADS 1
+#endif
+constexpr bool kProducerNTLoads = FUSED_NT_LOADS;  // producers' input loads bypass L2 residency
+constexpr int kSpinMax = 1 << 20;          // bounded waits: about 0.1 s of polling each
+
+struct __align__(16) ConsumerSmem {
+    h8 ring[kRingSlots][kFrags][64];
+};
+
+union __align__(16) FusedSmem {
+    intra::IntraSmem half[2];
+    ConsumerSmem cons;
+};
+
+struct FusedArgs {
+    IntraArgs in;           // producer side (fixed-length batches: in.cu == nullptr)
+    ChainArgs ch;           // consumer side (same intermediates; ch.cu == nullptr)
+    int32_t *flags;         // [slots * H] 1 once a (chunk, head)'s intermediates are in L2
+    int32_t *error;         // set to 1 when a bounded wait ran out
+    unsigned long long *counters;  // [8] the next producer item of each XCD
+    int nconsumers;         // consumer workgroups (multiple of 8); blockIdx [0, nconsumers)
+    int nproducers;         // producer workgroups (multiple of 8); the rest of the grid
+};
+
+__device__ __forceinline__ h8 pack_frag(const f4 &t0, const f4 &t1) {
+    h8 r;
+    r[0] = (_Float16)t0[0]; r[1] = (_Float16)t0[1]; r[2] = (_Float16)t0[2]; r[3] = (_Float16)t0[3];
+    r[4] = (_Float16)t1[0]; r[5] = (_Float16)t1[1]; r[6] = (_Float16)t1[2]; r[7] = (_Float16)t1[3];
+    return r;
+}
+
+// 16 bytes per lane from global memory straight into LDS, bypassing the CU's
+// L1 (sc0): the line was written by another CU of this XCD moments ago.
+__device__ __forceinline__ void dma16_l2(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)l, 16, 0, 1);
+}
+
+// A barrier over the four waves of one producer half, on an LDS counter: the
+// two halves of a workgroup then run independently (s_barrier would hold
+// both).  `target` counts the arrivals expected so far (4 per barrier).
+struct HalfBarrier {
+    uint32_t *ctr;
+    uint32_t target;
+    int32_t *error;
+    __device__ __forceinline__ void operator()() {
+        target += 4;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        int it = 0;
+        while ((int32_t)(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) - target) < 0) {
+            if (++it == kSpinMax) {
+                __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+    }
+};
+
+// The ready flags live in the L2 of the XCD that writes and reads them: the
+// producer stores a flag after its data has reached that L2, and the consumer
+// polls it with a load that bypasses only its CU's L1 (sc0).  An agent-scope
+// atomic would go past L2 to memory and back on every chunk step.
+__device__ __forceinline__ int32_t load_flag_l2(const int32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void store_flag_l2(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Wait until a chunk's ready flag is set (bounded).  Once any wait of the
+// call has run out, the others give up at once, so that a failed call still
+// drains quickly.
+__device__ __forceinline__ void wait_ready(const int32_t *flag, int32_t *error) {
+    int it = 0;
+    while (load_flag_l2(flag) == 0) {
+        if (++it == kSpinMax) {
+            __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        if ((it & 63) == 0 && __hip_atomic_load(error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    asm volatile("" ::: "memory");
+}
+
+// Chains and producer items of one XCD.  Chain i of XCD x is (sequence
+// i / (H/8), head 8 (i % (H/8)) + x).  The XCD's items are taken in rounds of
+// Q chains (Q = consumers per XCD; the last round may hold fewer), chunk by
+// chunk within a round, chain by chain within a chunk: the order in which the
+// consumers need them.
+struct XcdPlan {
+    int64_t H8, CH, Q, nc;
+    __device__ __forceinline__ int64_t items() const { return CH * nc; }
+    __device__ __forceinline__ void item(int64_t m, int64_t &chain, int64_t &c) const {
+        const int64_t full = CH / Q;           // full rounds
+        const int64_t F = full * Q * nc;       // items in the full rounds
+        if (m < F) {
+            const int64_t per_round = Q * nc;
+            const int64_t r = m / per_round, rem = m - r * per_round;
+            c = rem / Q;
+            chain = r * Q + (rem - c * Q);
+        } else {
+            const int64_t q = CH - full * Q, rem = m - F;
+            c = rem / q;
+            chain = full * Q + (rem - c * q);
+        }
+    }
+};
+
+// ---- producer half ----------------------------------------------------------
+// Items are handed out by a per-XCD counter, so that the halves finish within
+// one item of each other.  Thread 0 of the half fetches the next item while
+// the current one is computed; the half's barrier before the ready flag
+// publishes it to the other three waves.
+__device__ __forceinline__ void producer_half(FusedSmem &sm, uint32_t *bar_ctr, int64_t *next_item,
+                                              const FusedArgs &fa, int x, int hf) {
+    const IntraArgs &a = fa.in;
+    const XcdPlan plan{a.H / 8, a.N * (a.H / 8), fa.nconsumers / 8, a.nc_fixed};
+    HalfBarrier bar{bar_ctr, 0, fa.error};
+    unsigned long long *counter = fa.counters + x;
+    const int64_t M = plan.items();
+    const bool lead = (threadIdx.x & 255) == 0;
+    if (lead) *next_item = (int64_t)__hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bar();
+    int64_t m = *next_item;
+    while (m < M) {
+        int64_t mn = 0;
+        if (lead) mn = (int64_t)__hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int64_t chain, c;
+        plan.item(m, chain, c);
+        // the lane index made opaque inside the loop: otherwise the compiler
+        // hoists the chunk's lane-dependent set-up out of the loop and keeps it
+        // live throughout, which costs more registers than the intra-chunk
+        // computation has to spare
+        int tid = (int)(threadIdx.x & 255);
+        asm volatile("" : "+v"(tid));
+        const int64_t n = chain / plan.H8;
+        const int64_t h = __builtin_amdgcn_readfirstlane((int)(8 * (chain - n * plan.H8) + x));
+        const int64_t slot = n * plan.nc + c;
+        intra::intra_chunk<false, HalfBarrier &, kProducerNTLoads>(a, slot, h, sm.half[hf], tid, bar);
+        // every wave's stores have reached L2 before the flag says so
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lead) *next_item = mn;
+        bar();
+        if (lead) store_flag_l2(fa.flags + slot * a.H + h, 1);
+        m = *next_item;
+    }
+}
+
+// ---- consumer -----------------------------------------------------------------
+// Copy chunk `ws`'s operands into ring slot `rs`: loader wave 0 takes -W,
+// Kbar^T, U and exp(G_n) (49 copies), loader wave 1 Q_gamma and the 6 A_qk
+// fragments that are not identically zero (22 copies).
+__device__ __forceinline__ void consumer_copy(ConsumerSmem &sm, const ChainArgs &a, int64_t ws, int rs, int ld,
+                                              int lane) {
+    if (ld == 0) {
+        const h8 *W = reinterpret_cast<const h8 *>(a.Wf + ws * kWfElems) + lane;
+        const h8 *K = reinterpret_cast<const h8 *>(a.Kf + ws * kKfElems) + lane;
+        const h8 *U = reinterpret_cast<const h8 *>(a.Uf + ws * kUfElems) + lane;
+#pragma unroll
+        for (int f = 0; f < 16; ++f) dma16_l2(W + f * 64, &sm.ring[rs][kFW + f][0]);
+#pragma unroll
+        for (int f = 0; f < 16; ++f) dma16_l2(K + f * 64, &sm.ring[rs][kFK + f][0]);
+#pragma unroll
+        for (int f = 0; f < 16; ++f) dma16_l2(U + f * 64, &sm.ring[rs][kFU + f][0]);
+        if (lane < 32) dma16_l2(reinterpret_cast<const h8 *>(a.gn + ws * kGnElems) + lane, &sm.ring[rs][kFG][0]);
+    } else {
+        const h8 *Q = reinterpret_cast<const h8 *>(a.Qf + ws * kQfElems) + lane;
+        const h8 *A = reinterpret_cast<const h8 *>(a.Af + ws * kAfElems) + lane;
+#pragma unroll
+        for (int f = 0; f < 16; ++f) dma16_l2(Q + f * 64, &sm.ring[rs][kFQ + f][0]);
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+            if (f != 1 && f != 3) dma16_l2(A + f * 64, &sm.ring[rs][kFA + f][0]);  // [it][kb]: rows 0..31 stop at column 31
+    }
+}
+
+// One chunk step of chain wave cw (value blocks 2 cw, 2 cw + 1) from ring slot
+// rs, in three phases that each read their operand fragments from LDS in one
+// batch (one exposed LDS latency per phase): the pseudo-values Ut = U - W S,
+// the state update S <- Diag(exp(G_n)) S + Kbar^T Ut, and the outputs from
+// the state entering the chunk and Ut, O^T = S^T Q_gamma^T + Ut^T A_qk^T
+// (transposed so that a lane holds four consecutive value columns of one
+// token).
+__device__ __forceinline__ void consumer_step(ConsumerSmem &sm, f4 (&S)[2][8], int rs, int cw, int lane,
+                                              float scale, uint16_t *out_chunk, int64_t row_stride, int64_t rows) {
+    h8 Sb[2][4];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) Sb[bb][kb] = pack_frag(S[bb][2 * kb], S[bb][2 * kb + 1]);
+    h8 Ub[2][2];
+    {
+        h8 Wf[16];
+#pragma unroll
+        for (int f = 0; f < 16; ++f) Wf[f] = sm.ring[rs][kFW + f][lane];
+        f4 X[2][4];
+        const h4 *Ul = reinterpret_cast<const h4 *>(&sm.ring[rs][kFU][0]) + lane;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const h4 u = Ul[((2 * cw + bb) * 4 + it) * 64];
+                X[bb][it][0] = (float)u[0]; X[bb][it][1] = (float)u[1];
+                X[bb][it][2] = (float)u[2]; X[bb][it][3] = (float)u[3];
+            }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) X[bb][it] = mfma16x16x32_f16(Wf[it * 4 + kb], Sb[bb][kb], X[bb][it]);
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) Ub[bb][kb] = pack_frag(X[bb][2 * kb], X[bb][2 * kb + 1]);
+    }
+    {
+        h8 Kf[16];
+#pragma unroll
+        for (int f = 0; f < 16; ++f) Kf[f] = sm.ring[rs][kFK + f][lane];
+        const f4 *Gl = reinterpret_cast<const f4 *>(&sm.ring[rs][kFG][0]) + (lane >> 4);
+        f4 gd[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) gd[ct] = Gl[4 * ct];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) S[bb][ct] = S[bb][ct] * gd[ct];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) S[bb][ct] = mfma16x16x32_f16(Kf[ct * 2 + kb], Ub[bb][kb], S[bb][ct]);
+    }
+    {
+        h8 Qf[16], Af[8];
+#pragma unroll
+        for (int f = 0; f < 16; ++f) Qf[f] = sm.ring[rs][kFQ + f][lane];
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+            if (f != 1 && f != 3) Af[f] = sm.ring[rs][kFA + f][lane];
+        f4 O[2][4];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int it = 0; it < 4; ++it) O[bb][it] = f4{0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) O[bb][it] = mfma16x16x32_f16(Sb[bb][kb], Qf[it * 4 + kb], O[bb][it]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                if (kb == 0 || it >= 2)
+#pragma unroll
+                    for (int bb = 0; bb < 2; ++bb) O[bb][it] = mfma16x16x32_f16(Ub[bb][kb], Af[it * 2 + kb], O[bb][it]);
+        const int r = lane & 15;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int row = 16 * it + r;
+            if (row < rows) {
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) {
+                    uint2 pk;
+                    pk.x = (uint32_t)f32_to_bf16_bits(scale * O[bb][it][0]) |
+                           ((uint32_t)f32_to_bf16_bits(scale * O[bb][it][1]) << 16);
+                    pk.y = (uint32_t)f32_to_bf16_bits(scale * O[bb][it][2]) |
+                           ((uint32_t)f32_to_bf16_bits(scale * O[bb][it][3]) << 16);
+                    *reinterpret_cast<uint2 *>(out_chunk + row * row_stride + 16 * (2 * cw + bb)) = pk;
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void consumer(FusedSmem &smu, const FusedArgs &fa, int x, int j, int wave) {
+    ConsumerSmem &sm = smu.cons;
+    const ChainArgs &a = fa.ch;
+    const XcdPlan plan{a.H / 8, a.N * (a.H / 8), fa.nconsumers / 8, a.nc_fixed};
+    const int lane = (int)(threadIdx.x & 63);
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t H = a.H, nc = plan.nc;
+    for (int64_t chain = j; chain < plan.CH; chain += plan.Q) {
+        const int64_t n = chain / plan.H8;
+        const int64_t h = 8 * (chain - n * plan.H8) + x;
+        auto wsof = [&](int64_t c) { return (n * nc + c) * H + h; };
+        if (wave < kChainWaves) {
+            // per-chain lane set-up, kept inside the loop (see producer_half):
+            // the state's element offsets are 32-bit within the (n, h) slice
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int rr = ln & 15, gg = ln >> 4;
+            const int64_t sl = (n * H + h) * (int64_t)kK * kV;  // the (n, h) state slice
+            auto soff = [&](int bb, int ct, int e) { return (16 * ct + 4 * gg + e) * kV + 32 * wave + 16 * bb + rr; };
+            f4 S[2][8];
+            if (a.h0 && a.h0_bf16) {
+                const uint16_t *h0 = reinterpret_cast<const uint16_t *>(a.h0) + sl;
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) S[bb][ct][e] = bf16_bits_to_f32(h0[soff(bb, ct, e)]);
+            } else if (a.h0) {
+                const float *h0 = reinterpret_cast<const float *>(a.h0) + sl;
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) S[bb][ct][e] = h0[soff(bb, ct, e)];
+            } else {
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int ct = 0; ct < 8; ++ct) S[bb][ct] = f4{0, 0, 0, 0};
+            }
+            const int64_t row_stride = H * kV;
+            uint16_t *out0 = a.out + (n * a.T * H + h) * kV + 4 * gg;
+            for (int64_t c = 0; c < nc; ++c) {
+                lds_barrier();  // chunk c's ring slot is complete
+                int lc = lane;  // opaque in the loop (see producer_half)
+                asm volatile("" : "+v"(lc));
+                consumer_step(sm, S, (int)(c & 1), wave, lc, a.scale, out0 + kChunk * c * row_stride, row_stride,
+                              a.T - kChunk * c);
+            }
+            if (a.ht && a.ht_bf16) {
+                uint16_t *ht = reinterpret_cast<uint16_t *>(a.ht) + sl;
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ht[soff(bb, ct, e)] = f32_to_bf16_bits(S[bb][ct][e]);
+            } else if (a.ht) {
+                float *ht = reinterpret_cast<float *>(a.ht) + sl;
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ht[soff(bb, ct, e)] = S[bb][ct][e];
+            }
+        } else {
+            // loaders (waves 4 and 5): chunk c + 1 into the other slot while the
+            // chain waves work on chunk c.  Waves 6 and 7 copy nothing but pass
+            // the same barriers.
+            const int ld = wave - kChainWaves;
+            if (ld < 2) {
+                wait_ready(fa.flags + wsof(0), fa.error);
+                consumer_copy(sm, a, wsof(0), 0, ld, lane);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            lds_barrier();
+            for (int64_t c = 0; c + 1 < nc; ++c) {
+                if (ld < 2) {
+                    wait_ready(fa.flags + wsof(c + 1), fa.error);
+                    consumer_copy(sm, a, wsof(c + 1), (int)((c + 1) & 1), ld, lane);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+                lds_barrier();
+            }
+        }
+        lds_barrier();  // the ring is free for the next chain
+    }
+}
+
+__global__ __launch_bounds__(kFusedThreads, 1) void kda_fused_kernel(FusedArgs fa) {
+    __shared__ FusedSmem sm;
+    __shared__ uint32_t bar_ctr[2];
+    __shared__ int64_t next_item[2];
+    if (threadIdx.x < 2) bar_ctr[threadIdx.x] = 0;
+    __syncthreads();
+    const int b = (int)blockIdx.x;
+    const int x = b & 7;  // the XCD this workgroup runs on
+    // wave-uniform role indices (readfirstlane: the compiler then keeps the
+    // loop bounds and addresses derived from them in scalar registers)
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (b < fa.nconsumers) {
+        consumer(sm, fa, x, b >> 3, wave);
+    } else {
+        const int hf = wave >> 2;
+        producer_half(sm, &bar_ctr[hf], &next_item[hf], fa, x, hf);
+    }
+}
+
+// Clears the ready flags, the error word and the item counters of one call (a
+// kernel, not a memset, so that the call can be captured in a graph).
+__global__ __launch_bounds__(256) void kda_fused_clear_kernel(int32_t *flags, int64_t n, int32_t *error,
+                                                              unsigned long long *counters) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) flags[i] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *error = 0;
+    if (blockIdx.x == 0 && threadIdx.x < 8) counters[threadIdx.x] = 0;
+}
+
+}  // namespace
+
+// Consumer workgroups: 4 per XCD (fewer when the batch has fewer chains);
+// producers: the rest of the 256 CUs, one workgroup each.
+constexpr int kConsumersPerXcd = 4;
+constexpr int kFusedGrid = 256;
+
+bool kda_fused_applies(int64_t N, int64_t H, bool varlen) { return !varlen && H % 8 == 0 && N * H >= 8; }
+
+hipError_t kda_launch_fused(const IntraArgs &in, const ChainArgs &ch, int32_t *flags, int32_t *error,
+                            unsigned long long *counters, int64_t slots, hipStream_t s) {
+    const int64_t nflags = slots * in.H;
+    const int64_t blocks = (nflags + 255) / 256;
+    hipLaunchKernelGGL(kda_fused_clear_kernel, dim3((unsigned)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096)),
+                       dim3(256), 0, s, flags, nflags, error, counters);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    FusedArgs fa{};
+    fa.in = in;
+    fa.ch = ch;
+    fa.flags = flags;
+    fa.error = error;
+    fa.counters = counters;
+    const int64_t per_xcd_chains = in.N * in.H / 8;
+    const int64_t q = per_xcd_chains < kConsumersPerXcd ? per_xcd_chains : kConsumersPerXcd;
+    fa.nconsumers = (int)(8 * q);
+    fa.nproducers = kFusedGrid - fa.nconsumers;
+    hipLaunchKernelGGL(kda_fused_kernel, dim3(kFusedGrid), dim3(kFusedThreads), 0, s, fa);
+    return hipGetLastError();
+}

@@ -106,6 +106,15 @@ typedef struct {
      * several-launch path of very large ones.  Results are identical either
      * way.  Negative values are KDA_ERR_PARAM. */
     int64_t launch_piece;
+    /* 0: the two-kernel forward (intra-chunk kernel, then the state chain);
+     * 1: the pipelined forward where it applies -- batches without cu_seqlens,
+     * H a multiple of 8, no split chains -- otherwise the two-kernel one.  The
+     * pipelined forward runs the intra-chunk work and the state chains in one
+     * grid and passes the intermediates through L2; on MI355X it measures
+     * slower than the two-kernel forward on every workload tried, so it is
+     * not the default.  Other values are KDA_ERR_PARAM.  The two give the same
+     * bits. */
+    int64_t pipeline;
 } kda_desc_t;
 
 /* Bytes of workspace kda_fwd needs for these shapes (0 if the shapes are
@@ -119,6 +128,11 @@ size_t kda_fwd_workspace_size(const kda_desc_t *desc);
  * cu_seqlens never split), or -1 if the descriptor is invalid.  Pure host
  * arithmetic. */
 int64_t kda_fwd_chain_segments(const kda_desc_t *desc);
+
+/* 1 if kda_fwd runs these shapes and desc->pipeline (without cu_seqlens) on
+ * the pipelined forward, 0 if on the two-kernel one, -1 if the descriptor is
+ * invalid.  Pure host arithmetic. */
+int kda_fwd_pipelined(const kda_desc_t *desc);
 
 /* Enqueue the KDA forward pass on `stream` and return without synchronising.
  *

@@ -27,13 +27,13 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_gpu(w, device="cuda", workspace=None, out=None, final=None, chain_segments=0, launch_piece=0):
+def run_gpu(w, device="cuda", workspace=None, out=None, final=None, chain_segments=0, launch_piece=0, pipeline=0):
     wd = w.to(device)
     if final is None and w.final_state_dtype is not None:
         final = torch.empty((w.N, w.H, w.K, w.V), dtype=w.final_state_dtype, device=device)
     out, fin = kda.fwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, out, wd.A_log, wd.dt_bias,
                        w.lower_bound, wd.initial_state, final, wd.cu_seqlens, workspace=workspace,
-                       chain_segments=chain_segments, launch_piece=launch_piece)
+                       chain_segments=chain_segments, launch_piece=launch_piece, pipeline=pipeline)
     torch.cuda.synchronize()
     return out, fin
 
