@@ -1,4 +1,5 @@
-"""libkda: the KDA chunked forward pass on gfx950, and its thin Python binding.
+"""libkda: the KDA chunked forward pass on gfx950, its decode step and its
+gradient, and their thin Python binding.
 
 The binding only marshals arguments: it checks dtypes, devices and
 contiguity, allocates the output and workspace with torch when the caller
@@ -24,7 +25,8 @@ import torch
 from ._build import LIB as LIB_PATH
 from ._build import build
 
-__all__ = ["fwd", "fwd_noalloc", "noalloc_max_workspace", "decode", "workspace_size", "chain_segments_for",
+__all__ = ["fwd", "fwd_noalloc", "noalloc_max_workspace", "decode", "bwd", "bwd_workspace_size",
+           "workspace_size", "chain_segments_for",
            "pipelined_for", "KdaArgumentError", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
            "KDA_FP32"]
 
@@ -97,6 +99,11 @@ def library() -> ctypes.CDLL:
             lib.kda_fwd_pipelined.argtypes = [ctypes.POINTER(KdaDesc)]
             lib.kda_fwd_chain_segments.restype = ctypes.c_int64
             lib.kda_fwd_chain_segments.argtypes = [ctypes.POINTER(KdaDesc)]
+            lib.kda_bwd.restype = ctypes.c_int
+            lib.kda_bwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_float, P, P, P, P,
+                                    P, P, P, P, P, P, P, P, ctypes.POINTER(KdaDesc), P]
+            lib.kda_bwd_workspace_size.restype = ctypes.c_size_t
+            lib.kda_bwd_workspace_size.argtypes = [ctypes.POINTER(KdaDesc)]
             lib.kda_status_string.restype = ctypes.c_char_p
             lib.kda_status_string.argtypes = [ctypes.c_int]
             _lib = lib
@@ -269,6 +276,54 @@ def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
 def noalloc_max_workspace() -> int:
     """Bytes of the static scratch ``fwd_noalloc`` runs in."""
     return int(library().kda_fwd_noalloc_max_workspace())
+
+
+def bwd_workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None) -> int:
+    """Workspace bytes ``bwd`` needs for these shapes."""
+    d = _desc(B, T, H, B if num_seqs is None else num_seqs)
+    return int(library().kda_bwd_workspace_size(ctypes.byref(d)))
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+        scale: float, A_log: torch.Tensor, dt_bias: torch.Tensor, lower_bound: float,
+        d_out: torch.Tensor, d_final_state: Optional[torch.Tensor] = None,
+        initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, launch_piece: int = 0, chain_segments: int = 0,
+        with_d_initial: bool = True) -> dict:
+    """Gradient of ``fwd`` (``kda_bwd``) on the current HIP stream: for the loss
+    gradients ``d_out`` (bf16 [B,T,H,128]) and ``d_final_state`` (bf16 or fp32
+    [N,H,128,128], or None for zeros) returns a dict of fp32 tensors dq, dk, dg
+    ([B,T,H,128]), dv ([B,T,H,128]), dbeta ([B,T,H]), dA_log ([H]), ddt_bias
+    ([H,128]) and d_initial_state ([N,H,128,128], or None without
+    ``with_d_initial``).  Inputs as for ``fwd``."""
+    lib = library()
+    d, dev, d_out = _check_fwd_args(q, k, v, g, beta, d_out, A_log, dt_bias, initial_state, d_final_state,
+                                    cu_seqlens, chain_segments, launch_piece, allocate_out=False)
+    B, T, H, K = q.shape
+    N = d.num_seqs
+    need = int(lib.kda_bwd_workspace_size(ctypes.byref(d)))
+    f32 = dict(dtype=torch.float32, device=dev)
+    res = {"dq": torch.empty((B, T, H, K), **f32), "dk": torch.empty((B, T, H, K), **f32),
+           "dv": torch.empty((B, T, H, K), **f32), "dg": torch.empty((B, T, H, K), **f32),
+           "dbeta": torch.empty((B, T, H), **f32), "dA_log": torch.empty((H,), **f32),
+           "ddt_bias": torch.empty((H, K), **f32),
+           "d_initial_state": torch.empty((N, H, K, K), **f32) if with_d_initial else None}
+    with torch.cuda.device(dev):
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
+            raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
+        d.workspace = ctypes.c_void_p(workspace.data_ptr())
+        d.workspace_bytes = workspace.numel() * workspace.element_size()
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
+                         _ptr(dt_bias), float(lower_bound), _ptr(initial_state), _ptr(cu_seqlens), _ptr(d_out),
+                         _ptr(d_final_state), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dg"]),
+                         _ptr(res["dbeta"]), _ptr(res["d_initial_state"]), _ptr(res["dA_log"]),
+                         _ptr(res["ddt_bias"]), ctypes.byref(d), ctypes.c_void_p(stream))
+    if st != 0:
+        _raise_status(lib, st)
+    return res
 
 
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_intra.hip", "kda_chain.hip", "kda_fused.hip", "kda_segment.hip", "kda_decode.hip", "kda_api.hip"]
+SOURCES = ["kda_intra.hip", "kda_chain.hip", "kda_fused.hip", "kda_segment.hip", "kda_decode.hip", "kda_bwd.hip",
+           "kda_api.hip"]
 HEADERS = [os.path.join(CSRC, "kda_common.h"), os.path.join(CSRC, "kda_intra_body.h"), os.path.join(INCLUDE, "kda.h")]
 
 # -packed-fp32-ops off: hipcc must not emit packed fp32 VALU instructions.
@@ -34,7 +35,11 @@ def hipcc() -> str:
 # The intra-chunk kernel is scheduled for instruction-level parallelism (it
 # runs two workgroups per CU and spends much of each one's life on dependent
 # chains): 1.2% faster than the default scheduler over 10 paired runs.
+# The backward's per-chunk kernel runs one workgroup per CU (its LDS), so it may
+# use the whole register file; in this form its overflow goes to accumulator
+# registers rather than to scratch memory.
 EXTRA_FLAGS = {"kda_chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "kda_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "kda_fused.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
                "kda_intra.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 

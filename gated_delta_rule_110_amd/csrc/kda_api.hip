@@ -413,3 +413,172 @@ extern "C" kda_status_t kda_decode(const void *q, const void *k, const void *v, 
     da.piece_cap = desc->launch_piece;
     return kda_launch_decode(da, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
+
+// ---- backward -----------------------------------------------------------------
+
+namespace {
+
+struct BwdLayout {
+    WorkspaceLayout fwd;  // the forward's intermediates (unsplit, two-kernel)
+    size_t off_out, off_hs, off_dhs, off_dUt, off_qn, off_kn, off_G, off_rq, off_rk, off_bb, off_Mk, off_Tm, off_part;
+    size_t total;
+};
+
+// Geometry of a backward call: the forward's, never split nor pipelined.
+kda_status_t make_bwd_geometry(const kda_desc_t *d, bool varlen, Geometry &g) {
+    if (d->chain_segments >= 2) return KDA_ERR_UNSUPPORTED;
+    kda_desc_t e = *d;
+    e.chain_segments = 1;
+    e.pipeline = 0;
+    return make_geometry(&e, varlen, g);
+}
+
+BwdLayout make_bwd_layout(const Geometry &g) {
+    BwdLayout L{};
+    L.fwd = make_layout(g);
+    const size_t per = (size_t)g.slots * (size_t)g.H;
+    size_t o = L.fwd.total;
+    L.off_out = o;  o = align_up(o + (size_t)(g.B * g.T * g.H) * kV * 2, 256);
+    L.off_hs = o;   o = align_up(o + per * kK * kV * 4, 256);
+    L.off_dhs = o;  o = align_up(o + per * kK * kV * 4, 256);
+    L.off_dUt = o;  o = align_up(o + per * kChunk * kV * 4, 256);
+    L.off_qn = o;   o = align_up(o + per * kChunk * kK * 4, 256);
+    L.off_kn = o;   o = align_up(o + per * kChunk * kK * 4, 256);
+    L.off_G = o;    o = align_up(o + per * kChunk * kK * 4, 256);
+    L.off_rq = o;   o = align_up(o + per * kChunk * 4, 256);
+    L.off_rk = o;   o = align_up(o + per * kChunk * 4, 256);
+    L.off_bb = o;   o = align_up(o + per * kChunk * 4, 256);
+    L.off_Mk = o;   o = align_up(o + per * kChunk * kChunk * 4, 256);
+    L.off_Tm = o;   o = align_up(o + per * kChunk * kChunk * 4, 256);
+    L.off_part = o; o = align_up(o + per * (kK + 1) * 4, 256);
+    L.total = o;
+    return L;
+}
+
+}  // namespace
+
+extern "C" size_t kda_bwd_workspace_size(const kda_desc_t *desc) {
+    if (!desc) return 0;
+    Geometry g;
+    size_t need = 0;
+    bool ok = false;
+    if (make_bwd_geometry(desc, false, g) == KDA_OK) { need = make_bwd_layout(g).total; ok = true; }
+    if (desc->B == 1 && make_bwd_geometry(desc, true, g) == KDA_OK) {
+        const size_t p = make_bwd_layout(g).total;
+        need = p > need ? p : need;
+        ok = true;
+    }
+    return ok ? need : 0;
+}
+
+extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
+                                const void *beta, float scale, const float *A_log,
+                                const float *dt_bias, float lower_bound,
+                                const void *initial_state, const int64_t *cu_seqlens,
+                                const void *d_out, const void *d_final_state,
+                                float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                                float *d_initial_state, float *dA_log, float *ddt_bias,
+                                const kda_desc_t *desc, hipStream_t stream) {
+    if (!desc || !A_log || !dt_bias || !dA_log || !ddt_bias) return KDA_ERR_NULL;
+    Geometry geo;
+    kda_status_t st = make_bwd_geometry(desc, cu_seqlens != nullptr, geo);
+    if (st != KDA_OK) return st;
+    if (desc->launch_piece < 0) return KDA_ERR_PARAM;
+    if (geo.T > 0 && (!q || !k || !v || !g || !beta || !d_out || !dq || !dk || !dv || !dg || !dbeta))
+        return KDA_ERR_NULL;
+    if (!(lower_bound >= -5.0f && lower_bound <= 0.0f)) return KDA_ERR_PARAM;
+    if (!isfinite(scale)) return KDA_ERR_PARAM;
+    if (initial_state && desc->initial_state_dtype != KDA_BF16 && desc->initial_state_dtype != KDA_FP32)
+        return KDA_ERR_DTYPE;
+    if (d_final_state && desc->final_state_dtype != KDA_BF16 && desc->final_state_dtype != KDA_FP32)
+        return KDA_ERR_DTYPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(d_out, 16) ||
+        !aligned(dt_bias, 16) || !aligned(beta, 2) || !aligned(A_log, 4) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dg, 16) || !aligned(dbeta, 4) ||
+        !aligned(dA_log, 4) || !aligned(ddt_bias, 4) ||
+        (cu_seqlens && !aligned(cu_seqlens, 8)) || (initial_state && !aligned(initial_state, 4)) ||
+        (d_final_state && !aligned(d_final_state, 4)) || (d_initial_state && !aligned(d_initial_state, 4)))
+        return KDA_ERR_ALIGN;
+    if (cu_seqlens && validate_requested()) {
+        st = validate_cu_seqlens(cu_seqlens, geo.N, geo.T, stream);
+        if (st != KDA_OK) return st;
+    }
+    const BwdLayout lay = make_bwd_layout(geo);
+    char *ws = static_cast<char *>(desc->workspace);
+    bool owned = false;
+    if (ws) {
+        if (!aligned(ws, 256)) return KDA_ERR_ALIGN;
+        if (desc->workspace_bytes < lay.total) return KDA_ERR_WORKSPACE;
+    } else if (lay.total > 0) {
+        void *p = nullptr;
+        if (hipMallocAsync(&p, lay.total, stream) != hipSuccess) return KDA_ERR_HIP;
+        ws = static_cast<char *>(p);
+        owned = true;
+    }
+    const WorkspaceLayout &fl = lay.fwd;
+    int32_t *chunk_off = geo.varlen ? reinterpret_cast<int32_t *>(ws + fl.off_chunk_off) : nullptr;
+    int32_t *seq_order = geo.varlen ? reinterpret_cast<int32_t *>(ws + fl.off_seq_order) : nullptr;
+    hipError_t err = hipSuccess;
+    if (geo.varlen) err = kda_launch_chunk_table(cu_seqlens, geo.N, chunk_off, seq_order, stream);
+
+    // the forward: intermediates, then the chain storing every chunk's entering state
+    IntraArgs ia{};
+    ia.q = static_cast<const uint16_t *>(q); ia.k = static_cast<const uint16_t *>(k);
+    ia.v = static_cast<const uint16_t *>(v); ia.g = static_cast<const uint16_t *>(g);
+    ia.beta = static_cast<const uint16_t *>(beta);
+    ia.A_log = A_log; ia.dt_bias = dt_bias; ia.lower_bound = lower_bound;
+    ia.cu = cu_seqlens; ia.chunk_off = chunk_off;
+    ia.T = geo.T; ia.H = geo.H; ia.N = geo.N; ia.nc_fixed = geo.nc_fixed;
+    ia.Wf = reinterpret_cast<_Float16 *>(ws + fl.off_Wf);
+    ia.Qf = reinterpret_cast<_Float16 *>(ws + fl.off_Qf);
+    ia.Kf = reinterpret_cast<_Float16 *>(ws + fl.off_Kf);
+    ia.Af = reinterpret_cast<_Float16 *>(ws + fl.off_Af);
+    ia.Uf = reinterpret_cast<_Float16 *>(ws + fl.off_Uf);
+    ia.gn = reinterpret_cast<float *>(ws + fl.off_gn);
+    ia.piece_cap = desc->launch_piece;
+    if (err == hipSuccess && geo.T > 0) err = kda_launch_intra(ia, geo.slots, stream);
+    BwdArgs ba{};
+    ba.hs = reinterpret_cast<float *>(ws + lay.off_hs);
+    if (geo.T > 0) {
+        ChainArgs ca{};
+        ca.Wf = ia.Wf; ca.Qf = ia.Qf; ca.Kf = ia.Kf; ca.Af = ia.Af; ca.Uf = ia.Uf; ca.gn = ia.gn;
+        ca.cu = cu_seqlens; ca.chunk_off = chunk_off; ca.seq_order = seq_order;
+        ca.T = geo.T; ca.H = geo.H; ca.N = geo.N; ca.nc_fixed = geo.nc_fixed;
+        ca.scale = scale;
+        ca.h0 = initial_state; ca.ht = nullptr;
+        ca.h0_bf16 = desc->initial_state_dtype == KDA_BF16;
+        ca.out = reinterpret_cast<uint16_t *>(ws + lay.off_out);
+        ca.hs = ba.hs;
+        ca.piece_cap = desc->launch_piece;
+        if (err == hipSuccess) err = kda_launch_chain(ca, stream);
+    }
+    // the gradient
+    ba.q = ia.q; ba.k = ia.k; ba.v = ia.v; ba.g = ia.g; ba.beta = ia.beta;
+    ba.A_log = A_log; ba.dt_bias = dt_bias; ba.lower_bound = lower_bound; ba.scale = scale;
+    ba.dout = static_cast<const uint16_t *>(d_out);
+    ba.dht = d_final_state; ba.dht_bf16 = desc->final_state_dtype == KDA_BF16;
+    ba.cu = cu_seqlens; ba.chunk_off = chunk_off; ba.seq_order = seq_order;
+    ba.T = geo.T; ba.H = geo.H; ba.N = geo.N; ba.nc_fixed = geo.nc_fixed;
+    ba.slots = geo.T > 0 ? geo.slots : 0;
+    ba.Wf = ia.Wf; ba.Qf = ia.Qf; ba.Kf = ia.Kf; ba.Af = ia.Af; ba.gn = ia.gn;
+    ba.dhs = reinterpret_cast<float *>(ws + lay.off_dhs);
+    ba.dUt = reinterpret_cast<float *>(ws + lay.off_dUt);
+    ba.qn = reinterpret_cast<float *>(ws + lay.off_qn);
+    ba.kn = reinterpret_cast<float *>(ws + lay.off_kn);
+    ba.G = reinterpret_cast<float *>(ws + lay.off_G);
+    ba.rq = reinterpret_cast<float *>(ws + lay.off_rq);
+    ba.rk = reinterpret_cast<float *>(ws + lay.off_rk);
+    ba.bb = reinterpret_cast<float *>(ws + lay.off_bb);
+    ba.Mk = reinterpret_cast<float *>(ws + lay.off_Mk);
+    ba.Tm = reinterpret_cast<float *>(ws + lay.off_Tm);
+    ba.part = reinterpret_cast<float *>(ws + lay.off_part);
+    ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dg = dg; ba.dbeta = dbeta;
+    ba.dh0 = d_initial_state; ba.dA_log = dA_log; ba.ddt_bias = ddt_bias;
+    ba.piece_cap = desc->launch_piece;
+    if (err == hipSuccess) err = kda_launch_bwd(ba, stream);
+    if (owned) {
+        hipError_t e2 = hipFreeAsync(ws, stream);
+        if (err == hipSuccess) err = e2;
+    }
+    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}

@@ -1,0 +1,857 @@
+// kda_bwd.hip -- the backward pass of the KDA chunked forward (gfx950).
+//
+// The pages' kernels are forward-only ("性能与注意事项", zuobiaodaohang.com
+// FlashKDA page); this is the gradient of the same operation, in the chunked
+// form of the forward.  For one (sequence, head), with chunk c entering with
+// state S = h_c and leaving with S' (the forward: Ut = U - W S,
+// O = scale (Qg S + A_qk Ut), S' = Diag(exp(G_n)) S + Kbar^T Ut):
+//
+//   1. the forward chain, storing h_c (kda_chain.hip, save mode);
+//   2. kda_bwd_prep_kernel, per chunk: normalised q and k, b, the cumulative
+//      log-decay G, the decayed key Gram M (strictly lower) and
+//      T = (I + Diag(b) M)^-1, in fp32;
+//   3. kda_bwd_chain_kernel, per (sequence, head, 16 state columns), last
+//      chunk first, with dS the gradient of the state leaving the chunk:
+//        dUt = scale A_qk^T dO + Kbar dS
+//        dS <- Diag(exp(G_n)) dS - W^T dUt + scale Qg^T dO
+//      storing dh_c (= dS before the step) and dUt; the final dS is the
+//      initial state's gradient;
+//   4. kda_bwd_main_kernel, per chunk, independently: with Y = V - (gamma Khat) S,
+//      Ut = T Diag(b) Y and Z = T^T dUt,
+//        dv = Diag(b) Z,   dQg = scale dO S^T,   Zw = -Z S^T,   dKbar = Ut dS'^T,
+//        dA_qk = scale dO Ut^T (j <= i),   dA_kk = -Z Ut^T (j < i),
+//      then the decayed Gram matrices' gradients, the per-channel decays
+//      (a reverse cumulative sum of dG within the chunk), the gate, the norms
+//      and beta;
+//   5. kda_bwd_params_kernel: dA_log and ddt_bias, summed over the chunks.
+//
+// Every product here runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32):
+// lane (r, g) gives A[r][g] and B[g][r] of a 16x16x4 step and holds
+// C[4 g + e][r], so an operand can be read element by element from any layout.
+// The chain reads the forward's fp16 fragments (W, Kbar, Qg, A_qk) as they
+// are; the per-chunk kernels recompute their quantities in fp32.
+//
+// Decay factors exp(G_i - G_j) inside a chunk are split around a reference
+// row of each 16-row block (row 16 w + 8): with the log-decay >= -5 both
+// halves stay within exp(+-40) for the rows of the block, and rows of earlier
+// blocks only ever meet a factor <= 1.
+#include "kda_common.h"
+
+using namespace kda;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int64_t kMaxUnitsPerLaunch = int64_t(1) << 22;  // 2^30 work-items per launch
+constexpr int64_t kMaxGroupsPerLaunch = 65536;            // chain groups of 8 (8 x 8 x 320 threads each)
+
+__device__ __forceinline__ f4 mma(float a, float b, const f4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float softplus_acc(float x) { return x > 15.0f ? x : log1pf(expf(x)); }
+__device__ __forceinline__ float sigmoid_acc(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// Sum over the 16 lanes of a row group (lanes r = 0..15 with the same g).
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+// Sum over the four row groups (lanes with the same r).
+__device__ __forceinline__ float sum4g(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Token rows of chunk slot `slot`: first row t0 on the flattened [B*T] axis and
+// the valid count L (1..64); false for a slot past the last chunk of a packed batch.
+__device__ __forceinline__ bool chunk_rows(const BwdArgs &a, int64_t slot, int64_t &t0, int &L) {
+    if (a.cu) {
+        const int64_t total = a.chunk_off[a.N];
+        if (slot >= total) return false;
+        const int64_t n = seq_of_slot(a.chunk_off, a.N, slot);
+        const int64_t i = slot - a.chunk_off[n];
+        t0 = a.cu[n] + kChunk * i;
+        const int64_t rem = a.cu[n + 1] - t0;
+        L = (int)(rem < kChunk ? rem : kChunk);
+    } else {
+        const int64_t n = slot / a.nc_fixed;
+        const int64_t i = slot - n * a.nc_fixed;
+        t0 = n * a.T + kChunk * i;
+        const int64_t rem = a.T - kChunk * i;
+        L = (int)(rem < kChunk ? rem : kChunk);
+    }
+    return true;
+}
+
+// ---- 2. per-chunk preparation ------------------------------------------------
+
+struct PrepSmem {
+    float q[kChunk][kK + 1];
+    float k[kChunk][kK + 1];
+    float G[kChunk][kK + 1];
+    float M[kChunk][kChunk + 1];
+    float b[kChunk];
+    float xr[4][16];  // one row of T per wave, broadcast during the solve
+};
+
+__global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
+    __shared__ PrepSmem sm;
+    const int64_t ws = a.unit_base + blockIdx.x;  // chunk slot * H + head
+    const int64_t slot = ws / a.H, h = ws - slot * a.H;
+    int64_t t0;
+    int L;
+    if (!chunk_rows(a, slot, t0, L)) return;
+    const int64_t H = a.H;
+    const int tid = threadIdx.x;
+
+    // rows, norms, b and the per-channel log-decay; a quarter row per thread
+    {
+        const int row = tid >> 2, qt = tid & 3;
+        const bool valid = row < L;
+        const int64_t base = ((t0 + (valid ? row : 0)) * H + h) * kK + 32 * qt;
+        float qv[32], kv[32], gv[32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            unpack_bf16x8(*reinterpret_cast<const uint4 *>(a.q + base + 8 * i), qv + 8 * i);
+            unpack_bf16x8(*reinterpret_cast<const uint4 *>(a.k + base + 8 * i), kv + 8 * i);
+            unpack_bf16x8(*reinterpret_cast<const uint4 *>(a.g + base + 8 * i), gv + 8 * i);
+        }
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
+        sq += __shfl_xor(sq, 1); sq += __shfl_xor(sq, 2);
+        sk += __shfl_xor(sk, 1); sk += __shfl_xor(sk, 2);
+        const float rq = valid ? 1.0f / sqrtf(sq + 1e-6f) : 0.f;
+        const float rk = valid ? 1.0f / sqrtf(sk + 1e-6f) : 0.f;
+        const float nA = -expf(a.A_log[h]);
+        const float *dtb = a.dt_bias + h * kK + 32 * qt;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            sm.q[row][32 * qt + e] = qv[e] * rq;
+            sm.k[row][32 * qt + e] = kv[e] * rk;
+            const float z = nA * softplus_acc(gv[e] + dtb[e]);
+            sm.G[row][32 * qt + e] = valid ? fmaxf(a.lower_bound, z) : 0.f;
+        }
+        if (qt == 0) {
+            const float b = valid ? sigmoid_acc(bf16_bits_to_f32(a.beta[(t0 + row) * H + h])) : 0.f;
+            sm.b[row] = b;
+            a.rq[ws * kChunk + row] = rq;
+            a.rk[ws * kChunk + row] = rk;
+            a.bb[ws * kChunk + row] = b;
+        }
+    }
+    __syncthreads();
+    if (tid < kK) {  // G_i = sum_{t <= i} a_t, per channel
+        float run = 0.f;
+        for (int i = 0; i < kChunk; ++i) {
+            run += sm.G[i][tid];
+            sm.G[i][tid] = run;
+        }
+    }
+    __syncthreads();
+    {
+        float *qn = a.qn + ws * (kChunk * kK), *kn = a.kn + ws * (kChunk * kK), *G = a.G + ws * (kChunk * kK);
+        for (int idx = tid; idx < kChunk * kK; idx += kThreads) {
+            const int i = idx >> 7, d = idx & 127;
+            qn[idx] = sm.q[i][d];
+            kn[idx] = sm.k[i][d];
+            G[idx] = sm.G[i][d];
+        }
+    }
+
+    const int w = tid >> 6, lane = tid & 63, r = lane & 15, gq = lane >> 4;
+    // M[i][j] = sum_d khat_i khat_j exp(G_i - G_j), j < i; wave w takes row block w,
+    // with exp(G_i - G_j) = exp(G_i - ref) exp(ref - G_j), ref = G[16 w + 8]
+    float *Mk = a.Mk + ws * (kChunk * kChunk);
+    for (int J = 0; J < 4; ++J) {
+        f4 acc = f4{0, 0, 0, 0};
+        if (J <= w) {
+            for (int ks = 0; ks < 32; ++ks) {
+                const int d = 4 * ks + gq;
+                const float ref = sm.G[16 * w + 8][d];
+                const float av = sm.k[16 * w + r][d] * __expf(sm.G[16 * w + r][d] - ref);
+                const float bv = sm.k[16 * J + r][d] * __expf(ref - sm.G[16 * J + r][d]);
+                acc = mma(av, bv, acc);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * w + 4 * gq + e, j = 16 * J + r;
+            const float m = j < i ? acc[e] : 0.f;
+            sm.M[i][j] = m;
+            Mk[i * kChunk + j] = m;
+        }
+    }
+    __syncthreads();
+    // T = (I + Diag(b) M)^-1 by forward substitution, rows in lanes, wave w
+    // taking columns 16 w .. 16 w + 15: row c is final once rows < c are applied
+    {
+        const int j0 = 16 * w;
+        float x[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) x[jj] = lane == j0 + jj ? 1.f : 0.f;
+        const float br = sm.b[lane];
+        for (int c = 0; c < kChunk - 1; ++c) {
+            if (lane == c) {
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) sm.xr[w][jj] = x[jj];
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // one wave: LDS accesses in order
+            const float arc = lane > c ? br * sm.M[lane][c] : 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) x[jj] -= arc * sm.xr[w][jj];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        float *Tm = a.Tm + ws * (kChunk * kChunk) + lane * kChunk + j0;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) Tm[jj] = x[jj];
+    }
+}
+
+// ---- 3. the reverse state chain ----------------------------------------------
+
+constexpr int kChainWaves = 5;  // 4 compute waves + 1 loader
+constexpr int kFragK = 0, kFragA = 16, kFragW = 24, kFragQ = 40, kFrags = 56;
+
+struct __align__(16) BwdChainSmem {
+    h8 ops[2][kFrags][64];          // per slot: Kf, Af, Wf, Qf fragments of one chunk
+    float gn[2][kK];                // exp(G_n)
+    uint16_t dO[2][kChunk][16];     // the chunk's rows of the block's 16 columns (bf16)
+    f4 red[4][4][64];               // partial dUt tiles [wave][row tile][lane]
+    float dU[kChunk][17];           // dUt of the block
+};
+
+__device__ __forceinline__ void copy16(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+}
+
+__device__ __forceinline__ float ldh(const _Float16 *p, int idx) { return (float)p[idx]; }
+
+__global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdArgs a) {
+    __shared__ BwdChainSmem sm;
+    const int64_t H = a.H;
+    const int64_t NH = a.N * H;
+    const int64_t x = blockIdx.x;
+    const int64_t xcd = x & 7;
+    const int64_t sx = x >> 3;
+    const int vb = (int)(sx & 7);
+    const int64_t chain = a.chain_base + (sx >> 3) * 8 + xcd;  // the 8 blocks of a chain on one XCD
+    if (chain >= NH) return;
+    const int64_t i_seq = chain / H, h = chain - i_seq * H;
+    const int64_t n = a.seq_order ? (int64_t)a.seq_order[i_seq] : i_seq;
+    int64_t c0, nchunks, tseq, seqlen;
+    if (a.cu) {
+        c0 = a.chunk_off[n];
+        nchunks = a.chunk_off[n + 1] - c0;
+        tseq = a.cu[n];
+        seqlen = a.cu[n + 1] - tseq;
+    } else {
+        c0 = n * a.nc_fixed;
+        nchunks = a.nc_fixed;
+        tseq = n * a.T;
+        seqlen = a.T;
+    }
+    const int col0 = 16 * vb;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+
+    if (wave == 4) {
+        // ---- loader: chunk ci into slot s ------------------------------------
+        auto load = [&](int64_t ci, int s) {
+            const int64_t ws = (c0 + ci) * H + h;
+            const h8 *Kp = reinterpret_cast<const h8 *>(a.Kf + ws * kKfElems) + lane;
+            const h8 *Ap = reinterpret_cast<const h8 *>(a.Af + ws * kAfElems) + lane;
+            const h8 *Wp = reinterpret_cast<const h8 *>(a.Wf + ws * kWfElems) + lane;
+            const h8 *Qp = reinterpret_cast<const h8 *>(a.Qf + ws * kQfElems) + lane;
+#pragma unroll
+            for (int f = 0; f < 16; ++f) copy16(Kp + f * 64, &sm.ops[s][kFragK + f][0]);
+#pragma unroll
+            for (int f = 0; f < 8; ++f) copy16(Ap + f * 64, &sm.ops[s][kFragA + f][0]);
+#pragma unroll
+            for (int f = 0; f < 16; ++f) copy16(Wp + f * 64, &sm.ops[s][kFragW + f][0]);
+#pragma unroll
+            for (int f = 0; f < 16; ++f) copy16(Qp + f * 64, &sm.ops[s][kFragQ + f][0]);
+            if (lane < 32) copy16(reinterpret_cast<const h8 *>(a.gn + ws * kGnElems) + lane, &sm.gn[s][0]);
+            const int64_t rows = seqlen - kChunk * ci;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int p = lane + 64 * i, row = p >> 1, half = p & 1;
+                const int64_t tok = tseq + kChunk * ci + (row < rows ? row : 0);
+                copy16(a.dout + (tok * H + h) * kV + col0 + 8 * half,
+                       reinterpret_cast<char *>(&sm.dO[s][0][0]) + 64 * 16 * i);
+            }
+        };
+        if (nchunks > 0) {
+            load(nchunks - 1, 0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            for (int64_t s = 0; s < nchunks; ++s) {
+                if (s + 1 < nchunks) load(nchunks - 2 - s, (int)((s + 1) & 1));
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                lds_barrier();
+                lds_barrier();
+                lds_barrier();
+            }
+        }
+        return;
+    }
+
+    // ---- compute waves: wave w carries state rows 32 w .. 32 w + 31 ----------
+    const int w = wave;
+    f4 dS[2];  // tile t: rows 16 (2 w + t) + 4 g + e, column col0 + r
+    {
+        const int64_t sb = (n * H + h) * (int64_t)(kK * kV) + col0 + r;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t idx = sb + (int64_t)(16 * (2 * w + t) + 4 * g + e) * kV;
+                float v = 0.f;
+                if (a.dht) v = a.dht_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.dht)[idx])
+                                          : reinterpret_cast<const float *>(a.dht)[idx];
+                dS[t][e] = v;
+            }
+    }
+    if (nchunks > 0) {
+        lds_barrier();
+        for (int64_t s = 0; s < nchunks; ++s) {
+            const int64_t ci = nchunks - 1 - s;
+            const int slot = (int)(s & 1);
+            const int64_t ws = (c0 + ci) * H + h;
+            const int rows = (int)(seqlen - kChunk * ci < kChunk ? seqlen - kChunk * ci : kChunk);
+            const _Float16 *ops = reinterpret_cast<const _Float16 *>(&sm.ops[slot][0][0]);
+            // the gradient of the state leaving this chunk
+            {
+                float *dh = a.dhs + ws * (int64_t)(kK * kV) + col0 + r;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dh[(16 * (2 * w + t) + 4 * g + e) * kV] = dS[t][e];
+            }
+            // partial dUt over this wave's 32 state rows: Kbar[:, rows] dS[rows]
+            f4 acc[4];
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) acc[jt] = f4{0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ct = 2 * w + t;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float bv = dS[t][e];
+                    // Kbar[16 jt + r][16 ct + 4 g + e]: fragment (ct, jt / 2), lane 4 g + e + 16 (r / 4)
+#pragma unroll
+                    for (int jt = 0; jt < 4; ++jt) {
+                        const int idx = ((kFragK + ct * 2 + (jt >> 1)) * 64 + 4 * g + e + 16 * (r >> 2)) * 8 +
+                                        4 * (jt & 1) + (r & 3);
+                        acc[jt] = mma(ldh(ops, idx), bv, acc[jt]);
+                    }
+                }
+            }
+            // scale A_qk^T dO for row tile w: A_qk[i][16 w + r], i = 4 ks + g
+            {
+                f4 aq = f4{0, 0, 0, 0};
+                const int j = 16 * w + r;
+#pragma unroll 4
+                for (int ks = 0; ks < 16; ++ks) {
+                    const int i = 4 * ks + g;
+                    const int idx = ((kFragA + (i >> 4) * 2 + (w >> 1)) * 64 + (i & 15) + 16 * (r >> 2)) * 8 +
+                                    4 * (w & 1) + (r & 3);
+                    const float av = j <= i ? ldh(ops, idx) : 0.f;
+                    const float bv = i < rows ? bf16_bits_to_f32(sm.dO[slot][i][r]) : 0.f;
+                    aq = mma(av, bv, aq);
+                }
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt)
+                    if (jt == w) acc[jt] += a.scale * aq;
+            }
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) sm.red[w][jt][lane] = acc[jt];
+            lds_barrier();
+            // row tile w of dUt: lane holds dUt[16 w + 4 g + e][col0 + r]
+            {
+                const f4 u = sm.red[0][w][lane] + sm.red[1][w][lane] + sm.red[2][w][lane] + sm.red[3][w][lane];
+                float *du = a.dUt + ws * (int64_t)(kChunk * kV) + col0 + r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * w + 4 * g + e;
+                    sm.dU[i][r] = u[e];
+                    du[i * kV] = u[e];
+                }
+            }
+            lds_barrier();
+            // dS <- Diag(exp(G_n)) dS - W^T dUt + scale Qg^T dO   (Wf holds -W)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ct = 2 * w + t;
+                f4 nd;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nd[e] = sm.gn[slot][16 * ct + 4 * g + e] * dS[t][e];
+#pragma unroll 4
+                for (int ks = 0; ks < 16; ++ks) {
+                    const int i = 4 * ks + g;
+                    const int off = (((i >> 4) * 4 + (ct >> 1)) * 64 + (i & 15) + 16 * (r >> 2)) * 8 + 4 * (ct & 1) +
+                                    (r & 3);
+                    const float bo = i < rows ? a.scale * bf16_bits_to_f32(sm.dO[slot][i][r]) : 0.f;
+                    nd = mma(ldh(ops, kFragW * 64 * 8 + off), sm.dU[i][r], nd);
+                    nd = mma(ldh(ops, kFragQ * 64 * 8 + off), bo, nd);
+                }
+                dS[t] = nd;
+            }
+            lds_barrier();
+        }
+    }
+    if (a.dh0) {
+        float *d0 = a.dh0 + (n * H + h) * (int64_t)(kK * kV) + col0 + r;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d0[(16 * (2 * w + t) + 4 * g + e) * kV] = dS[t][e];
+    }
+}
+
+// ---- 4. the per-chunk gradient -----------------------------------------------
+
+constexpr int kRP = 132;  // row pitch of the 64 x 128 tiles
+constexpr int kTP = 68;   // row pitch of the 64 x 64 tiles
+
+struct MainSmem {
+    float U[kChunk][kRP];   // Ut, then dG and its reverse cumulative sum
+    float Z[kChunk][kRP];   // Diag(b) Y, then Z = T^T dUt
+    float D[kChunk][kRP];   // dO
+    float T[kChunk][kTP];   // T, then dA_qk
+    float X[kChunk][kTP];   // dM = Diag(b) dA_kk
+    float db[kChunk];
+    float b[kChunk];
+    float red[4][kK];       // per-wave column sums
+    float gns[kK];          // exp(G_n) * sum_v S * dS'
+    float pa[4];            // per-wave dA_log sums
+};
+
+__global__ __launch_bounds__(kThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
+    __shared__ MainSmem sm;
+    const int64_t ws = a.unit_base + blockIdx.x;
+    const int64_t slot = ws / a.H, h = ws - slot * a.H;
+    int64_t t0;
+    int L;
+    if (!chunk_rows(a, slot, t0, L)) return;
+    const int64_t H = a.H;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, r = lane & 15, gq = lane >> 4;
+    const float *S = a.hs + ws * (int64_t)(kK * kV);
+    const float *dSp = a.dhs + ws * (int64_t)(kK * kV);
+    const float *dUt = a.dUt + ws * (int64_t)(kChunk * kV);
+    const float *qn = a.qn + ws * (kChunk * kK);
+    const float *kn = a.kn + ws * (kChunk * kK);
+    const float *G = a.G + ws * (kChunk * kK);
+    const float *Mk = a.Mk + ws * (kChunk * kChunk);
+    const float scale = a.scale;
+    auto vval = [&](int i, int c) -> float {
+        return i < L ? bf16_bits_to_f32(a.v[((t0 + i) * H + h) * kV + c]) : 0.f;
+    };
+
+    // P0: dO, T and b into LDS
+    for (int idx = tid; idx < kChunk * kV; idx += kThreads) {
+        const int i = idx >> 7, c = idx & 127;
+        sm.D[i][c] = i < L ? bf16_bits_to_f32(a.dout[((t0 + i) * H + h) * kV + c]) : 0.f;
+    }
+    for (int idx = tid; idx < kChunk * kChunk; idx += kThreads)
+        sm.T[idx >> 6][idx & 63] = a.Tm[ws * (kChunk * kChunk) + idx];
+    if (tid < kChunk) {
+        sm.b[tid] = a.bb[ws * kChunk + tid];
+        sm.db[tid] = 0.f;
+    }
+    __syncthreads();
+
+    // wave w owns rows 16 w .. 16 w + 15 of every 64 x 128 result; lane (r, gq)
+    // of column tile ct holds rows 16 w + 4 gq + e of column 16 ct + r.  dG stays
+    // in registers; the gradients of qhat and khat are summed in place in dq and
+    // dk (each element has one owning lane), which the last phase turns into the
+    // gradients of q and k.
+    f4 dG[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) dG[ct] = f4{0, 0, 0, 0};
+    const int row0 = 16 * w + 4 * gq;  // + e
+    auto out_at = [&](int i, int d) -> int64_t { return ((t0 + i) * H + h) * kK + d; };
+
+    // P1: Diag(b) Y, Y = V - (gamma Khat) S
+    {
+        f4 acc[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
+        const int i = 16 * w + r;
+        #pragma unroll 2
+        for (int ks = 0; ks < 32; ++ks) {
+            const int d = 4 * ks + gq;
+            const float av = kn[i * kK + d] * __expf(G[i * kK + d]);
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) acc[ct] = mma(av, S[d * kV + 16 * ct + r], acc[ct]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ii = row0 + e, c = 16 * ct + r;
+                sm.Z[ii][c] = sm.b[ii] * (vval(ii, c) - acc[ct][e]);
+            }
+    }
+    __syncthreads();
+    // P2: Ut = T (Diag(b) Y); T[i][j] = 0 for j > i
+    {
+        f4 acc[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
+        #pragma unroll 2
+        for (int ks = 0; ks < 4 * (w + 1); ++ks) {
+            const float av = sm.T[16 * w + r][4 * ks + gq];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) acc[ct] = mma(av, sm.Z[4 * ks + gq][16 * ct + r], acc[ct]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.U[row0 + e][16 * ct + r] = acc[ct][e];
+    }
+    __syncthreads();
+    // P3: Z = T^T dUt; dv = Diag(b) Z; db += Z . v
+    {
+        f4 acc[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
+        #pragma unroll 2
+        for (int ks = 4 * w; ks < 16; ++ks) {
+            const float av = sm.T[4 * ks + gq][16 * w + r];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) acc[ct] = mma(av, dUt[(4 * ks + gq) * kV + 16 * ct + r], acc[ct]);
+        }
+        float dbp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ii = row0 + e, c = 16 * ct + r;
+                const float z = acc[ct][e];
+                sm.Z[ii][c] = z;
+                if (ii < L) {
+                    a.dv[((t0 + ii) * H + h) * kV + c] = sm.b[ii] * z;
+                    dbp[e] += z * vval(ii, c);
+                }
+            }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float s = sum16(dbp[e]);
+            if (r == 0) sm.db[row0 + e] += s;
+        }
+    }
+    __syncthreads();
+    // P4: dQg = scale dO S^T and Zw = -Z S^T
+    {
+        f4 aq[8], az[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) { aq[ct] = f4{0, 0, 0, 0}; az[ct] = aq[ct]; }
+        #pragma unroll 2
+        for (int ks = 0; ks < 32; ++ks) {
+            const float a1 = sm.D[16 * w + r][4 * ks + gq];
+            const float a2 = sm.Z[16 * w + r][4 * ks + gq];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                const float bv = S[(16 * ct + r) * kV + 4 * ks + gq];
+                aq[ct] = mma(a1, bv, aq[ct]);
+                az[ct] = mma(a2, bv, az[ct]);
+            }
+        }
+        float dbp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ii = row0 + e, d = 16 * ct + r;
+                const float qh = qn[ii * kK + d], kh = kn[ii * kK + d];
+                const float gam = __expf(G[ii * kK + d]);
+                const float bi = sm.b[ii];
+                const float dQg = scale * aq[ct][e], Zw = -az[ct][e];
+                if (ii < L) {
+                    a.dq[out_at(ii, d)] = gam * dQg;
+                    a.dk[out_at(ii, d)] = bi * gam * Zw;
+                }
+                dG[ct][e] += gam * qh * dQg + bi * gam * kh * Zw;
+                dbp[e] += Zw * gam * kh;
+            }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float s = sum16(dbp[e]);
+            if (r == 0) sm.db[row0 + e] += s;
+        }
+    }
+    // P5: dKbar = Ut dS'^T; dG_n
+    {
+        f4 acc[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
+        #pragma unroll 2
+        for (int ks = 0; ks < 32; ++ks) {
+            const float a1 = sm.U[16 * w + r][4 * ks + gq];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) acc[ct] = mma(a1, dSp[(16 * ct + r) * kV + 4 * ks + gq], acc[ct]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const int d = 16 * ct + r;
+            const float Gn = G[(L - 1) * kK + d];
+            float colp = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ii = row0 + e;
+                const float eK = __expf(Gn - G[ii * kK + d]);
+                const float kb = eK * kn[ii * kK + d];
+                const float dk = acc[ct][e];
+                if (ii < L) a.dk[out_at(ii, d)] += eK * dk;
+                dG[ct][e] -= kb * dk;
+                colp += kb * dk;
+            }
+            colp = sum4g(colp);
+            if (gq == 0) sm.red[w][d] = colp;
+        }
+        // exp(G_n) sum_v S[d][v] dS'[d][v], two threads per state row
+        {
+            const int d = tid >> 1, half = tid & 1;
+            const float *sr = S + d * kV + 64 * half, *dr = dSp + d * kV + 64 * half;
+            float s = 0.f;
+            for (int v = 0; v < 64; ++v) s += sr[v] * dr[v];
+            s += __shfl_xor(s, 1);
+            if (half == 0) sm.gns[d] = __expf(G[(L - 1) * kK + d]) * s;
+        }
+    }
+    // P6: dA_qk = scale dO Ut^T (j <= i), dA_kk = -Z Ut^T (j < i); db += dA_kk . M; dM = Diag(b) dA_kk
+    {
+        f4 accA[4], accK[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) { accA[jt] = f4{0, 0, 0, 0}; accK[jt] = accA[jt]; }
+        #pragma unroll 2
+        for (int ks = 0; ks < 32; ++ks) {
+            const float a1 = sm.D[16 * w + r][4 * ks + gq];
+            const float a2 = sm.Z[16 * w + r][4 * ks + gq];
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                if (jt <= w) {
+                    const float bv = sm.U[16 * jt + r][4 * ks + gq];
+                    accA[jt] = mma(a1, bv, accA[jt]);
+                    accK[jt] = mma(a2, bv, accK[jt]);
+                }
+            }
+        }
+        float dbp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ii = row0 + e, j = 16 * jt + r;
+                const float dAq = (jt <= w && j <= ii) ? scale * accA[jt][e] : 0.f;
+                const float dAk = (jt <= w && j < ii) ? -accK[jt][e] : 0.f;
+                dbp[e] += dAk * Mk[ii * kChunk + j];
+                sm.T[ii][j] = dAq;
+                sm.X[ii][j] = sm.b[ii] * dAk;
+            }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float s = sum16(dbp[e]);
+            if (r == 0) sm.db[row0 + e] += s;
+        }
+    }
+    __syncthreads();
+    // P7: the decayed Gram matrices P[i][j] = sum_d x_i y_j exp(G_i - G_j): for M
+    // (x = y = khat, gradient dM) and A_qk (x = qhat, y = khat, gradient dA_qk)
+    {
+        float refc[8];  // G at the reference row 16 w + 8, this lane's columns
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) refc[ct] = G[(16 * w + 8) * kK + 16 * ct + r];
+        // rows i of block w: sum_{j <= 16 w + 15} dP[i][j] y_j exp(ref - G_j), times exp(G_i - ref)
+        {
+            f4 rm[8], ra[8];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) { rm[ct] = f4{0, 0, 0, 0}; ra[ct] = rm[ct]; }
+            #pragma unroll 2
+        for (int ks = 0; ks < 4 * (w + 1); ++ks) {
+                const int j = 4 * ks + gq;
+                const float a1 = sm.X[16 * w + r][j], a2 = sm.T[16 * w + r][j];
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) {
+                    const int d = 16 * ct + r;
+                    const float bv = kn[j * kK + d] * __expf(refc[ct] - G[j * kK + d]);
+                    rm[ct] = mma(a1, bv, rm[ct]);
+                    ra[ct] = mma(a2, bv, ra[ct]);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ii = row0 + e, d = 16 * ct + r;
+                    const float s = __expf(G[ii * kK + d] - refc[ct]);
+                    const float RxM = rm[ct][e] * s, RxA = ra[ct][e] * s;
+                    if (ii < L) {
+                        a.dk[out_at(ii, d)] += RxM;
+                        a.dq[out_at(ii, d)] += RxA;
+                    }
+                    dG[ct][e] += kn[ii * kK + d] * RxM + qn[ii * kK + d] * RxA;
+                }
+        }
+        // columns j of block w: sum_{i >= 16 w} (dM[i][j] khat_i + dA_qk[i][j] qhat_i) exp(G_i - ref),
+        // times exp(ref - G_j)
+        {
+            f4 ry[8];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) ry[ct] = f4{0, 0, 0, 0};
+            #pragma unroll 2
+        for (int ks = 4 * w; ks < 16; ++ks) {
+                const int i = 4 * ks + gq;
+                const float a1 = sm.X[i][16 * w + r], a2 = sm.T[i][16 * w + r];
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) {
+                    const int d = 16 * ct + r;
+                    const float eg = __expf(G[i * kK + d] - refc[ct]);
+                    ry[ct] = mma(a1, kn[i * kK + d] * eg, ry[ct]);
+                    ry[ct] = mma(a2, qn[i * kK + d] * eg, ry[ct]);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int jj = row0 + e, d = 16 * ct + r;
+                    const float Ry = ry[ct][e] * __expf(refc[ct] - G[jj * kK + d]);
+                    if (jj < L) a.dk[out_at(jj, d)] += Ry;
+                    dG[ct][e] -= kn[jj * kK + d] * Ry;
+                }
+        }
+    }
+    // P8: dG_n into the last valid row, then da_t = sum_{i >= t} dG_i
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ii = row0 + e, d = 16 * ct + r;
+            float v = dG[ct][e];
+            if (ii == L - 1) v += sm.gns[d] + sm.red[0][d] + sm.red[1][d] + sm.red[2][d] + sm.red[3][d];
+            sm.U[ii][d] = ii < L ? v : 0.f;
+        }
+    __syncthreads();
+    if (tid < kK) {
+        float run = 0.f;
+        for (int i = kChunk - 1; i >= 0; --i) {
+            run += sm.U[i][tid];
+            sm.U[i][tid] = run;
+        }
+    }
+    __syncthreads();
+    // P9: norms, gate, outputs
+    {
+        float sq[4], sk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ii = row0 + e;
+            float a1 = 0.f, a2 = 0.f;
+            if (ii < L) {
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) {
+                    a1 += qn[ii * kK + 16 * ct + r] * a.dq[out_at(ii, 16 * ct + r)];
+                    a2 += kn[ii * kK + 16 * ct + r] * a.dk[out_at(ii, 16 * ct + r)];
+                }
+            }
+            sq[e] = sum16(a1);
+            sk[e] = sum16(a2);
+        }
+        const float nA = -expf(a.A_log[h]);
+        float pa = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const int d = 16 * ct + r;
+            const float dtb = a.dt_bias[h * kK + d];
+            float colp = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ii = row0 + e;
+                if (ii < L) {
+                    const int64_t o = out_at(ii, d);
+                    const float rq = a.rq[ws * kChunk + ii], rk = a.rk[ws * kChunk + ii];
+                    a.dq[o] = rq * (a.dq[o] - sq[e] * qn[ii * kK + d]);
+                    a.dk[o] = rk * (a.dk[o] - sk[e] * kn[ii * kK + d]);
+                    const float xg = bf16_bits_to_f32(a.g[o]) + dtb;
+                    const float z = nA * softplus_acc(xg);
+                    const float da = sm.U[ii][d];
+                    float dx = 0.f;
+                    if (z > a.lower_bound) {
+                        dx = da * nA * sigmoid_acc(xg);
+                        pa += da * z;
+                    }
+                    a.dg[o] = dx;
+                    colp += dx;
+                }
+            }
+            colp = sum4g(colp);
+            if (gq == 0) sm.red[w][d] = colp;
+        }
+        pa = sum4g(sum16(pa));
+        if (lane == 0) sm.pa[w] = pa;
+    }
+    __syncthreads();
+    float *part = a.part + ws * (kK + 1);
+    if (tid < kK) part[tid] = sm.red[0][tid] + sm.red[1][tid] + sm.red[2][tid] + sm.red[3][tid];
+    if (tid == kK) part[kK] = sm.pa[0] + sm.pa[1] + sm.pa[2] + sm.pa[3];
+    if (tid < L) {
+        const float b = sm.b[tid];
+        a.dbeta[(t0 + tid) * H + h] = sm.db[tid] * b * (1.f - b);
+    }
+}
+
+// ---- 5. the shared parameters ------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void kda_bwd_params_kernel(BwdArgs a) {
+    const int64_t h = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid > kK) return;
+    const int64_t total = a.cu ? (int64_t)a.chunk_off[a.N] : a.slots;
+    double s = 0.0;
+    for (int64_t slot = 0; slot < total; ++slot) s += (double)a.part[(slot * a.H + h) * (kK + 1) + tid];
+    if (tid < kK) a.ddt_bias[h * kK + tid] = (float)s;
+    else a.dA_log[h] = (float)s;
+}
+
+}  // namespace
+
+hipError_t kda_launch_bwd(const BwdArgs &a0, hipStream_t s) {
+    BwdArgs a = a0;
+    const int64_t units = a.slots * a.H;
+    const int64_t piece = launch_piece(kMaxUnitsPerLaunch, a.piece_cap);
+    for (int64_t u0 = 0; u0 < units; u0 += piece) {
+        a.unit_base = u0;
+        const int64_t nu = units - u0 < piece ? units - u0 : piece;
+        hipLaunchKernelGGL(kda_bwd_prep_kernel, dim3((unsigned)nu), dim3(kThreads), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t NH = a.N * a.H;
+    const int64_t groups = (NH + 7) / 8;
+    const int64_t gpiece = launch_piece(kMaxGroupsPerLaunch, a.piece_cap);
+    for (int64_t g0 = 0; g0 < groups; g0 += gpiece) {
+        a.chain_base = 8 * g0;
+        const int64_t ng = groups - g0 < gpiece ? groups - g0 : gpiece;
+        hipLaunchKernelGGL(kda_bwd_chain_kernel, dim3((unsigned)(ng * 64)), dim3(64 * kChainWaves), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    for (int64_t u0 = 0; u0 < units; u0 += piece) {
+        a.unit_base = u0;
+        const int64_t nu = units - u0 < piece ? units - u0 : piece;
+        hipLaunchKernelGGL(kda_bwd_main_kernel, dim3((unsigned)nu), dim3(kThreads), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kda_bwd_params_kernel, dim3((unsigned)a.H), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}

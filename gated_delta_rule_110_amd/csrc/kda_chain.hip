@@ -317,8 +317,10 @@ __device__ __forceinline__ void out_wave(ChainSmem<kCB> &sm, const ChainArgs &a,
 }
 
 // The chain kernel's body; kMap selects map mode (ChainArgs::map_mode), which
-// is a kernel of its own so that the ordinary chain is compiled without it.
-template <bool kMap, int kCB>
+// is a kernel of its own so that the ordinary chain is compiled without it;
+// kSave stores the state entering every chunk to ChainArgs::hs (the backward's
+// forward pass), also a kernel of its own.
+template <bool kMap, int kCB, bool kSave = false>
 __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &a) {
     using Sh = Shape<kCB>;
 
@@ -381,6 +383,14 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
             lds_barrier();  // ring slot 0 written by the loader
             int rs = 0;     // ring slot of chunk s
             for (int64_t s = 0; s < nchunks; ++s) {
+                if constexpr (kSave) {
+                    // lane (r, g) holds rows 16 ct + 4 g + e of column col0 + r
+                    float *hs = a.hs + wsof(s) * (int64_t)(kK * kV) + col0 + r;
+#pragma unroll
+                    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) hs[(16 * ct + 4 * g + e) * kV] = S[ct][e];
+                }
                 if (!kMap) chain_step<kCB, false, true>(sm, S, rs, (int)(s & 1), c, lane);
                 else if (linear_part) chain_step<kCB, true, false>(sm, S, rs, (int)(s & 1), c, lane);
                 else chain_step<kCB, false, false>(sm, S, rs, (int)(s & 1), c, lane);
@@ -472,6 +482,14 @@ __global__ __launch_bounds__(Shape<1>::kThreads, 1) void kda_chain_kernel(ChainA
 __global__ __launch_bounds__(Shape<2>::kThreads, 1) void kda_chain_x2_kernel(ChainArgs a) {
     __shared__ ChainSmem<2> sm;
     chain_body<false, 2>(sm, a);
+}
+__global__ __launch_bounds__(Shape<1>::kThreads, 1) void kda_chain_save_kernel(ChainArgs a) {
+    __shared__ ChainSmem<1> sm;
+    chain_body<false, 1, true>(sm, a);
+}
+__global__ __launch_bounds__(Shape<2>::kThreads, 1) void kda_chain_save_x2_kernel(ChainArgs a) {
+    __shared__ ChainSmem<2> sm;
+    chain_body<false, 2, true>(sm, a);
 }
 __global__ __launch_bounds__(Shape<1>::kThreads, 1) void kda_chain_map_kernel(ChainArgs a) {
     __shared__ ChainSmem<1> sm;
@@ -568,6 +586,12 @@ hipError_t kda_launch_chain(const ChainArgs &a, hipStream_t s) {
                                dim3(Shape<2>::kThreads), 0, s, b);
         else if (a.map_mode)
             hipLaunchKernelGGL(kda_chain_map_kernel, dim3((unsigned)(ng * 8 * Shape<1>::kNVB)),
+                               dim3(Shape<1>::kThreads), 0, s, b);
+        else if (a.hs && wide)
+            hipLaunchKernelGGL(kda_chain_save_x2_kernel, dim3((unsigned)(ng * 8 * Shape<2>::kNVB)),
+                               dim3(Shape<2>::kThreads), 0, s, b);
+        else if (a.hs)
+            hipLaunchKernelGGL(kda_chain_save_kernel, dim3((unsigned)(ng * 8 * Shape<1>::kNVB)),
                                dim3(Shape<1>::kThreads), 0, s, b);
         else if (wide)
             hipLaunchKernelGGL(kda_chain_x2_kernel, dim3((unsigned)(ng * 8 * Shape<2>::kNVB)),

@@ -104,6 +104,9 @@ struct ChainArgs {
     // offset and the linear part of the chain's affine map S -> M S + N.
     int map_mode;
     float *mapM, *mapN;
+    // With hs set (the backward's forward pass), the chain also stores the
+    // fp32 state entering every chunk: hs[chunk slot * H + h][K][V].
+    float *hs;
     int64_t chain_base;  // first chain (in dispatch order) of this launch; set by the launcher
     int64_t piece_cap;   // kda_desc_t::launch_piece (0: launch size by the default rule)
 };
@@ -132,6 +135,35 @@ struct DecodeArgs {
     uint16_t *out;       // [N,H,V] bf16
     int64_t unit_base;   // first (sequence, head) of this launch; set by the launcher
     int64_t piece_cap;   // kda_desc_t::launch_piece (0: launch size by the default rule)
+};
+
+// The backward pass (kda_bwd.hip).  Per (chunk slot, head) unit ws = slot * H + h
+// the workspace holds, besides the forward's fragment intermediates:
+//   hs, dhs [ws][K][V] fp32   state entering the chunk / gradient of the state leaving it
+//   dUt     [ws][64][V] fp32  gradient of the chunk's pseudo-values Ut = U - W S
+//   qn, kn, G [ws][64][K] fp32  normalised q and k, cumulative log-decay within the chunk
+//   rq, rk, bb [ws][64] fp32    reciprocal norms of q and k, b = sigmoid(beta)
+//   Mk, Tm [ws][64][64] fp32    decayed key Gram (strictly lower, without b) and T = (I + Diag(b) Mk)^-1
+//   part [ws][K + 1] fp32       this chunk's share of ddt_bias (K) and of dA_log (1)
+// Rows past the end of a ragged chunk are zero in qn, kn, bb and keep G constant.
+struct BwdArgs {
+    const uint16_t *q, *k, *v, *g, *beta;   // bf16 inputs
+    const float *A_log, *dt_bias;
+    float lower_bound, scale;
+    const uint16_t *dout;                   // [B,T,H,V] bf16, gradient of out
+    const void *dht;                        // [N,H,K,V] gradient of the final state, or nullptr
+    int dht_bf16;
+    const int64_t *cu;
+    const int32_t *chunk_off, *seq_order;
+    int64_t T, H, N, nc_fixed, slots;
+    const _Float16 *Wf, *Qf, *Kf, *Af;      // the forward's intermediates
+    const float *gn;
+    float *hs, *dhs, *dUt, *qn, *kn, *G, *rq, *rk, *bb, *Mk, *Tm, *part;
+    float *dq, *dk, *dv, *dg, *dbeta;       // [B,T,H,K] / [B,T,H,V] / [B,T,H] fp32
+    float *dh0;                             // [N,H,K,V] fp32 or nullptr
+    float *dA_log, *ddt_bias;               // [H] / [H,K] fp32
+    int64_t unit_base, chain_base;          // first unit / chain of a launch; set by the launchers
+    int64_t piece_cap;                      // kda_desc_t::launch_piece (0: launch size by the default rule)
 };
 
 // ---- small numeric helpers --------------------------------------------------
@@ -278,6 +310,10 @@ hipError_t kda_launch_seg_table(int64_t B, int64_t T, int64_t segs, int64_t segc
                                 hipStream_t s);
 hipError_t kda_launch_seg_scan(const kda::ScanArgs &a, hipStream_t s);
 hipError_t kda_launch_decode(const kda::DecodeArgs &a, hipStream_t s);
+// The backward's own kernels (kda_bwd.hip): per-chunk preparation, the
+// reverse state chain, the per-chunk gradient, and the sum of the shared
+// parameters' partial gradients.
+hipError_t kda_launch_bwd(const kda::BwdArgs &a, hipStream_t s);
 // The pipelined forward (kda_fused.hip): whether it handles these shapes, and
 // its launch (the flag clear and the fused producer / consumer grid).
 bool kda_fused_applies(int64_t N, int64_t H, bool varlen);

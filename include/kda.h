@@ -1,6 +1,7 @@
 /*
  * kda.h -- C ABI of libkda, the gfx950 (MI355X) forward pass of Kimi Delta
- * Attention (KDA) in chunk-parallel form.
+ * Attention (KDA) in chunk-parallel form, its recurrent decode step and its
+ * gradient.
  *
  * The operation.  KDA is a delta-rule linear attention with a fixed-size state
  * matrix per (sequence, head), a forget gate, and a per-channel decay that
@@ -250,6 +251,53 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
                         const float *dt_bias, float lower_bound,
                         const void *initial_state, void *final_state, void *out,
                         const kda_desc_t *desc, hipStream_t stream);
+
+/* Bytes of workspace kda_bwd needs for these shapes (0 if the shapes are
+ * invalid or chain_segments >= 2).  Pure host arithmetic.  About 370 KiB per
+ * 64-token chunk and head (the forward's 72.5 KiB of intermediates, the fp32
+ * state entering every chunk and its gradient, 64 KiB each, and 168 KiB of
+ * fp32 per-chunk quantities), plus B * T * H * V * 2 bytes for the recomputed
+ * forward output. */
+size_t kda_bwd_workspace_size(const kda_desc_t *desc);
+
+/* Enqueue the gradient of kda_fwd on `stream` and return without
+ * synchronising.  The pages' kernels have no backward pass ("性能与注意事项",
+ * zuobiaodaohang.com FlashKDA page: forward only); this is the vector-Jacobian
+ * product of the operation stated at the top of this header: for the loss
+ * gradients d_out (of out) and d_final_state (of final_state) it returns the
+ * gradient of
+ *     L = <d_out, out> + <d_final_state, final_state>
+ * with respect to every input.  The forward is recomputed inside the call
+ * (nothing from an earlier kda_fwd is needed).
+ *
+ *   q ... lower_bound, initial_state, cu_seqlens : as for kda_fwd (the same
+ *                      shapes, dtypes and rules; desc->initial_state_dtype
+ *                      describes initial_state).
+ *   d_out            : bf16 [B, T, H, V] (may be NULL when T == 0).
+ *   d_final_state    : [N, H, K, V] of desc->final_state_dtype, or NULL for zeros.
+ *   dq, dk, dg       : fp32 [B, T, H, K] outputs (gradients of q, k and of g,
+ *                      the gate before activation).
+ *   dv               : fp32 [B, T, H, V];  dbeta : fp32 [B, T, H] (of the logits).
+ *   d_initial_state  : fp32 [N, H, K, V], or NULL to skip it.
+ *   dA_log           : fp32 [H];  ddt_bias : fp32 [H, K] -- summed over every
+ *                      sequence and token (each is shared by all of them).
+ * All outputs are overwritten, never accumulated into.  Where the gate is
+ * clamped (-exp(A_log) softplus(g + dt_bias) <= lower_bound) no gradient
+ * reaches g, dt_bias or A_log; at the kink itself the clamped side is taken.
+ * desc->chain_segments >= 2 is KDA_ERR_UNSUPPORTED (the backward never splits
+ * chains; 0 and 1 both mean unsplit); desc->pipeline and phase_events are
+ * ignored; launch_piece and the workspace rules are as for kda_fwd, with
+ * kda_bwd_workspace_size() in place of kda_fwd_workspace_size().  The
+ * forward's value range applies.  Gradients are computed on the fp32 matrix
+ * cores from the forward's fp16 intermediates and states. */
+kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, float scale, const float *A_log,
+                     const float *dt_bias, float lower_bound,
+                     const void *initial_state, const int64_t *cu_seqlens,
+                     const void *d_out, const void *d_final_state,
+                     float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                     float *d_initial_state, float *dA_log, float *ddt_bias,
+                     const kda_desc_t *desc, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(kda_status_t status);

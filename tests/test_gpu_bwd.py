@@ -1,0 +1,141 @@
+"""The backward pass (kda_bwd) against the oracle's fp64 gradient, element by
+element, through the C ABI.
+
+Tolerances, per gradient tensor: relative RMS (over the whole tensor) and the
+largest absolute error relative to the largest reference entry.  The backward
+recomputes the forward from its fp16 intermediates (so the states it
+differentiates through carry the forward's ~5e-4 relative error) and runs every
+product of the gradient on the fp32 matrix cores; a gradient's error is of the
+order of that state error, so it is held to the forward output's relative-RMS
+bar, 5e-3, and to 2e-2 of its largest entry.  Where the gate clamp decides
+whether g receives a gradient, the fp64 oracle and the fp32 kernel may decide
+differently for inputs within rounding of the kink: entries of dg whose
+unclamped log-decay lies within 1e-4 of lower_bound are left out of the dg
+comparison."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_110_amd as kda
+import oracle
+import workloads as W
+from tests.parity import say
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL_RMS = 5e-3
+GRAD_MAX_ABS_REL = 2e-2
+NAMES = ["dq", "dk", "dv", "dg", "dbeta", "d_initial_state", "dA_log", "ddt_bias"]
+REF_NAME = {"d_initial_state": "d_initial"}
+
+
+def _gpu(w, d_out, d_fin, **kw):
+    wd = w.to("cuda")
+    res = kda.bwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, wd.A_log, wd.dt_bias, w.lower_bound,
+                  d_out.cuda(), d_final_state=None if d_fin is None else d_fin.cuda(),
+                  initial_state=wd.initial_state, cu_seqlens=wd.cu_seqlens, **kw)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.cpu().double().numpy()) for k, v in res.items()}
+
+
+def _oracle(w, d_out, d_fin):
+    return oracle.bwd(w.q, w.k, w.v, w.g, w.beta, w.scale, w.A_log, w.dt_bias, w.lower_bound, d_out,
+                      d_final=d_fin, initial_state=w.initial_state, cu_seqlens=w.cu_seqlens)
+
+
+def _near_kink(w):
+    x = w.g.double().numpy() + w.dt_bias.double().numpy()[None, None]
+    z = -np.exp(w.A_log.double().numpy())[None, None, :, None] * np.logaddexp(0.0, x)
+    return np.abs(z - w.lower_bound) < 1e-4
+
+
+def _compare(got, ref, w, label):
+    near = _near_kink(w)
+    stats = {}
+    for name in NAMES:
+        g_, r_ = got[name], ref[REF_NAME.get(name, name)]
+        if name == "dg":
+            g_, r_ = np.where(near, 0.0, g_), np.where(near, 0.0, r_)
+        assert np.isfinite(g_).all(), (label, name, "non-finite")
+        if r_.size == 0:
+            continue
+        nr = float(np.linalg.norm(r_))
+        rel = float(np.linalg.norm(g_ - r_)) / nr if nr > 0 else float(np.linalg.norm(g_))
+        mx = float(np.abs(g_ - r_).max()) / max(float(np.abs(r_).max()), 1e-30)
+        stats[name] = (rel, mx)
+    say("%s: %s" % (label, " ".join("%s %.2e/%.2e" % (k, a, b) for k, (a, b) in stats.items())))
+    for name, (rel, mx) in stats.items():
+        assert rel <= GRAD_REL_RMS, (label, name, rel)
+        assert mx <= GRAD_MAX_ABS_REL, (label, name, mx)
+
+
+CASES = {
+    # ragged last chunk, three chunks, fp32 states
+    "fixed": lambda: (W.make("bwd_fixed", 2, 150, 3, 7001, init="fp32", final="fp32"), 7101, "fp32"),
+    # packed with an empty and a one-chunk sequence, bf16 states
+    "packed": lambda: (W.make("bwd_packed", 1, 265, 2, 7002, init="bf16", final="bf16",
+                              seqlens=[37, 0, 163, 65]), 7102, "bf16"),
+    # no states at all
+    "nostate": lambda: (W.make("bwd_nostate", 1, 64, 2, 7003, init=None, final=None), 7103, None),
+    # no decay
+    "lb0": lambda: (W.make("bwd_lb0", 1, 200, 2, 7004, lower_bound=0.0, init="fp32"), 7104, "fp32"),
+    # weak decay, spread b
+    "weak": lambda: (W.make("bwd_weak", 1, 300, 2, 7005, lower_bound=-1.0, g_mean=-2.0, beta_std=3.0,
+                            init="fp32"), 7105, "fp32"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_bwd_matches_oracle(case):
+    w, seed, fin = CASES[case]()
+    d_out, d_fin = W.loss_grads(w, seed, final=fin)
+    say("bwd %s: B=%d T=%d H=%d N=%d" % (case, w.B, w.T, w.H, w.N))
+    got = _gpu(w, d_out, d_fin)
+    ref = _oracle(w, d_out, d_fin)
+    _compare(got, ref, w, case)
+
+
+def test_bwd_empty_batch():
+    # T = 0: the initial state's gradient is the final state's, everything else is empty or zero
+    w = W.make("bwd_empty", 2, 0, 2, 7006, init="fp32", final="fp32")
+    d_out, d_fin = W.loss_grads(w, 7106, final="fp32")
+    got = _gpu(w, d_out, d_fin)
+    assert np.array_equal(got["d_initial_state"], d_fin.double().numpy())
+    assert not got["dA_log"].any() and not got["ddt_bias"].any()
+
+
+def test_bwd_launch_pieces_and_determinism():
+    w = W.make("bwd_pieces", 1, 330, 3, 7007, init="fp32", final="fp32", seqlens=[100, 1, 229])
+    d_out, d_fin = W.loss_grads(w, 7107, final="fp32")
+    a = _gpu(w, d_out, d_fin)
+    b = _gpu(w, d_out, d_fin)
+    c = _gpu(w, d_out, d_fin, launch_piece=1)
+    for name in NAMES:
+        assert np.array_equal(a[name], b[name]), name
+        assert np.array_equal(a[name], c[name]), name
+
+
+def test_bwd_full_size_heads():
+    # T = 8192, H = 32 (the headline forward shape) on the GPU; the oracle on heads 0 and 31
+    w = W.config(1)
+    d_out, d_fin = W.loss_grads(w, 7108, final="fp32")
+    say("bwd full: %s" % w.name)
+    got = _gpu(w, d_out, d_fin)
+    heads = [0, w.H - 1]
+    ws = w.head_slice(heads)
+    idx = torch.tensor(heads)
+    ref = _oracle(ws, d_out.index_select(2, idx).contiguous(), d_fin.index_select(1, idx).contiguous())
+    sub = {}
+    for name in NAMES:
+        x = got[name]
+        if name in ("dq", "dk", "dv", "dg"):
+            sub[name] = x[:, :, heads]
+        elif name == "dbeta":
+            sub[name] = x[:, :, heads]
+        elif name == "d_initial_state":
+            sub[name] = x[:, heads]
+        else:
+            sub[name] = x[heads]
+    _compare(sub, ref, ws, "full")

@@ -146,6 +146,19 @@ def make(name: str, B: int, T: int, H: int, seed: int, *, lower_bound: float = -
                     h0, fdt, cu, list(seqlens) if seqlens is not None else [T] * B)
 
 
+def loss_grads(w: Workload, seed: int, final: Optional[str] = "fp32"):
+    """Seeded loss gradients for the backward pass of workload ``w``: d_out ~ N(0, 1)
+    bf16 [B, T, H, V] and d_final ~ N(0, 1) [N, H, K, V] ("fp32", "bf16" or None)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    d_out = _normal_bf16(rng, (w.B, w.T, w.H, w.V))
+    d_fin = None
+    if final is not None:
+        d_fin = torch.from_numpy(rng.standard_normal(size=(w.N, w.H, w.K, w.V), dtype=np.float32))
+        if final == "bf16":
+            d_fin = d_fin.to(torch.bfloat16)
+    return d_out, d_fin
+
+
 # The five workloads the library is measured and checked on.
 CONFIG_NAMES = [
     "tiny_T512_H4",
