@@ -1,6 +1,6 @@
 """Throughput of the KDA chunked forward pass on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline] [--bwd]
 
 One step = one kda_fwd call (chunk table when packed, intra-chunk kernel,
 state-chain kernel) over the whole workload, with inputs already resident in
@@ -277,6 +277,83 @@ def load_limiter(kernel: str):
     return lim.get("limiter")
 
 
+# The backward (kda_bwd): the forward recomputed (F_ALG), then per token-head
+#   reverse state chain: scale A_qk^T dO (C V, triangular), Kbar dS, W^T dUt, Qg^T dO (2 K V each)
+#   per-chunk gradient: gamma Khat S, dO S^T, Z S^T, Ut dS'^T (2 K V each); T X, T^T dUt,
+#     dO Ut^T, Z Ut^T (C V each, triangular); the four Gram gradients (C K each, triangular)
+#   preparation: the decayed key Gram (C K, triangular)
+F_BWD_CHAIN = 64 * 128 + 3 * 2 * 128 * 128
+F_BWD_MAIN = 4 * 2 * 128 * 128 + 4 * 64 * 128 + 4 * 64 * 128
+F_BWD_PREP = 64 * 128
+F_BWD = F_ALG + F_BWD_CHAIN + F_BWD_MAIN + F_BWD_PREP
+# Algorithmic bytes per token-head: q, k, v, g, beta and d_out read (bf16), dq, dk, dv, dg (fp32)
+# and dbeta (fp32) written; plus the states (initial state and d_final read, d_initial written).
+BYTES_BWD = 4 * 256 + 2 + 256 + 4 * 512 + 4
+MFMA_FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA, vendor figure
+
+
+def bench_bwd(kda, args, dev, wname) -> int:
+    """The backward: K timed kda_bwd calls on the workload, with d_out ~ N(0, 1)
+    and an fp32 d_final when the workload has a final state."""
+    w_host = W.by_name(wname)
+    w = w_host.to(dev)
+    d_out, d_fin = W.loss_grads(w_host, 8000, final="fp32" if w.final_state_dtype is not None else None)
+    d_out = d_out.to(dev)
+    d_fin = None if d_fin is None else d_fin.to(dev)
+    nbytes = kda.bwd_workspace_size(w.B, w.T, w.H, num_seqs=w.N)
+    workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in ev:
+        e.record(stream)
+    torch.cuda.synchronize(dev)
+    ev_arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in ev])
+
+    def step(events=None):
+        return kda.bwd(w.q, w.k, w.v, w.g, w.beta, w.scale, w.A_log, w.dt_bias, w.lower_bound, d_out,
+                       d_final_state=d_fin, initial_state=w.initial_state, cu_seqlens=w.cu_seqlens,
+                       workspace=workspace, phase_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(ctypes.cast(ev_arr, ctypes.c_void_p) if i == args.steps - 1 else None)
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = t0.elapsed_time(t1) / args.steps
+    names = ["fwd_intra", "fwd_chain_save", "kda_bwd_prep_kernel", "kda_bwd_chain_kernel", "kda_bwd_main_kernel"]
+    kernel_ms = {n: round(ev[i].elapsed_time(ev[i + 1]), 5) for i, n in enumerate(names)}
+    tok_heads = w.B * w.T * w.H
+    flops = {"kda_bwd_prep_kernel": F_BWD_PREP, "kda_bwd_chain_kernel": F_BWD_CHAIN,
+             "kda_bwd_main_kernel": F_BWD_MAIN}
+    per_kernel = {n: {"alg_tflops": round(f * tok_heads / (kernel_ms[n] / 1e3) / 1e12, 2),
+                      "frac_fp32_mfma": round(f * tok_heads / (kernel_ms[n] / 1e3) / 1e12 / MFMA_FP32_PEAK_TFLOPS, 4)}
+                  for n, f in flops.items()}
+    dom = max(flops, key=lambda n: kernel_ms[n])
+    achieved = flops[dom] * tok_heads / (kernel_ms[dom] / 1e3) / 1e12
+    sb = state_bytes(w) + (0 if d_fin is None else w.N * w.H * 128 * 128 * 4) + w.N * w.H * 128 * 128 * 4
+    alg_bytes = BYTES_BWD * tok_heads + sb
+    result = {
+        "metric": "KDA backward tokens/s (gradient of the prefill, recomputing the forward)",
+        "value": round(w.B * w.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in, fp32 gradients", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V, "num_seqs": w.N},
+        "kernel_ms": kernel_ms,
+        "tflops_alg": round(F_BWD * tok_heads / (ms / 1e3) / 1e12, 2),
+        "gbs_alg": round(alg_bytes / (ms / 1e3) / 1e9, 1),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
+                     "alg_flops": flops[dom] * tok_heads, "traffic": None, "kernels": per_kernel},
+        "mfma_operands": "fp32 (16x16x4) for every gradient product; the recomputed forward as kda_fwd",
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def decode_name(N: int, H: int) -> str:
     return "decode_N%d_H%d" % (N, H)
 
@@ -349,6 +426,8 @@ def main(argv=None) -> int:
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="time the single-token recurrent step (kda_decode) for N sequences of the "
                          "chosen workload's head count, fp32 state updated in place, and exit")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (kda_bwd) on the chosen workload and exit")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV folders in DIR and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -386,6 +465,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     if args.decode:
         return bench_decode(kda, args, dev, decode_H)
+    if args.bwd:
+        return bench_bwd(kda, args, dev, wname)
     w_host = W.by_name(wname)
     w = w_host.to(dev)
     out = torch.empty((w.B, w.T, w.H, w.V), dtype=torch.bfloat16, device=dev)

@@ -289,13 +289,14 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         d_out: torch.Tensor, d_final_state: Optional[torch.Tensor] = None,
         initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None, launch_piece: int = 0, chain_segments: int = 0,
-        with_d_initial: bool = True) -> dict:
+        with_d_initial: bool = True, phase_events=None) -> dict:
     """Gradient of ``fwd`` (``kda_bwd``) on the current HIP stream: for the loss
     gradients ``d_out`` (bf16 [B,T,H,128]) and ``d_final_state`` (bf16 or fp32
     [N,H,128,128], or None for zeros) returns a dict of fp32 tensors dq, dk, dg
     ([B,T,H,128]), dv ([B,T,H,128]), dbeta ([B,T,H]), dA_log ([H]), ddt_bias
     ([H,128]) and d_initial_state ([N,H,128,128], or None without
-    ``with_d_initial``).  Inputs as for ``fwd``."""
+    ``with_d_initial``).  Inputs as for ``fwd``; phase_events: None or the
+    address of a caller-owned array of 6 hipEvent_t (instrumentation)."""
     lib = library()
     d, dev, d_out = _check_fwd_args(q, k, v, g, beta, d_out, A_log, dt_bias, initial_state, d_final_state,
                                     cu_seqlens, chain_segments, launch_piece, allocate_out=False)
@@ -315,6 +316,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
             raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
         d.workspace = ctypes.c_void_p(workspace.data_ptr())
         d.workspace_bytes = workspace.numel() * workspace.element_size()
+        d.phase_events = phase_events
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
                          _ptr(dt_bias), float(lower_bound), _ptr(initial_state), _ptr(cu_seqlens), _ptr(d_out),

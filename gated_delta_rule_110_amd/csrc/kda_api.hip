@@ -518,8 +518,10 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
     const WorkspaceLayout &fl = lay.fwd;
     int32_t *chunk_off = geo.varlen ? reinterpret_cast<int32_t *>(ws + fl.off_chunk_off) : nullptr;
     int32_t *seq_order = geo.varlen ? reinterpret_cast<int32_t *>(ws + fl.off_seq_order) : nullptr;
+    hipEvent_t *ev = desc->phase_events;
     hipError_t err = hipSuccess;
-    if (geo.varlen) err = kda_launch_chunk_table(cu_seqlens, geo.N, chunk_off, seq_order, stream);
+    if (ev) err = hipEventRecord(ev[0], stream);
+    if (err == hipSuccess && geo.varlen) err = kda_launch_chunk_table(cu_seqlens, geo.N, chunk_off, seq_order, stream);
 
     // the forward: intermediates, then the chain storing every chunk's entering state
     IntraArgs ia{};
@@ -537,6 +539,7 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
     ia.gn = reinterpret_cast<float *>(ws + fl.off_gn);
     ia.piece_cap = desc->launch_piece;
     if (err == hipSuccess && geo.T > 0) err = kda_launch_intra(ia, geo.slots, stream);
+    if (ev && err == hipSuccess) err = hipEventRecord(ev[1], stream);
     BwdArgs ba{};
     ba.hs = reinterpret_cast<float *>(ws + lay.off_hs);
     if (geo.T > 0) {
@@ -552,6 +555,7 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
         ca.piece_cap = desc->launch_piece;
         if (err == hipSuccess) err = kda_launch_chain(ca, stream);
     }
+    if (ev && err == hipSuccess) err = hipEventRecord(ev[2], stream);
     // the gradient
     ba.q = ia.q; ba.k = ia.k; ba.v = ia.v; ba.g = ia.g; ba.beta = ia.beta;
     ba.A_log = A_log; ba.dt_bias = dt_bias; ba.lower_bound = lower_bound; ba.scale = scale;
@@ -575,7 +579,7 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
     ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dg = dg; ba.dbeta = dbeta;
     ba.dh0 = d_initial_state; ba.dA_log = dA_log; ba.ddt_bias = ddt_bias;
     ba.piece_cap = desc->launch_piece;
-    if (err == hipSuccess) err = kda_launch_bwd(ba, stream);
+    if (err == hipSuccess) err = kda_launch_bwd(ba, stream, ev ? ev + 3 : nullptr);
     if (owned) {
         hipError_t e2 = hipFreeAsync(ws, stream);
         if (err == hipSuccess) err = e2;

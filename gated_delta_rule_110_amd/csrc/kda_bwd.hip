@@ -416,23 +416,38 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
 
 // ---- 4. the per-chunk gradient -----------------------------------------------
 
-constexpr int kRP = 132;  // row pitch of the 64 x 128 tiles
-constexpr int kTP = 68;   // row pitch of the 64 x 64 tiles
+constexpr int kMainThreads = 512;  // 8 waves: row block w = wave & 3, column half hf = wave >> 2
+constexpr int kRP = 132;           // row pitch of the 128-column tiles
+constexpr int kTP = 68;            // row pitch of the 64 x 64 tiles
 
 struct MainSmem {
-    float U[kChunk][kRP];   // Ut, then dG and its reverse cumulative sum
-    float Z[kChunk][kRP];   // Diag(b) Y, then Z = T^T dUt
-    float D[kChunk][kRP];   // dO
-    float T[kChunk][kTP];   // T, then dA_qk
-    float X[kChunk][kTP];   // dM = Diag(b) dA_kk
-    float db[kChunk];
+    float U[kChunk][kRP];   // gamma Khat (P1), Ut (P2-P6), khat (P7), then dG and its reverse cumulative sum
+    float Z[kChunk][kRP];   // Diag(b) Y (P1-P2), dUt (P3), Z (P3-P6), G (P7)
+    float SB[kK][kRP];      // S (P1-P4), dS' (P5); in P7 dM in rows 0..63 and qhat in rows 64..127
+    float T[kChunk][kTP];   // T (P0-P3), dA_qk (P6-P7)
     float b[kChunk];
-    float red[4][kK];       // per-wave column sums
+    float db[2][kChunk];    // per column half
+    float rs[2][2][kChunk]; // row sums qhat . dqhat and khat . dkhat, per column half
+    float red[4][kK];       // column sums per row block
     float gns[kK];          // exp(G_n) * sum_v S * dS'
-    float pa[4];            // per-wave dA_log sums
+    float pa[8];            // per-wave dA_log sums
 };
 
-__global__ __launch_bounds__(kThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
+// Copy a [rows][128] fp32 row-major block from global memory into an LDS tile
+// of pitch kRP, optionally scaled element by element by f(row, col, value).
+template <typename F>
+__device__ __forceinline__ void stage_rows(float (*dst)[kRP], const float *src, int rows, int tid, F f) {
+    for (int idx = tid; idx < rows * 32; idx += kMainThreads) {
+        const int i = idx >> 5, c4 = (idx & 31) * 4;
+        const float4 v = *reinterpret_cast<const float4 *>(src + i * 128 + c4);
+        dst[i][c4] = f(i, c4, v.x);
+        dst[i][c4 + 1] = f(i, c4 + 1, v.y);
+        dst[i][c4 + 2] = f(i, c4 + 2, v.z);
+        dst[i][c4 + 3] = f(i, c4 + 3, v.w);
+    }
+}
+
+__global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
     __shared__ MainSmem sm;
     const int64_t ws = a.unit_base + blockIdx.x;
     const int64_t slot = ws / a.H, h = ws - slot * a.H;
@@ -441,7 +456,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
     if (!chunk_rows(a, slot, t0, L)) return;
     const int64_t H = a.H;
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = wv & 3, hf = wv >> 2;
     const int lane = tid & 63, r = lane & 15, gq = lane >> 4;
     const float *S = a.hs + ws * (int64_t)(kK * kV);
     const float *dSp = a.dhs + ws * (int64_t)(kK * kV);
@@ -451,157 +467,185 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
     const float *G = a.G + ws * (kChunk * kK);
     const float *Mk = a.Mk + ws * (kChunk * kChunk);
     const float scale = a.scale;
+    const auto ident = [](int, int, float x) { return x; };
     auto vval = [&](int i, int c) -> float {
         return i < L ? bf16_bits_to_f32(a.v[((t0 + i) * H + h) * kV + c]) : 0.f;
     };
+    // this lane's row 16 w + r of dO (the A operand of P4 and P6), zero past the end
+    const bool arow_ok = 16 * w + r < L;
+    const uint16_t *arow = a.dout + ((t0 + (arow_ok ? 16 * w + r : 0)) * H + h) * kV;
+    auto dov_a = [&](int c) -> float { return arow_ok ? bf16_bits_to_f32(arow[c]) : 0.f; };
+    const int64_t HK = H * kK;
+    const int64_t obase = (t0 * H + h) * kK;
+    auto out_at = [&](int i, int d) -> int64_t { return obase + i * HK + d; };
 
-    // P0: dO, T and b into LDS
-    for (int idx = tid; idx < kChunk * kV; idx += kThreads) {
-        const int i = idx >> 7, c = idx & 127;
-        sm.D[i][c] = i < L ? bf16_bits_to_f32(a.dout[((t0 + i) * H + h) * kV + c]) : 0.f;
-    }
-    for (int idx = tid; idx < kChunk * kChunk; idx += kThreads)
+    // wave (w, hf) owns rows 16 w .. 16 w + 15 and column tiles ct = 4 hf + c
+    // (c = 0..3) of every 64 x 128 result; lane (r, gq) holds rows 16 w + 4 gq + e
+    // of column 16 ct + r.  dG stays in registers; the gradients of qhat and
+    // khat are summed in place in dq and dk (the owning lane only), which the
+    // last phase turns into the gradients of q and k.
+    const int row0 = 16 * w + 4 * gq;  // + e
+    f4 dG[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dG[c] = f4{0, 0, 0, 0};
+
+    // P0: T, b, gamma Khat and S into LDS
+    for (int idx = tid; idx < kChunk * kChunk; idx += kMainThreads)
         sm.T[idx >> 6][idx & 63] = a.Tm[ws * (kChunk * kChunk) + idx];
     if (tid < kChunk) {
         sm.b[tid] = a.bb[ws * kChunk + tid];
-        sm.db[tid] = 0.f;
+        sm.db[0][tid] = 0.f;
+        sm.db[1][tid] = 0.f;
     }
+    stage_rows(sm.U, kn, kChunk, tid, [&](int i, int d, float x) { return x * __expf(G[i * kK + d]); });
+    stage_rows(sm.SB, S, kK, tid, ident);
     __syncthreads();
-
-    // wave w owns rows 16 w .. 16 w + 15 of every 64 x 128 result; lane (r, gq)
-    // of column tile ct holds rows 16 w + 4 gq + e of column 16 ct + r.  dG stays
-    // in registers; the gradients of qhat and khat are summed in place in dq and
-    // dk (each element has one owning lane), which the last phase turns into the
-    // gradients of q and k.
-    f4 dG[8];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) dG[ct] = f4{0, 0, 0, 0};
-    const int row0 = 16 * w + 4 * gq;  // + e
-    auto out_at = [&](int i, int d) -> int64_t { return ((t0 + i) * H + h) * kK + d; };
 
     // P1: Diag(b) Y, Y = V - (gamma Khat) S
     {
-        f4 acc[8];
+        f4 acc[4];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
-        const int i = 16 * w + r;
-        #pragma unroll 2
+        for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
+#pragma unroll 4
         for (int ks = 0; ks < 32; ++ks) {
-            const int d = 4 * ks + gq;
-            const float av = kn[i * kK + d] * __expf(G[i * kK + d]);
+            const float av = sm.U[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) acc[ct] = mma(av, S[d * kV + 16 * ct + r], acc[ct]);
+            for (int c = 0; c < 4; ++c) acc[c] = mma(av, sm.SB[4 * ks + gq][16 * (4 * hf + c) + r], acc[c]);
         }
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int ii = row0 + e, c = 16 * ct + r;
-                sm.Z[ii][c] = sm.b[ii] * (vval(ii, c) - acc[ct][e]);
+                const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
+                sm.Z[ii][d] = sm.b[ii] * (vval(ii, d) - acc[c][e]);
             }
     }
     __syncthreads();
     // P2: Ut = T (Diag(b) Y); T[i][j] = 0 for j > i
     {
-        f4 acc[8];
+        f4 acc[4];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
-        #pragma unroll 2
+        for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
+#pragma unroll 4
         for (int ks = 0; ks < 4 * (w + 1); ++ks) {
             const float av = sm.T[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) acc[ct] = mma(av, sm.Z[4 * ks + gq][16 * ct + r], acc[ct]);
+            for (int c = 0; c < 4; ++c) acc[c] = mma(av, sm.Z[4 * ks + gq][16 * (4 * hf + c) + r], acc[c]);
         }
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.U[row0 + e][16 * ct + r] = acc[ct][e];
+            for (int e = 0; e < 4; ++e) sm.U[row0 + e][16 * (4 * hf + c) + r] = acc[c][e];
     }
+    __syncthreads();
+    stage_rows(sm.Z, dUt, kChunk, tid, ident);
     __syncthreads();
     // P3: Z = T^T dUt; dv = Diag(b) Z; db += Z . v
     {
-        f4 acc[8];
+        f4 acc[4];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
-        #pragma unroll 2
+        for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
+#pragma unroll 4
         for (int ks = 4 * w; ks < 16; ++ks) {
             const float av = sm.T[4 * ks + gq][16 * w + r];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) acc[ct] = mma(av, dUt[(4 * ks + gq) * kV + 16 * ct + r], acc[ct]);
+            for (int c = 0; c < 4; ++c) acc[c] = mma(av, sm.Z[4 * ks + gq][16 * (4 * hf + c) + r], acc[c]);
         }
+        __syncthreads();  // every wave has read dUt
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int ii = row0 + e, c = 16 * ct + r;
-                const float z = acc[ct][e];
-                sm.Z[ii][c] = z;
+                const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
+                const float z = acc[c][e];
+                sm.Z[ii][d] = z;
                 if (ii < L) {
-                    a.dv[((t0 + ii) * H + h) * kV + c] = sm.b[ii] * z;
-                    dbp[e] += z * vval(ii, c);
+                    a.dv[((t0 + ii) * H + h) * kV + d] = sm.b[ii] * z;
+                    dbp[e] += z * vval(ii, d);
                 }
             }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float s = sum16(dbp[e]);
-            if (r == 0) sm.db[row0 + e] += s;
+            if (r == 0) sm.db[hf][row0 + e] += s;
         }
     }
     __syncthreads();
     // P4: dQg = scale dO S^T and Zw = -Z S^T
     {
-        f4 aq[8], az[8];
+        f4 aq[4], az[4];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) { aq[ct] = f4{0, 0, 0, 0}; az[ct] = aq[ct]; }
-        #pragma unroll 2
+        for (int c = 0; c < 4; ++c) { aq[c] = f4{0, 0, 0, 0}; az[c] = aq[c]; }
+#pragma unroll 4
         for (int ks = 0; ks < 32; ++ks) {
-            const float a1 = sm.D[16 * w + r][4 * ks + gq];
+            const float a1 = dov_a(4 * ks + gq);
             const float a2 = sm.Z[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-                const float bv = S[(16 * ct + r) * kV + 4 * ks + gq];
-                aq[ct] = mma(a1, bv, aq[ct]);
-                az[ct] = mma(a2, bv, az[ct]);
+            for (int c = 0; c < 4; ++c) {
+                const float bv = sm.SB[16 * (4 * hf + c) + r][4 * ks + gq];
+                aq[c] = mma(a1, bv, aq[c]);
+                az[c] = mma(a2, bv, az[c]);
             }
         }
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int ii = row0 + e, d = 16 * ct + r;
+                const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
                 const float qh = qn[ii * kK + d], kh = kn[ii * kK + d];
                 const float gam = __expf(G[ii * kK + d]);
                 const float bi = sm.b[ii];
-                const float dQg = scale * aq[ct][e], Zw = -az[ct][e];
+                const float dQg = scale * aq[c][e], Zw = -az[c][e];
                 if (ii < L) {
                     a.dq[out_at(ii, d)] = gam * dQg;
                     a.dk[out_at(ii, d)] = bi * gam * Zw;
                 }
-                dG[ct][e] += gam * qh * dQg + bi * gam * kh * Zw;
+                dG[c][e] += gam * qh * dQg + bi * gam * kh * Zw;
                 dbp[e] += Zw * gam * kh;
             }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float s = sum16(dbp[e]);
-            if (r == 0) sm.db[row0 + e] += s;
+            if (r == 0) sm.db[hf][row0 + e] += s;
         }
     }
-    // P5: dKbar = Ut dS'^T; dG_n
+    __syncthreads();
+    // dS' into LDS; exp(G_n) sum_v S[d][v] dS'[d][v] on the way (four threads per state row)
     {
-        f4 acc[8];
+        const int d = tid >> 2, qt = tid & 3;
+        const float *sr = S + d * kV + 32 * qt, *dr = dSp + d * kV + 32 * qt;
+        float s = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
-        #pragma unroll 2
+        for (int c4 = 0; c4 < 32; c4 += 4) {
+            const float4 x = *reinterpret_cast<const float4 *>(sr + c4);
+            const float4 y = *reinterpret_cast<const float4 *>(dr + c4);
+            s += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+            sm.SB[d][32 * qt + c4] = y.x;
+            sm.SB[d][32 * qt + c4 + 1] = y.y;
+            sm.SB[d][32 * qt + c4 + 2] = y.z;
+            sm.SB[d][32 * qt + c4 + 3] = y.w;
+        }
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if (qt == 0) sm.gns[d] = __expf(G[(L - 1) * kK + d]) * s;
+    }
+    __syncthreads();
+    // P5: dKbar = Ut dS'^T
+    {
+        f4 acc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
+#pragma unroll 4
         for (int ks = 0; ks < 32; ++ks) {
-            const float a1 = sm.U[16 * w + r][4 * ks + gq];
+            const float av = sm.U[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) acc[ct] = mma(a1, dSp[(16 * ct + r) * kV + 4 * ks + gq], acc[ct]);
+            for (int c = 0; c < 4; ++c) acc[c] = mma(av, sm.SB[16 * (4 * hf + c) + r][4 * ks + gq], acc[c]);
         }
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const int d = 16 * ct + r;
+        for (int c = 0; c < 4; ++c) {
+            const int d = 16 * (4 * hf + c) + r;
             const float Gn = G[(L - 1) * kK + d];
             float colp = 0.f;
 #pragma unroll
@@ -609,134 +653,140 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
                 const int ii = row0 + e;
                 const float eK = __expf(Gn - G[ii * kK + d]);
                 const float kb = eK * kn[ii * kK + d];
-                const float dk = acc[ct][e];
+                const float dk = acc[c][e];
                 if (ii < L) a.dk[out_at(ii, d)] += eK * dk;
-                dG[ct][e] -= kb * dk;
+                dG[c][e] -= kb * dk;
                 colp += kb * dk;
             }
             colp = sum4g(colp);
             if (gq == 0) sm.red[w][d] = colp;
         }
-        // exp(G_n) sum_v S[d][v] dS'[d][v], two threads per state row
-        {
-            const int d = tid >> 1, half = tid & 1;
-            const float *sr = S + d * kV + 64 * half, *dr = dSp + d * kV + 64 * half;
-            float s = 0.f;
-            for (int v = 0; v < 64; ++v) s += sr[v] * dr[v];
-            s += __shfl_xor(s, 1);
-            if (half == 0) sm.gns[d] = __expf(G[(L - 1) * kK + d]) * s;
-        }
     }
-    // P6: dA_qk = scale dO Ut^T (j <= i), dA_kk = -Z Ut^T (j < i); db += dA_kk . M; dM = Diag(b) dA_kk
+    __syncthreads();
+    // P6: dA_qk = scale dO Ut^T (j <= i), dA_kk = -Z Ut^T (j < i); db += dA_kk . M;
+    // dM = Diag(b) dA_kk.  Wave (w, hf) takes column tiles jt = 2 hf, 2 hf + 1.
     {
-        f4 accA[4], accK[4];
+        f4 accA[2], accK[2];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) { accA[jt] = f4{0, 0, 0, 0}; accK[jt] = accA[jt]; }
-        #pragma unroll 2
-        for (int ks = 0; ks < 32; ++ks) {
-            const float a1 = sm.D[16 * w + r][4 * ks + gq];
-            const float a2 = sm.Z[16 * w + r][4 * ks + gq];
+        for (int jj = 0; jj < 2; ++jj) { accA[jj] = f4{0, 0, 0, 0}; accK[jj] = accA[jj]; }
+        if (2 * hf <= w) {
+#pragma unroll 4
+            for (int ks = 0; ks < 32; ++ks) {
+                const float a1 = dov_a(4 * ks + gq);
+                const float a2 = sm.Z[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                if (jt <= w) {
-                    const float bv = sm.U[16 * jt + r][4 * ks + gq];
-                    accA[jt] = mma(a1, bv, accA[jt]);
-                    accK[jt] = mma(a2, bv, accK[jt]);
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int jt = 2 * hf + jj;
+                    if (jt <= w) {
+                        const float bv = sm.U[16 * jt + r][4 * ks + gq];
+                        accA[jj] = mma(a1, bv, accA[jj]);
+                        accK[jj] = mma(a2, bv, accK[jj]);
+                    }
                 }
             }
         }
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                const int jt = 2 * hf + jj;
                 const int ii = row0 + e, j = 16 * jt + r;
-                const float dAq = (jt <= w && j <= ii) ? scale * accA[jt][e] : 0.f;
-                const float dAk = (jt <= w && j < ii) ? -accK[jt][e] : 0.f;
+                const float dAq = (jt <= w && j <= ii) ? scale * accA[jj][e] : 0.f;
+                const float dAk = (jt <= w && j < ii) ? -accK[jj][e] : 0.f;
                 dbp[e] += dAk * Mk[ii * kChunk + j];
                 sm.T[ii][j] = dAq;
-                sm.X[ii][j] = sm.b[ii] * dAk;
+                sm.SB[ii][j] = sm.b[ii] * dAk;
             }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float s = sum16(dbp[e]);
-            if (r == 0) sm.db[row0 + e] += s;
+            if (r == 0) sm.db[hf][row0 + e] += s;
         }
     }
+    __syncthreads();
+    // khat, G and qhat into LDS for the Gram gradients
+    stage_rows(sm.U, kn, kChunk, tid, ident);
+    stage_rows(sm.Z, G, kChunk, tid, ident);
+    stage_rows(&sm.SB[kChunk], qn, kChunk, tid, ident);
     __syncthreads();
     // P7: the decayed Gram matrices P[i][j] = sum_d x_i y_j exp(G_i - G_j): for M
     // (x = y = khat, gradient dM) and A_qk (x = qhat, y = khat, gradient dA_qk)
     {
-        float refc[8];  // G at the reference row 16 w + 8, this lane's columns
+        const float(*kh)[kRP] = sm.U;
+        const float(*Gs)[kRP] = sm.Z;
+        const float(*qh)[kRP] = &sm.SB[kChunk];
+        float refc[4];  // G at the reference row 16 w + 8, this lane's columns
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) refc[ct] = G[(16 * w + 8) * kK + 16 * ct + r];
+        for (int c = 0; c < 4; ++c) refc[c] = Gs[16 * w + 8][16 * (4 * hf + c) + r];
         // rows i of block w: sum_{j <= 16 w + 15} dP[i][j] y_j exp(ref - G_j), times exp(G_i - ref)
         {
-            f4 rm[8], ra[8];
+            f4 rm[4], ra[4];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) { rm[ct] = f4{0, 0, 0, 0}; ra[ct] = rm[ct]; }
-            #pragma unroll 2
-        for (int ks = 0; ks < 4 * (w + 1); ++ks) {
+            for (int c = 0; c < 4; ++c) { rm[c] = f4{0, 0, 0, 0}; ra[c] = rm[c]; }
+#pragma unroll 2
+            for (int ks = 0; ks < 4 * (w + 1); ++ks) {
                 const int j = 4 * ks + gq;
-                const float a1 = sm.X[16 * w + r][j], a2 = sm.T[16 * w + r][j];
+                const float a1 = sm.SB[16 * w + r][j], a2 = sm.T[16 * w + r][j];
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct) {
-                    const int d = 16 * ct + r;
-                    const float bv = kn[j * kK + d] * __expf(refc[ct] - G[j * kK + d]);
-                    rm[ct] = mma(a1, bv, rm[ct]);
-                    ra[ct] = mma(a2, bv, ra[ct]);
+                for (int c = 0; c < 4; ++c) {
+                    const int d = 16 * (4 * hf + c) + r;
+                    const float bv = kh[j][d] * __expf(refc[c] - Gs[j][d]);
+                    rm[c] = mma(a1, bv, rm[c]);
+                    ra[c] = mma(a2, bv, ra[c]);
                 }
             }
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int ii = row0 + e, d = 16 * ct + r;
-                    const float s = __expf(G[ii * kK + d] - refc[ct]);
-                    const float RxM = rm[ct][e] * s, RxA = ra[ct][e] * s;
+                    const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
+                    const float s = __expf(Gs[ii][d] - refc[c]);
+                    const float RxM = rm[c][e] * s, RxA = ra[c][e] * s;
                     if (ii < L) {
                         a.dk[out_at(ii, d)] += RxM;
                         a.dq[out_at(ii, d)] += RxA;
                     }
-                    dG[ct][e] += kn[ii * kK + d] * RxM + qn[ii * kK + d] * RxA;
+                    dG[c][e] += kh[ii][d] * RxM + qh[ii][d] * RxA;
                 }
         }
         // columns j of block w: sum_{i >= 16 w} (dM[i][j] khat_i + dA_qk[i][j] qhat_i) exp(G_i - ref),
         // times exp(ref - G_j)
         {
-            f4 ry[8];
+            f4 ry[4];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) ry[ct] = f4{0, 0, 0, 0};
-            #pragma unroll 2
-        for (int ks = 4 * w; ks < 16; ++ks) {
+            for (int c = 0; c < 4; ++c) ry[c] = f4{0, 0, 0, 0};
+#pragma unroll 2
+            for (int ks = 4 * w; ks < 16; ++ks) {
                 const int i = 4 * ks + gq;
-                const float a1 = sm.X[i][16 * w + r], a2 = sm.T[i][16 * w + r];
+                const float a1 = sm.SB[i][16 * w + r], a2 = sm.T[i][16 * w + r];
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct) {
-                    const int d = 16 * ct + r;
-                    const float eg = __expf(G[i * kK + d] - refc[ct]);
-                    ry[ct] = mma(a1, kn[i * kK + d] * eg, ry[ct]);
-                    ry[ct] = mma(a2, qn[i * kK + d] * eg, ry[ct]);
+                for (int c = 0; c < 4; ++c) {
+                    const int d = 16 * (4 * hf + c) + r;
+                    const float eg = __expf(Gs[i][d] - refc[c]);
+                    ry[c] = mma(a1, kh[i][d] * eg, ry[c]);
+                    ry[c] = mma(a2, qh[i][d] * eg, ry[c]);
                 }
             }
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int jj = row0 + e, d = 16 * ct + r;
-                    const float Ry = ry[ct][e] * __expf(refc[ct] - G[jj * kK + d]);
+                    const int jj = row0 + e, d = 16 * (4 * hf + c) + r;
+                    const float Ry = ry[c][e] * __expf(refc[c] - Gs[jj][d]);
                     if (jj < L) a.dk[out_at(jj, d)] += Ry;
-                    dG[ct][e] -= kn[jj * kK + d] * Ry;
+                    dG[c][e] -= kh[jj][d] * Ry;
                 }
         }
     }
+    __syncthreads();
     // P8: dG_n into the last valid row, then da_t = sum_{i >= t} dG_i
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int ii = row0 + e, d = 16 * ct + r;
-            float v = dG[ct][e];
+            const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
+            float v = dG[c][e];
             if (ii == L - 1) v += sm.gns[d] + sm.red[0][d] + sm.red[1][d] + sm.red[2][d] + sm.red[3][d];
             sm.U[ii][d] = ii < L ? v : 0.f;
         }
@@ -748,29 +798,33 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
             sm.U[i][tid] = run;
         }
     }
-    __syncthreads();
-    // P9: norms, gate, outputs
-    {
-        float sq[4], sk[4];
+    // P9: norms, gate, outputs.  Row sums of qhat . dqhat and khat . dkhat first.
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int ii = row0 + e;
-            float a1 = 0.f, a2 = 0.f;
-            if (ii < L) {
+    for (int e = 0; e < 4; ++e) {
+        const int ii = row0 + e;
+        float a1 = 0.f, a2 = 0.f;
+        if (ii < L) {
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct) {
-                    a1 += qn[ii * kK + 16 * ct + r] * a.dq[out_at(ii, 16 * ct + r)];
-                    a2 += kn[ii * kK + 16 * ct + r] * a.dk[out_at(ii, 16 * ct + r)];
-                }
+            for (int c = 0; c < 4; ++c) {
+                const int d = 16 * (4 * hf + c) + r;
+                a1 += qn[ii * kK + d] * a.dq[out_at(ii, d)];
+                a2 += kn[ii * kK + d] * a.dk[out_at(ii, d)];
             }
-            sq[e] = sum16(a1);
-            sk[e] = sum16(a2);
         }
+        a1 = sum16(a1);
+        a2 = sum16(a2);
+        if (r == 0) {
+            sm.rs[0][hf][ii] = a1;
+            sm.rs[1][hf][ii] = a2;
+        }
+    }
+    __syncthreads();
+    {
         const float nA = -expf(a.A_log[h]);
         float pa = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const int d = 16 * ct + r;
+        for (int c = 0; c < 4; ++c) {
+            const int d = 16 * (4 * hf + c) + r;
             const float dtb = a.dt_bias[h * kK + d];
             float colp = 0.f;
 #pragma unroll
@@ -778,9 +832,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
                 const int ii = row0 + e;
                 if (ii < L) {
                     const int64_t o = out_at(ii, d);
+                    const float sq = sm.rs[0][0][ii] + sm.rs[0][1][ii];
+                    const float sk = sm.rs[1][0][ii] + sm.rs[1][1][ii];
                     const float rq = a.rq[ws * kChunk + ii], rk = a.rk[ws * kChunk + ii];
-                    a.dq[o] = rq * (a.dq[o] - sq[e] * qn[ii * kK + d]);
-                    a.dk[o] = rk * (a.dk[o] - sk[e] * kn[ii * kK + d]);
+                    a.dq[o] = rq * (a.dq[o] - sq * qn[ii * kK + d]);
+                    a.dk[o] = rk * (a.dk[o] - sk * kn[ii * kK + d]);
                     const float xg = bf16_bits_to_f32(a.g[o]) + dtb;
                     const float z = nA * softplus_acc(xg);
                     const float da = sm.U[ii][d];
@@ -797,15 +853,19 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
             if (gq == 0) sm.red[w][d] = colp;
         }
         pa = sum4g(sum16(pa));
-        if (lane == 0) sm.pa[w] = pa;
+        if (lane == 0) sm.pa[wv] = pa;
     }
     __syncthreads();
     float *part = a.part + ws * (kK + 1);
     if (tid < kK) part[tid] = sm.red[0][tid] + sm.red[1][tid] + sm.red[2][tid] + sm.red[3][tid];
-    if (tid == kK) part[kK] = sm.pa[0] + sm.pa[1] + sm.pa[2] + sm.pa[3];
+    if (tid == kK) {
+        float s = 0.f;
+        for (int i = 0; i < 8; ++i) s += sm.pa[i];
+        part[kK] = s;
+    }
     if (tid < L) {
         const float b = sm.b[tid];
-        a.dbeta[(t0 + tid) * H + h] = sm.db[tid] * b * (1.f - b);
+        a.dbeta[(t0 + tid) * H + h] = (sm.db[0][tid] + sm.db[1][tid]) * b * (1.f - b);
     }
 }
 
@@ -824,7 +884,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_params_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t kda_launch_bwd(const BwdArgs &a0, hipStream_t s) {
+hipError_t kda_launch_bwd(const BwdArgs &a0, hipStream_t s, hipEvent_t *ev) {
     BwdArgs a = a0;
     const int64_t units = a.slots * a.H;
     const int64_t piece = launch_piece(kMaxUnitsPerLaunch, a.piece_cap);
@@ -835,6 +895,7 @@ hipError_t kda_launch_bwd(const BwdArgs &a0, hipStream_t s) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return hipErrorUnknown;
     const int64_t NH = a.N * a.H;
     const int64_t groups = (NH + 7) / 8;
     const int64_t gpiece = launch_piece(kMaxGroupsPerLaunch, a.piece_cap);
@@ -845,13 +906,16 @@ hipError_t kda_launch_bwd(const BwdArgs &a0, hipStream_t s) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (ev && hipEventRecord(ev[1], s) != hipSuccess) return hipErrorUnknown;
     for (int64_t u0 = 0; u0 < units; u0 += piece) {
         a.unit_base = u0;
         const int64_t nu = units - u0 < piece ? units - u0 : piece;
-        hipLaunchKernelGGL(kda_bwd_main_kernel, dim3((unsigned)nu), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(kda_bwd_main_kernel, dim3((unsigned)nu), dim3(kMainThreads), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kda_bwd_params_kernel, dim3((unsigned)a.H), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && ev) return hipEventRecord(ev[2], s);
+    return e;
 }

@@ -313,7 +313,9 @@ hipError_t kda_launch_decode(const kda::DecodeArgs &a, hipStream_t s);
 // The backward's own kernels (kda_bwd.hip): per-chunk preparation, the
 // reverse state chain, the per-chunk gradient, and the sum of the shared
 // parameters' partial gradients.
-hipError_t kda_launch_bwd(const kda::BwdArgs &a, hipStream_t s);
+// With ev (3 events) it records ev[0] after the preparation kernel, ev[1] after
+// the reverse chain and ev[2] after the per-chunk gradient and the parameter sum.
+hipError_t kda_launch_bwd(const kda::BwdArgs &a, hipStream_t s, hipEvent_t *ev = nullptr);
 // The pipelined forward (kda_fused.hip): whether it handles these shapes, and
 // its launch (the flag clear and the fused producer / consumer grid).
 bool kda_fused_applies(int64_t N, int64_t H, bool varlen);
