@@ -426,6 +426,7 @@ struct BwdLayout {
 
 // Geometry of a backward call: the forward's, never split nor pipelined.
 kda_status_t make_bwd_geometry(const kda_desc_t *d, bool varlen, Geometry &g) {
+    if (d->chain_segments < 0) return KDA_ERR_PARAM;
     if (d->chain_segments >= 2) return KDA_ERR_UNSUPPORTED;
     kda_desc_t e = *d;
     e.chain_segments = 1;

@@ -285,7 +285,8 @@ size_t kda_bwd_workspace_size(const kda_desc_t *desc);
  * clamped (-exp(A_log) softplus(g + dt_bias) <= lower_bound) no gradient
  * reaches g, dt_bias or A_log; at the kink itself the clamped side is taken.
  * desc->chain_segments >= 2 is KDA_ERR_UNSUPPORTED (the backward never splits
- * chains; 0 and 1 both mean unsplit); desc->pipeline is ignored;
+ * chains; 0 and 1 both mean unsplit; negative is KDA_ERR_PARAM);
+ * desc->pipeline is ignored;
  * desc->phase_events, when set, is an array of 6 events recorded before the
  * first kernel (0), after the forward's intra-chunk kernel (1) and state
  * chain (2), after the gradient's preparation kernel (3), its reverse state

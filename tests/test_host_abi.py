@@ -214,3 +214,53 @@ def test_noalloc_validation_and_limit(lib):
     assert kda.workspace_size(1, 8192, 32) > cap
     assert call(big) == 9
     assert lib.kda_status_string(9).startswith(b"workspace need exceeds the static scratch")
+
+
+def _call_bwd(lib, d, lb=-5.0, scale=0.1, null=(), align=None, cu=None):
+    names = ("q", "k", "v", "g", "beta", "A_log", "dt_bias", "d_out", "dq", "dk", "dv", "dg", "dbeta",
+             "dA_log", "ddt_bias")
+    ptrs = {n: ctypes.c_void_p(FAKE) for n in names}
+    for n in null:
+        ptrs[n] = None
+    if align:
+        ptrs[align] = ctypes.c_void_p(FAKE + 2)
+    return lib.kda_bwd(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["g"], ptrs["beta"], scale, ptrs["A_log"],
+                       ptrs["dt_bias"], lb, None, cu, ptrs["d_out"], None, ptrs["dq"], ptrs["dk"], ptrs["dv"],
+                       ptrs["dg"], ptrs["dbeta"], None, ptrs["dA_log"], ptrs["ddt_bias"], ctypes.byref(d), None)
+
+
+def test_bwd_validation_errors(lib):
+    # the backward checks its arguments like the forward, before any device work
+    assert _call_bwd(lib, _desc(K=64)) == 3
+    assert _call_bwd(lib, _desc(B=0)) == 2
+    assert _call_bwd(lib, _desc(B=2, num_seqs=2), cu=ctypes.c_void_p(FAKE)) == 2
+    assert _call_bwd(lib, _desc(chain_segments=2)) == 3       # the backward never splits chains
+    assert _call_bwd(lib, _desc(chain_segments=-1)) == 4
+    assert _call_bwd(lib, _desc(launch_piece=-1)) == 4
+    assert _call_bwd(lib, _desc(), lb=-6.0) == 4
+    assert _call_bwd(lib, _desc(), scale=float("nan")) == 4
+    for n in ("q", "k", "v", "g", "beta", "d_out", "dq", "dk", "dv", "dg", "dbeta", "A_log", "dt_bias",
+              "dA_log", "ddt_bias"):
+        assert _call_bwd(lib, _desc(), null=(n,)) == 1, n
+    for n in ("q", "d_out", "dq", "dk", "dv", "dg", "dt_bias"):
+        assert _call_bwd(lib, _desc(), align=n) == 6, n
+    d = _desc(workspace=ctypes.c_void_p(0x100000), workspace_bytes=1024)
+    assert _call_bwd(lib, d) == 7
+    d = _desc(initial_state_dtype=9)
+    assert lib.kda_bwd(*([ctypes.c_void_p(FAKE)] * 5), 0.1, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), -5.0,
+                       ctypes.c_void_p(FAKE), None, ctypes.c_void_p(FAKE), None,
+                       *([ctypes.c_void_p(FAKE)] * 5), None, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                       ctypes.byref(d), None) == 5
+
+
+def test_bwd_workspace_size(lib):
+    # the forward's 72.5 KiB per (chunk, head) plus 2 x 64 KiB of states, 32 KiB of dUt,
+    # 3 x 32 KiB + 2 x 16 KiB of per-chunk fp32 quantities, 768 B of row scalars and 516 B of
+    # parameter partials; plus the recomputed output (B T H V bf16)
+    per = (kda.bwd_workspace_size(4, 64 * 100, 8) - kda.bwd_workspace_size(4, 64 * 50, 8)) / (4 * 50 * 8)
+    expect = 72.5 * 1024 + 2 * 65536 + 32768 + 3 * 32768 + 2 * 16384 + 3 * 256 + 516 + 64 * 128 * 2
+    assert abs(per - expect) < 1024
+    assert kda.bwd_workspace_size(1, 0, 4) > 0 or kda.bwd_workspace_size(1, 0, 4) == 0
+    assert kda.bwd_workspace_size(2, 64, 2, num_seqs=3) == 0
+    d = _desc(chain_segments=4)
+    assert lib.kda_bwd_workspace_size(ctypes.byref(d)) == 0
