@@ -44,10 +44,7 @@ constexpr int kChainWaves = 4;            // consumer: 32 value columns each
 constexpr int kRingSlots = 2;
 // Consumer ring slot: -W 16 frags, Kbar^T 16, U (all 8 column blocks) 16, exp(G_n) 1, Q_gamma 16, A_qk 8
 constexpr int kFW = 0, kFK = 16, kFU = 32, kFG = 48, kFQ = 49, kFA = 65, kFrags = 73;
-#ifndef FUSED_NT_LOADS
-#define FUSED_NT_LOADS 1
-#endif
-constexpr bool kProducerNTLoads = FUSED_NT_LOADS;  // producers' input loads bypass L2 residency
+constexpr bool kProducerNTLoads = true;  // producers' input loads bypass L2 residency
 constexpr int kSpinMax = 1 << 20;          // bounded waits: about 0.1 s of polling each
 
 struct __align__(16) ConsumerSmem {
