@@ -420,7 +420,8 @@ namespace {
 
 struct BwdLayout {
     WorkspaceLayout fwd;  // the forward's intermediates (unsplit, two-kernel)
-    size_t off_out, off_hs, off_dhs, off_dUt, off_qn, off_kn, off_G, off_rq, off_rk, off_bb, off_Mk, off_Tm, off_part;
+    size_t off_out, off_hs, off_dhs, off_dUt, off_qn, off_kn, off_G, off_rq, off_rk, off_bb, off_Mk, off_Tm, off_part,
+        off_co;
     size_t total;
 };
 
@@ -452,6 +453,7 @@ BwdLayout make_bwd_layout(const Geometry &g) {
     L.off_Mk = o;   o = align_up(o + per * kChunk * kChunk * 4, 256);
     L.off_Tm = o;   o = align_up(o + per * kChunk * kChunk * 4, 256);
     L.off_part = o; o = align_up(o + per * (kK + 1) * 4, 256);
+    L.off_co = o;   o = align_up(o + per * kBwdChainOperandBytes, 256);
     L.total = o;
     return L;
 }
@@ -577,6 +579,7 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
     ba.Mk = reinterpret_cast<float *>(ws + lay.off_Mk);
     ba.Tm = reinterpret_cast<float *>(ws + lay.off_Tm);
     ba.part = reinterpret_cast<float *>(ws + lay.off_part);
+    ba.co = reinterpret_cast<unsigned char *>(ws + lay.off_co);
     ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dg = dg; ba.dbeta = dbeta;
     ba.dh0 = d_initial_state; ba.dA_log = dA_log; ba.ddt_bias = ddt_bias;
     ba.piece_cap = desc->launch_piece;

@@ -90,11 +90,29 @@ __device__ __forceinline__ bool chunk_rows(const BwdArgs &a, int64_t slot, int64
 
 // ---- 2. per-chunk preparation ------------------------------------------------
 
+// The reverse chain's operands of one (chunk, head), fp16, written by the
+// preparation kernel in the padded row-major layouts the chain reads them in
+// (every part a whole number of KiB, so the chain copies it with 1 KiB
+// global_load_lds instructions):
+//   Kn  [64][136]   Kbar[i][d] = exp(G_n[d] - G_i[d]) khat_i[d]
+//   AqT [64][72]    A_qk^T[j][i], A_qk[i][j] = sum_d qhat_i khat_j exp(G_i - G_j) (j <= i)
+//   WT  [128][72]   -W^T[d][i], W = T Diag(b) (gamma * Khat)
+//   QgT [128][72]   Qg^T[d][i], Qg = gamma * qhat
+//   gn  [128] fp32  exp(G_n)
+constexpr int kKnP = 136, kTkP = 72;
+constexpr int kCoKn = 0;
+constexpr int kCoAq = kCoKn + kChunk * kKnP * 2;   // 17408
+constexpr int kCoW = kCoAq + kChunk * kTkP * 2;    // 26624
+constexpr int kCoQ = kCoW + kK * kTkP * 2;         // 45056
+constexpr int kCoGn = kCoQ + kK * kTkP * 2;        // 63488
+constexpr int kCoBytes = kCoGn + kK * 4;           // 64000
+static_assert(kCoGn % 1024 == 0 && kCoBytes == kBwdChainOperandBytes, "chain operand block layout");
+
 struct PrepSmem {
     float q[kChunk][kK + 1];
     float k[kChunk][kK + 1];
     float G[kChunk][kK + 1];
-    float M[kChunk][kChunk + 1];
+    float M[kChunk][kChunk + 1];   // M, then T
     float b[kChunk];
     float xr[4][16];  // one row of T per wave, broadcast during the solve
 };
@@ -108,6 +126,12 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
     if (!chunk_rows(a, slot, t0, L)) return;
     const int64_t H = a.H;
     const int tid = threadIdx.x;
+    unsigned char *co = a.co + ws * (int64_t)kCoBytes;
+    _Float16 *Kn = reinterpret_cast<_Float16 *>(co + kCoKn);
+    _Float16 *AqT = reinterpret_cast<_Float16 *>(co + kCoAq);
+    _Float16 *WT = reinterpret_cast<_Float16 *>(co + kCoW);
+    _Float16 *QgT = reinterpret_cast<_Float16 *>(co + kCoQ);
+    float *gno = reinterpret_cast<float *>(co + kCoGn);
 
     // rows, norms, b and the per-channel log-decay; a quarter row per thread
     {
@@ -162,37 +186,65 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
             kn[idx] = sm.k[i][d];
             G[idx] = sm.G[i][d];
         }
+        // Kbar (natural) and Qg^T (four rows per store), exp(G_n)
+        const float *Gn = sm.G[L - 1];
+        for (int idx = tid; idx < kChunk * kK; idx += kThreads) {
+            const int i = idx >> 7, d = idx & 127;
+            Kn[i * kKnP + d] = (_Float16)(__expf(Gn[d] - sm.G[i][d]) * sm.k[i][d]);
+        }
+        for (int idx = tid; idx < kK * (kChunk / 4); idx += kThreads) {
+            const int d = idx >> 4, i0 = 4 * (idx & 15);
+            h4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (_Float16)(__expf(sm.G[i0 + e][d]) * sm.q[i0 + e][d]);
+            *reinterpret_cast<h4 *>(QgT + d * kTkP + i0) = v;
+        }
+        if (tid < kK) gno[tid] = __expf(Gn[tid]);
     }
 
     const int w = tid >> 6, lane = tid & 63, r = lane & 15, gq = lane >> 4;
-    // M[i][j] = sum_d khat_i khat_j exp(G_i - G_j), j < i; wave w takes row block w,
-    // with exp(G_i - G_j) = exp(G_i - ref) exp(ref - G_j), ref = G[16 w + 8]
-    float *Mk = a.Mk + ws * (kChunk * kChunk);
-    for (int J = 0; J < 4; ++J) {
-        f4 acc = f4{0, 0, 0, 0};
-        if (J <= w) {
-            for (int ks = 0; ks < 32; ++ks) {
-                const int d = 4 * ks + gq;
-                const float ref = sm.G[16 * w + 8][d];
-                const float av = sm.k[16 * w + r][d] * __expf(sm.G[16 * w + r][d] - ref);
-                const float bv = sm.k[16 * J + r][d] * __expf(ref - sm.G[16 * J + r][d]);
-                acc = mma(av, bv, acc);
+    // M[i][j] = sum_d khat_i khat_j exp(G_i - G_j) (j < i) and A_qk (qhat_i, j <= i); wave w
+    // takes row block w, with exp(G_i - G_j) = exp(G_i - ref) exp(ref - G_j), ref = G[16 w + 8]
+    {
+        f4 accM[4], accA[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) { accM[J] = f4{0, 0, 0, 0}; accA[J] = accM[J]; }
+        for (int ks = 0; ks < 32; ++ks) {
+            const int d = 4 * ks + gq;
+            const float ref = sm.G[16 * w + 8][d];
+            const float fa = __expf(sm.G[16 * w + r][d] - ref);
+            const float ak = sm.k[16 * w + r][d] * fa, aq = sm.q[16 * w + r][d] * fa;
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                if (J <= w) {
+                    const float bv = sm.k[16 * J + r][d] * __expf(ref - sm.G[16 * J + r][d]);
+                    accM[J] = mma(ak, bv, accM[J]);
+                    accA[J] = mma(aq, bv, accA[J]);
+                }
             }
         }
+        float *Mk = a.Mk + ws * (kChunk * kChunk);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * w + 4 * gq + e, j = 16 * J + r;
-            const float m = j < i ? acc[e] : 0.f;
-            sm.M[i][j] = m;
-            Mk[i * kChunk + j] = m;
+        for (int J = 0; J < 4; ++J) {
+            h4 at;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * w + 4 * gq + e, j = 16 * J + r;
+                const float m = (J <= w && j < i) ? accM[J][e] : 0.f;
+                sm.M[i][j] = m;
+                Mk[i * kChunk + j] = m;
+                at[e] = (_Float16)((J <= w && j <= i) ? accA[J][e] : 0.f);
+            }
+            // A_qk^T[16 J + r][16 w + 4 gq .. + 3]
+            *reinterpret_cast<h4 *>(AqT + (16 * J + r) * kTkP + 16 * w + 4 * gq) = at;
         }
     }
     __syncthreads();
     // T = (I + Diag(b) M)^-1 by forward substitution, rows in lanes, wave w
     // taking columns 16 w .. 16 w + 15: row c is final once rows < c are applied
+    float x[16];
     {
         const int j0 = 16 * w;
-        float x[16];
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) x[jj] = lane == j0 + jj ? 1.f : 0.f;
         const float br = sm.b[lane];
@@ -211,19 +263,48 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) Tm[jj] = x[jj];
     }
+    __syncthreads();  // every wave is done with M
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) sm.M[lane][16 * w + jj] = x[jj];
+    __syncthreads();
+    // W = T Diag(b) (gamma * Khat), stored as -W^T; T[i][j] = 0 for j > i
+    {
+        f4 acc[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
+        for (int ks = 0; ks < 4 * (w + 1); ++ks) {
+            const int j = 4 * ks + gq;
+            const float av = sm.M[16 * w + r][j];
+            const float bj = sm.b[j];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                const int d = 16 * ct + r;
+                acc[ct] = mma(av, bj * __expf(sm.G[j][d]) * sm.k[j][d], acc[ct]);
+            }
+        }
+        // lane holds W[16 w + 4 gq + e][16 ct + r] -> -W^T[16 ct + r][16 w + 4 gq .. + 3]
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            h4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (_Float16)(-acc[ct][e]);
+            *reinterpret_cast<h4 *>(WT + (16 * ct + r) * kTkP + 16 * w + 4 * gq) = v;
+        }
+    }
 }
 
 // ---- 3. the reverse state chain ----------------------------------------------
 
-constexpr int kChainWaves = 5;  // 4 compute waves + 1 loader
-constexpr int kFragK = 0, kFragA = 16, kFragW = 24, kFragQ = 40, kFrags = 56;
+constexpr int kChainWaves = 6;  // 4 compute waves, the loader, the L2 prefetch
+constexpr int kChainAhead = 3;  // chunks the L2 prefetch runs ahead of the chain
+constexpr int kTouchInFlight = 8;  // L2 prefetch loads allowed in flight (two per chunk)
 
 struct __align__(16) BwdChainSmem {
-    h8 ops[2][kFrags][64];          // per slot: Kf, Af, Wf, Qf fragments of one chunk
-    float gn[2][kK];                // exp(G_n)
-    uint16_t dO[2][kChunk][16];     // the chunk's rows of the block's 16 columns (bf16)
-    f4 red[4][4][64];               // partial dUt tiles [wave][row tile][lane]
-    float dU[kChunk][17];           // dUt of the block
+    unsigned char ops[2][kCoBytes];   // one chunk's operand block per slot (layout above)
+    _Float16 dOT[2][16][kTkP];        // dO^T of the block's 16 columns (fp16)
+    f4 red[4][4][64];                 // partial dUt tiles [wave][row tile][lane]
+    _Float16 dUT[16][kTkP];           // dUt^T of the block (fp16)
+    uint32_t dump[64];                // landing place of the L2 prefetch copies (never read)
 };
 
 __device__ __forceinline__ void copy16(const void *g, void *l) {
@@ -231,7 +312,11 @@ __device__ __forceinline__ void copy16(const void *g, void *l) {
                                      (__attribute__((address_space(3))) void *)l, 16, 0, 0);
 }
 
-__device__ __forceinline__ float ldh(const _Float16 *p, int idx) { return (float)p[idx]; }
+__device__ __forceinline__ h4 pack_h4(const f4 &x) {
+    h4 r;
+    r[0] = (_Float16)x[0]; r[1] = (_Float16)x[1]; r[2] = (_Float16)x[2]; r[3] = (_Float16)x[3];
+    return r;
+}
 
 __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdArgs a) {
     __shared__ BwdChainSmem sm;
@@ -260,30 +345,55 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
     const int col0 = 16 * vb;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
 
+    if (wave == 5) {
+        // ---- L2 prefetch: this block's eighth of the operand lines of chunk
+        // step s + kChainAhead, while the others work on step s (no destination
+        // registers: the copies land in an LDS area nobody reads) ----------------
+        if (nchunks > 0) {
+            const int line = vb + 8 * lane;  // 500 lines of 128 B per chunk; lanes past the end repeat line vb
+            const int64_t off = 128 * (int64_t)(line < kCoBytes / 128 ? line : vb);
+            for (int64_t s = -1; s < nchunks; ++s) {
+                const int64_t u = s + kChainAhead;
+                const int64_t ci = nchunks - 1 - (u < nchunks ? u : nchunks - 1);
+                lds_copy4(a.co + ((c0 + ci) * H + h) * (int64_t)kCoBytes + off, lds_addr(&sm.dump[0]));
+                // and the chunk's dO rows of this block (one 32-byte piece per token row)
+                const int64_t rows = seqlen - kChunk * ci;
+                const int64_t tok = tseq + kChunk * ci + (lane < rows ? lane : 0);
+                lds_copy4(a.dout + (tok * H + h) * kV + col0, lds_addr(&sm.dump[0]));
+                asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTouchInFlight) : "memory");
+                lds_barrier();
+                if (s >= 0) {
+                    lds_barrier();
+                    lds_barrier();
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        return;
+    }
     if (wave == 4) {
         // ---- loader: chunk ci into slot s ------------------------------------
         auto load = [&](int64_t ci, int s) {
             const int64_t ws = (c0 + ci) * H + h;
-            const h8 *Kp = reinterpret_cast<const h8 *>(a.Kf + ws * kKfElems) + lane;
-            const h8 *Ap = reinterpret_cast<const h8 *>(a.Af + ws * kAfElems) + lane;
-            const h8 *Wp = reinterpret_cast<const h8 *>(a.Wf + ws * kWfElems) + lane;
-            const h8 *Qp = reinterpret_cast<const h8 *>(a.Qf + ws * kQfElems) + lane;
-#pragma unroll
-            for (int f = 0; f < 16; ++f) copy16(Kp + f * 64, &sm.ops[s][kFragK + f][0]);
-#pragma unroll
-            for (int f = 0; f < 8; ++f) copy16(Ap + f * 64, &sm.ops[s][kFragA + f][0]);
-#pragma unroll
-            for (int f = 0; f < 16; ++f) copy16(Wp + f * 64, &sm.ops[s][kFragW + f][0]);
-#pragma unroll
-            for (int f = 0; f < 16; ++f) copy16(Qp + f * 64, &sm.ops[s][kFragQ + f][0]);
-            if (lane < 32) copy16(reinterpret_cast<const h8 *>(a.gn + ws * kGnElems) + lane, &sm.gn[s][0]);
+            const unsigned char *src = a.co + ws * (int64_t)kCoBytes + 16 * lane;
+#pragma unroll 4
+            for (int f = 0; f < kCoGn / 1024; ++f) copy16(src + 1024 * f, &sm.ops[s][1024 * f]);
+            if (lane < 32) copy16(src + kCoGn, &sm.ops[s][kCoGn]);
+            // dO^T: lane = token row (zero past the end), bf16 -> fp16
             const int64_t rows = seqlen - kChunk * ci;
+            h8 v0 = h8{0, 0, 0, 0, 0, 0, 0, 0}, v1 = v0;
+            if (lane < rows) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(a.dout + ((tseq + kChunk * ci + lane) * H + h) * kV + col0);
+                float f[16];
+                unpack_bf16x8(p[0], f);
+                unpack_bf16x8(p[1], f + 8);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int p = lane + 64 * i, row = p >> 1, half = p & 1;
-                const int64_t tok = tseq + kChunk * ci + (row < rows ? row : 0);
-                copy16(a.dout + (tok * H + h) * kV + col0 + 8 * half,
-                       reinterpret_cast<char *>(&sm.dO[s][0][0]) + 64 * 16 * i);
+                for (int c = 0; c < 8; ++c) { v0[c] = (_Float16)f[c]; v1[c] = (_Float16)f[8 + c]; }
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                sm.dOT[s][c][lane] = v0[c];
+                sm.dOT[s][8 + c][lane] = v1[c];
             }
         };
         if (nchunks > 0) {
@@ -323,8 +433,11 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
             const int64_t ci = nchunks - 1 - s;
             const int slot = (int)(s & 1);
             const int64_t ws = (c0 + ci) * H + h;
-            const int rows = (int)(seqlen - kChunk * ci < kChunk ? seqlen - kChunk * ci : kChunk);
-            const _Float16 *ops = reinterpret_cast<const _Float16 *>(&sm.ops[slot][0][0]);
+            const _Float16 *Kn = reinterpret_cast<const _Float16 *>(&sm.ops[slot][kCoKn]);
+            const _Float16 *AqT = reinterpret_cast<const _Float16 *>(&sm.ops[slot][kCoAq]);
+            const _Float16 *WT = reinterpret_cast<const _Float16 *>(&sm.ops[slot][kCoW]);
+            const _Float16 *QgT = reinterpret_cast<const _Float16 *>(&sm.ops[slot][kCoQ]);
+            const float *gn = reinterpret_cast<const float *>(&sm.ops[slot][kCoGn]);
             // the gradient of the state leaving this chunk
             {
                 float *dh = a.dhs + ws * (int64_t)(kK * kV) + col0 + r;
@@ -333,37 +446,29 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
 #pragma unroll
                     for (int e = 0; e < 4; ++e) dh[(16 * (2 * w + t) + 4 * g + e) * kV] = dS[t][e];
             }
-            // partial dUt over this wave's 32 state rows: Kbar[:, rows] dS[rows]
+            // partial dUt over this wave's 32 state rows: Kbar[:, rows] dS[rows]; the B
+            // operand of channel tile ct is the lane's own accumulator tile, in fp16
             f4 acc[4];
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) acc[jt] = f4{0, 0, 0, 0};
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int ct = 2 * w + t;
+                const h4 bv = pack_h4(dS[t]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float bv = dS[t][e];
-                    // Kbar[16 jt + r][16 ct + 4 g + e]: fragment (ct, jt / 2), lane 4 g + e + 16 (r / 4)
-#pragma unroll
-                    for (int jt = 0; jt < 4; ++jt) {
-                        const int idx = ((kFragK + ct * 2 + (jt >> 1)) * 64 + 4 * g + e + 16 * (r >> 2)) * 8 +
-                                        4 * (jt & 1) + (r & 3);
-                        acc[jt] = mma(ldh(ops, idx), bv, acc[jt]);
-                    }
+                for (int jt = 0; jt < 4; ++jt) {
+                    const h4 av = *reinterpret_cast<const h4 *>(Kn + (16 * jt + r) * kKnP + 16 * ct + 4 * g);
+                    acc[jt] = mfma16x16x16_f16(av, bv, acc[jt]);
                 }
             }
-            // scale A_qk^T dO for row tile w: A_qk[i][16 w + r], i = 4 ks + g
+            // scale A_qk^T dO for row tile w
             {
                 f4 aq = f4{0, 0, 0, 0};
-                const int j = 16 * w + r;
-#pragma unroll 4
-                for (int ks = 0; ks < 16; ++ks) {
-                    const int i = 4 * ks + g;
-                    const int idx = ((kFragA + (i >> 4) * 2 + (w >> 1)) * 64 + (i & 15) + 16 * (r >> 2)) * 8 +
-                                    4 * (w & 1) + (r & 3);
-                    const float av = j <= i ? ldh(ops, idx) : 0.f;
-                    const float bv = i < rows ? bf16_bits_to_f32(sm.dO[slot][i][r]) : 0.f;
-                    aq = mma(av, bv, aq);
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const h4 av = *reinterpret_cast<const h4 *>(AqT + (16 * w + r) * kTkP + 16 * kb + 4 * g);
+                    const h4 bv = *reinterpret_cast<const h4 *>(&sm.dOT[slot][r][16 * kb + 4 * g]);
+                    aq = mfma16x16x16_f16(av, bv, aq);
                 }
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt)
@@ -377,30 +482,27 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
                 const f4 u = sm.red[0][w][lane] + sm.red[1][w][lane] + sm.red[2][w][lane] + sm.red[3][w][lane];
                 float *du = a.dUt + ws * (int64_t)(kChunk * kV) + col0 + r;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * w + 4 * g + e;
-                    sm.dU[i][r] = u[e];
-                    du[i * kV] = u[e];
-                }
+                for (int e = 0; e < 4; ++e) du[(16 * w + 4 * g + e) * kV] = u[e];
+                *reinterpret_cast<h4 *>(&sm.dUT[r][16 * w + 4 * g]) = pack_h4(u);
             }
             lds_barrier();
-            // dS <- Diag(exp(G_n)) dS - W^T dUt + scale Qg^T dO   (Wf holds -W)
+            // dS <- Diag(exp(G_n)) dS - W^T dUt + scale Qg^T dO   (WT holds -W^T)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int ct = 2 * w + t;
-                f4 nd;
+                f4 nd, nq = f4{0, 0, 0, 0};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) nd[e] = sm.gn[slot][16 * ct + 4 * g + e] * dS[t][e];
-#pragma unroll 4
-                for (int ks = 0; ks < 16; ++ks) {
-                    const int i = 4 * ks + g;
-                    const int off = (((i >> 4) * 4 + (ct >> 1)) * 64 + (i & 15) + 16 * (r >> 2)) * 8 + 4 * (ct & 1) +
-                                    (r & 3);
-                    const float bo = i < rows ? a.scale * bf16_bits_to_f32(sm.dO[slot][i][r]) : 0.f;
-                    nd = mma(ldh(ops, kFragW * 64 * 8 + off), sm.dU[i][r], nd);
-                    nd = mma(ldh(ops, kFragQ * 64 * 8 + off), bo, nd);
+                for (int e = 0; e < 4; ++e) nd[e] = gn[16 * ct + 4 * g + e] * dS[t][e];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const h4 aw = *reinterpret_cast<const h4 *>(WT + (16 * ct + r) * kTkP + 16 * kb + 4 * g);
+                    const h4 bu = *reinterpret_cast<const h4 *>(&sm.dUT[r][16 * kb + 4 * g]);
+                    nd = mfma16x16x16_f16(aw, bu, nd);
+                    const h4 aq = *reinterpret_cast<const h4 *>(QgT + (16 * ct + r) * kTkP + 16 * kb + 4 * g);
+                    const h4 bo = *reinterpret_cast<const h4 *>(&sm.dOT[slot][r][16 * kb + 4 * g]);
+                    nq = mfma16x16x16_f16(aq, bo, nq);
                 }
-                dS[t] = nd;
+                dS[t] = nd + a.scale * nq;
             }
             lds_barrier();
         }

@@ -145,7 +145,10 @@ struct DecodeArgs {
 //   rq, rk, bb [ws][64] fp32    reciprocal norms of q and k, b = sigmoid(beta)
 //   Mk, Tm [ws][64][64] fp32    decayed key Gram (strictly lower, without b) and T = (I + Diag(b) Mk)^-1
 //   part [ws][K + 1] fp32       this chunk's share of ddt_bias (K) and of dA_log (1)
+//   co [ws][64000 B]            the reverse chain's fp16 operands (layout in kda_bwd.hip)
 // Rows past the end of a ragged chunk are zero in qn, kn, bb and keep G constant.
+constexpr int64_t kBwdChainOperandBytes = 64000;  // per (chunk, head): the reverse chain's fp16 operands
+
 struct BwdArgs {
     const uint16_t *q, *k, *v, *g, *beta;   // bf16 inputs
     const float *A_log, *dt_bias;
@@ -159,6 +162,7 @@ struct BwdArgs {
     const _Float16 *Wf, *Qf, *Kf, *Af;      // the forward's intermediates
     const float *gn;
     float *hs, *dhs, *dUt, *qn, *kn, *G, *rq, *rk, *bb, *Mk, *Tm, *part;
+    unsigned char *co;                      // [ws][64000 B] the reverse chain's fp16 operands
     float *dq, *dk, *dv, *dg, *dbeta;       // [B,T,H,K] / [B,T,H,V] / [B,T,H] fp32
     float *dh0;                             // [N,H,K,V] fp32 or nullptr
     float *dA_log, *ddt_bias;               // [H] / [H,K] fp32
