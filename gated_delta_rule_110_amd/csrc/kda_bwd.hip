@@ -50,6 +50,15 @@ __device__ __forceinline__ f4 mma(float a, float b, const f4 &c) {
 }
 
 __device__ __forceinline__ float softplus_acc(float x) { return x > 15.0f ? x : log1pf(expf(x)); }
+// softplus on the hardware exp / log, in the three ranges of the forward's gate
+// (series below e^x = 2^-6, x itself above 15, log(1 + e^x) between)
+__device__ __forceinline__ float softplus_fast(float x) {
+    const float t = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+    const float series = t * (1.0f - t * (0.5f - t * (1.0f / 3.0f)));
+    float sp = __builtin_amdgcn_logf(1.0f + t) * 0.6931471805599453f;
+    sp = t < 0.015625f ? series : sp;
+    return x > 15.0f ? x : sp;
+}
 __device__ __forceinline__ float sigmoid_acc(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 // Sum over the 16 lanes of a row group (lanes r = 0..15 with the same g).
@@ -526,14 +535,27 @@ struct MainSmem {
     float U[kChunk][kRP];   // gamma Khat (P1), Ut (P2-P6), khat (P7), then dG and its reverse cumulative sum
     float Z[kChunk][kRP];   // Diag(b) Y (P1-P2), dUt (P3), Z (P3-P6), G (P7)
     float SB[kK][kRP];      // S (P1-P4), dS' (P5); in P7 dM in rows 0..63 and qhat in rows 64..127
-    float T[kChunk][kTP];   // T (P0-P3), dA_qk (P6-P7)
+    union {
+        float T[kChunk][kTP];        // T (P0-P3)
+        uint16_t D[kChunk][136];     // dO, bf16 (P4-P6)
+    } t;
     float b[kChunk];
     float db[2][kChunk];    // per column half
     float rs[2][2][kChunk]; // row sums qhat . dqhat and khat . dkhat, per column half
     float red[4][kK];       // column sums per row block
     float gns[kK];          // exp(G_n) * sum_v S * dS'
+    float tot[4][kK];       // segment totals of the reverse cumulative sum
     float pa[8];            // per-wave dA_log sums
 };
+
+// The same pointer, hidden from the compiler: loads through it are not merged
+// with loads of the same addresses in other phases, which would keep those
+// values alive (in registers) across the whole kernel.
+template <typename T>
+__device__ __forceinline__ T *opaque(T *p) {
+    asm volatile("" : "+s"(p));
+    return p;
+}
 
 // Copy a [rows][128] fp32 row-major block from global memory into an LDS tile
 // of pitch kRP, optionally scaled element by element by f(row, col, value).
@@ -561,41 +583,56 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int w = wv & 3, hf = wv >> 2;
     const int lane = tid & 63, r = lane & 15, gq = lane >> 4;
-    const float *S = a.hs + ws * (int64_t)(kK * kV);
-    const float *dSp = a.dhs + ws * (int64_t)(kK * kV);
-    const float *dUt = a.dUt + ws * (int64_t)(kChunk * kV);
-    const float *qn = a.qn + ws * (kChunk * kK);
-    const float *kn = a.kn + ws * (kChunk * kK);
-    const float *G = a.G + ws * (kChunk * kK);
-    const float *Mk = a.Mk + ws * (kChunk * kChunk);
+    // Every buffer the kernel touches is distinct, and saying so lets the compiler
+    // issue the epilogues' loads ahead of their stores instead of one after another.
+    const float *__restrict__ S = a.hs + ws * (int64_t)(kK * kV);
+    const float *__restrict__ dSp = a.dhs + ws * (int64_t)(kK * kV);
+    const float *__restrict__ dUt = a.dUt + ws * (int64_t)(kChunk * kV);
+    const float *__restrict__ qn_all = a.qn + ws * (kChunk * kK);
+    const float *__restrict__ kn_all = a.kn + ws * (kChunk * kK);
+    const float *__restrict__ G_all = a.G + ws * (kChunk * kK);
+    const float *__restrict__ qn = qn_all;
+    const float *__restrict__ kn = kn_all;
+    const float *__restrict__ G = G_all;
+    const float *__restrict__ Mk = a.Mk + ws * (kChunk * kChunk);
+    const float *__restrict__ Tm = a.Tm + ws * (kChunk * kChunk);
+    const float *__restrict__ rqv = a.rq + ws * kChunk;
+    const float *__restrict__ rkv = a.rk + ws * kChunk;
+    const float *__restrict__ bbv = a.bb + ws * kChunk;
+    const uint16_t *__restrict__ vin = a.v;
+    const uint16_t *__restrict__ gin = a.g;
+    const float *__restrict__ dtb_h = a.dt_bias + h * kK;
+    float *__restrict__ dqo = a.dq;
+    float *__restrict__ dko = a.dk;
+    float *__restrict__ dvo = a.dv;
+    float *__restrict__ dgo = a.dg;
+    float *__restrict__ dbo = a.dbeta;
+    float *__restrict__ part = a.part + ws * (kK + 1);
     const float scale = a.scale;
     const auto ident = [](int, int, float x) { return x; };
     auto vval = [&](int i, int c) -> float {
-        return i < L ? bf16_bits_to_f32(a.v[((t0 + i) * H + h) * kV + c]) : 0.f;
+        return i < L ? bf16_bits_to_f32(vin[((t0 + i) * H + h) * kV + c]) : 0.f;
     };
-    // this lane's row 16 w + r of dO (the A operand of P4 and P6), zero past the end
-    const bool arow_ok = 16 * w + r < L;
-    const uint16_t *arow = a.dout + ((t0 + (arow_ok ? 16 * w + r : 0)) * H + h) * kV;
-    auto dov_a = [&](int c) -> float { return arow_ok ? bf16_bits_to_f32(arow[c]) : 0.f; };
+    // dO (the A operand of P4 and P6) from LDS, where it replaces T after P3
+    auto dov_a = [&](int c) -> float { return bf16_bits_to_f32(sm.t.D[16 * w + r][c]); };
     const int64_t HK = H * kK;
     const int64_t obase = (t0 * H + h) * kK;
     auto out_at = [&](int i, int d) -> int64_t { return obase + i * HK + d; };
 
     // wave (w, hf) owns rows 16 w .. 16 w + 15 and column tiles ct = 4 hf + c
     // (c = 0..3) of every 64 x 128 result; lane (r, gq) holds rows 16 w + 4 gq + e
-    // of column 16 ct + r.  dG stays in registers; the gradients of qhat and
-    // khat are summed in place in dq and dk (the owning lane only), which the
-    // last phase turns into the gradients of q and k.
+    // of column 16 ct + r.  The gradients of qhat, khat and G accumulate in
+    // registers, each element in its owning lane.
     const int row0 = 16 * w + 4 * gq;  // + e
-    f4 dG[4];
+    f4 dG[4], dqh[4], dkh[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dG[c] = f4{0, 0, 0, 0};
+    for (int c = 0; c < 4; ++c) { dG[c] = f4{0, 0, 0, 0}; dqh[c] = dG[c]; dkh[c] = dG[c]; }
 
     // P0: T, b, gamma Khat and S into LDS
     for (int idx = tid; idx < kChunk * kChunk; idx += kMainThreads)
-        sm.T[idx >> 6][idx & 63] = a.Tm[ws * (kChunk * kChunk) + idx];
+        sm.t.T[idx >> 6][idx & 63] = Tm[idx];
     if (tid < kChunk) {
-        sm.b[tid] = a.bb[ws * kChunk + tid];
+        sm.b[tid] = bbv[tid];
         sm.db[0][tid] = 0.f;
         sm.db[1][tid] = 0.f;
     }
@@ -630,7 +667,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
 #pragma unroll 4
         for (int ks = 0; ks < 4 * (w + 1); ++ks) {
-            const float av = sm.T[16 * w + r][4 * ks + gq];
+            const float av = sm.t.T[16 * w + r][4 * ks + gq];
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[c] = mma(av, sm.Z[4 * ks + gq][16 * (4 * hf + c) + r], acc[c]);
         }
@@ -649,7 +686,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
 #pragma unroll 4
         for (int ks = 4 * w; ks < 16; ++ks) {
-            const float av = sm.T[4 * ks + gq][16 * w + r];
+            const float av = sm.t.T[4 * ks + gq][16 * w + r];
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[c] = mma(av, sm.Z[4 * ks + gq][16 * (4 * hf + c) + r], acc[c]);
         }
@@ -663,7 +700,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                 const float z = acc[c][e];
                 sm.Z[ii][d] = z;
                 if (ii < L) {
-                    a.dv[((t0 + ii) * H + h) * kV + d] = sm.b[ii] * z;
+                    dvo[((t0 + ii) * H + h) * kV + d] = sm.b[ii] * z;
                     dbp[e] += z * vval(ii, d);
                 }
             }
@@ -674,8 +711,17 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         }
     }
     __syncthreads();
+    // dO into the T area (rows past the end zero); 16 bytes per thread and pass
+    for (int idx = tid; idx < kChunk * 16; idx += kMainThreads) {
+        const int i = idx >> 4, c8 = (idx & 15) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (i < L) v = *reinterpret_cast<const uint4 *>(a.dout + ((t0 + i) * H + h) * kV + c8);
+        *reinterpret_cast<uint4 *>(&sm.t.D[i][c8]) = v;
+    }
+    __syncthreads();
     // P4: dQg = scale dO S^T and Zw = -Z S^T
     {
+        const float *__restrict__ qn = opaque(qn_all), *__restrict__ kn = opaque(kn_all), *__restrict__ G = opaque(G_all);
         f4 aq[4], az[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) { aq[c] = f4{0, 0, 0, 0}; az[c] = aq[c]; }
@@ -700,10 +746,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                 const float gam = __expf(G[ii * kK + d]);
                 const float bi = sm.b[ii];
                 const float dQg = scale * aq[c][e], Zw = -az[c][e];
-                if (ii < L) {
-                    a.dq[out_at(ii, d)] = gam * dQg;
-                    a.dk[out_at(ii, d)] = bi * gam * Zw;
-                }
+                dqh[c][e] = gam * dQg;
+                dkh[c][e] = bi * gam * Zw;
                 dG[c][e] += gam * qh * dQg + bi * gam * kh * Zw;
                 dbp[e] += Zw * gam * kh;
             }
@@ -736,6 +780,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     __syncthreads();
     // P5: dKbar = Ut dS'^T
     {
+        const float *__restrict__ qn = opaque(qn_all), *__restrict__ kn = opaque(kn_all), *__restrict__ G = opaque(G_all);
         f4 acc[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
@@ -755,10 +800,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                 const int ii = row0 + e;
                 const float eK = __expf(Gn - G[ii * kK + d]);
                 const float kb = eK * kn[ii * kK + d];
-                const float dk = acc[c][e];
-                if (ii < L) a.dk[out_at(ii, d)] += eK * dk;
-                dG[c][e] -= kb * dk;
-                colp += kb * dk;
+                const float dkb = acc[c][e];
+                dkh[c][e] += eK * dkb;
+                dG[c][e] -= kb * dkb;
+                colp += kb * dkb;
             }
             colp = sum4g(colp);
             if (gq == 0) sm.red[w][d] = colp;
@@ -797,7 +842,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                 const float dAq = (jt <= w && j <= ii) ? scale * accA[jj][e] : 0.f;
                 const float dAk = (jt <= w && j < ii) ? -accK[jj][e] : 0.f;
                 dbp[e] += dAk * Mk[ii * kChunk + j];
-                sm.T[ii][j] = dAq;
+                sm.SB[ii][64 + j] = dAq;
                 sm.SB[ii][j] = sm.b[ii] * dAk;
             }
 #pragma unroll
@@ -829,7 +874,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll 2
             for (int ks = 0; ks < 4 * (w + 1); ++ks) {
                 const int j = 4 * ks + gq;
-                const float a1 = sm.SB[16 * w + r][j], a2 = sm.T[16 * w + r][j];
+                const float a1 = sm.SB[16 * w + r][j], a2 = sm.SB[16 * w + r][64 + j];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int d = 16 * (4 * hf + c) + r;
@@ -845,10 +890,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                     const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
                     const float s = __expf(Gs[ii][d] - refc[c]);
                     const float RxM = rm[c][e] * s, RxA = ra[c][e] * s;
-                    if (ii < L) {
-                        a.dk[out_at(ii, d)] += RxM;
-                        a.dq[out_at(ii, d)] += RxA;
-                    }
+                    dkh[c][e] += RxM;
+                    dqh[c][e] += RxA;
                     dG[c][e] += kh[ii][d] * RxM + qh[ii][d] * RxA;
                 }
         }
@@ -861,7 +904,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll 2
             for (int ks = 4 * w; ks < 16; ++ks) {
                 const int i = 4 * ks + gq;
-                const float a1 = sm.SB[i][16 * w + r], a2 = sm.T[i][16 * w + r];
+                const float a1 = sm.SB[i][16 * w + r], a2 = sm.SB[i][64 + 16 * w + r];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int d = 16 * (4 * hf + c) + r;
@@ -876,7 +919,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                 for (int e = 0; e < 4; ++e) {
                     const int jj = row0 + e, d = 16 * (4 * hf + c) + r;
                     const float Ry = ry[c][e] * __expf(refc[c] - Gs[jj][d]);
-                    if (jj < L) a.dk[out_at(jj, d)] += Ry;
+                    dkh[c][e] += Ry;
                     dG[c][e] -= kh[jj][d] * Ry;
                 }
         }
@@ -890,17 +933,29 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
             const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
             float v = dG[c][e];
             if (ii == L - 1) v += sm.gns[d] + sm.red[0][d] + sm.red[1][d] + sm.red[2][d] + sm.red[3][d];
-            sm.U[ii][d] = ii < L ? v : 0.f;
+            sm.Z[ii][d] = ii < L ? v : 0.f;
         }
     __syncthreads();
-    if (tid < kK) {
+    {  // four threads per column, 16 rows each: sums within the segment, then the later segments' totals
+        const int d = tid & (kK - 1), sg = tid >> 7;
         float run = 0.f;
-        for (int i = kChunk - 1; i >= 0; --i) {
-            run += sm.U[i][tid];
-            sm.U[i][tid] = run;
+#pragma unroll
+        for (int i = 16 * sg + 15; i >= 16 * sg; --i) {
+            run += sm.Z[i][d];
+            sm.Z[i][d] = run;
         }
+        sm.tot[sg][d] = run;
+        __syncthreads();
+        float carry = 0.f;
+        for (int s2 = sg + 1; s2 < 4; ++s2) carry += sm.tot[s2][d];
+#pragma unroll
+        for (int i = 16 * sg; i < 16 * sg + 16; ++i) sm.Z[i][d] += carry;
     }
-    // P9: norms, gate, outputs.  Row sums of qhat . dqhat and khat . dkhat first.
+    // P9: norms, gate, outputs.  Row sums of qhat . dqhat and khat . dkhat first
+    // (khat and qhat are still in LDS from P7).
+    {
+    const float(*kh)[kRP] = sm.U;
+    const float(*qh)[kRP] = &sm.SB[kChunk];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int ii = row0 + e;
@@ -909,8 +964,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int d = 16 * (4 * hf + c) + r;
-                a1 += qn[ii * kK + d] * a.dq[out_at(ii, d)];
-                a2 += kn[ii * kK + d] * a.dk[out_at(ii, d)];
+                a1 += qh[ii][d] * dqh[c][e];
+                a2 += kh[ii][d] * dkh[c][e];
             }
         }
         a1 = sum16(a1);
@@ -927,7 +982,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int d = 16 * (4 * hf + c) + r;
-            const float dtb = a.dt_bias[h * kK + d];
+            const float dtb = dtb_h[d];
             float colp = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -936,18 +991,18 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                     const int64_t o = out_at(ii, d);
                     const float sq = sm.rs[0][0][ii] + sm.rs[0][1][ii];
                     const float sk = sm.rs[1][0][ii] + sm.rs[1][1][ii];
-                    const float rq = a.rq[ws * kChunk + ii], rk = a.rk[ws * kChunk + ii];
-                    a.dq[o] = rq * (a.dq[o] - sq * qn[ii * kK + d]);
-                    a.dk[o] = rk * (a.dk[o] - sk * kn[ii * kK + d]);
-                    const float xg = bf16_bits_to_f32(a.g[o]) + dtb;
-                    const float z = nA * softplus_acc(xg);
-                    const float da = sm.U[ii][d];
+                    const float rq = rqv[ii], rk = rkv[ii];
+                    dqo[o] = rq * (dqh[c][e] - sq * qh[ii][d]);
+                    dko[o] = rk * (dkh[c][e] - sk * kh[ii][d]);
+                    const float xg = bf16_bits_to_f32(gin[o]) + dtb;
+                    const float z = nA * softplus_fast(xg);
+                    const float da = sm.Z[ii][d];
                     float dx = 0.f;
                     if (z > a.lower_bound) {
-                        dx = da * nA * sigmoid_acc(xg);
+                        dx = da * nA * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-xg * 1.4426950408889634f));
                         pa += da * z;
                     }
-                    a.dg[o] = dx;
+                    dgo[o] = dx;
                     colp += dx;
                 }
             }
@@ -957,8 +1012,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         pa = sum4g(sum16(pa));
         if (lane == 0) sm.pa[wv] = pa;
     }
+    }
     __syncthreads();
-    float *part = a.part + ws * (kK + 1);
     if (tid < kK) part[tid] = sm.red[0][tid] + sm.red[1][tid] + sm.red[2][tid] + sm.red[3][tid];
     if (tid == kK) {
         float s = 0.f;
@@ -967,7 +1022,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     }
     if (tid < L) {
         const float b = sm.b[tid];
-        a.dbeta[(t0 + tid) * H + h] = (sm.db[0][tid] + sm.db[1][tid]) * b * (1.f - b);
+        dbo[(t0 + tid) * H + h] = (sm.db[0][tid] + sm.db[1][tid]) * b * (1.f - b);
     }
 }
 
