@@ -115,7 +115,7 @@ def cpu_baseline(w, target_s: float = 10.0):
 # build flags; for split chains also kda_api.hip, which chooses the segments.
 _COMMON_SOURCES = ["kda_common.h", "../../include/kda.h", "../_build.py"]
 KERNEL_SOURCES = {
-    "kda_intra_kernel": ["kda_intra.hip"],
+    "kda_intra_kernel": ["kda_intra.hip", "kda_intra_body.h"],
     "kda_chain_kernel": ["kda_chain.hip"],
     "kda_chain_x2_kernel": ["kda_chain.hip"],
     "kda_chunk_table_kernel": ["kda_chain.hip"],
@@ -124,6 +124,11 @@ KERNEL_SOURCES = {
     "kda_decode_stream_kernel": ["kda_decode.hip"],
     "kda_decode_split2_kernel": ["kda_decode.hip"],
     "kda_decode_split4_kernel": ["kda_decode.hip"],
+    "kda_chain_save_kernel": ["kda_chain.hip"],
+    "kda_bwd_prep_kernel": ["kda_bwd.hip"],
+    "kda_bwd_chain_kernel": ["kda_bwd.hip"],
+    "kda_bwd_main_kernel": ["kda_bwd.hip"],
+    "kda_bwd_params_kernel": ["kda_bwd.hip"],
 }
 # The library's choice of decode kernel, mirrored to name it: states of this
 # many bytes or more are streamed past the Infinity Cache; otherwise each head
@@ -220,7 +225,8 @@ def write_traffic(pmc_dir: str, workload_name: str) -> dict:
                 key = None
                 for kn in ("kda_intra_kernel", "kda_chain_kernel", "kda_chain_x2_kernel", "kda_chunk_table_kernel",
                            "kda_decode_kernel", "kda_decode_stream_kernel", "kda_decode_split2_kernel",
-                           "kda_decode_split4_kernel", "copyBuffer"):
+                           "kda_decode_split4_kernel", "kda_chain_save_kernel", "kda_bwd_prep_kernel",
+                           "kda_bwd_chain_kernel", "kda_bwd_main_kernel", "kda_bwd_params_kernel", "copyBuffer"):
                     if kn in name:
                         key = kn
                 if key is None:
@@ -330,7 +336,8 @@ def bench_bwd(kda, args, dev, wname) -> int:
     flops = {"kda_bwd_prep_kernel": F_BWD_PREP, "kda_bwd_chain_kernel": F_BWD_CHAIN,
              "kda_bwd_main_kernel": F_BWD_MAIN}
     per_kernel = {n: {"alg_tflops": round(f * tok_heads / (kernel_ms[n] / 1e3) / 1e12, 2),
-                      "frac_fp32_mfma": round(f * tok_heads / (kernel_ms[n] / 1e3) / 1e12 / MFMA_FP32_PEAK_TFLOPS, 4)}
+                      "frac_fp32_mfma": round(f * tok_heads / (kernel_ms[n] / 1e3) / 1e12 / MFMA_FP32_PEAK_TFLOPS, 4),
+                      "traffic": load_traffic("bwd_" + wname, n)}
                   for n, f in flops.items()}
     dom = max(flops, key=lambda n: kernel_ms[n])
     achieved = flops[dom] * tok_heads / (kernel_ms[dom] / 1e3) / 1e12
@@ -347,7 +354,8 @@ def bench_bwd(kda, args, dev, wname) -> int:
         "gbs_alg": round(alg_bytes / (ms / 1e3) / 1e9, 1),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
-                     "alg_flops": flops[dom] * tok_heads, "traffic": None, "kernels": per_kernel},
+                     "alg_flops": flops[dom] * tok_heads, "traffic": load_traffic("bwd_" + wname, dom),
+                     "kernels": per_kernel},
         "mfma_operands": "fp32 (16x16x4) for every gradient product; the recomputed forward as kda_fwd",
     }
     print(json.dumps(result), flush=True)
@@ -445,7 +453,7 @@ def main(argv=None) -> int:
     if args.decode:
         wname = decode_name(args.decode, decode_H)
     if args.traffic_from:
-        print(json.dumps(write_traffic(args.traffic_from, wname)))
+        print(json.dumps(write_traffic(args.traffic_from, "bwd_" + wname if args.bwd else wname)))
         return 0
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
