@@ -253,11 +253,11 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
                         const kda_desc_t *desc, hipStream_t stream);
 
 /* Bytes of workspace kda_bwd needs for these shapes (0 if the shapes are
- * invalid or chain_segments >= 2).  Pure host arithmetic.  About 370 KiB per
+ * invalid or chain_segments >= 2).  Pure host arithmetic.  About 425 KiB per
  * 64-token chunk and head (the forward's 72.5 KiB of intermediates, the fp32
- * state entering every chunk and its gradient, 64 KiB each, and 168 KiB of
- * fp32 per-chunk quantities), plus B * T * H * V * 2 bytes for the recomputed
- * forward output. */
+ * state entering every chunk and its gradient, 64 KiB each, 161 KiB of fp32
+ * per-chunk quantities and 62.5 KiB of fp16 operands for the reverse chain),
+ * plus B * T * H * V * 2 bytes for the recomputed forward output. */
 size_t kda_bwd_workspace_size(const kda_desc_t *desc);
 
 /* Enqueue the gradient of kda_fwd on `stream` and return without
