@@ -49,7 +49,9 @@ __device__ __forceinline__ f4 mma(float a, float b, const f4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float softplus_acc(float x) { return x > 15.0f ? x : log1pf(expf(x)); }
+__device__ __forceinline__ float sigmoid_fast(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
 // softplus on the hardware exp / log, in the three ranges of the forward's gate
 // (series below e^x = 2^-6, x itself above 15, log(1 + e^x) between)
 __device__ __forceinline__ float softplus_fast(float x) {
@@ -59,7 +61,6 @@ __device__ __forceinline__ float softplus_fast(float x) {
     sp = t < 0.015625f ? series : sp;
     return x > 15.0f ? x : sp;
 }
-__device__ __forceinline__ float sigmoid_acc(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 // Sum over the 16 lanes of a row group (lanes r = 0..15 with the same g).
 __device__ __forceinline__ float sum16(float x) {
@@ -117,13 +118,15 @@ constexpr int kCoGn = kCoQ + kK * kTkP * 2;        // 63488
 constexpr int kCoBytes = kCoGn + kK * 4;           // 64000
 static_assert(kCoGn % 1024 == 0 && kCoBytes == kBwdChainOperandBytes, "chain operand block layout");
 
+constexpr int kPP = kK + 1;  // row pitch (an odd pitch measured best over the kernel's access patterns)
 struct PrepSmem {
-    float q[kChunk][kK + 1];
-    float k[kChunk][kK + 1];
-    float G[kChunk][kK + 1];
-    float M[kChunk][kChunk + 1];   // M, then T
+    float q[kChunk][kPP];
+    float k[kChunk][kPP];
+    float G[kChunk][kPP];
+    float M[kChunk][kChunk + 1];   // M
+    float T[kChunk][kChunk + 1];   // T = (I + Diag(b) M)^-1
+    float P[4][16][17];            // one 16 x 16 block product per wave
     float b[kChunk];
-    float xr[4][16];  // one row of T per wave, broadcast during the solve
 };
 
 __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
@@ -167,11 +170,11 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
         for (int e = 0; e < 32; ++e) {
             sm.q[row][32 * qt + e] = qv[e] * rq;
             sm.k[row][32 * qt + e] = kv[e] * rk;
-            const float z = nA * softplus_acc(gv[e] + dtb[e]);
+            const float z = nA * softplus_fast(gv[e] + dtb[e]);
             sm.G[row][32 * qt + e] = valid ? fmaxf(a.lower_bound, z) : 0.f;
         }
         if (qt == 0) {
-            const float b = valid ? sigmoid_acc(bf16_bits_to_f32(a.beta[(t0 + row) * H + h])) : 0.f;
+            const float b = valid ? sigmoid_fast(bf16_bits_to_f32(a.beta[(t0 + row) * H + h])) : 0.f;
             sm.b[row] = b;
             a.rq[ws * kChunk + row] = rq;
             a.rk[ws * kChunk + row] = rk;
@@ -212,70 +215,107 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
     }
 
     const int w = tid >> 6, lane = tid & 63, r = lane & 15, gq = lane >> 4;
-    // M[i][j] = sum_d khat_i khat_j exp(G_i - G_j) (j < i) and A_qk (qhat_i, j <= i); wave w
-    // takes row block w, with exp(G_i - G_j) = exp(G_i - ref) exp(ref - G_j), ref = G[16 w + 8]
+    // M[i][j] = sum_d khat_i khat_j exp(G_i - G_j) (j < i) and A_qk (qhat_i, j <= i), by 16 x 16
+    // tiles (I, J), J <= I: pair p of the ten goes to wave p % 4, so that the waves get 3, 3, 2
+    // and 2 tiles.  exp(G_i - G_j) = exp(G_i - ref) exp(ref - G_j), ref = G[16 I + 8].
     {
-        f4 accM[4], accA[4];
-#pragma unroll
-        for (int J = 0; J < 4; ++J) { accM[J] = f4{0, 0, 0, 0}; accA[J] = accM[J]; }
-        for (int ks = 0; ks < 32; ++ks) {
-            const int d = 4 * ks + gq;
-            const float ref = sm.G[16 * w + 8][d];
-            const float fa = __expf(sm.G[16 * w + r][d] - ref);
-            const float ak = sm.k[16 * w + r][d] * fa, aq = sm.q[16 * w + r][d] * fa;
-#pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                if (J <= w) {
-                    const float bv = sm.k[16 * J + r][d] * __expf(ref - sm.G[16 * J + r][d]);
-                    accM[J] = mma(ak, bv, accM[J]);
-                    accA[J] = mma(aq, bv, accA[J]);
-                }
-            }
-        }
         float *Mk = a.Mk + ws * (kChunk * kChunk);
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
+        for (int p = w; p < 10; p += 4) {
+            const int I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+            const int J = p - I * (I + 1) / 2;
+            f4 accM = f4{0, 0, 0, 0}, accA = accM;
+#pragma unroll 8
+            for (int ks = 0; ks < 32; ++ks) {
+                const int d = 4 * ks + gq;
+                const float ref = sm.G[16 * I + 8][d];
+                const float fa = __expf(sm.G[16 * I + r][d] - ref);
+                const float bv = sm.k[16 * J + r][d] * __expf(ref - sm.G[16 * J + r][d]);
+                accM = mma(sm.k[16 * I + r][d] * fa, bv, accM);
+                accA = mma(sm.q[16 * I + r][d] * fa, bv, accA);
+            }
             h4 at;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w + 4 * gq + e, j = 16 * J + r;
-                const float m = (J <= w && j < i) ? accM[J][e] : 0.f;
+                const int i = 16 * I + 4 * gq + e, j = 16 * J + r;
+                const float m = j < i ? accM[e] : 0.f;
                 sm.M[i][j] = m;
                 Mk[i * kChunk + j] = m;
-                at[e] = (_Float16)((J <= w && j <= i) ? accA[J][e] : 0.f);
+                at[e] = (_Float16)(j <= i ? accA[e] : 0.f);
             }
-            // A_qk^T[16 J + r][16 w + 4 gq .. + 3]
-            *reinterpret_cast<h4 *>(AqT + (16 * J + r) * kTkP + 16 * w + 4 * gq) = at;
+            // A_qk^T[16 J + r][16 I + 4 gq .. + 3]
+            *reinterpret_cast<h4 *>(AqT + (16 * J + r) * kTkP + 16 * I + 4 * gq) = at;
+        }
+        // the tiles above the diagonal blocks are zero
+        for (int idx = tid; idx < kChunk * kChunk; idx += kThreads) {
+            const int i = idx >> 6, j = idx & 63;
+            if ((j >> 4) > (i >> 4)) {
+                sm.M[i][j] = 0.f;
+                Mk[idx] = 0.f;
+                AqT[j * kTkP + i] = (_Float16)0.f;
+            }
         }
     }
     __syncthreads();
-    // T = (I + Diag(b) M)^-1 by forward substitution, rows in lanes, wave w
-    // taking columns 16 w .. 16 w + 15: row c is final once rows < c are applied
-    float x[16];
-    {
-        const int j0 = 16 * w;
+    // T = (I + A)^-1, A = Diag(b) M strictly lower, by 16 x 16 blocks.  First each
+    // wave inverts its diagonal block by forward substitution down the columns,
+    // one column per lane and the block's strict lower triangle in registers, so
+    // only one multiply-add per column is on the serial path.
+    if (gq == 0) {
+        const int j = r;
+        const int i0 = 16 * w;
+        float Lt[120];  // A[i0 + rr][i0 + cc], cc < rr, row rr at offset rr (rr - 1) / 2
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) x[jj] = lane == j0 + jj ? 1.f : 0.f;
-        const float br = sm.b[lane];
-        for (int c = 0; c < kChunk - 1; ++c) {
-            if (lane == c) {
+        for (int rr = 1; rr < 16; ++rr)
 #pragma unroll
-                for (int jj = 0; jj < 16; ++jj) sm.xr[w][jj] = x[jj];
+            for (int cc = 0; cc < rr; ++cc) Lt[rr * (rr - 1) / 2 + cc] = sm.b[i0 + rr] * sm.M[i0 + rr][i0 + cc];
+        float xv[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) xv[rr] = rr == j ? 1.f : 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 15; ++cc)
+#pragma unroll
+            for (int rr = cc + 1; rr < 16; ++rr) xv[rr] -= Lt[rr * (rr - 1) / 2 + cc] * xv[cc];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sm.T[i0 + rr][i0 + j] = xv[rr];
+    }
+    // zeros above the diagonal blocks
+    for (int idx = tid; idx < kChunk * kChunk; idx += kThreads) {
+        const int i = idx >> 6, j = idx & 63;
+        if ((j >> 4) > (i >> 4)) sm.T[i][j] = 0.f;
+    }
+    __syncthreads();
+    // Then column block J = w (w < 3), down its block rows:
+    //   T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,   I = J + 1 .. 3
+    if (w < 3) {
+        const int J = w;
+        for (int I = J + 1; I < 4; ++I) {
+            f4 pr = f4{0, 0, 0, 0};
+            for (int K = J; K < I; ++K) {
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int kk = 16 * K + 4 * s4 + gq;
+                    const float av = sm.b[16 * I + r] * sm.M[16 * I + r][kk];
+                    pr = mma(av, sm.T[kk][16 * J + r], pr);
+                }
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // one wave: LDS accesses in order
-            const float arc = lane > c ? br * sm.M[lane][c] : 0.f;
+            // lane (r, gq) holds P[4 gq + e][r]; through LDS for the B operand of T_II P
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) x[jj] -= arc * sm.xr[w][jj];
+            for (int e = 0; e < 4; ++e) sm.P[w][4 * gq + e][r] = pr[e];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // one wave: LDS accesses in order
+            f4 t = f4{0, 0, 0, 0};
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                t = mma(sm.T[16 * I + r][16 * I + 4 * s4 + gq], sm.P[w][4 * s4 + gq][r], t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.T[16 * I + 4 * gq + e][16 * J + r] = -t[e];
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
-        float *Tm = a.Tm + ws * (kChunk * kChunk) + lane * kChunk + j0;
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) Tm[jj] = x[jj];
     }
-    __syncthreads();  // every wave is done with M
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) sm.M[lane][16 * w + jj] = x[jj];
     __syncthreads();
+    {
+        float *Tm = a.Tm + ws * (kChunk * kChunk);
+        for (int idx = tid; idx < kChunk * kChunk; idx += kThreads) Tm[idx] = sm.T[idx >> 6][idx & 63];
+    }
     // W = T Diag(b) (gamma * Khat), stored as -W^T; T[i][j] = 0 for j > i
     {
         f4 acc[8];
@@ -283,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
         for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
         for (int ks = 0; ks < 4 * (w + 1); ++ks) {
             const int j = 4 * ks + gq;
-            const float av = sm.M[16 * w + r][j];
+            const float av = sm.T[16 * w + r][j];
             const float bj = sm.b[j];
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) {
@@ -999,7 +1039,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                     const float da = sm.Z[ii][d];
                     float dx = 0.f;
                     if (z > a.lower_bound) {
-                        dx = da * nA * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-xg * 1.4426950408889634f));
+                        dx = da * nA * sigmoid_fast(xg);
                         pa += da * z;
                     }
                     dgo[o] = dx;
