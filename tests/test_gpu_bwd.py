@@ -12,6 +12,7 @@ whether g receives a gradient, the fp64 oracle and the fp32 kernel may decide
 differently for inputs within rounding of the kink: entries of dg whose
 unclamped log-decay lies within 1e-4 of lower_bound are left out of the dg
 comparison."""
+import dataclasses
 import math
 
 import numpy as np
@@ -47,8 +48,9 @@ def _oracle(w, d_out, d_fin):
 
 def _near_kink(w):
     x = w.g.double().numpy() + w.dt_bias.double().numpy()[None, None]
-    z = -np.exp(w.A_log.double().numpy())[None, None, :, None] * np.logaddexp(0.0, x)
-    return np.abs(z - w.lower_bound) < 1e-4
+    with np.errstate(invalid="ignore"):
+        z = -np.exp(w.A_log.double().numpy())[None, None, :, None] * np.logaddexp(0.0, x)
+        return np.abs(z - w.lower_bound) < 1e-4
 
 
 def _compare(got, ref, w, label):
@@ -139,3 +141,39 @@ def test_bwd_full_size_heads():
         else:
             sub[name] = x[heads]
     _compare(sub, ref, ws, "full")
+
+
+def _with_extremes(w, seed):
+    """The same workload with the activations' extreme inputs planted (the forward's edge
+    cases, here for the gradient): beta = +inf (b = 1) and -inf (b = 0) tokens, gate inputs
+    g = +inf (clamped), -inf (no decay) and far beyond fp32 exp overflow, and all-zero q and
+    k rows inside chunks.  Where the gate is clamped, or b is 0 or 1, no gradient reaches
+    g or beta; a zero row's norm is the epsilon's."""
+    rng = np.random.default_rng(seed)
+    q, k, g, be = w.q.clone(), w.k.clone(), w.g.clone(), w.beta.clone()
+    B, T, H, K = q.shape
+    inf = float("inf")
+    for tokens, val in ((rng.choice(T, 6, replace=False), inf), (rng.choice(T, 6, replace=False), -inf)):
+        be[:, tokens] = val
+    gi = rng.choice(T, 5, replace=False)
+    g[:, gi, :, :16] = inf
+    g[:, gi, :, 16:32] = -inf
+    g[:, gi, :, 32:48] = 100.0
+    zq, zk = rng.choice(T, 3, replace=False), rng.choice(T, 3, replace=False)
+    q[:, zq] = 0
+    k[:, zk] = 0
+    return dataclasses.replace(w, q=q, k=k, g=g, beta=be,
+                               A_log=torch.full_like(w.A_log, -8.0))  # so that g = 100 stays above lb
+
+
+@pytest.mark.parametrize("lb", [-5.0, -0.5])
+def test_bwd_activation_extremes(lb):
+    w = _with_extremes(W.make("bwd_extremes", 2, 200, 2, 7009, lower_bound=lb, init="fp32", final="fp32"), 7209)
+    d_out, d_fin = W.loss_grads(w, 7109, final="fp32")
+    say("bwd extremes lb=%g" % lb)
+    got = _gpu(w, d_out, d_fin)
+    ref = _oracle(w, d_out, d_fin)
+    _compare(got, ref, w, "extremes lb=%g" % lb)
+    # b = 0 or 1: no gradient reaches beta
+    be = w.beta.float().numpy()
+    assert not got["dbeta"][np.isinf(be)].any()
