@@ -289,14 +289,16 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         d_out: torch.Tensor, d_final_state: Optional[torch.Tensor] = None,
         initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None, launch_piece: int = 0, chain_segments: int = 0,
-        with_d_initial: bool = True, phase_events=None) -> dict:
+        with_d_initial: bool = True, phase_events=None, outputs: Optional[dict] = None) -> dict:
     """Gradient of ``fwd`` (``kda_bwd``) on the current HIP stream: for the loss
     gradients ``d_out`` (bf16 [B,T,H,128]) and ``d_final_state`` (bf16 or fp32
     [N,H,128,128], or None for zeros) returns a dict of fp32 tensors dq, dk, dg
     ([B,T,H,128]), dv ([B,T,H,128]), dbeta ([B,T,H]), dA_log ([H]), ddt_bias
     ([H,128]) and d_initial_state ([N,H,128,128], or None without
     ``with_d_initial``).  Inputs as for ``fwd``; phase_events: None or the
-    address of a caller-owned array of 6 hipEvent_t (instrumentation)."""
+    address of a caller-owned array of 6 hipEvent_t (instrumentation);
+    outputs: None, or a dict of caller-allocated fp32 tensors of those names and
+    shapes that the call writes into (what graph capture needs)."""
     lib = library()
     d, dev, d_out = _check_fwd_args(q, k, v, g, beta, d_out, A_log, dt_bias, initial_state, d_final_state,
                                     cu_seqlens, chain_segments, launch_piece, allocate_out=False)
@@ -304,11 +306,22 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     N = d.num_seqs
     need = int(lib.kda_bwd_workspace_size(ctypes.byref(d)))
     f32 = dict(dtype=torch.float32, device=dev)
-    res = {"dq": torch.empty((B, T, H, K), **f32), "dk": torch.empty((B, T, H, K), **f32),
-           "dv": torch.empty((B, T, H, K), **f32), "dg": torch.empty((B, T, H, K), **f32),
-           "dbeta": torch.empty((B, T, H), **f32), "dA_log": torch.empty((H,), **f32),
-           "ddt_bias": torch.empty((H, K), **f32),
-           "d_initial_state": torch.empty((N, H, K, K), **f32) if with_d_initial else None}
+    shapes = {"dq": (B, T, H, K), "dk": (B, T, H, K), "dv": (B, T, H, K), "dg": (B, T, H, K), "dbeta": (B, T, H),
+              "dA_log": (H,), "ddt_bias": (H, K), "d_initial_state": (N, H, K, K)}
+    if outputs is None:
+        res = {n: torch.empty(sh, **f32) for n, sh in shapes.items()}
+        if not with_d_initial:
+            res["d_initial_state"] = None
+    else:
+        res = dict(outputs)
+        for n, sh in shapes.items():
+            t = res.get(n)
+            if t is None and n == "d_initial_state":
+                res[n] = None
+                continue
+            if t is None or t.dtype != torch.float32 or tuple(t.shape) != sh or t.device != dev or \
+                    not t.is_contiguous():
+                raise ValueError("outputs[%r] must be a contiguous fp32 %s tensor on %s" % (n, sh, dev))
     with torch.cuda.device(dev):
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

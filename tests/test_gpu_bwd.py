@@ -177,3 +177,63 @@ def test_bwd_activation_extremes(lb):
     # b = 0 or 1: no gradient reaches beta
     be = w.beta.float().numpy()
     assert not got["dbeta"][np.isinf(be)].any()
+
+
+def test_bwd_graph_replays_match_eager():
+    # with a caller-owned workspace and outputs the backward enqueues kernels only, so it can be
+    # captured once and replayed; every replay, with the outputs and workspace clobbered eagerly
+    # in between, must equal the eager call bit for bit
+    w = W.make("bwd_graph", 1, 260, 3, 7010, init="fp32", final="fp32", seqlens=[100, 0, 97, 63])
+    d_out, d_fin = W.loss_grads(w, 7110, final="fp32")
+    wd = w.to("cuda")
+    d_out, d_fin = d_out.cuda(), d_fin.cuda()
+    nbytes = kda.bwd_workspace_size(w.B, w.T, w.H, num_seqs=w.N)
+
+    def buffers():
+        outs = {n: torch.empty(sh, dtype=torch.float32, device="cuda") for n, sh in
+                (("dq", (w.B, w.T, w.H, w.K)), ("dk", (w.B, w.T, w.H, w.K)), ("dv", (w.B, w.T, w.H, w.V)),
+                 ("dg", (w.B, w.T, w.H, w.K)), ("dbeta", (w.B, w.T, w.H)), ("dA_log", (w.H,)),
+                 ("ddt_bias", (w.H, w.K)), ("d_initial_state", (w.N, w.H, w.K, w.V)))}
+        return torch.empty(nbytes, dtype=torch.uint8, device="cuda"), outs
+
+    def call(ws, outs):
+        kda.bwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, wd.A_log, wd.dt_bias, w.lower_bound, d_out,
+                d_final_state=d_fin, initial_state=wd.initial_state, cu_seqlens=wd.cu_seqlens, workspace=ws,
+                outputs=outs)
+
+    ws_e, eager = buffers()
+    call(ws_e, eager)
+    torch.cuda.synchronize()
+    ws, outs = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(ws, outs)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(ws, outs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs.values():
+            t.fill_(float("nan"))
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in outs:
+            assert torch.equal(outs[n], eager[n]), (rep, n)
+
+
+def test_bwd_many_short_sequences():
+    # a packed batch of 40 sequences of 1 to 150 tokens (some empty), bf16 states
+    rng = np.random.default_rng(7011)
+    lens = [int(x) for x in rng.integers(0, 151, 40)]
+    lens[3], lens[17] = 0, 1
+    w = W.make("bwd_short", 1, sum(lens), 2, 7011, init="bf16", final="bf16", seqlens=lens)
+    d_out, d_fin = W.loss_grads(w, 7111, final="bf16")
+    say("bwd short: N=%d T=%d" % (w.N, w.T))
+    got = _gpu(w, d_out, d_fin)
+    ref = _oracle(w, d_out, d_fin)
+    _compare(got, ref, w, "short")
