@@ -355,7 +355,7 @@ def bench_bwd(kda, args, dev, wname) -> int:
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
                      "alg_flops": flops[dom] * tok_heads, "traffic": load_traffic("bwd_" + wname, dom),
-                     "kernels": per_kernel},
+                     "limiter": load_limiter(dom), "kernels": per_kernel},
         "mfma_operands": "fp32 (16x16x4) for every gradient product; the recomputed forward as kda_fwd",
     }
     print(json.dumps(result), flush=True)
