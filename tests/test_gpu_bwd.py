@@ -237,3 +237,14 @@ def test_bwd_many_short_sequences():
     got = _gpu(w, d_out, d_fin)
     ref = _oracle(w, d_out, d_fin)
     _compare(got, ref, w, "short")
+
+
+def test_bwd_long_chain():
+    # 65536 tokens (1024 chunks in each reverse chain), g ~ N(-1, 1) as the 128K workload draws
+    # it: the gradient state is carried through the whole chain without drifting from the oracle
+    w = W.make("bwd_long", 1, 65536, 2, 7012, init="fp32", final="fp32", g_mean=-1.0)
+    d_out, d_fin = W.loss_grads(w, 7112, final="fp32")
+    say("bwd long: T=%d H=%d" % (w.T, w.H))
+    got = _gpu(w, d_out, d_fin)
+    ref = _oracle(w, d_out, d_fin)
+    _compare(got, ref, w, "long")
