@@ -306,7 +306,9 @@ def bench_bwd(kda, args, dev, wname) -> int:
     d_out, d_fin = W.loss_grads(w_host, 8000, final="fp32" if w.final_state_dtype is not None else None)
     d_out = d_out.to(dev)
     d_fin = None if d_fin is None else d_fin.to(dev)
-    nbytes = kda.bwd_workspace_size(w.B, w.T, w.H, num_seqs=w.N)
+    segs_req = args.chain_segments if w.cu_seqlens is None else 0
+    nbytes = kda.bwd_workspace_size(w.B, w.T, w.H, num_seqs=w.N, chain_segments=segs_req)
+    segs = kda.chain_segments_for(w.B, w.T, w.H, segs_req) if w.cu_seqlens is None else 1
     workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
@@ -318,7 +320,7 @@ def bench_bwd(kda, args, dev, wname) -> int:
     def step(events=None):
         return kda.bwd(w.q, w.k, w.v, w.g, w.beta, w.scale, w.A_log, w.dt_bias, w.lower_bound, d_out,
                        d_final_state=d_fin, initial_state=w.initial_state, cu_seqlens=w.cu_seqlens,
-                       workspace=workspace, phase_events=events)
+                       workspace=workspace, phase_events=events, chain_segments=segs_req)
 
     for _ in range(args.warmup):
         step()
@@ -330,6 +332,7 @@ def bench_bwd(kda, args, dev, wname) -> int:
     t1.record(stream)
     torch.cuda.synchronize(dev)
     ms = t0.elapsed_time(t1) / args.steps
+    # with split chains the two chain entries time the three launches of each side
     names = ["fwd_intra", "fwd_chain_save", "kda_bwd_prep_kernel", "kda_bwd_chain_kernel", "kda_bwd_main_kernel"]
     kernel_ms = {n: round(ev[i].elapsed_time(ev[i + 1]), 5) for i, n in enumerate(names)}
     tok_heads = w.B * w.T * w.H
@@ -348,7 +351,8 @@ def bench_bwd(kda, args, dev, wname) -> int:
         "value": round(w.B * w.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 in, fp32 gradients", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V, "num_seqs": w.N},
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V, "num_seqs": w.N,
+                   "chain_segments": segs},
         "kernel_ms": kernel_ms,
         "tflops_alg": round(F_BWD * tok_heads / (ms / 1e3) / 1e12, 2),
         "gbs_alg": round(alg_bytes / (ms / 1e3) / 1e9, 1),

@@ -278,9 +278,9 @@ def noalloc_max_workspace() -> int:
     return int(library().kda_fwd_noalloc_max_workspace())
 
 
-def bwd_workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None) -> int:
+def bwd_workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None, chain_segments: int = 0) -> int:
     """Workspace bytes ``bwd`` needs for these shapes."""
-    d = _desc(B, T, H, B if num_seqs is None else num_seqs)
+    d = _desc(B, T, H, B if num_seqs is None else num_seqs, chain_segments=chain_segments)
     return int(library().kda_bwd_workspace_size(ctypes.byref(d)))
 
 
@@ -295,7 +295,8 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     [N,H,128,128], or None for zeros) returns a dict of fp32 tensors dq, dk, dg
     ([B,T,H,128]), dv ([B,T,H,128]), dbeta ([B,T,H]), dA_log ([H]), ddt_bias
     ([H,128]) and d_initial_state ([N,H,128,128], or None without
-    ``with_d_initial``).  Inputs as for ``fwd``; phase_events: None or the
+    ``with_d_initial``).  Inputs as for ``fwd``, chain_segments included (the
+    reverse chains split as the forward's do); phase_events: None or the
     address of a caller-owned array of 6 hipEvent_t (instrumentation);
     outputs: None, or a dict of caller-allocated fp32 tensors of those names and
     shapes that the call writes into (what graph capture needs)."""

@@ -196,6 +196,79 @@ namespace {
 
 void *scratch_on_device(int dev);
 
+// The split chains' view of a batch: segment s of batch row b is packed
+// sequence b * segs + s (its token and chunk ranges from the segment table).
+struct SegmentView {
+    int64_t *cu;
+    int32_t *off;
+    float *mapM, *mapN, *sin;
+};
+
+SegmentView segment_view(const WorkspaceLayout &lay, char *ws) {
+    SegmentView v;
+    v.cu = reinterpret_cast<int64_t *>(ws + lay.off_seg_cu);
+    v.off = reinterpret_cast<int32_t *>(ws + lay.off_seg_off);
+    v.mapM = reinterpret_cast<float *>(ws + lay.off_mapM);
+    v.mapN = reinterpret_cast<float *>(ws + lay.off_mapN);
+    v.sin = reinterpret_cast<float *>(ws + lay.off_sin);
+    return v;
+}
+
+// The forward's state chains: one launch, or with split chains the segment
+// table, the map of every segment, the scan over the segments (the entering
+// states and ca.ht) and the chain from every segment's entering state.  With
+// ca.hs set the chain also stores the state entering every chunk.
+hipError_t launch_chains(const ChainArgs &ca, const Geometry &geo, const WorkspaceLayout &lay, char *ws,
+                         hipStream_t stream) {
+    if (geo.segs <= 1) return kda_launch_chain(ca, stream);
+    const SegmentView sv = segment_view(lay, ws);
+    ChainArgs seg = ca;
+    seg.cu = sv.cu; seg.chunk_off = sv.off; seg.seq_order = nullptr;
+    seg.N = geo.B * geo.segs; seg.nc_fixed = 0;
+    hipError_t err = kda_launch_seg_table(geo.B, geo.T, geo.segs, geo.segc, sv.cu, sv.off, stream);
+    ChainArgs maps = seg;  // 1. the map of every segment
+    maps.h0 = nullptr; maps.ht = nullptr; maps.out = nullptr; maps.hs = nullptr;
+    maps.map_mode = 1; maps.mapM = sv.mapM; maps.mapN = sv.mapN;
+    if (err == hipSuccess) err = kda_launch_chain(maps, stream);
+    ScanArgs sa{};     // 2. entering states and the final state
+    sa.mapM = sv.mapM; sa.mapN = sv.mapN; sa.sin = sv.sin;
+    sa.h0 = ca.h0; sa.ht = ca.ht;
+    sa.h0_bf16 = ca.h0_bf16; sa.ht_bf16 = ca.ht_bf16;
+    sa.B = geo.B; sa.H = geo.H; sa.segs = geo.segs;
+    if (err == hipSuccess) err = kda_launch_seg_scan(sa, stream);
+    seg.h0 = sv.sin; seg.h0_bf16 = 0; seg.ht = nullptr;  // 3. outputs
+    if (err == hipSuccess) err = kda_launch_chain(seg, stream);
+    return err;
+}
+
+// The gradient's reverse state chains.  With split chains: the reverse chain of
+// every segment from a zero gradient (the offsets of the segments' reverse maps,
+// into mapN, whose forward contents the forward scan has consumed), the
+// reverse scan with the transposed forward maps (the gradient leaving every
+// segment, into sin, and the gradient of the initial state), and the reverse
+// chain of every segment from the gradient leaving it.
+hipError_t launch_bwd_chains(const BwdArgs &ba, const Geometry &geo, const WorkspaceLayout &lay, char *ws,
+                             hipStream_t stream) {
+    if (geo.segs <= 1) return kda_launch_bwd_chain(ba, stream);
+    const SegmentView sv = segment_view(lay, ws);
+    BwdArgs seg = ba;
+    seg.cu = sv.cu; seg.chunk_off = sv.off; seg.seq_order = nullptr;
+    seg.N = geo.B * geo.segs; seg.nc_fixed = 0;
+    BwdArgs maps = seg;  // 1. offsets
+    maps.chain_map = 1; maps.dht = nullptr; maps.dh0 = sv.mapN;
+    hipError_t err = kda_launch_bwd_chain(maps, stream);
+    ScanArgs sa{};       // 2. the gradient leaving every segment; the initial state's
+    sa.mapM = sv.mapM; sa.mapN = sv.mapN; sa.sin = sv.sin;
+    sa.h0 = ba.dht; sa.h0_bf16 = ba.dht_bf16;
+    sa.ht = ba.dh0; sa.ht_bf16 = 0;
+    sa.reverse = 1;
+    sa.B = geo.B; sa.H = geo.H; sa.segs = geo.segs;
+    if (err == hipSuccess) err = kda_launch_seg_scan(sa, stream);
+    seg.dht = sv.sin; seg.dht_bf16 = 0; seg.dh0 = nullptr;  // 3. per-chunk gradients
+    if (err == hipSuccess) err = kda_launch_bwd_chain(seg, stream);
+    return err;
+}
+
 // The forward pass behind kda_fwd and kda_fwd_noalloc.  With `noalloc` the
 // call runs in the library's static scratch (the descriptor's workspace is
 // ignored) and allocates nothing, on the device or the host; otherwise it runs
@@ -303,32 +376,7 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
     ca.ht_bf16 = desc->final_state_dtype == KDA_BF16;
     ca.out = static_cast<uint16_t *>(out);
     ca.piece_cap = desc->launch_piece;
-    if (geo.segs > 1) {
-        // split chains: every segment is a packed sequence of the chain kernel
-        int64_t *seg_cu = reinterpret_cast<int64_t *>(ws + lay.off_seg_cu);
-        int32_t *seg_off = reinterpret_cast<int32_t *>(ws + lay.off_seg_off);
-        float *mapM = reinterpret_cast<float *>(ws + lay.off_mapM);
-        float *mapN = reinterpret_cast<float *>(ws + lay.off_mapN);
-        float *sin = reinterpret_cast<float *>(ws + lay.off_sin);
-        ChainArgs seg = ca;
-        seg.cu = seg_cu; seg.chunk_off = seg_off; seg.seq_order = nullptr;
-        seg.N = geo.B * geo.segs; seg.nc_fixed = 0;
-        if (err == hipSuccess) err = kda_launch_seg_table(geo.B, geo.T, geo.segs, geo.segc, seg_cu, seg_off, stream);
-        ChainArgs maps = seg;  // 1. the map of every segment
-        maps.h0 = nullptr; maps.ht = nullptr; maps.out = nullptr;
-        maps.map_mode = 1; maps.mapM = mapM; maps.mapN = mapN;
-        if (err == hipSuccess) err = kda_launch_chain(maps, stream);
-        ScanArgs sa{};     // 2. entering states and the final state
-        sa.mapM = mapM; sa.mapN = mapN; sa.sin = sin;
-        sa.h0 = initial_state; sa.ht = final_state;
-        sa.h0_bf16 = ca.h0_bf16; sa.ht_bf16 = ca.ht_bf16;
-        sa.B = geo.B; sa.H = geo.H; sa.segs = geo.segs;
-        if (err == hipSuccess) err = kda_launch_seg_scan(sa, stream);
-        seg.h0 = sin; seg.h0_bf16 = 0; seg.ht = nullptr;  // 3. outputs
-        if (err == hipSuccess) err = kda_launch_chain(seg, stream);
-    } else if (err == hipSuccess) {
-        err = kda_launch_chain(ca, stream);
-    }
+    if (err == hipSuccess) err = launch_chains(ca, geo, lay, ws, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[3], stream);
 
     if (owned) {
@@ -425,12 +473,10 @@ struct BwdLayout {
     size_t total;
 };
 
-// Geometry of a backward call: the forward's, never split nor pipelined.
+// Geometry of a backward call: the forward's (split chains by the same rule),
+// never pipelined.
 kda_status_t make_bwd_geometry(const kda_desc_t *d, bool varlen, Geometry &g) {
-    if (d->chain_segments < 0) return KDA_ERR_PARAM;
-    if (d->chain_segments >= 2) return KDA_ERR_UNSUPPORTED;
     kda_desc_t e = *d;
-    e.chain_segments = 1;
     e.pipeline = 0;
     return make_geometry(&e, varlen, g);
 }
@@ -556,7 +602,7 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
         ca.out = reinterpret_cast<uint16_t *>(ws + lay.off_out);
         ca.hs = ba.hs;
         ca.piece_cap = desc->launch_piece;
-        if (err == hipSuccess) err = kda_launch_chain(ca, stream);
+        if (err == hipSuccess) err = launch_chains(ca, geo, fl, ws, stream);
     }
     if (ev && err == hipSuccess) err = hipEventRecord(ev[2], stream);
     // the gradient
@@ -583,7 +629,12 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
     ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dg = dg; ba.dbeta = dbeta;
     ba.dh0 = d_initial_state; ba.dA_log = dA_log; ba.ddt_bias = ddt_bias;
     ba.piece_cap = desc->launch_piece;
-    if (err == hipSuccess) err = kda_launch_bwd(ba, stream, ev ? ev + 3 : nullptr);
+    if (err == hipSuccess) err = kda_launch_bwd_prep(ba, stream);
+    if (ev && err == hipSuccess) err = hipEventRecord(ev[3], stream);
+    if (err == hipSuccess) err = launch_bwd_chains(ba, geo, fl, ws, stream);
+    if (ev && err == hipSuccess) err = hipEventRecord(ev[4], stream);
+    if (err == hipSuccess) err = kda_launch_bwd_grad(ba, stream);
+    if (ev && err == hipSuccess) err = hipEventRecord(ev[5], stream);
     if (owned) {
         hipError_t e2 = hipFreeAsync(ws, stream);
         if (err == hipSuccess) err = e2;

@@ -9,13 +9,18 @@
 //   1. the forward chain, storing h_c (kda_chain.hip, save mode);
 //   2. kda_bwd_prep_kernel, per chunk: normalised q and k, b, the cumulative
 //      log-decay G, the decayed key Gram M (strictly lower) and
-//      T = (I + Diag(b) M)^-1, in fp32;
+//      T = (I + Diag(b) M)^-1, in fp32, and the reverse chain's operands
+//      (Kbar, A_qk^T, -W^T, Qg^T in fp16, exp(G_n) in fp32) in one block;
 //   3. kda_bwd_chain_kernel, per (sequence, head, 16 state columns), last
 //      chunk first, with dS the gradient of the state leaving the chunk:
 //        dUt = scale A_qk^T dO + Kbar dS
 //        dS <- Diag(exp(G_n)) dS - W^T dUt + scale Qg^T dO
 //      storing dh_c (= dS before the step) and dUt; the final dS is the
-//      initial state's gradient;
+//      initial state's gradient.  The step is affine in dS with the
+//      transpose of the forward step's linear part, so split chains run it per
+//      segment: from a zero gradient (map mode: the offset of the segment's
+//      reverse map), then, after a scan with the forward maps transposed
+//      (kda_segment.hip), from the gradient leaving the segment;
 //   4. kda_bwd_main_kernel, per chunk, independently: with Y = V - (gamma Khat) S,
 //      Ut = T Diag(b) Y and Z = T^T dUt,
 //        dv = Diag(b) Z,   dQg = scale dO S^T,   Zw = -Z S^T,   dKbar = Ut dS'^T,
@@ -25,11 +30,11 @@
 //      and beta;
 //   5. kda_bwd_params_kernel: dA_log and ddt_bias, summed over the chunks.
 //
-// Every product here runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32):
-// lane (r, g) gives A[r][g] and B[g][r] of a 16x16x4 step and holds
-// C[4 g + e][r], so an operand can be read element by element from any layout.
-// The chain reads the forward's fp16 fragments (W, Kbar, Qg, A_qk) as they
-// are; the per-chunk kernels recompute their quantities in fp32.
+// The per-chunk kernels run their products on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32): lane (r, g) gives A[r][g] and B[g][r] of a 16x16x4
+// step and holds C[4 g + e][r], so an operand can be read element by element
+// from any layout.  The reverse chain, whose steps are serial, runs the fp16
+// 16x16x16 product with fp32 accumulation on its fp16 operand block.
 //
 // Decay factors exp(G_i - G_j) inside a chunk are split around a reference
 // row of each 16-row block (row 16 w + 8): with the log-decay >= -5 both
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
             const _Float16 *QgT = reinterpret_cast<const _Float16 *>(&sm.ops[slot][kCoQ]);
             const float *gn = reinterpret_cast<const float *>(&sm.ops[slot][kCoGn]);
             // the gradient of the state leaving this chunk
-            {
+            if (!a.chain_map) {
                 float *dh = a.dhs + ws * (int64_t)(kK * kV) + col0 + r;
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
@@ -529,9 +534,11 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
             // row tile w of dUt: lane holds dUt[16 w + 4 g + e][col0 + r]
             {
                 const f4 u = sm.red[0][w][lane] + sm.red[1][w][lane] + sm.red[2][w][lane] + sm.red[3][w][lane];
-                float *du = a.dUt + ws * (int64_t)(kChunk * kV) + col0 + r;
+                if (!a.chain_map) {
+                    float *du = a.dUt + ws * (int64_t)(kChunk * kV) + col0 + r;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) du[(16 * w + 4 * g + e) * kV] = u[e];
+                    for (int e = 0; e < 4; ++e) du[(16 * w + 4 * g + e) * kV] = u[e];
+                }
                 *reinterpret_cast<h4 *>(&sm.dUT[r][16 * w + 4 * g]) = pack_h4(u);
             }
             lds_barrier();
@@ -1081,7 +1088,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_params_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t kda_launch_bwd(const BwdArgs &a0, hipStream_t s, hipEvent_t *ev) {
+hipError_t kda_launch_bwd_prep(const BwdArgs &a0, hipStream_t s) {
     BwdArgs a = a0;
     const int64_t units = a.slots * a.H;
     const int64_t piece = launch_piece(kMaxUnitsPerLaunch, a.piece_cap);
@@ -1092,7 +1099,11 @@ hipError_t kda_launch_bwd(const BwdArgs &a0, hipStream_t s, hipEvent_t *ev) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return hipErrorUnknown;
+    return hipSuccess;
+}
+
+hipError_t kda_launch_bwd_chain(const BwdArgs &a0, hipStream_t s) {
+    BwdArgs a = a0;
     const int64_t NH = a.N * a.H;
     const int64_t groups = (NH + 7) / 8;
     const int64_t gpiece = launch_piece(kMaxGroupsPerLaunch, a.piece_cap);
@@ -1103,7 +1114,13 @@ hipError_t kda_launch_bwd(const BwdArgs &a0, hipStream_t s, hipEvent_t *ev) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (ev && hipEventRecord(ev[1], s) != hipSuccess) return hipErrorUnknown;
+    return hipSuccess;
+}
+
+hipError_t kda_launch_bwd_grad(const BwdArgs &a0, hipStream_t s) {
+    BwdArgs a = a0;
+    const int64_t units = a.slots * a.H;
+    const int64_t piece = launch_piece(kMaxUnitsPerLaunch, a.piece_cap);
     for (int64_t u0 = 0; u0 < units; u0 += piece) {
         a.unit_base = u0;
         const int64_t nu = units - u0 < piece ? units - u0 : piece;
@@ -1112,7 +1129,5 @@ hipError_t kda_launch_bwd(const BwdArgs &a0, hipStream_t s, hipEvent_t *ev) {
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kda_bwd_params_kernel, dim3((unsigned)a.H), dim3(kThreads), 0, s, a);
-    const hipError_t e = hipGetLastError();
-    if (e == hipSuccess && ev) return hipEventRecord(ev[2], s);
-    return e;
+    return hipGetLastError();
 }

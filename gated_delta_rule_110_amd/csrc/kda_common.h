@@ -115,12 +115,18 @@ struct ChainArgs {
 // head h, S_0 = h0[b, h] (zeros when h0 is null) and, for s = 0 .. segs - 1,
 // S_{s+1} = M_s S_s + N_s with (M_s, N_s) the map of segment s; S_s (s < segs)
 // goes to sin, S_segs to ht.
+// With reverse set it is the same pass for the gradient of the state, last
+// segment first: D_segs = h0[b, h] (the gradient of the final state, or zeros)
+// and D_s = M_s^T D_{s+1} + N_s, with N_s the reverse chain of segment s run
+// from a zero gradient; D_{s+1} (s < segs) goes to sin[segment s], the
+// gradient leaving it, and D_0 to ht, the gradient of the initial state.
 struct ScanArgs {
     const float *mapM, *mapN;   // [B segs, H, K, K] / [B segs, H, K, V] fp32
     float *sin;                 // [B segs, H, K, V] fp32
     const void *h0;             // [B, H, K, V] or nullptr
     void *ht;                   // [B, H, K, V] or nullptr
     int h0_bf16, ht_bf16;
+    int reverse;
     int64_t B, H, segs;
 };
 
@@ -166,6 +172,10 @@ struct BwdArgs {
     float *dq, *dk, *dv, *dg, *dbeta;       // [B,T,H,K] / [B,T,H,V] / [B,T,H] fp32
     float *dh0;                             // [N,H,K,V] fp32 or nullptr
     float *dA_log, *ddt_bias;               // [H] / [H,K] fp32
+    // Map mode of the reverse chain (chain_map != 0): it stores neither dhs nor
+    // dUt, only the gradient entering every sequence (dh0): with no gradient
+    // of the final state (dht null) that is the offset of a segment's map.
+    int chain_map;
     int64_t unit_base, chain_base;          // first unit / chain of a launch; set by the launchers
     int64_t piece_cap;                      // kda_desc_t::launch_piece (0: launch size by the default rule)
 };
@@ -314,12 +324,13 @@ hipError_t kda_launch_seg_table(int64_t B, int64_t T, int64_t segs, int64_t segc
                                 hipStream_t s);
 hipError_t kda_launch_seg_scan(const kda::ScanArgs &a, hipStream_t s);
 hipError_t kda_launch_decode(const kda::DecodeArgs &a, hipStream_t s);
-// The backward's own kernels (kda_bwd.hip): per-chunk preparation, the
-// reverse state chain, the per-chunk gradient, and the sum of the shared
-// parameters' partial gradients.
-// With ev (3 events) it records ev[0] after the preparation kernel, ev[1] after
-// the reverse chain and ev[2] after the per-chunk gradient and the parameter sum.
-hipError_t kda_launch_bwd(const kda::BwdArgs &a, hipStream_t s, hipEvent_t *ev = nullptr);
+// The backward's own kernels (kda_bwd.hip), in this order: per-chunk
+// preparation, the reverse state chain (over BwdArgs' sequences, which may be
+// the segments of split chains), then the per-chunk gradient and the sum of the
+// shared parameters' partial gradients.
+hipError_t kda_launch_bwd_prep(const kda::BwdArgs &a, hipStream_t s);
+hipError_t kda_launch_bwd_chain(const kda::BwdArgs &a, hipStream_t s);
+hipError_t kda_launch_bwd_grad(const kda::BwdArgs &a, hipStream_t s);
 // The pipelined forward (kda_fused.hip): whether it handles these shapes, and
 // its launch (the flag clear and the fused producer / consumer grid).
 bool kda_fused_applies(int64_t N, int64_t H, bool varlen);

@@ -60,9 +60,13 @@ __global__ __launch_bounds__(kThreads) void kda_seg_table_kernel(int64_t B, int6
 // segment's M and N rows are loaded while the current product runs: the
 // scan is a chain of dependent steps, and each step's loads would otherwise
 // be exposed.
+// kRev is the gradient's pass (ScanArgs::reverse): segments last to first and
+// the product M_s^T D, whose A operand is read down the columns of M_s (four
+// 64-byte row pieces per kq instead of one 16-byte load).
 constexpr int kScanThreads = 512;
 
-__global__ __launch_bounds__(kScanThreads) void kda_seg_scan_kernel(ScanArgs a) {
+template <bool kRev>
+__device__ __forceinline__ void seg_scan(const ScanArgs &a) {
     __shared__ float st[2][kCols * kSP];  // [buffer][column * kSP + row]
 
     const int64_t bh = blockIdx.x;  // on x: a grid's y extent is small
@@ -73,11 +77,14 @@ __global__ __launch_bounds__(kScanThreads) void kda_seg_scan_kernel(ScanArgs a) 
     constexpr int64_t KV = (int64_t)kK * kV;
     const int64_t col0 = (int64_t)kCols * vb;
     auto seg_index = [&](int64_t s) { return (b * a.segs + s) * a.H + h; };
+    // the i-th step works on segment first + dir * i
+    const int64_t first = kRev ? a.segs - 1 : 0, dir = kRev ? -1 : 1;
 
-    {   // S_0 = h0[b, h] (or zeros): thread t holds column t % 16, rows 4 (t / 16) .. + 3
+    {   // the starting value (h0[b, h] or zeros): thread t holds column t % 16, rows 4 (t / 16) .. + 3;
+        // forward it enters segment 0, reverse it leaves the last segment
         const int c = tid & 15, r0 = 4 * (tid >> 4);
         const int64_t src = bh * KV + col0 + c;
-        float *dst = a.sin + seg_index(0) * KV + col0 + c;
+        float *dst = a.sin + seg_index(first) * KV + col0 + c;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = r0 + i;
@@ -89,26 +96,34 @@ __global__ __launch_bounds__(kScanThreads) void kda_seg_scan_kernel(ScanArgs a) 
         }
     }
 
-    // this lane's operands of segment s: M[16 w + r][16 kq + 4 q .. + 3] and
-    // N[16 w + 4 q + e][col0 + r]
+    // this lane's operands of segment s: the A rows 16 w + r, k = 16 kq + 4 q .. + 3
+    // (M_s, or M_s^T), and N[16 w + 4 q + e][col0 + r]
     f4 am[8], an;
     auto load = [&](int64_t s) {
-        const float *M = a.mapM + seg_index(s) * KV + (16 * w + r) * kK + 4 * q;
+        const float *M = a.mapM + seg_index(s) * KV;
 #pragma unroll
-        for (int kq = 0; kq < 8; ++kq) am[kq] = *reinterpret_cast<const f4 *>(M + 16 * kq);
+        for (int kq = 0; kq < 8; ++kq) {
+            if constexpr (kRev) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) am[kq][j] = M[(16 * kq + 4 * q + j) * kK + 16 * w + r];
+            } else {
+                am[kq] = *reinterpret_cast<const f4 *>(M + (16 * w + r) * kK + 16 * kq + 4 * q);
+            }
+        }
         const float *N = a.mapN + seg_index(s) * KV + (16 * w + 4 * q) * kV + col0 + r;
 #pragma unroll
         for (int e = 0; e < 4; ++e) an[e] = N[e * kV];
     };
-    load(0);
+    load(first);
     __syncthreads();
 
-    for (int64_t s = 0; s < a.segs; ++s) {
-        const int p = (int)(s & 1);
+    for (int64_t i = 0; i < a.segs; ++i) {
+        const int64_t s = first + dir * i;
+        const int p = (int)(i & 1);
         f4 m[8], n = an;
 #pragma unroll
         for (int kq = 0; kq < 8; ++kq) m[kq] = am[kq];
-        if (s + 1 < a.segs) load(s + 1);
+        if (i + 1 < a.segs) load(s + dir);
         f4 acc = f4{0, 0, 0, 0};
 #pragma unroll
         for (int kq = 0; kq < 8; ++kq) {
@@ -122,8 +137,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_seg_scan_kernel(ScanArgs a) 
             const int row = 16 * w + 4 * q + e;
             const float v = acc[e] + n[e];
             st[p ^ 1][r * kSP + row] = v;
-            if (s + 1 < a.segs) {
-                a.sin[seg_index(s + 1) * KV + row * kV + col0 + r] = v;
+            if (i + 1 < a.segs) {
+                a.sin[seg_index(s + dir) * KV + row * kV + col0 + r] = v;
             } else if (a.ht) {
                 const int64_t idx = bh * KV + row * kV + col0 + r;
                 if (a.ht_bf16) static_cast<uint16_t *>(a.ht)[idx] = f32_to_bf16_bits(v);
@@ -133,6 +148,9 @@ __global__ __launch_bounds__(kScanThreads) void kda_seg_scan_kernel(ScanArgs a) 
         __syncthreads();
     }
 }
+
+__global__ __launch_bounds__(kScanThreads) void kda_seg_scan_kernel(ScanArgs a) { seg_scan<false>(a); }
+__global__ __launch_bounds__(kScanThreads) void kda_seg_scan_rev_kernel(ScanArgs a) { seg_scan<true>(a); }
 
 }  // namespace
 
@@ -145,6 +163,11 @@ hipError_t kda_launch_seg_table(int64_t B, int64_t T, int64_t segs, int64_t segc
 hipError_t kda_launch_seg_scan(const ScanArgs &a, hipStream_t s) {
     const int64_t bh = a.B * a.H;
     if (bh <= 0 || a.segs <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_seg_scan_kernel, dim3((unsigned)bh, (unsigned)(kV / kCols)), dim3(kScanThreads), 0, s, a);
+    if (a.reverse)
+        hipLaunchKernelGGL(kda_seg_scan_rev_kernel, dim3((unsigned)bh, (unsigned)(kV / kCols)), dim3(kScanThreads), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL(kda_seg_scan_kernel, dim3((unsigned)bh, (unsigned)(kV / kCols)), dim3(kScanThreads), 0,
+                           s, a);
     return hipGetLastError();
 }

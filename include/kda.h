@@ -253,11 +253,12 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
                         const kda_desc_t *desc, hipStream_t stream);
 
 /* Bytes of workspace kda_bwd needs for these shapes (0 if the shapes are
- * invalid or chain_segments >= 2).  Pure host arithmetic.  About 425 KiB per
- * 64-token chunk and head (the forward's 72.5 KiB of intermediates, the fp32
- * state entering every chunk and its gradient, 64 KiB each, 161 KiB of fp32
- * per-chunk quantities and 62.5 KiB of fp16 operands for the reverse chain),
- * plus B * T * H * V * 2 bytes for the recomputed forward output. */
+ * invalid).  Pure host arithmetic.  About 425 KiB per 64-token chunk and head
+ * (the forward's 72.5 KiB of intermediates, the fp32 state entering every
+ * chunk and its gradient, 64 KiB each, 161 KiB of fp32 per-chunk quantities
+ * and 62.5 KiB of fp16 operands for the reverse chain), plus B * T * H * V * 2
+ * bytes for the recomputed forward output, plus kda_fwd's 192 KiB per
+ * (segment, head) when chains are split (the reverse chains reuse it). */
 size_t kda_bwd_workspace_size(const kda_desc_t *desc);
 
 /* Enqueue the gradient of kda_fwd on `stream` and return without
@@ -284,8 +285,16 @@ size_t kda_bwd_workspace_size(const kda_desc_t *desc);
  * All outputs are overwritten, never accumulated into.  Where the gate is
  * clamped (-exp(A_log) softplus(g + dt_bias) <= lower_bound) no gradient
  * reaches g, dt_bias or A_log; at the kink itself the clamped side is taken.
- * desc->chain_segments >= 2 is KDA_ERR_UNSUPPORTED (the backward never splits
- * chains; 0 and 1 both mean unsplit; negative is KDA_ERR_PARAM);
+ * desc->chain_segments splits chains as for kda_fwd (the same rule and the
+ * same errors; kda_fwd_chain_segments() gives the count): the recomputed
+ * forward chain runs as kda_fwd's split chains (also storing the state
+ * entering every chunk), and the reverse chain, whose step is affine in the
+ * state's gradient with the transpose of the forward step's linear part, runs
+ * in three launches too: every segment's reverse chain from a zero gradient,
+ * an fp32 scan from the last segment to the first with the forward's segment
+ * maps transposed (the gradient leaving every segment, and d_initial_state),
+ * and every segment's reverse chain from the gradient leaving it.  The result
+ * is the same function of the inputs either way, up to rounding;
  * desc->pipeline is ignored;
  * desc->phase_events, when set, is an array of 6 events recorded before the
  * first kernel (0), after the forward's intra-chunk kernel (1) and state

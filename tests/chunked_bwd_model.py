@@ -21,6 +21,14 @@ head) it runs the same three passes as the GPU:
 T = (I + Diag(b) M)^-1 with M the strictly lower decayed key Gram, and
 U - W S = T Diag(b) Y, so W and U are never needed apart: the gradient of
 (I + Diag(b) M) is -T^T dT T^T = -Z Ut^T.
+
+With ``segments`` the two state chains are split as the GPU splits them: the
+chunks of a sequence are cut into segments of ceil(chunks / segments) chunks;
+the forward composes every segment's affine map S -> M S + N (M from S = I
+with U = 0, N from S = 0) in order; the backward runs every segment's reverse
+chain from a zero gradient (N'), composes D_s = M_s^T D_{s+1} + N'_s from the
+last segment to the first, and runs every segment again from the gradient
+leaving it.  Both are the unsplit chains in exact arithmetic.
 """
 from __future__ import annotations
 
@@ -52,8 +60,16 @@ def _chunk_prep(q, k, g, be, A, dtb, lb):
     return dict(qn=qn, kn=kn, rq=rq, rk=rk, b=b, z=z, G=G, M=M, Aqk=Aqk, T=T, E=E, low=low, lowd=lowd)
 
 
+def _segments(n, segments):
+    """Chunk index ranges of the segments of an n-chunk chain (one range when unsplit)."""
+    if not segments or segments < 2 or n < 2:
+        return [range(n)]
+    segc = -(-n // min(segments, n))
+    return [range(s, min(s + segc, n)) for s in range(0, n, segc)]
+
+
 def chunked_backward(q, k, v, g, beta, scale, A_log, dt_bias, lb, d_out, d_final=None, initial_state=None,
-                     cu_seqlens=None, C: int = 64):
+                     cu_seqlens=None, C: int = 64, segments=None):
     """Gradient of the forward pass, computed chunk by chunk.  fp64 numpy inputs as
     oracle.bwd takes them; returns the same dict of arrays."""
     B, T_, H, K = q.shape
@@ -68,9 +84,7 @@ def chunked_backward(q, k, v, g, beta, scale, A_log, dt_bias, lb, d_out, d_final
         for h in range(H):
             A, dtb = A_log[h], dt_bias[h]
             chunks = [(c0, min(c0 + C, s1)) for c0 in range(s0, s1, C)]
-            preps, wy, hs = [], [], []
-            S = np.zeros((K, V)) if initial_state is None else initial_state[n, h].copy()
-            # 1. forward states
+            preps, wy = [], []
             for c0, c1 in chunks:
                 p = _chunk_prep(q[bb, c0:c1, h], k[bb, c0:c1, h], g[bb, c0:c1, h], beta[bb, c0:c1, h], A, dtb, lb)
                 gam = np.exp(p["G"])
@@ -80,20 +94,52 @@ def chunked_backward(q, k, v, g, beta, scale, A_log, dt_bias, lb, d_out, d_final
                 Kbar = np.exp(p["G"][-1][None, :] - p["G"]) * p["kn"]
                 preps.append(p)
                 wy.append((W, U, Kbar, gam * p["qn"], gn))
-                hs.append(S.copy())
-                S = gn[:, None] * S + Kbar.T @ (U - W @ S)
-            # 2. backward chain
-            dS = np.zeros((K, V)) if d_final is None else d_final[n, h].copy()
-            dhs, dUts = [None] * len(chunks), [None] * len(chunks)
-            for ci in range(len(chunks) - 1, -1, -1):
+
+            def fstep(S, ci, linear=False):
+                W, U, Kbar, _, gn = wy[ci]
+                return gn[:, None] * S + Kbar.T @ ((0.0 if linear else U) - W @ S)
+
+            def rstep(dS, ci):
+                W, _, Kbar, Qg, gn = wy[ci]
                 c0, c1 = chunks[ci]
-                W, U, Kbar, Qg, gn = wy[ci]
                 dO = d_out[bb, c0:c1, h]
-                dhs[ci] = dS.copy()
                 dUt = scale * preps[ci]["Aqk"].T @ dO + Kbar @ dS
-                dUts[ci] = dUt
-                dS = gn[:, None] * dS - W.T @ dUt + scale * Qg.T @ dO
+                return gn[:, None] * dS - W.T @ dUt + scale * Qg.T @ dO, dUt
+
+            segs = _segments(len(chunks), segments)
+            # 1. forward states: the state entering every segment (composed maps), then
+            # every chunk's from it
+            S = np.zeros((K, V)) if initial_state is None else initial_state[n, h].copy()
+            maps, s_in = [], []
+            for seg in segs:
+                M, Nn = np.eye(K), np.zeros((K, V))
+                for ci in seg:
+                    M, Nn = fstep(M, ci, linear=True), fstep(Nn, ci)
+                maps.append(M)
+                s_in.append(S)
+                S = M @ S + Nn
+            hs = [None] * len(chunks)
+            for seg, S in zip(segs, s_in):
+                for ci in seg:
+                    hs[ci] = S.copy()
+                    S = fstep(S, ci)
+            # 2. backward chain: the gradient leaving every segment (reverse maps: M_s^T
+            # and the chain from zero), then every chunk's from it
+            dS = np.zeros((K, V)) if d_final is None else d_final[n, h].copy()
+            d_leave = [None] * len(segs)
+            for si in range(len(segs) - 1, -1, -1):
+                d_leave[si] = dS
+                off = np.zeros((K, V))
+                for ci in reversed(segs[si]):
+                    off, _ = rstep(off, ci)
+                dS = maps[si].T @ dS + off
             res["d_initial"][n, h] = dS
+            dhs, dUts = [None] * len(chunks), [None] * len(chunks)
+            for si, seg in enumerate(segs):
+                dS = d_leave[si]
+                for ci in reversed(seg):
+                    dhs[ci] = dS.copy()
+                    dS, dUts[ci] = rstep(dS, ci)
             # 3. per chunk
             for ci, (c0, c1) in enumerate(chunks):
                 p = preps[ci]

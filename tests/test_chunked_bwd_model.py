@@ -36,3 +36,19 @@ def test_chunked_gradient_matches_oracle(B, T, H, K, V, C, cu, lb):
     for name in ref:
         err = np.abs(ref[name] - got[name]).max()
         assert err <= 1e-11 * max(1.0, np.abs(ref[name]).max()), (name, err)
+
+
+@pytest.mark.parametrize("segments", [2, 3, 13])
+def test_split_chains_match_oracle(segments):
+    # the split chains of the GPU plan (forward maps composed in order; reverse chains from a
+    # zero gradient composed with the transposed forward maps, last segment first) give the
+    # same gradient: 13 chunks of 8 tokens (the last ragged) in 2, 3 and 13 segments
+    B, T, H, K, V, C = 2, 8 * 12 + 5, 2, 8, 6, 8
+    x = _case(B, T, H, K, V, seed=977, lb=-2.0)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], 0.4, x["A_log"], x["dt_bias"], -2.0, x["d_out"])
+    ref = oracle.bwd(*args, d_final=x["d_final"], initial_state=x["initial_state"])
+    got = chunked_backward(*args, d_final=x["d_final"], initial_state=x["initial_state"], C=C,
+                           segments=segments)
+    for name in ref:
+        err = np.abs(ref[name] - got[name]).max()
+        assert err <= 1e-11 * max(1.0, np.abs(ref[name]).max()), (name, err)

@@ -179,15 +179,21 @@ def test_bwd_activation_extremes(lb):
     assert not got["dbeta"][np.isinf(be)].any()
 
 
-def test_bwd_graph_replays_match_eager():
+@pytest.mark.parametrize("case", ["packed", "split"])
+def test_bwd_graph_replays_match_eager(case):
     # with a caller-owned workspace and outputs the backward enqueues kernels only, so it can be
     # captured once and replayed; every replay, with the outputs and workspace clobbered eagerly
-    # in between, must equal the eager call bit for bit
-    w = W.make("bwd_graph", 1, 260, 3, 7010, init="fp32", final="fp32", seqlens=[100, 0, 97, 63])
+    # in between, must equal the eager call bit for bit (a packed batch; split chains)
+    if case == "packed":
+        w = W.make("bwd_graph", 1, 260, 3, 7010, init="fp32", final="fp32", seqlens=[100, 0, 97, 63])
+        segs = 0
+    else:
+        w = W.make("bwd_graph_split", 2, 64 * 12 + 5, 2, 7014, init="fp32", final="fp32")
+        segs = 3
     d_out, d_fin = W.loss_grads(w, 7110, final="fp32")
     wd = w.to("cuda")
     d_out, d_fin = d_out.cuda(), d_fin.cuda()
-    nbytes = kda.bwd_workspace_size(w.B, w.T, w.H, num_seqs=w.N)
+    nbytes = kda.bwd_workspace_size(w.B, w.T, w.H, num_seqs=w.N, chain_segments=segs)
 
     def buffers():
         outs = {n: torch.empty(sh, dtype=torch.float32, device="cuda") for n, sh in
@@ -199,7 +205,7 @@ def test_bwd_graph_replays_match_eager():
     def call(ws, outs):
         kda.bwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, wd.A_log, wd.dt_bias, w.lower_bound, d_out,
                 d_final_state=d_fin, initial_state=wd.initial_state, cu_seqlens=wd.cu_seqlens, workspace=ws,
-                outputs=outs)
+                outputs=outs, chain_segments=segs)
 
     ws_e, eager = buffers()
     call(ws_e, eager)
@@ -241,10 +247,42 @@ def test_bwd_many_short_sequences():
 
 def test_bwd_long_chain():
     # 65536 tokens (1024 chunks in each reverse chain), g ~ N(-1, 1) as the 128K workload draws
-    # it: the gradient state is carried through the whole chain without drifting from the oracle
+    # it: the gradient state is carried through the whole chain without drifting from the oracle,
+    # unsplit and in the automatic split (16 segments of 64 chunks at H = 2)
     w = W.make("bwd_long", 1, 65536, 2, 7012, init="fp32", final="fp32", g_mean=-1.0)
     d_out, d_fin = W.loss_grads(w, 7112, final="fp32")
-    say("bwd long: T=%d H=%d" % (w.T, w.H))
-    got = _gpu(w, d_out, d_fin)
+    assert kda.chain_segments_for(w.B, w.T, w.H) == 16
     ref = _oracle(w, d_out, d_fin)
-    _compare(got, ref, w, "long")
+    for segs in (1, 0):
+        say("bwd long: T=%d H=%d chain_segments=%d" % (w.T, w.H, segs))
+        got = _gpu(w, d_out, d_fin, chain_segments=segs)
+        _compare(got, ref, w, "long segs=%d" % segs)
+
+
+_SPLIT_REF = {}
+
+
+@pytest.mark.parametrize("segs,states", [(3, "fp32"), (4, "bf16"), (41, "fp32"), (4, None)])
+def test_bwd_split_chains(segs, states):
+    # split chains in the backward: the forward's segment maps, the reverse chain of every
+    # segment from a zero gradient, the scan with the maps transposed, the reverse chain from
+    # the gradient leaving every segment.  Two rows of 41 chunks (the last ragged) in 3, 4 and
+    # 41 (one chunk each) segments; bf16 states; no states and no initial-state gradient.
+    key = states
+    if key not in _SPLIT_REF:
+        w = W.make("bwd_split", 2, 64 * 40 + 17, 2, 7013, init=states, final=states)
+        d_out, d_fin = W.loss_grads(w, 7113, final=states)
+        _SPLIT_REF[key] = (w, d_out, d_fin, _oracle(w, d_out, d_fin), _gpu(w, d_out, d_fin, chain_segments=1))
+    w, d_out, d_fin, ref, unsplit = _SPLIT_REF[key]
+    assert kda.chain_segments_for(w.B, w.T, w.H, segs) == segs
+    say("bwd split: segs=%d states=%s" % (segs, states))
+    got = _gpu(w, d_out, d_fin, chain_segments=segs, with_d_initial=states is not None)
+    if states is None:
+        assert got["d_initial_state"] is None
+        got["d_initial_state"] = unsplit["d_initial_state"]
+    _compare(got, ref, w, "split segs=%d states=%s" % (segs, states))
+    # the split only changes rounding: close to the unsplit gradient
+    for name in NAMES:
+        a, b = got[name], unsplit[name]
+        scale_ = max(float(np.abs(b).max()), 1e-30)
+        assert float(np.abs(a - b).max()) / scale_ <= 2e-3, (name, segs)

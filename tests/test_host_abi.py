@@ -234,7 +234,7 @@ def test_bwd_validation_errors(lib):
     assert _call_bwd(lib, _desc(K=64)) == 3
     assert _call_bwd(lib, _desc(B=0)) == 2
     assert _call_bwd(lib, _desc(B=2, num_seqs=2), cu=ctypes.c_void_p(FAKE)) == 2
-    assert _call_bwd(lib, _desc(chain_segments=2)) == 3       # the backward never splits chains
+    assert _call_bwd(lib, _desc(chain_segments=2), cu=ctypes.c_void_p(FAKE)) == 3   # packed: never split
     assert _call_bwd(lib, _desc(chain_segments=-1)) == 4
     assert _call_bwd(lib, _desc(launch_piece=-1)) == 4
     assert _call_bwd(lib, _desc(), lb=-6.0) == 4
@@ -263,5 +263,15 @@ def test_bwd_workspace_size(lib):
     assert abs(per - expect) < 1024
     assert kda.bwd_workspace_size(1, 0, 4) > 0 or kda.bwd_workspace_size(1, 0, 4) == 0
     assert kda.bwd_workspace_size(2, 64, 2, num_seqs=3) == 0
-    d = _desc(chain_segments=4)
+    # split chains: the forward's segment table and three fp32 maps per (segment, head) on top
+    # (the reverse chains reuse them)
+    # (B = 2: the packed layout, which B = 1 also covers, plays no part)
+    unsplit = kda.bwd_workspace_size(2, 64 * 64, 2, chain_segments=1)
+    split = kda.bwd_workspace_size(2, 64 * 64, 2, chain_segments=4)
+    assert split - unsplit == kda.workspace_size(2, 64 * 64, 2, chain_segments=4) - \
+        kda.workspace_size(2, 64 * 64, 2, chain_segments=1)
+    assert split - unsplit >= 3 * 2 * 4 * 2 * 65536
+    assert kda.bwd_workspace_size(2, 64 * 64, 2) == kda.bwd_workspace_size(
+        2, 64 * 64, 2, chain_segments=kda.chain_segments_for(2, 64 * 64, 2))
+    d = _desc(chain_segments=-1)
     assert lib.kda_bwd_workspace_size(ctypes.byref(d)) == 0
