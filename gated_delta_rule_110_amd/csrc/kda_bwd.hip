@@ -1075,15 +1075,43 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 
 // ---- 5. the shared parameters ------------------------------------------------
 
-__global__ __launch_bounds__(kThreads) void kda_bwd_params_kernel(BwdArgs a) {
+// One 1024-thread workgroup per head: thread (slice j, column c) sums column c
+// (c < K: dt_bias channel c; c = K: A_log) over the chunk slots j, j + 7, j + 14,
+// ... in increasing order, eight loads in flight, then the seven slice sums are
+// added in slice order: a fixed order, so the result is the same bits on every
+// call.  (One thread per column would wait out one load per chunk in turn.)
+constexpr int kParamThreads = 1024;
+constexpr int kParamSlices = kParamThreads / (kK + 1);  // 7
+
+__global__ __launch_bounds__(kParamThreads) void kda_bwd_params_kernel(BwdArgs a) {
+    __shared__ double red[kParamSlices][kK + 1];
     const int64_t h = blockIdx.x;
     const int tid = threadIdx.x;
-    if (tid > kK) return;
+    const int j = tid / (kK + 1), c = tid - j * (kK + 1);
     const int64_t total = a.cu ? (int64_t)a.chunk_off[a.N] : a.slots;
-    double s = 0.0;
-    for (int64_t slot = 0; slot < total; ++slot) s += (double)a.part[(slot * a.H + h) * (kK + 1) + tid];
-    if (tid < kK) a.ddt_bias[h * kK + tid] = (float)s;
-    else a.dA_log[h] = (float)s;
+    if (j < kParamSlices) {
+        const float *p = a.part + h * (kK + 1) + c;
+        const int64_t step = a.H * (kK + 1);  // one slot
+        double s = 0.0;
+        int64_t slot = j;
+        for (; slot + 7 * kParamSlices < total; slot += 8 * kParamSlices) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = p[(slot + u * kParamSlices) * step];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += (double)v[u];
+        }
+        for (; slot < total; slot += kParamSlices) s += (double)p[slot * step];
+        red[j][c] = s;
+    }
+    __syncthreads();
+    if (tid <= kK) {
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < kParamSlices; ++i) s += red[i][tid];
+        if (tid < kK) a.ddt_bias[h * kK + tid] = (float)s;
+        else a.dA_log[h] = (float)s;
+    }
 }
 
 }  // namespace
@@ -1128,6 +1156,6 @@ hipError_t kda_launch_bwd_grad(const BwdArgs &a0, hipStream_t s) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kda_bwd_params_kernel, dim3((unsigned)a.H), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(kda_bwd_params_kernel, dim3((unsigned)a.H), dim3(kParamThreads), 0, s, a);
     return hipGetLastError();
 }
