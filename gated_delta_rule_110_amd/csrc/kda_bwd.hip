@@ -123,18 +123,33 @@ constexpr int kCoGn = kCoQ + kK * kTkP * 2;        // 63488
 constexpr int kCoBytes = kCoGn + kK * 4;           // 64000
 static_assert(kCoGn % 1024 == 0 && kCoBytes == kBwdChainOperandBytes, "chain operand block layout");
 
-constexpr int kPP = kK + 1;  // row pitch (an odd pitch measured best over the kernel's access patterns)
+// The preparation kernel holds 64 of the 128 channels of q-hat, k-hat and G in
+// LDS at a time (two passes), so that two workgroups fit on a CU (71 KB each):
+// its phases are chains of dependent steps, and a second workgroup fills the
+// waits.  The Gram sums of the two passes accumulate in registers in the same
+// k order as one pass would; T takes the place of the q-hat tile once the Gram
+// is done, and W, which needs T, is formed for the second half straight away
+// and for the first half after reloading its k-hat and G from the outputs
+// already written.
+constexpr int kHC = 64;       // channels per pass
+constexpr int kHP = kHC + 1;  // row pitch of the half-channel tiles
 struct PrepSmem {
-    float q[kChunk][kPP];
-    float k[kChunk][kPP];
-    float G[kChunk][kPP];
-    float M[kChunk][kChunk + 1];   // M
-    float T[kChunk][kChunk + 1];   // T = (I + Diag(b) M)^-1
-    float P[4][16][17];            // one 16 x 16 block product per wave
+    union {
+        float q[kChunk][kHP];  // qhat, the pass's channels (through the Gram)
+        float T[kChunk][kHP];  // T = (I + Diag(b) M)^-1 (after it)
+    } u;
+    float k[kChunk][kHP];      // khat, the pass's channels
+    float G[kChunk][kHP];      // per-channel log-decay, cumulated in place
+    float M[kChunk][kChunk + 1];
+    union {
+        float P[4][16][17];    // one 16 x 16 block product per wave (T solve)
+        float tot[4][kHC];     // row-segment totals (cumulative sum)
+    } v;
     float b[kChunk];
 };
+static_assert(sizeof(PrepSmem) <= 80 * 1024, "two preparation workgroups per CU");
 
-__global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
     __shared__ PrepSmem sm;
     const int64_t ws = a.unit_base + blockIdx.x;  // chunk slot * H + head
     const int64_t slot = ws / a.H, h = ws - slot * a.H;
@@ -149,8 +164,12 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
     _Float16 *WT = reinterpret_cast<_Float16 *>(co + kCoW);
     _Float16 *QgT = reinterpret_cast<_Float16 *>(co + kCoQ);
     float *gno = reinterpret_cast<float *>(co + kCoGn);
+    float *qn = a.qn + ws * (kChunk * kK), *kn = a.kn + ws * (kChunk * kK), *Go = a.G + ws * (kChunk * kK);
 
-    // rows, norms, b and the per-channel log-decay; a quarter row per thread
+    // rows, norms, b and the per-channel log-decay; a quarter row per thread.
+    // qhat and khat go out as they are; the log-decay goes out uncumulated for
+    // now (the second pass reads its half back).  The first pass's half goes
+    // to LDS.
     {
         const int row = tid >> 2, qt = tid & 3;
         const bool valid = row < L;
@@ -173,10 +192,27 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
         const float *dtb = a.dt_bias + h * kK + 32 * qt;
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
-            sm.q[row][32 * qt + e] = qv[e] * rq;
-            sm.k[row][32 * qt + e] = kv[e] * rk;
-            const float z = nA * softplus_fast(gv[e] + dtb[e]);
-            sm.G[row][32 * qt + e] = valid ? fmaxf(a.lower_bound, z) : 0.f;
+            qv[e] *= rq;
+            kv[e] *= rk;
+            gv[e] = valid ? fmaxf(a.lower_bound, nA * softplus_fast(gv[e] + dtb[e])) : 0.f;
+        }
+        float *qo = qn + row * kK + 32 * qt, *ko = kn + row * kK + 32 * qt, *go = Go + row * kK + 32 * qt;
+#pragma unroll
+        for (int e = 0; e < 32; e += 4) {
+            *reinterpret_cast<float4 *>(qo + e) = make_float4(qv[e], qv[e + 1], qv[e + 2], qv[e + 3]);
+            *reinterpret_cast<float4 *>(ko + e) = make_float4(kv[e], kv[e + 1], kv[e + 2], kv[e + 3]);
+        }
+        if (qt < 2) {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                sm.u.q[row][32 * qt + e] = qv[e];
+                sm.k[row][32 * qt + e] = kv[e];
+                sm.G[row][32 * qt + e] = gv[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 32; e += 4)
+                *reinterpret_cast<float4 *>(go + e) = make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
         }
         if (qt == 0) {
             const float b = valid ? sigmoid_fast(bf16_bits_to_f32(a.beta[(t0 + row) * H + h])) : 0.f;
@@ -186,66 +222,105 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
             a.bb[ws * kChunk + row] = b;
         }
     }
-    __syncthreads();
-    if (tid < kK) {  // G_i = sum_{t <= i} a_t, per channel
-        float run = 0.f;
-        for (int i = 0; i < kChunk; ++i) {
-            run += sm.G[i][tid];
-            sm.G[i][tid] = run;
-        }
-    }
-    __syncthreads();
-    {
-        float *qn = a.qn + ws * (kChunk * kK), *kn = a.kn + ws * (kChunk * kK), *G = a.G + ws * (kChunk * kK);
-        for (int idx = tid; idx < kChunk * kK; idx += kThreads) {
-            const int i = idx >> 7, d = idx & 127;
-            qn[idx] = sm.q[i][d];
-            kn[idx] = sm.k[i][d];
-            G[idx] = sm.G[i][d];
-        }
-        // Kbar (natural) and Qg^T (four rows per store), exp(G_n)
-        const float *Gn = sm.G[L - 1];
-        for (int idx = tid; idx < kChunk * kK; idx += kThreads) {
-            const int i = idx >> 7, d = idx & 127;
-            Kn[i * kKnP + d] = (_Float16)(__expf(Gn[d] - sm.G[i][d]) * sm.k[i][d]);
-        }
-        for (int idx = tid; idx < kK * (kChunk / 4); idx += kThreads) {
-            const int d = idx >> 4, i0 = 4 * (idx & 15);
-            h4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (_Float16)(__expf(sm.G[i0 + e][d]) * sm.q[i0 + e][d]);
-            *reinterpret_cast<h4 *>(QgT + d * kTkP + i0) = v;
-        }
-        if (tid < kK) gno[tid] = __expf(Gn[tid]);
-    }
 
     const int w = tid >> 6, lane = tid & 63, r = lane & 15, gq = lane >> 4;
     // M[i][j] = sum_d khat_i khat_j exp(G_i - G_j) (j < i) and A_qk (qhat_i, j <= i), by 16 x 16
     // tiles (I, J), J <= I: pair p of the ten goes to wave p % 4, so that the waves get 3, 3, 2
     // and 2 tiles.  exp(G_i - G_j) = exp(G_i - ref) exp(ref - G_j), ref = G[16 I + 8].
-    {
-        float *Mk = a.Mk + ws * (kChunk * kChunk);
-        for (int p = w; p < 10; p += 4) {
+    f4 accM[3], accA[3];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) { accM[t] = f4{0, 0, 0, 0}; accA[t] = accM[t]; }
+
+    for (int half = 0; half < 2; ++half) {
+        const int c0 = kHC * half;  // first channel of the pass
+        if (half == 1) {
+            // the second half of qhat, khat and the log-decay, back from the outputs
+            __syncthreads();
+            for (int idx = tid; idx < kChunk * (kHC / 4); idx += kThreads) {
+                const int i = idx >> 4, d = 4 * (idx & 15);
+                const float4 x = *reinterpret_cast<const float4 *>(qn + i * kK + c0 + d);
+                const float4 y = *reinterpret_cast<const float4 *>(kn + i * kK + c0 + d);
+                const float4 z = *reinterpret_cast<const float4 *>(Go + i * kK + c0 + d);
+                sm.u.q[i][d] = x.x; sm.u.q[i][d + 1] = x.y; sm.u.q[i][d + 2] = x.z; sm.u.q[i][d + 3] = x.w;
+                sm.k[i][d] = y.x; sm.k[i][d + 1] = y.y; sm.k[i][d + 2] = y.z; sm.k[i][d + 3] = y.w;
+                sm.G[i][d] = z.x; sm.G[i][d + 1] = z.y; sm.G[i][d + 2] = z.z; sm.G[i][d + 3] = z.w;
+            }
+        }
+        __syncthreads();
+        // G_i = sum_{t <= i} a_t per channel: thread (channel c, row segment sg) sums 16 rows,
+        // then adds the totals of the segments above it
+        {
+            const int c = tid & (kHC - 1), sg = tid >> 6;
+            float run = 0.f;
+#pragma unroll
+            for (int i = 16 * sg; i < 16 * sg + 16; ++i) {
+                run += sm.G[i][c];
+                sm.G[i][c] = run;
+            }
+            sm.v.tot[sg][c] = run;
+            __syncthreads();
+            float off = 0.f;
+            for (int s2 = 0; s2 < sg; ++s2) off += sm.v.tot[s2][c];
+            if (sg > 0) {
+#pragma unroll
+                for (int i = 16 * sg; i < 16 * sg + 16; ++i) sm.G[i][c] += off;
+            }
+        }
+        __syncthreads();
+        {
+            // the cumulated log-decay, Kbar (natural), Qg^T (four rows per store), exp(G_n)
+            const float *Gn = sm.G[L - 1];
+            for (int idx = tid; idx < kChunk * kHC; idx += kThreads) {
+                const int i = idx >> 6, d = idx & (kHC - 1);
+                Go[i * kK + c0 + d] = sm.G[i][d];
+                Kn[i * kKnP + c0 + d] = (_Float16)(__expf(Gn[d] - sm.G[i][d]) * sm.k[i][d]);
+            }
+            for (int idx = tid; idx < kHC * (kChunk / 4); idx += kThreads) {
+                const int d = idx >> 4, i0 = 4 * (idx & 15);
+                h4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (_Float16)(__expf(sm.G[i0 + e][d]) * sm.u.q[i0 + e][d]);
+                *reinterpret_cast<h4 *>(QgT + (c0 + d) * kTkP + i0) = v;
+            }
+            if (tid < kHC) gno[c0 + tid] = __expf(Gn[tid]);
+        }
+        // this pass's part of the Gram sums (k = 4 ks + gq over the pass's channels)
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const int p = w + 4 * t;
+            if (p >= 10) break;
             const int I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
             const int J = p - I * (I + 1) / 2;
-            f4 accM = f4{0, 0, 0, 0}, accA = accM;
 #pragma unroll 8
-            for (int ks = 0; ks < 32; ++ks) {
+            for (int ks = 0; ks < kHC / 4; ++ks) {
                 const int d = 4 * ks + gq;
                 const float ref = sm.G[16 * I + 8][d];
                 const float fa = __expf(sm.G[16 * I + r][d] - ref);
                 const float bv = sm.k[16 * J + r][d] * __expf(ref - sm.G[16 * J + r][d]);
-                accM = mma(sm.k[16 * I + r][d] * fa, bv, accM);
-                accA = mma(sm.q[16 * I + r][d] * fa, bv, accA);
+                accM[t] = mma(sm.k[16 * I + r][d] * fa, bv, accM[t]);
+                accA[t] = mma(sm.u.q[16 * I + r][d] * fa, bv, accA[t]);
             }
+        }
+        if (half == 1) break;
+        // W needs T, so the first half's part of it waits for the reload below
+    }
+    __syncthreads();  // the Gram is done: the qhat tile becomes T
+    {
+        float *Mk = a.Mk + ws * (kChunk * kChunk);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const int p = w + 4 * t;
+            if (p >= 10) break;
+            const int I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+            const int J = p - I * (I + 1) / 2;
             h4 at;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * gq + e, j = 16 * J + r;
-                const float m = j < i ? accM[e] : 0.f;
+                const float m = j < i ? accM[t][e] : 0.f;
                 sm.M[i][j] = m;
                 Mk[i * kChunk + j] = m;
-                at[e] = (_Float16)(j <= i ? accA[e] : 0.f);
+                at[e] = (_Float16)(j <= i ? accA[t][e] : 0.f);
             }
             // A_qk^T[16 J + r][16 I + 4 gq .. + 3]
             *reinterpret_cast<h4 *>(AqT + (16 * J + r) * kTkP + 16 * I + 4 * gq) = at;
@@ -257,6 +332,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
                 sm.M[i][j] = 0.f;
                 Mk[idx] = 0.f;
                 AqT[j * kTkP + i] = (_Float16)0.f;
+                sm.u.T[i][j] = 0.f;
             }
         }
     }
@@ -281,12 +357,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
             for (int rr = cc + 1; rr < 16; ++rr) xv[rr] -= Lt[rr * (rr - 1) / 2 + cc] * xv[cc];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sm.T[i0 + rr][i0 + j] = xv[rr];
-    }
-    // zeros above the diagonal blocks
-    for (int idx = tid; idx < kChunk * kChunk; idx += kThreads) {
-        const int i = idx >> 6, j = idx & 63;
-        if ((j >> 4) > (i >> 4)) sm.T[i][j] = 0.f;
+        for (int rr = 0; rr < 16; ++rr) sm.u.T[i0 + rr][i0 + j] = xv[rr];
     }
     __syncthreads();
     // Then column block J = w (w < 3), down its block rows:
@@ -300,49 +371,62 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_prep_kernel(BwdArgs a) {
                 for (int s4 = 0; s4 < 4; ++s4) {
                     const int kk = 16 * K + 4 * s4 + gq;
                     const float av = sm.b[16 * I + r] * sm.M[16 * I + r][kk];
-                    pr = mma(av, sm.T[kk][16 * J + r], pr);
+                    pr = mma(av, sm.u.T[kk][16 * J + r], pr);
                 }
             }
             // lane (r, gq) holds P[4 gq + e][r]; through LDS for the B operand of T_II P
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.P[w][4 * gq + e][r] = pr[e];
+            for (int e = 0; e < 4; ++e) sm.v.P[w][4 * gq + e][r] = pr[e];
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // one wave: LDS accesses in order
             f4 t = f4{0, 0, 0, 0};
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4)
-                t = mma(sm.T[16 * I + r][16 * I + 4 * s4 + gq], sm.P[w][4 * s4 + gq][r], t);
+                t = mma(sm.u.T[16 * I + r][16 * I + 4 * s4 + gq], sm.v.P[w][4 * s4 + gq][r], t);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.T[16 * I + 4 * gq + e][16 * J + r] = -t[e];
+            for (int e = 0; e < 4; ++e) sm.u.T[16 * I + 4 * gq + e][16 * J + r] = -t[e];
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
     }
     __syncthreads();
     {
         float *Tm = a.Tm + ws * (kChunk * kChunk);
-        for (int idx = tid; idx < kChunk * kChunk; idx += kThreads) Tm[idx] = sm.T[idx >> 6][idx & 63];
+        for (int idx = tid; idx < kChunk * kChunk; idx += kThreads) Tm[idx] = sm.u.T[idx >> 6][idx & 63];
     }
-    // W = T Diag(b) (gamma * Khat), stored as -W^T; T[i][j] = 0 for j > i
-    {
-        f4 acc[8];
+    // W = T Diag(b) (gamma * Khat), stored as -W^T; T[i][j] = 0 for j > i.  The second
+    // half's channels are in LDS; then the first half's come back from the outputs.
+    for (int half = 1; half >= 0; --half) {
+        const int c0 = kHC * half;
+        if (half == 0) {
+            __syncthreads();
+            for (int idx = tid; idx < kChunk * (kHC / 4); idx += kThreads) {
+                const int i = idx >> 4, d = 4 * (idx & 15);
+                const float4 y = *reinterpret_cast<const float4 *>(kn + i * kK + d);
+                const float4 z = *reinterpret_cast<const float4 *>(Go + i * kK + d);
+                sm.k[i][d] = y.x; sm.k[i][d + 1] = y.y; sm.k[i][d + 2] = y.z; sm.k[i][d + 3] = y.w;
+                sm.G[i][d] = z.x; sm.G[i][d + 1] = z.y; sm.G[i][d + 2] = z.z; sm.G[i][d + 3] = z.w;
+            }
+            __syncthreads();
+        }
+        f4 acc[4];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0, 0, 0, 0};
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = f4{0, 0, 0, 0};
         for (int ks = 0; ks < 4 * (w + 1); ++ks) {
             const int j = 4 * ks + gq;
-            const float av = sm.T[16 * w + r][j];
+            const float av = sm.u.T[16 * w + r][j];
             const float bj = sm.b[j];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
+            for (int ct = 0; ct < 4; ++ct) {
                 const int d = 16 * ct + r;
                 acc[ct] = mma(av, bj * __expf(sm.G[j][d]) * sm.k[j][d], acc[ct]);
             }
         }
-        // lane holds W[16 w + 4 gq + e][16 ct + r] -> -W^T[16 ct + r][16 w + 4 gq .. + 3]
+        // lane holds W[16 w + 4 gq + e][c0 + 16 ct + r] -> -W^T[c0 + 16 ct + r][16 w + 4 gq .. + 3]
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
+        for (int ct = 0; ct < 4; ++ct) {
             h4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = (_Float16)(-acc[ct][e]);
-            *reinterpret_cast<h4 *>(WT + (16 * ct + r) * kTkP + 16 * w + 4 * gq) = v;
+            *reinterpret_cast<h4 *>(WT + (c0 + 16 * ct + r) * kTkP + 16 * w + 4 * gq) = v;
         }
     }
 }
