@@ -167,14 +167,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
     float *qn = a.qn + ws * (kChunk * kK), *kn = a.kn + ws * (kChunk * kK), *Go = a.G + ws * (kChunk * kK);
 
     // rows, norms, b and the per-channel log-decay; a quarter row per thread.
-    // qhat and khat go out as they are; the log-decay goes out uncumulated for
-    // now (the second pass reads its half back).  The first pass's half goes
-    // to LDS.
+    // qhat and khat go out as they are; the first pass's half goes to LDS, and
+    // the threads holding the second half keep it in registers until then.
+    const int row = tid >> 2, qt = tid & 3;
+    float qv[32], kv[32], gv[32];
     {
-        const int row = tid >> 2, qt = tid & 3;
         const bool valid = row < L;
         const int64_t base = ((t0 + (valid ? row : 0)) * H + h) * kK + 32 * qt;
-        float qv[32], kv[32], gv[32];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             unpack_bf16x8(*reinterpret_cast<const uint4 *>(a.q + base + 8 * i), qv + 8 * i);
@@ -196,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
             kv[e] *= rk;
             gv[e] = valid ? fmaxf(a.lower_bound, nA * softplus_fast(gv[e] + dtb[e])) : 0.f;
         }
-        float *qo = qn + row * kK + 32 * qt, *ko = kn + row * kK + 32 * qt, *go = Go + row * kK + 32 * qt;
+        float *qo = qn + row * kK + 32 * qt, *ko = kn + row * kK + 32 * qt;
 #pragma unroll
         for (int e = 0; e < 32; e += 4) {
             *reinterpret_cast<float4 *>(qo + e) = make_float4(qv[e], qv[e + 1], qv[e + 2], qv[e + 3]);
@@ -209,10 +208,6 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
                 sm.k[row][32 * qt + e] = kv[e];
                 sm.G[row][32 * qt + e] = gv[e];
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 32; e += 4)
-                *reinterpret_cast<float4 *>(go + e) = make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
         }
         if (qt == 0) {
             const float b = valid ? sigmoid_fast(bf16_bits_to_f32(a.beta[(t0 + row) * H + h])) : 0.f;
@@ -234,16 +229,15 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
     for (int half = 0; half < 2; ++half) {
         const int c0 = kHC * half;  // first channel of the pass
         if (half == 1) {
-            // the second half of qhat, khat and the log-decay, back from the outputs
+            // the second half of qhat, khat and the log-decay, from the registers that hold it
             __syncthreads();
-            for (int idx = tid; idx < kChunk * (kHC / 4); idx += kThreads) {
-                const int i = idx >> 4, d = 4 * (idx & 15);
-                const float4 x = *reinterpret_cast<const float4 *>(qn + i * kK + c0 + d);
-                const float4 y = *reinterpret_cast<const float4 *>(kn + i * kK + c0 + d);
-                const float4 z = *reinterpret_cast<const float4 *>(Go + i * kK + c0 + d);
-                sm.u.q[i][d] = x.x; sm.u.q[i][d + 1] = x.y; sm.u.q[i][d + 2] = x.z; sm.u.q[i][d + 3] = x.w;
-                sm.k[i][d] = y.x; sm.k[i][d + 1] = y.y; sm.k[i][d + 2] = y.z; sm.k[i][d + 3] = y.w;
-                sm.G[i][d] = z.x; sm.G[i][d + 1] = z.y; sm.G[i][d + 2] = z.z; sm.G[i][d + 3] = z.w;
+            if (qt >= 2) {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    sm.u.q[row][32 * (qt - 2) + e] = qv[e];
+                    sm.k[row][32 * (qt - 2) + e] = kv[e];
+                    sm.G[row][32 * (qt - 2) + e] = gv[e];
+                }
             }
         }
         __syncthreads();
