@@ -129,8 +129,9 @@ static_assert(kCoGn % 1024 == 0 && kCoBytes == kBwdChainOperandBytes, "chain ope
 // waits.  The Gram sums of the two passes accumulate in registers in the same
 // k order as one pass would; T takes the place of the q-hat tile once the Gram
 // is done, and W, which needs T, is formed for the second half straight away
-// and for the first half after reloading its k-hat and G from the outputs
-// already written.
+// and for the first half from the k-hat and G its threads kept in registers.
+// (Two workgroups per CU leave each lane 256 registers; round trips of the
+// halves through global memory instead missed L2 and cost 7%.)
 constexpr int kHC = 64;       // channels per pass
 constexpr int kHP = kHC + 1;  // row pitch of the half-channel tiles
 struct PrepSmem {
@@ -277,6 +278,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
                 *reinterpret_cast<h4 *>(QgT + (c0 + d) * kTkP + i0) = v;
             }
             if (tid < kHC) gno[c0 + tid] = __expf(Gn[tid]);
+            // the first half's cumulated log-decay stays with the threads that hold its khat, for W
+            if (half == 0 && qt < 2) {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) gv[e] = sm.G[row][32 * qt + e];
+            }
         }
         // this pass's part of the Gram sums (k = 4 ks + gq over the pass's channels)
 #pragma unroll
@@ -387,17 +393,17 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
         for (int idx = tid; idx < kChunk * kChunk; idx += kThreads) Tm[idx] = sm.u.T[idx >> 6][idx & 63];
     }
     // W = T Diag(b) (gamma * Khat), stored as -W^T; T[i][j] = 0 for j > i.  The second
-    // half's channels are in LDS; then the first half's come back from the outputs.
+    // half's channels are in LDS; then the first half's come back from registers.
     for (int half = 1; half >= 0; --half) {
         const int c0 = kHC * half;
         if (half == 0) {
             __syncthreads();
-            for (int idx = tid; idx < kChunk * (kHC / 4); idx += kThreads) {
-                const int i = idx >> 4, d = 4 * (idx & 15);
-                const float4 y = *reinterpret_cast<const float4 *>(kn + i * kK + d);
-                const float4 z = *reinterpret_cast<const float4 *>(Go + i * kK + d);
-                sm.k[i][d] = y.x; sm.k[i][d + 1] = y.y; sm.k[i][d + 2] = y.z; sm.k[i][d + 3] = y.w;
-                sm.G[i][d] = z.x; sm.G[i][d + 1] = z.y; sm.G[i][d + 2] = z.z; sm.G[i][d + 3] = z.w;
+            if (qt < 2) {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    sm.k[row][32 * qt + e] = kv[e];
+                    sm.G[row][32 * qt + e] = gv[e];
+                }
             }
             __syncthreads();
         }
