@@ -658,7 +658,12 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
 
 // ---- 4. the per-chunk gradient -----------------------------------------------
 
-constexpr int kMainThreads = 512;  // 8 waves: row block w = wave & 3, column half hf = wave >> 2
+constexpr int kMainQ = 4;                      // column groups
+constexpr int kMainThreads = 256 * kMainQ;     // waves: row block w = wave & 3, column group cq = wave >> 2
+constexpr int kMainNC = 8 / kMainQ;            // 16-column tiles of a wave in the 64 x 128 results
+constexpr int kMainJT = 4 / kMainQ;            // 16-column tiles of a wave in the 64 x 64 results
+constexpr int kMainSegs = kMainThreads / kK;   // row segments of the reverse cumulative sum
+constexpr int kMainTPR = kMainThreads / kK;    // threads per state row when staging dS'
 constexpr int kRP = 132;           // row pitch of the 128-column tiles
 constexpr int kTP = 68;            // row pitch of the 64 x 64 tiles
 
@@ -671,12 +676,12 @@ struct MainSmem {
         uint16_t D[kChunk][136];     // dO, bf16 (P4-P6)
     } t;
     float b[kChunk];
-    float db[2][kChunk];    // per column half
-    float rs[2][2][kChunk]; // row sums qhat . dqhat and khat . dkhat, per column half
+    float db[kMainQ][kChunk];      // per column group
+    float rs[2][kMainQ][kChunk];   // row sums qhat . dqhat and khat . dkhat, per column group
     float red[4][kK];       // column sums per row block
     float gns[kK];          // exp(G_n) * sum_v S * dS'
-    float tot[4][kK];       // segment totals of the reverse cumulative sum
-    float pa[8];            // per-wave dA_log sums
+    float tot[kMainSegs][kK];      // segment totals of the reverse cumulative sum
+    float pa[4 * kMainQ];          // per-wave dA_log sums
 };
 
 // The same pointer, hidden from the compiler: loads through it are not merged
@@ -712,7 +717,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     const int64_t H = a.H;
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int w = wv & 3, hf = wv >> 2;
+    const int w = wv & 3, cq = wv >> 2;
     const int lane = tid & 63, r = lane & 15, gq = lane >> 4;
     // Every buffer the kernel touches is distinct, and saying so lets the compiler
     // issue the epilogues' loads ahead of their stores instead of one after another.
@@ -750,22 +755,22 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     const int64_t obase = (t0 * H + h) * kK;
     auto out_at = [&](int i, int d) -> int64_t { return obase + i * HK + d; };
 
-    // wave (w, hf) owns rows 16 w .. 16 w + 15 and column tiles ct = 4 hf + c
-    // (c = 0..3) of every 64 x 128 result; lane (r, gq) holds rows 16 w + 4 gq + e
+    // wave (w, cq) owns rows 16 w .. 16 w + 15 and column tiles ct = kMainNC cq + c
+    // (c < kMainNC) of every 64 x 128 result; lane (r, gq) holds rows 16 w + 4 gq + e
     // of column 16 ct + r.  The gradients of qhat, khat and G accumulate in
     // registers, each element in its owning lane.
     const int row0 = 16 * w + 4 * gq;  // + e
-    f4 dG[4], dqh[4], dkh[4];
+    f4 dG[kMainNC], dqh[kMainNC], dkh[kMainNC];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) { dG[c] = f4{0, 0, 0, 0}; dqh[c] = dG[c]; dkh[c] = dG[c]; }
+    for (int c = 0; c < kMainNC; ++c) { dG[c] = f4{0, 0, 0, 0}; dqh[c] = dG[c]; dkh[c] = dG[c]; }
 
     // P0: T, b, gamma Khat and S into LDS
     for (int idx = tid; idx < kChunk * kChunk; idx += kMainThreads)
         sm.t.T[idx >> 6][idx & 63] = Tm[idx];
     if (tid < kChunk) {
         sm.b[tid] = bbv[tid];
-        sm.db[0][tid] = 0.f;
-        sm.db[1][tid] = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < kMainQ; ++g2) sm.db[g2][tid] = 0.f;
     }
     stage_rows(sm.U, kn, kChunk, tid, [&](int i, int d, float x) { return x * __expf(G[i * kK + d]); });
     stage_rows(sm.SB, S, kK, tid, ident);
@@ -773,61 +778,61 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 
     // P1: Diag(b) Y, Y = V - (gamma Khat) S
     {
-        f4 acc[4];
+        f4 acc[kMainNC];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
+        for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
 #pragma unroll 4
         for (int ks = 0; ks < 32; ++ks) {
             const float av = sm.U[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = mma(av, sm.SB[4 * ks + gq][16 * (4 * hf + c) + r], acc[c]);
+            for (int c = 0; c < kMainNC; ++c) acc[c] = mma(av, sm.SB[4 * ks + gq][16 * (kMainNC * cq + c) + r], acc[c]);
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < kMainNC; ++c)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
+                const int ii = row0 + e, d = 16 * (kMainNC * cq + c) + r;
                 sm.Z[ii][d] = sm.b[ii] * (vval(ii, d) - acc[c][e]);
             }
     }
     __syncthreads();
     // P2: Ut = T (Diag(b) Y); T[i][j] = 0 for j > i
     {
-        f4 acc[4];
+        f4 acc[kMainNC];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
+        for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
 #pragma unroll 4
         for (int ks = 0; ks < 4 * (w + 1); ++ks) {
             const float av = sm.t.T[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = mma(av, sm.Z[4 * ks + gq][16 * (4 * hf + c) + r], acc[c]);
+            for (int c = 0; c < kMainNC; ++c) acc[c] = mma(av, sm.Z[4 * ks + gq][16 * (kMainNC * cq + c) + r], acc[c]);
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < kMainNC; ++c)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.U[row0 + e][16 * (4 * hf + c) + r] = acc[c][e];
+            for (int e = 0; e < 4; ++e) sm.U[row0 + e][16 * (kMainNC * cq + c) + r] = acc[c][e];
     }
     __syncthreads();
     stage_rows(sm.Z, dUt, kChunk, tid, ident);
     __syncthreads();
     // P3: Z = T^T dUt; dv = Diag(b) Z; db += Z . v
     {
-        f4 acc[4];
+        f4 acc[kMainNC];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
+        for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
 #pragma unroll 4
         for (int ks = 4 * w; ks < 16; ++ks) {
             const float av = sm.t.T[4 * ks + gq][16 * w + r];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = mma(av, sm.Z[4 * ks + gq][16 * (4 * hf + c) + r], acc[c]);
+            for (int c = 0; c < kMainNC; ++c) acc[c] = mma(av, sm.Z[4 * ks + gq][16 * (kMainNC * cq + c) + r], acc[c]);
         }
         __syncthreads();  // every wave has read dUt
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < kMainNC; ++c)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
+                const int ii = row0 + e, d = 16 * (kMainNC * cq + c) + r;
                 const float z = acc[c][e];
                 sm.Z[ii][d] = z;
                 if (ii < L) {
@@ -838,7 +843,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float s = sum16(dbp[e]);
-            if (r == 0) sm.db[hf][row0 + e] += s;
+            if (r == 0) sm.db[cq][row0 + e] += s;
         }
     }
     __syncthreads();
@@ -853,26 +858,26 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     // P4: dQg = scale dO S^T and Zw = -Z S^T
     {
         const float *__restrict__ qn = opaque(qn_all), *__restrict__ kn = opaque(kn_all), *__restrict__ G = opaque(G_all);
-        f4 aq[4], az[4];
+        f4 aq[kMainNC], az[kMainNC];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) { aq[c] = f4{0, 0, 0, 0}; az[c] = aq[c]; }
+        for (int c = 0; c < kMainNC; ++c) { aq[c] = f4{0, 0, 0, 0}; az[c] = aq[c]; }
 #pragma unroll 4
         for (int ks = 0; ks < 32; ++ks) {
             const float a1 = dov_a(4 * ks + gq);
             const float a2 = sm.Z[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float bv = sm.SB[16 * (4 * hf + c) + r][4 * ks + gq];
+            for (int c = 0; c < kMainNC; ++c) {
+                const float bv = sm.SB[16 * (kMainNC * cq + c) + r][4 * ks + gq];
                 aq[c] = mma(a1, bv, aq[c]);
                 az[c] = mma(a2, bv, az[c]);
             }
         }
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < kMainNC; ++c)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
+                const int ii = row0 + e, d = 16 * (kMainNC * cq + c) + r;
                 const float qh = qn[ii * kK + d], kh = kn[ii * kK + d];
                 const float gam = __expf(G[ii * kK + d]);
                 const float bi = sm.b[ii];
@@ -885,45 +890,46 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float s = sum16(dbp[e]);
-            if (r == 0) sm.db[hf][row0 + e] += s;
+            if (r == 0) sm.db[cq][row0 + e] += s;
         }
     }
     __syncthreads();
     // dS' into LDS; exp(G_n) sum_v S[d][v] dS'[d][v] on the way (four threads per state row)
     {
-        const int d = tid >> 2, qt = tid & 3;
-        const float *sr = S + d * kV + 32 * qt, *dr = dSp + d * kV + 32 * qt;
+        constexpr int kCols = kV / kMainTPR;
+        const int d = tid / kMainTPR, qt = tid % kMainTPR;
+        const float *sr = S + d * kV + kCols * qt, *dr = dSp + d * kV + kCols * qt;
         float s = 0.f;
 #pragma unroll
-        for (int c4 = 0; c4 < 32; c4 += 4) {
+        for (int c4 = 0; c4 < kCols; c4 += 4) {
             const float4 x = *reinterpret_cast<const float4 *>(sr + c4);
             const float4 y = *reinterpret_cast<const float4 *>(dr + c4);
             s += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
-            sm.SB[d][32 * qt + c4] = y.x;
-            sm.SB[d][32 * qt + c4 + 1] = y.y;
-            sm.SB[d][32 * qt + c4 + 2] = y.z;
-            sm.SB[d][32 * qt + c4 + 3] = y.w;
+            sm.SB[d][kCols * qt + c4] = y.x;
+            sm.SB[d][kCols * qt + c4 + 1] = y.y;
+            sm.SB[d][kCols * qt + c4 + 2] = y.z;
+            sm.SB[d][kCols * qt + c4 + 3] = y.w;
         }
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
+#pragma unroll
+        for (int o = 1; o < kMainTPR; o <<= 1) s += __shfl_xor(s, o);
         if (qt == 0) sm.gns[d] = __expf(G[(L - 1) * kK + d]) * s;
     }
     __syncthreads();
     // P5: dKbar = Ut dS'^T
     {
         const float *__restrict__ qn = opaque(qn_all), *__restrict__ kn = opaque(kn_all), *__restrict__ G = opaque(G_all);
-        f4 acc[4];
+        f4 acc[kMainNC];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = f4{0, 0, 0, 0};
+        for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
 #pragma unroll 4
         for (int ks = 0; ks < 32; ++ks) {
             const float av = sm.U[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = mma(av, sm.SB[16 * (4 * hf + c) + r][4 * ks + gq], acc[c]);
+            for (int c = 0; c < kMainNC; ++c) acc[c] = mma(av, sm.SB[16 * (kMainNC * cq + c) + r][4 * ks + gq], acc[c]);
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int d = 16 * (4 * hf + c) + r;
+        for (int c = 0; c < kMainNC; ++c) {
+            const int d = 16 * (kMainNC * cq + c) + r;
             const float Gn = G[(L - 1) * kK + d];
             float colp = 0.f;
 #pragma unroll
@@ -942,19 +948,19 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     }
     __syncthreads();
     // P6: dA_qk = scale dO Ut^T (j <= i), dA_kk = -Z Ut^T (j < i); db += dA_kk . M;
-    // dM = Diag(b) dA_kk.  Wave (w, hf) takes column tiles jt = 2 hf, 2 hf + 1.
+    // dM = Diag(b) dA_kk.  Wave (w, cq) takes column tiles jt = kMainJT cq + jj.
     {
-        f4 accA[2], accK[2];
+        f4 accA[kMainJT], accK[kMainJT];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) { accA[jj] = f4{0, 0, 0, 0}; accK[jj] = accA[jj]; }
-        if (2 * hf <= w) {
+        for (int jj = 0; jj < kMainJT; ++jj) { accA[jj] = f4{0, 0, 0, 0}; accK[jj] = accA[jj]; }
+        if (kMainJT * cq <= w) {
 #pragma unroll 4
             for (int ks = 0; ks < 32; ++ks) {
                 const float a1 = dov_a(4 * ks + gq);
                 const float a2 = sm.Z[16 * w + r][4 * ks + gq];
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int jt = 2 * hf + jj;
+                for (int jj = 0; jj < kMainJT; ++jj) {
+                    const int jt = kMainJT * cq + jj;
                     if (jt <= w) {
                         const float bv = sm.U[16 * jt + r][4 * ks + gq];
                         accA[jj] = mma(a1, bv, accA[jj]);
@@ -965,10 +971,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         }
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int jj = 0; jj < kMainJT; ++jj)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int jt = 2 * hf + jj;
+                const int jt = kMainJT * cq + jj;
                 const int ii = row0 + e, j = 16 * jt + r;
                 const float dAq = (jt <= w && j <= ii) ? scale * accA[jj][e] : 0.f;
                 const float dAk = (jt <= w && j < ii) ? -accK[jj][e] : 0.f;
@@ -979,7 +985,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float s = sum16(dbp[e]);
-            if (r == 0) sm.db[hf][row0 + e] += s;
+            if (r == 0) sm.db[cq][row0 + e] += s;
         }
     }
     __syncthreads();
@@ -994,31 +1000,31 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         const float(*kh)[kRP] = sm.U;
         const float(*Gs)[kRP] = sm.Z;
         const float(*qh)[kRP] = &sm.SB[kChunk];
-        float refc[4];  // G at the reference row 16 w + 8, this lane's columns
+        float refc[kMainNC];  // G at the reference row 16 w + 8, this lane's columns
 #pragma unroll
-        for (int c = 0; c < 4; ++c) refc[c] = Gs[16 * w + 8][16 * (4 * hf + c) + r];
+        for (int c = 0; c < kMainNC; ++c) refc[c] = Gs[16 * w + 8][16 * (kMainNC * cq + c) + r];
         // rows i of block w: sum_{j <= 16 w + 15} dP[i][j] y_j exp(ref - G_j), times exp(G_i - ref)
         {
-            f4 rm[4], ra[4];
+            f4 rm[kMainNC], ra[kMainNC];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) { rm[c] = f4{0, 0, 0, 0}; ra[c] = rm[c]; }
+            for (int c = 0; c < kMainNC; ++c) { rm[c] = f4{0, 0, 0, 0}; ra[c] = rm[c]; }
 #pragma unroll 2
             for (int ks = 0; ks < 4 * (w + 1); ++ks) {
                 const int j = 4 * ks + gq;
                 const float a1 = sm.SB[16 * w + r][j], a2 = sm.SB[16 * w + r][64 + j];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int d = 16 * (4 * hf + c) + r;
+                for (int c = 0; c < kMainNC; ++c) {
+                    const int d = 16 * (kMainNC * cq + c) + r;
                     const float bv = kh[j][d] * __expf(refc[c] - Gs[j][d]);
                     rm[c] = mma(a1, bv, rm[c]);
                     ra[c] = mma(a2, bv, ra[c]);
                 }
             }
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < kMainNC; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
+                    const int ii = row0 + e, d = 16 * (kMainNC * cq + c) + r;
                     const float s = __expf(Gs[ii][d] - refc[c]);
                     const float RxM = rm[c][e] * s, RxA = ra[c][e] * s;
                     dkh[c][e] += RxM;
@@ -1029,26 +1035,26 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         // columns j of block w: sum_{i >= 16 w} (dM[i][j] khat_i + dA_qk[i][j] qhat_i) exp(G_i - ref),
         // times exp(ref - G_j)
         {
-            f4 ry[4];
+            f4 ry[kMainNC];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) ry[c] = f4{0, 0, 0, 0};
+            for (int c = 0; c < kMainNC; ++c) ry[c] = f4{0, 0, 0, 0};
 #pragma unroll 2
             for (int ks = 4 * w; ks < 16; ++ks) {
                 const int i = 4 * ks + gq;
                 const float a1 = sm.SB[i][16 * w + r], a2 = sm.SB[i][64 + 16 * w + r];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int d = 16 * (4 * hf + c) + r;
+                for (int c = 0; c < kMainNC; ++c) {
+                    const int d = 16 * (kMainNC * cq + c) + r;
                     const float eg = __expf(Gs[i][d] - refc[c]);
                     ry[c] = mma(a1, kh[i][d] * eg, ry[c]);
                     ry[c] = mma(a2, qh[i][d] * eg, ry[c]);
                 }
             }
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < kMainNC; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int jj = row0 + e, d = 16 * (4 * hf + c) + r;
+                    const int jj = row0 + e, d = 16 * (kMainNC * cq + c) + r;
                     const float Ry = ry[c][e] * __expf(refc[c] - Gs[jj][d]);
                     dkh[c][e] += Ry;
                     dG[c][e] -= kh[jj][d] * Ry;
@@ -1058,29 +1064,31 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     __syncthreads();
     // P8: dG_n into the last valid row, then da_t = sum_{i >= t} dG_i
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < kMainNC; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int ii = row0 + e, d = 16 * (4 * hf + c) + r;
+            const int ii = row0 + e, d = 16 * (kMainNC * cq + c) + r;
             float v = dG[c][e];
             if (ii == L - 1) v += sm.gns[d] + sm.red[0][d] + sm.red[1][d] + sm.red[2][d] + sm.red[3][d];
             sm.Z[ii][d] = ii < L ? v : 0.f;
         }
     __syncthreads();
-    {  // four threads per column, 16 rows each: sums within the segment, then the later segments' totals
-        const int d = tid & (kK - 1), sg = tid >> 7;
+    {  // kMainSegs threads per column, each a segment of rows: sums within the segment, then the
+       // later segments' totals
+        constexpr int kSR = kChunk / kMainSegs;
+        const int d = tid & (kK - 1), sg = tid / kK;
         float run = 0.f;
 #pragma unroll
-        for (int i = 16 * sg + 15; i >= 16 * sg; --i) {
+        for (int i = kSR * sg + kSR - 1; i >= kSR * sg; --i) {
             run += sm.Z[i][d];
             sm.Z[i][d] = run;
         }
         sm.tot[sg][d] = run;
         __syncthreads();
         float carry = 0.f;
-        for (int s2 = sg + 1; s2 < 4; ++s2) carry += sm.tot[s2][d];
+        for (int s2 = sg + 1; s2 < kMainSegs; ++s2) carry += sm.tot[s2][d];
 #pragma unroll
-        for (int i = 16 * sg; i < 16 * sg + 16; ++i) sm.Z[i][d] += carry;
+        for (int i = kSR * sg; i < kSR * sg + kSR; ++i) sm.Z[i][d] += carry;
     }
     // P9: norms, gate, outputs.  Row sums of qhat . dqhat and khat . dkhat first
     // (khat and qhat are still in LDS from P7).
@@ -1093,8 +1101,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         float a1 = 0.f, a2 = 0.f;
         if (ii < L) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int d = 16 * (4 * hf + c) + r;
+            for (int c = 0; c < kMainNC; ++c) {
+                const int d = 16 * (kMainNC * cq + c) + r;
                 a1 += qh[ii][d] * dqh[c][e];
                 a2 += kh[ii][d] * dkh[c][e];
             }
@@ -1102,8 +1110,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         a1 = sum16(a1);
         a2 = sum16(a2);
         if (r == 0) {
-            sm.rs[0][hf][ii] = a1;
-            sm.rs[1][hf][ii] = a2;
+            sm.rs[0][cq][ii] = a1;
+            sm.rs[1][cq][ii] = a2;
         }
     }
     __syncthreads();
@@ -1111,8 +1119,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         const float nA = -expf(a.A_log[h]);
         float pa = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int d = 16 * (4 * hf + c) + r;
+        for (int c = 0; c < kMainNC; ++c) {
+            const int d = 16 * (kMainNC * cq + c) + r;
             const float dtb = dtb_h[d];
             float colp = 0.f;
 #pragma unroll
@@ -1120,8 +1128,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                 const int ii = row0 + e;
                 if (ii < L) {
                     const int64_t o = out_at(ii, d);
-                    const float sq = sm.rs[0][0][ii] + sm.rs[0][1][ii];
-                    const float sk = sm.rs[1][0][ii] + sm.rs[1][1][ii];
+                    float sq = 0.f, sk = 0.f;
+#pragma unroll
+                    for (int g2 = 0; g2 < kMainQ; ++g2) { sq += sm.rs[0][g2][ii]; sk += sm.rs[1][g2][ii]; }
                     const float rq = rqv[ii], rk = rkv[ii];
                     dqo[o] = rq * (dqh[c][e] - sq * qh[ii][d]);
                     dko[o] = rk * (dkh[c][e] - sk * kh[ii][d]);
@@ -1148,12 +1157,15 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     if (tid < kK) part[tid] = sm.red[0][tid] + sm.red[1][tid] + sm.red[2][tid] + sm.red[3][tid];
     if (tid == kK) {
         float s = 0.f;
-        for (int i = 0; i < 8; ++i) s += sm.pa[i];
+        for (int i = 0; i < 4 * kMainQ; ++i) s += sm.pa[i];
         part[kK] = s;
     }
     if (tid < L) {
         const float b = sm.b[tid];
-        dbo[(t0 + tid) * H + h] = (sm.db[0][tid] + sm.db[1][tid]) * b * (1.f - b);
+        float dbs = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < kMainQ; ++g2) dbs += sm.db[g2][tid];
+        dbo[(t0 + tid) * H + h] = dbs * b * (1.f - b);
     }
 }
 
