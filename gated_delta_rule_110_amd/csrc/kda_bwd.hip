@@ -67,6 +67,26 @@ __device__ __forceinline__ float softplus_fast(float x) {
     return x > 15.0f ? x : sp;
 }
 
+// Eight fp32 values split into bf16 hi + lo operands (hi + lo carries about 16 bits of
+// the significand, so a product of two split operands, the lo * lo term dropped, is good to
+// about 2^-16 relative).
+__device__ __forceinline__ void split8r(const float *x, s8 &hi, s8 &lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        short h, l;
+        split_bf16(x[e], h, l);
+        hi[e] = h;
+        lo[e] = l;
+    }
+}
+// ... of eight consecutive fp32 values (16-byte aligned).
+__device__ __forceinline__ void split8(const float *p, s8 &hi, s8 &lo) {
+    const float4 x0 = *reinterpret_cast<const float4 *>(p);
+    const float4 x1 = *reinterpret_cast<const float4 *>(p + 4);
+    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    split8r(x, hi, lo);
+}
+
 // Sum over the 16 lanes of a row group (lanes r = 0..15 with the same g).
 __device__ __forceinline__ float sum16(float x) {
     x += __shfl_xor(x, 1);
@@ -792,11 +812,23 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         f4 acc[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
-#pragma unroll 4
-        for (int ks = 0; ks < 32; ++ks) {
-            const float av = sm.U[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int c = 0; c < kMainNC; ++c) acc[c] = mma(av, sm.SB[4 * ks + gq][16 * (kMainNC * cq + c) + r], acc[c]);
+        for (int ks = 0; ks < 4; ++ks) {
+            const int k0 = 32 * ks + 8 * gq;
+            s8 ah, al;
+            split8(&sm.U[16 * w + r][k0], ah, al);
+#pragma unroll
+            for (int c = 0; c < kMainNC; ++c) {
+                const int col = 16 * (kMainNC * cq + c) + r;
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = sm.SB[k0 + e][col];
+                s8 bh, bl;
+                split8r(x, bh, bl);
+                acc[c] = mfma16x16x32_bf16(ah, bh, acc[c]);
+                acc[c] = mfma16x16x32_bf16(ah, bl, acc[c]);
+                acc[c] = mfma16x16x32_bf16(al, bh, acc[c]);
+            }
         }
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c)
@@ -812,11 +844,23 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         f4 acc[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
-#pragma unroll 4
-        for (int ks = 0; ks < 4 * (w + 1); ++ks) {
-            const float av = sm.t.T[16 * w + r][4 * ks + gq];
+        // k = j < 32 (w + 2) / 2 covers j <= 16 w + 15 (the rest of T's row is zero)
+        for (int ks = 0; ks < (w + 2) / 2; ++ks) {
+            const int k0 = 32 * ks + 8 * gq;
+            s8 th, tl;
+            split8(&sm.t.T[16 * w + r][k0], th, tl);
 #pragma unroll
-            for (int c = 0; c < kMainNC; ++c) acc[c] = mma(av, sm.Z[4 * ks + gq][16 * (kMainNC * cq + c) + r], acc[c]);
+            for (int c = 0; c < kMainNC; ++c) {
+                const int col = 16 * (kMainNC * cq + c) + r;
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = sm.Z[k0 + e][col];
+                s8 bh, bl;
+                split8r(x, bh, bl);
+                acc[c] = mfma16x16x32_bf16(th, bh, acc[c]);
+                acc[c] = mfma16x16x32_bf16(th, bl, acc[c]);
+                acc[c] = mfma16x16x32_bf16(tl, bh, acc[c]);
+            }
         }
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c)
@@ -831,11 +875,26 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         f4 acc[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
-#pragma unroll 4
-        for (int ks = 4 * w; ks < 16; ++ks) {
-            const float av = sm.t.T[4 * ks + gq][16 * w + r];
+        // k = i >= 32 (w / 2) covers i >= 16 w (T[i][j] is zero for i < j)
+        for (int ks = w / 2; ks < 2; ++ks) {
+            const int k0 = 32 * ks + 8 * gq;
+            float y[8];
 #pragma unroll
-            for (int c = 0; c < kMainNC; ++c) acc[c] = mma(av, sm.Z[4 * ks + gq][16 * (kMainNC * cq + c) + r], acc[c]);
+            for (int e = 0; e < 8; ++e) y[e] = sm.t.T[k0 + e][16 * w + r];
+            s8 th, tl;
+            split8r(y, th, tl);
+#pragma unroll
+            for (int c = 0; c < kMainNC; ++c) {
+                const int col = 16 * (kMainNC * cq + c) + r;
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = sm.Z[k0 + e][col];
+                s8 bh, bl;
+                split8r(x, bh, bl);
+                acc[c] = mfma16x16x32_bf16(th, bh, acc[c]);
+                acc[c] = mfma16x16x32_bf16(th, bl, acc[c]);
+                acc[c] = mfma16x16x32_bf16(tl, bh, acc[c]);
+            }
         }
         __syncthreads();  // every wave has read dUt
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};
@@ -872,15 +931,24 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         f4 aq[kMainNC], az[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) { aq[c] = f4{0, 0, 0, 0}; az[c] = aq[c]; }
-#pragma unroll 4
-        for (int ks = 0; ks < 32; ++ks) {
-            const float a1 = dov_a(4 * ks + gq);
-            const float a2 = sm.Z[16 * w + r][4 * ks + gq];
+        // bf16 16x16x32 products, lane (r, gq) holding k = 32 ks + 8 gq .. + 7: dO is bf16
+        // already, S and Z are split into bf16 hi + lo (S twice, Z S^T three times: products
+        // good to about 2^-16, the lo * lo term dropped)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int k0 = 32 * ks + 8 * gq;
+            const s8 a1 = __builtin_bit_cast(s8, *reinterpret_cast<const uint4 *>(&sm.t.D[16 * w + r][k0]));
+            s8 zh, zl;
+            split8(&sm.Z[16 * w + r][k0], zh, zl);
 #pragma unroll
             for (int c = 0; c < kMainNC; ++c) {
-                const float bv = sm.SB[16 * (kMainNC * cq + c) + r][4 * ks + gq];
-                aq[c] = mma(a1, bv, aq[c]);
-                az[c] = mma(a2, bv, az[c]);
+                s8 sh, sl;
+                split8(&sm.SB[16 * (kMainNC * cq + c) + r][k0], sh, sl);
+                aq[c] = mfma16x16x32_bf16(a1, sh, aq[c]);
+                aq[c] = mfma16x16x32_bf16(a1, sl, aq[c]);
+                az[c] = mfma16x16x32_bf16(zh, sh, az[c]);
+                az[c] = mfma16x16x32_bf16(zh, sl, az[c]);
+                az[c] = mfma16x16x32_bf16(zl, sh, az[c]);
             }
         }
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};
@@ -905,7 +973,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         }
     }
     __syncthreads();
-    // dS' into LDS; exp(G_n) sum_v S[d][v] dS'[d][v] on the way (four threads per state row)
+    // dS' into LDS; exp(G_n) sum_v S[d][v] dS'[d][v] on the way (kMainTPR threads per state row)
     {
         constexpr int kCols = kV / kMainTPR;
         const int d = tid / kMainTPR, qt = tid % kMainTPR;
@@ -932,11 +1000,19 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         f4 acc[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
-#pragma unroll 4
-        for (int ks = 0; ks < 32; ++ks) {
-            const float av = sm.U[16 * w + r][4 * ks + gq];
 #pragma unroll
-            for (int c = 0; c < kMainNC; ++c) acc[c] = mma(av, sm.SB[16 * (kMainNC * cq + c) + r][4 * ks + gq], acc[c]);
+        for (int ks = 0; ks < 4; ++ks) {
+            const int k0 = 32 * ks + 8 * gq;
+            s8 uh, ul;
+            split8(&sm.U[16 * w + r][k0], uh, ul);
+#pragma unroll
+            for (int c = 0; c < kMainNC; ++c) {
+                s8 dh, dl;
+                split8(&sm.SB[16 * (kMainNC * cq + c) + r][k0], dh, dl);
+                acc[c] = mfma16x16x32_bf16(uh, dh, acc[c]);
+                acc[c] = mfma16x16x32_bf16(uh, dl, acc[c]);
+                acc[c] = mfma16x16x32_bf16(ul, dh, acc[c]);
+            }
         }
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) {
@@ -965,17 +1041,23 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll
         for (int jj = 0; jj < kMainJT; ++jj) { accA[jj] = f4{0, 0, 0, 0}; accK[jj] = accA[jj]; }
         if (kMainJT * cq <= w) {
-#pragma unroll 4
-            for (int ks = 0; ks < 32; ++ks) {
-                const float a1 = dov_a(4 * ks + gq);
-                const float a2 = sm.Z[16 * w + r][4 * ks + gq];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int k0 = 32 * ks + 8 * gq;
+                const s8 a1 = __builtin_bit_cast(s8, *reinterpret_cast<const uint4 *>(&sm.t.D[16 * w + r][k0]));
+                s8 zh, zl;
+                split8(&sm.Z[16 * w + r][k0], zh, zl);
 #pragma unroll
                 for (int jj = 0; jj < kMainJT; ++jj) {
                     const int jt = kMainJT * cq + jj;
                     if (jt <= w) {
-                        const float bv = sm.U[16 * jt + r][4 * ks + gq];
-                        accA[jj] = mma(a1, bv, accA[jj]);
-                        accK[jj] = mma(a2, bv, accK[jj]);
+                        s8 uh, ul;
+                        split8(&sm.U[16 * jt + r][k0], uh, ul);
+                        accA[jj] = mfma16x16x32_bf16(a1, uh, accA[jj]);
+                        accA[jj] = mfma16x16x32_bf16(a1, ul, accA[jj]);
+                        accK[jj] = mfma16x16x32_bf16(zh, uh, accK[jj]);
+                        accK[jj] = mfma16x16x32_bf16(zh, ul, accK[jj]);
+                        accK[jj] = mfma16x16x32_bf16(zl, uh, accK[jj]);
                     }
                 }
             }
