@@ -1088,7 +1088,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     stage_rows(&sm.SB[kChunk], qn, kChunk, tid, ident);
     __syncthreads();
     // P7: the decayed Gram matrices P[i][j] = sum_d x_i y_j exp(G_i - G_j): for M
-    // (x = y = khat, gradient dM) and A_qk (x = qhat, y = khat, gradient dA_qk)
+    // (x = y = khat, gradient dM) and A_qk (x = qhat, y = khat, gradient dA_qk).  These stay on
+    // the fp32 matrix cores: the gate's gradient is a difference of these decay-weighted sums,
+    // which cancel, and bf16 hi + lo products (about 2^-16) put dA_log past 5e-3 relative.
     {
         const float(*kh)[kRP] = sm.U;
         const float(*Gs)[kRP] = sm.Z;
