@@ -360,7 +360,9 @@ def bench_bwd(kda, args, dev, wname) -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
                      "alg_flops": flops[dom] * tok_heads, "traffic": load_traffic("bwd_" + wname, dom),
                      "limiter": load_limiter(dom), "kernels": per_kernel},
-        "mfma_operands": "fp32 (16x16x4) for every gradient product; the recomputed forward as kda_fwd",
+        "mfma_operands": ("per-chunk gradient: bf16 hi + lo splits of the fp32 operands (16x16x32) against S, dS', "
+                          "Ut, T, dUt, fp32 (16x16x4) for the Gram gradients; preparation fp32; reverse chain fp16; "
+                          "the recomputed forward as kda_fwd"),
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -30,10 +30,14 @@
 //      and beta;
 //   5. kda_bwd_params_kernel: dA_log and ddt_bias, summed over the chunks.
 //
-// The per-chunk kernels run their products on the fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32): lane (r, g) gives A[r][g] and B[g][r] of a 16x16x4
-// step and holds C[4 g + e][r], so an operand can be read element by element
-// from any layout.  The reverse chain, whose steps are serial, runs the fp16
+// The preparation kernel and the per-chunk gradient's Gram-gradient phase run
+// their products on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): lane (r, g)
+// gives A[r][g] and B[g][r] of a 16x16x4 step and holds C[4 g + e][r], so an
+// operand can be read element by element from any layout.  The per-chunk
+// gradient's other products (against S, dS', Ut, T and dUt) run on bf16
+// 16x16x32 MFMAs with each fp32 operand split into bf16 hi + lo (dO is bf16
+// already): three products (two against dO), good to about 2^-16 relative, in
+// the same C layout.  The reverse chain, whose steps are serial, runs the fp16
 // 16x16x16 product with fp32 accumulation on its fp16 operand block.
 //
 // Decay factors exp(G_i - G_j) inside a chunk are split around a reference

@@ -303,8 +303,9 @@ size_t kda_bwd_workspace_size(const kda_desc_t *desc);
  * launch_piece and the workspace rules are as for kda_fwd, with
  * kda_bwd_workspace_size() in place of kda_fwd_workspace_size().  The
  * forward's value range applies, and d_out must stay within fp16's range
- * (|d_out| < 65504): the reverse state chain takes it as an fp16 operand.  Gradients are computed on the fp32 matrix
- * cores from the forward's fp16 intermediates and states. */
+ * (|d_out| < 65504): the reverse state chain takes it as an fp16 operand.  Gradients are computed from the
+ * forward's fp16 intermediates and states on the matrix cores: fp32 products, or bf16 hi + lo splits of the
+ * fp32 operands (good to about 2^-16 relative) where the sums do not cancel. */
 kda_status_t kda_bwd(const void *q, const void *k, const void *v, const void *g,
                      const void *beta, float scale, const float *A_log,
                      const float *dt_bias, float lower_bound,
