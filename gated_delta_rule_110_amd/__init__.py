@@ -26,7 +26,7 @@ from ._build import LIB as LIB_PATH
 from ._build import build
 
 __all__ = ["fwd", "fwd_noalloc", "noalloc_max_workspace", "decode", "bwd", "bwd_workspace_size",
-           "workspace_size", "chain_segments_for",
+           "kda_attention", "KdaFunction", "workspace_size", "chain_segments_for",
            "pipelined_for", "KdaArgumentError", "library", "KdaError", "build", "LIB_PATH", "KDA_BF16",
            "KDA_FP32"]
 
@@ -340,6 +340,58 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     if st != 0:
         _raise_status(lib, st)
     return res
+
+
+class KdaFunction(torch.autograd.Function):
+    """``fwd`` with ``bwd`` as its gradient, for autograd.  Inputs as for ``fwd``
+    (q, k, v, g, beta bf16; A_log, dt_bias fp32; initial_state bf16, fp32 or
+    None); ``final_dtype`` is the dtype of the returned final state, or None for
+    no final state.  The gradients come from one ``kda_bwd`` call, in fp32,
+    cast to each input's dtype."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, A_log, dt_bias, initial_state, scale, lower_bound, cu_seqlens,
+                final_dtype, chain_segments):
+        final = None
+        if final_dtype is not None:
+            B, T, H, K = q.shape
+            N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+            final = torch.empty((N, H, K, v.shape[-1]), dtype=final_dtype, device=q.device)
+        out, fin = fwd(q, k, v, g, beta, scale, None, A_log, dt_bias, lower_bound, initial_state, final,
+                       cu_seqlens, chain_segments=chain_segments)
+        ctx.save_for_backward(q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens)
+        ctx.scale, ctx.lower_bound, ctx.chain_segments = float(scale), float(lower_bound), int(chain_segments)
+        return out, fin
+
+    @staticmethod
+    def backward(ctx, d_out, d_fin):
+        q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens = ctx.saved_tensors
+        if d_out is None:
+            d_out = torch.zeros(v.shape, dtype=torch.bfloat16, device=v.device)
+        d_out = d_out.to(torch.bfloat16).contiguous()
+        if d_fin is not None:
+            d_fin = d_fin.contiguous()
+        want_h0 = initial_state is not None and ctx.needs_input_grad[7]
+        res = bwd(q, k, v, g, beta, ctx.scale, A_log, dt_bias, ctx.lower_bound, d_out, d_final_state=d_fin,
+                  initial_state=initial_state, cu_seqlens=cu_seqlens, chain_segments=ctx.chain_segments,
+                  with_d_initial=want_h0)
+        d_h0 = res["d_initial_state"].to(initial_state.dtype) if want_h0 else None
+        return (res["dq"].to(q.dtype), res["dk"].to(k.dtype), res["dv"].to(v.dtype), res["dg"].to(g.dtype),
+                res["dbeta"].to(beta.dtype), res["dA_log"], res["ddt_bias"], d_h0,
+                None, None, None, None, None)
+
+
+def kda_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                  scale: float, A_log: torch.Tensor, dt_bias: torch.Tensor, lower_bound: float,
+                  initial_state: Optional[torch.Tensor] = None, final_state_dtype: Optional[torch.dtype] = None,
+                  cu_seqlens: Optional[torch.Tensor] = None,
+                  chain_segments: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The KDA forward as an autograd operation (``KdaFunction``): returns
+    ``(out, final_state)``, the final state in ``final_state_dtype`` (bf16 or
+    fp32) or None, and backpropagates into q, k, v, g, beta, A_log, dt_bias and
+    the initial state through ``kda_bwd``."""
+    return KdaFunction.apply(q, k, v, g, beta, A_log, dt_bias, initial_state, scale, lower_bound, cu_seqlens,
+                             final_state_dtype, chain_segments)
 
 
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

@@ -1,0 +1,62 @@
+"""The autograd operation (kda_attention / KdaFunction): its forward is kda_fwd
+and its gradients are one kda_bwd call, cast to the inputs' dtypes, so they
+must equal that call's results exactly (kda_bwd itself is checked against the
+gradient oracle in test_gpu_bwd.py)."""
+import pytest
+import torch
+
+import gated_delta_rule_110_amd as kda
+import workloads as W
+from tests.parity import say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("case", ["fixed", "packed", "nostate", "split"])
+def test_autograd_matches_bwd(case):
+    if case == "fixed":
+        w = W.make("ag_fixed", 2, 150, 3, 7301, init="fp32", final="fp32")
+        fin, segs = "fp32", 0
+    elif case == "packed":
+        w = W.make("ag_packed", 1, 265, 2, 7302, init="bf16", final="bf16", seqlens=[37, 0, 163, 65])
+        fin, segs = "bf16", 0
+    elif case == "nostate":
+        w = W.make("ag_nostate", 1, 200, 2, 7303, init=None, final=None)
+        fin, segs = None, 0
+    else:
+        w = W.make("ag_split", 2, 64 * 12 + 5, 2, 7304, init="fp32", final="fp32")
+        fin, segs = "fp32", 3
+    say("autograd %s: B=%d T=%d H=%d N=%d" % (case, w.B, w.T, w.H, w.N))
+    d_out, d_fin = W.loss_grads(w, 7401, final=fin)
+    wd = w.to("cuda")
+    d_out, d_fin = d_out.cuda(), None if d_fin is None else d_fin.cuda()
+    leaves = {n: getattr(wd, n).detach().clone().requires_grad_(True)
+              for n in ("q", "k", "v", "g", "beta", "A_log", "dt_bias")}
+    h0 = None if wd.initial_state is None else wd.initial_state.detach().clone().requires_grad_(True)
+    out, final = kda.kda_attention(leaves["q"], leaves["k"], leaves["v"], leaves["g"], leaves["beta"], w.scale,
+                                   leaves["A_log"], leaves["dt_bias"], w.lower_bound, initial_state=h0,
+                                   final_state_dtype=None if d_fin is None else d_fin.dtype,
+                                   cu_seqlens=wd.cu_seqlens, chain_segments=segs)
+    loss = (out.float() * d_out.float()).sum()
+    if final is not None:
+        loss = loss + (final.float() * d_fin.float()).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = kda.bwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, wd.A_log, wd.dt_bias, w.lower_bound, d_out,
+                  d_final_state=d_fin, initial_state=wd.initial_state, cu_seqlens=wd.cu_seqlens,
+                  chain_segments=segs, with_d_initial=h0 is not None)
+    torch.cuda.synchronize()
+    names = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "A_log": "dA_log",
+             "dt_bias": "ddt_bias"}
+    for n, rn in names.items():
+        assert leaves[n].grad is not None, n
+        assert torch.equal(leaves[n].grad, ref[rn].to(leaves[n].dtype)), n
+    if h0 is not None:
+        assert torch.equal(h0.grad, ref["d_initial_state"].to(h0.dtype))
+    # the forward is kda_fwd's
+    o2, f2 = kda.fwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, None, wd.A_log, wd.dt_bias, w.lower_bound,
+                     wd.initial_state, None if final is None else torch.empty_like(final), wd.cu_seqlens,
+                     chain_segments=segs)
+    assert torch.equal(out, o2)
+    if final is not None:
+        assert torch.equal(final, f2)
