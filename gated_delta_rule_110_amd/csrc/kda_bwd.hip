@@ -235,7 +235,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
             }
         }
         if (qt == 0) {
-            const float b = valid ? sigmoid_fast(bf16_bits_to_f32(a.beta[(t0 + row) * H + h])) : 0.f;
+            // rows past the end read row 0's beta (in bounds) and discard it
+            const float bl = bf16_bits_to_f32(a.beta[(t0 + (valid ? row : 0)) * H + h]);
+            const float b = valid ? sigmoid_fast(bl) : 0.f;
             sm.b[row] = b;
             a.rq[ws * kChunk + row] = rq;
             a.rk[ws * kChunk + row] = rk;
@@ -781,8 +783,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     float *__restrict__ part = a.part + ws * (kK + 1);
     const float scale = a.scale;
     const auto ident = [](int, int, float x) { return x; };
-    auto vval = [&](int i, int c) -> float {
-        return i < L ? bf16_bits_to_f32(vin[((t0 + i) * H + h) * kV + c]) : 0.f;
+    auto vval = [&](int i, int c) -> float {  // v[i][c], 0 past the end (read in bounds, at row 0)
+        const float x = bf16_bits_to_f32(vin[((t0 + (i < L ? i : 0)) * H + h) * kV + c]);
+        return i < L ? x : 0.f;
     };
     // dO (the A operand of P4 and P6) from LDS, where it replaces T after P3
     auto dov_a = [&](int c) -> float { return bf16_bits_to_f32(sm.t.D[16 * w + r][c]); };
