@@ -468,7 +468,7 @@ namespace {
 
 struct BwdLayout {
     WorkspaceLayout fwd;  // the forward's intermediates (unsplit, two-kernel)
-    size_t off_out, off_hs, off_dhs, off_dUt, off_qn, off_kn, off_G, off_rq, off_rk, off_bb, off_Mk, off_Tm, off_part,
+    size_t off_hs, off_dhs, off_dUt, off_qn, off_kn, off_G, off_rq, off_rk, off_bb, off_Mk, off_Tm, off_part,
         off_co;
     size_t total;
 };
@@ -486,7 +486,6 @@ BwdLayout make_bwd_layout(const Geometry &g) {
     L.fwd = make_layout(g);
     const size_t per = (size_t)g.slots * (size_t)g.H;
     size_t o = L.fwd.total;
-    L.off_out = o;  o = align_up(o + (size_t)(g.B * g.T * g.H) * kV * 2, 256);
     L.off_hs = o;   o = align_up(o + per * kK * kV * 4, 256);
     L.off_dhs = o;  o = align_up(o + per * kK * kV * 4, 256);
     L.off_dUt = o;  o = align_up(o + per * kChunk * kV * 4, 256);
@@ -599,7 +598,7 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
         ca.scale = scale;
         ca.h0 = initial_state; ca.ht = nullptr;
         ca.h0_bf16 = desc->initial_state_dtype == KDA_BF16;
-        ca.out = reinterpret_cast<uint16_t *>(ws + lay.off_out);
+        ca.out = nullptr;  // the states only: save mode writes no outputs
         ca.hs = ba.hs;
         ca.piece_cap = desc->launch_piece;
         if (err == hipSuccess) err = launch_chains(ca, geo, fl, ws, stream);

@@ -161,10 +161,10 @@ __device__ __forceinline__ void dma_ring(ChainSmem<kCB> &sm, const ChainArgs &a,
 // workgroups of a head split the head's cache lines: copy j covers the share of
 // 16-column block vb kCB + j (one dword per 128-byte line).  The loads copy
 // into an LDS area nobody reads: no destination registers, so this wave never
-// has to wait for one except to bound how many are in flight.  Map mode reads
-// no Qg and no A_qk, so those lanes repeat a line the wave already touches
-// (one request per line and instruction).
-template <int kCB, bool kMap>
+// has to wait for one except to bound how many are in flight.  Map mode and
+// save mode read no Qg and no A_qk (kNoOut), so those lanes repeat a line the
+// wave already touches (one request per line and instruction).
+template <int kCB, bool kNoOut>
 __device__ __forceinline__ void touch_lines(ChainSmem<kCB> &sm, const ChainArgs &a, int64_t ws, int vb, int lane) {
     const char *wf = reinterpret_cast<const char *>(a.Wf + ws * kWfElems);
     const char *qf = reinterpret_cast<const char *>(a.Qf + ws * kQfElems);
@@ -178,11 +178,11 @@ __device__ __forceinline__ void touch_lines(ChainSmem<kCB> &sm, const ChainArgs 
         const int b = vb * kCB + j;
         const char *p0;  // lines 0..63 of the share: W, Qg, Kbar, U
         if (l < 16) p0 = wf + (16 * b + l) * 128;
-        else if (l < 32) p0 = kMap ? wf + (16 * b + l - 16) * 128 : qf + (16 * b + l - 16) * 128;
+        else if (l < 32) p0 = kNoOut ? wf + (16 * b + l - 16) * 128 : qf + (16 * b + l - 16) * 128;
         else if (l < 48) p0 = kf + (16 * b + l - 32) * 128;
         else p0 = uf + (16 * b + l - 48) * 128;
         const char *p1;  // lines 64..72: A_qk and exp(G_n) (lanes >= 8 share one line)
-        if (l < 8 && !kMap) p1 = af + (8 * b + l) * 128;
+        if (l < 8 && !kNoOut) p1 = af + (8 * b + l) * 128;
         else p1 = gn + (b & 3) * 128;
         lds_copy4(p0, lds_addr(&sm.dump[0][0]));
         lds_copy4(p1, lds_addr(&sm.dump[1][0]));
@@ -318,8 +318,10 @@ __device__ __forceinline__ void out_wave(ChainSmem<kCB> &sm, const ChainArgs &a,
 
 // The chain kernel's body; kMap selects map mode (ChainArgs::map_mode), which
 // is a kernel of its own so that the ordinary chain is compiled without it;
-// kSave stores the state entering every chunk to ChainArgs::hs (the backward's
-// forward pass), also a kernel of its own.
+// kSave stores the state entering every chunk to ChainArgs::hs and writes no
+// outputs (the backward's forward pass, which needs the states only), also a
+// kernel of its own: its output waves only keep the barrier count, and its L2
+// prefetch, like map mode's, skips Qg and A_qk.
 template <bool kMap, int kCB, bool kSave = false>
 __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &a) {
     using Sh = Shape<kCB>;
@@ -391,7 +393,7 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
 #pragma unroll
                         for (int e = 0; e < 4; ++e) hs[(16 * ct + 4 * g + e) * kV] = S[ct][e];
                 }
-                if (!kMap) chain_step<kCB, false, true>(sm, S, rs, (int)(s & 1), c, lane);
+                if (!kMap) chain_step<kCB, false, !kSave>(sm, S, rs, (int)(s & 1), c, lane);
                 else if (linear_part) chain_step<kCB, true, false>(sm, S, rs, (int)(s & 1), c, lane);
                 else chain_step<kCB, false, false>(sm, S, rs, (int)(s & 1), c, lane);
                 rs = rs + 1 == Sh::kSlots ? 0 : rs + 1;
@@ -415,7 +417,12 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
         }
     } else if (wave < 2 * kCB) {
         // ---- outputs: row tiles of every block of the workgroup -------------
-        if (nchunks > 0) {
+        if constexpr (kSave) {
+            if (nchunks > 0) {  // no outputs: the prologue barrier and one per chunk
+                lds_barrier();
+                for (int64_t s = 0; s < nchunks; ++s) lds_barrier();
+            }
+        } else if (nchunks > 0) {
             const int64_t row_stride = H * kV;
             uint16_t *out0 = a.out + (tseq * H + h) * kV + kVB * (vb * kCB) + 4 * g;
             constexpr int kNt = Sh::kOutTiles;
@@ -462,7 +469,7 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
             const int64_t nu = nchunks + kAhead - 1;
             bool prologue_done = false;
             for (int64_t u = 0; u < nu; ++u) {
-                touch_lines<kCB, kMap>(sm, a, wsof(u + 1), vb, lane);
+                touch_lines<kCB, kMap || kSave>(sm, a, wsof(u + 1), vb, lane);
                 asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTouchInFlight) : "memory");
                 if (u >= kAhead - 1) {
                     if (!prologue_done) { lds_barrier(); prologue_done = true; }

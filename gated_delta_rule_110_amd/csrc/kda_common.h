@@ -104,8 +104,9 @@ struct ChainArgs {
     // offset and the linear part of the chain's affine map S -> M S + N.
     int map_mode;
     float *mapM, *mapN;
-    // With hs set (the backward's forward pass), the chain also stores the
-    // fp32 state entering every chunk: hs[chunk slot * H + h][K][V].
+    // With hs set (the backward's forward pass), the chain stores the fp32
+    // state entering every chunk, hs[chunk slot * H + h][K][V], and writes no
+    // outputs (out is not used).
     float *hs;
     int64_t chain_base;  // first chain (in dispatch order) of this launch; set by the launcher
     int64_t piece_cap;   // kda_desc_t::launch_piece (0: launch size by the default rule)
