@@ -723,26 +723,42 @@ struct MainSmem {
 
 // The same pointer, hidden from the compiler: loads through it are not merged
 // with loads of the same addresses in other phases, which would keep those
-// values alive (in registers) across the whole kernel.
-template <typename T>
-__device__ __forceinline__ T *opaque(T *p) {
+// values alive (in registers) across the whole kernel.  It stays a global
+// (address space 1) pointer, so that the loads take a scalar base and a 32-bit
+// offset instead of a 64-bit flat address per element.
+typedef const __attribute__((address_space(1))) float gfloat;
+__device__ __forceinline__ gfloat *__restrict__ opaque(const float *p) {
     asm volatile("" : "+s"(p));
-    return p;
+    return (gfloat *)p;
 }
 
-// Copy a [rows][128] fp32 row-major block from global memory into an LDS tile
-// of pitch kRP, optionally scaled element by element by f(row, col, value).
-template <typename F>
-__device__ __forceinline__ void stage_rows(float (*dst)[kRP], const float *src, int rows, int tid, F f) {
-    for (int idx = tid; idx < rows * 32; idx += kMainThreads) {
-        const int i = idx >> 5, c4 = (idx & 31) * 4;
-        const float4 v = *reinterpret_cast<const float4 *>(src + i * 128 + c4);
-        dst[i][c4] = f(i, c4, v.x);
-        dst[i][c4 + 1] = f(i, c4 + 1, v.y);
-        dst[i][c4 + 2] = f(i, c4 + 2, v.z);
-        dst[i][c4 + 3] = f(i, c4 + 3, v.w);
+// Staging of [kRows][128] fp32 row-major blocks from global memory into LDS
+// tiles of pitch kRP, 16 bytes per thread and pass: load() issues every load
+// of the block into registers, store() writes them (after the caller's other
+// loads, so that the latencies overlap rather than add up).
+template <int kRows>
+struct RowStage {
+    static constexpr int kN = kRows * 32 / kMainThreads;
+    float4 v[kN];
+    __device__ __forceinline__ void load(const float *src, int tid) {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+            const int idx = tid + n * kMainThreads;
+            v[n] = *reinterpret_cast<const float4 *>(src + (idx >> 5) * 128 + (idx & 31) * 4);
+        }
     }
-}
+    __device__ __forceinline__ void store(float (*dst)[kRP], int tid) const {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+            const int idx = tid + n * kMainThreads;
+            const int i = idx >> 5, c4 = (idx & 31) * 4;
+            dst[i][c4] = v[n].x;
+            dst[i][c4 + 1] = v[n].y;
+            dst[i][c4 + 2] = v[n].z;
+            dst[i][c4 + 3] = v[n].w;
+        }
+    }
+};
 
 __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
     __shared__ MainSmem sm;
@@ -782,10 +798,21 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     float *__restrict__ dbo = a.dbeta;
     float *__restrict__ part = a.part + ws * (kK + 1);
     const float scale = a.scale;
-    const auto ident = [](int, int, float x) { return x; };
-    auto vval = [&](int i, int c) -> float {  // v[i][c], 0 past the end (read in bounds, at row 0)
-        const float x = bf16_bits_to_f32(vin[((t0 + (i < L ? i : 0)) * H + h) * kV + c]);
-        return i < L ? x : 0.f;
+    // v[i][c] of this lane's elements (rows row0 + e, columns 16 (kMainNC cq + c) + r),
+    // 0 past the end (read in bounds, at row 0); loaded ahead of the products that use them
+    auto load_v = [&](float (&vv)[kMainNC][4]) {
+#pragma unroll
+        for (int c = 0; c < kMainNC; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * w + 4 * gq + e, d = 16 * (kMainNC * cq + c) + r;
+                vv[c][e] = bf16_bits_to_f32(vin[((t0 + (i < L ? i : 0)) * H + h) * kV + d]);
+            }
+#pragma unroll
+        for (int c = 0; c < kMainNC; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (16 * w + 4 * gq + e >= L) vv[c][e] = 0.f;
     };
     // dO (the A operand of P4 and P6) from LDS, where it replaces T after P3
     auto dov_a = [&](int c) -> float { return bf16_bits_to_f32(sm.t.D[16 * w + r][c]); };
@@ -802,20 +829,38 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll
     for (int c = 0; c < kMainNC; ++c) { dG[c] = f4{0, 0, 0, 0}; dqh[c] = dG[c]; dkh[c] = dG[c]; }
 
-    // P0: T, b, gamma Khat and S into LDS
-    for (int idx = tid; idx < kChunk * kChunk; idx += kMainThreads)
-        sm.t.T[idx >> 6][idx & 63] = Tm[idx];
-    if (tid < kChunk) {
-        sm.b[tid] = bbv[tid];
+    // P0: T, b, gamma Khat and S into LDS (every load issued first)
+    {
+        static_assert(kChunk * kChunk == 4 * kMainThreads, "one float4 of T per thread");
+        const float4 tv = *reinterpret_cast<const float4 *>(Tm + 4 * tid);
+        const float bv = tid < kChunk ? bbv[tid] : 0.f;
+        RowStage<kChunk> ks, gs;
+        RowStage<kK> ss;
+        ks.load(kn, tid);
+        gs.load(G, tid);
+        ss.load(S, tid);
+        *reinterpret_cast<float4 *>(&sm.t.T[tid >> 4][4 * (tid & 15)]) = tv;
+        if (tid < kChunk) {
+            sm.b[tid] = bv;
 #pragma unroll
-        for (int g2 = 0; g2 < kMainQ; ++g2) sm.db[g2][tid] = 0.f;
+            for (int g2 = 0; g2 < kMainQ; ++g2) sm.db[g2][tid] = 0.f;
+        }
+#pragma unroll
+        for (int n = 0; n < RowStage<kChunk>::kN; ++n) {
+            ks.v[n].x *= __expf(gs.v[n].x);
+            ks.v[n].y *= __expf(gs.v[n].y);
+            ks.v[n].z *= __expf(gs.v[n].z);
+            ks.v[n].w *= __expf(gs.v[n].w);
+        }
+        ks.store(sm.U, tid);
+        ss.store(sm.SB, tid);
     }
-    stage_rows(sm.U, kn, kChunk, tid, [&](int i, int d, float x) { return x * __expf(G[i * kK + d]); });
-    stage_rows(sm.SB, S, kK, tid, ident);
     __syncthreads();
 
     // P1: Diag(b) Y, Y = V - (gamma Khat) S
     {
+        float vv[kMainNC][4];
+        load_v(vv);
         f4 acc[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
@@ -842,7 +887,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int ii = row0 + e, d = 16 * (kMainNC * cq + c) + r;
-                sm.Z[ii][d] = sm.b[ii] * (vval(ii, d) - acc[c][e]);
+                sm.Z[ii][d] = sm.b[ii] * (vv[c][e] - acc[c][e]);
             }
     }
     __syncthreads();
@@ -875,10 +920,16 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
             for (int e = 0; e < 4; ++e) sm.U[row0 + e][16 * (kMainNC * cq + c) + r] = acc[c][e];
     }
     __syncthreads();
-    stage_rows(sm.Z, dUt, kChunk, tid, ident);
+    {
+        RowStage<kChunk> us;
+        us.load(dUt, tid);
+        us.store(sm.Z, tid);
+    }
     __syncthreads();
     // P3: Z = T^T dUt; dv = Diag(b) Z; db += Z . v
     {
+        float vv[kMainNC][4];
+        load_v(vv);
         f4 acc[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
@@ -914,7 +965,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                 sm.Z[ii][d] = z;
                 if (ii < L) {
                     dvo[((t0 + ii) * H + h) * kV + d] = sm.b[ii] * z;
-                    dbp[e] += z * vval(ii, d);
+                    dbp[e] += z * vv[c][e];
                 }
             }
 #pragma unroll
@@ -934,7 +985,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     __syncthreads();
     // P4: dQg = scale dO S^T and Zw = -Z S^T
     {
-        const float *__restrict__ qn = opaque(qn_all), *__restrict__ kn = opaque(kn_all), *__restrict__ G = opaque(G_all);
+        gfloat *__restrict__ qn = opaque(qn_all), *__restrict__ kn = opaque(kn_all), *__restrict__ G = opaque(G_all);
         f4 aq[kMainNC], az[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) { aq[c] = f4{0, 0, 0, 0}; az[c] = aq[c]; }
@@ -960,7 +1011,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         }
         float dbp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < kMainNC; ++c)
+        for (int c = 0; c < kMainNC; ++c) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int ii = row0 + e, d = 16 * (kMainNC * cq + c) + r;
@@ -973,6 +1024,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                 dG[c][e] += gam * qh * dQg + bi * gam * kh * Zw;
                 dbp[e] += Zw * gam * kh;
             }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float s = sum16(dbp[e]);
@@ -1003,7 +1055,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     __syncthreads();
     // P5: dKbar = Ut dS'^T
     {
-        const float *__restrict__ qn = opaque(qn_all), *__restrict__ kn = opaque(kn_all), *__restrict__ G = opaque(G_all);
+        gfloat *__restrict__ qn = opaque(qn_all), *__restrict__ kn = opaque(kn_all), *__restrict__ G = opaque(G_all);
         f4 acc[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
@@ -1090,9 +1142,15 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     }
     __syncthreads();
     // khat, G and qhat into LDS for the Gram gradients
-    stage_rows(sm.U, kn, kChunk, tid, ident);
-    stage_rows(sm.Z, G, kChunk, tid, ident);
-    stage_rows(&sm.SB[kChunk], qn, kChunk, tid, ident);
+    {
+        RowStage<kChunk> ks, gs, qs;
+        ks.load(kn, tid);
+        gs.load(G, tid);
+        qs.load(qn, tid);
+        ks.store(sm.U, tid);
+        gs.store(sm.Z, tid);
+        qs.store(&sm.SB[kChunk], tid);
+    }
     __syncthreads();
     // P7: the decayed Gram matrices P[i][j] = sum_d x_i y_j exp(G_i - G_j): for M
     // (x = y = khat, gradient dM) and A_qk (x = qhat, y = khat, gradient dA_qk).  These stay on
