@@ -760,6 +760,16 @@ struct RowStage {
     }
 };
 
+// Keep the accumulators' current values in registers here: without this the
+// compiler sinks a phase's updates into the last phase that reads them, and
+// the operands it keeps alive for that (loaded values, products) run out of
+// registers and are spilled.
+template <int kN>
+__device__ __forceinline__ void pin(f4 (&x)[kN]) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) asm volatile("" : "+v"(x[i]));
+}
+
 __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
     __shared__ MainSmem sm;
     const int64_t ws = a.unit_base + blockIdx.x;
@@ -814,8 +824,6 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
             for (int e = 0; e < 4; ++e)
                 if (16 * w + 4 * gq + e >= L) vv[c][e] = 0.f;
     };
-    // dO (the A operand of P4 and P6) from LDS, where it replaces T after P3
-    auto dov_a = [&](int c) -> float { return bf16_bits_to_f32(sm.t.D[16 * w + r][c]); };
     const int64_t HK = H * kK;
     const int64_t obase = (t0 * H + h) * kK;
     auto out_at = [&](int i, int d) -> int64_t { return obase + i * HK + d; };
@@ -1024,6 +1032,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
                 dG[c][e] += gam * qh * dQg + bi * gam * kh * Zw;
                 dbp[e] += Zw * gam * kh;
             }
+            // per column tile: its 12 loads are issued together, the next tile's after
+            pin(dqh);
+            pin(dkh);
+            pin(dG);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1091,6 +1103,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
             colp = sum4g(colp);
             if (gq == 0) sm.red[w][d] = colp;
         }
+        pin(dkh);
+        pin(dG);
     }
     __syncthreads();
     // P6: dA_qk = scale dO Ut^T (j <= i), dA_kk = -Z Ut^T (j < i); db += dA_kk . M;
@@ -1277,33 +1291,47 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     __syncthreads();
     {
         const float nA = -expf(a.A_log[h]);
+        // branch-free, so that the loads (rows past the end read at row 0, their results
+        // unused) are issued together rather than each inside its row's condition
+        float rqe[4], rke[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int il = row0 + e < L ? row0 + e : 0;
+            rqe[e] = rqv[il];
+            rke[e] = rkv[il];
+        }
         float pa = 0.f;
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) {
             const int d = 16 * (kMainNC * cq + c) + r;
             const float dtb = dtb_h[d];
+            float xg[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int il = row0 + e < L ? row0 + e : 0;
+                xg[e] = bf16_bits_to_f32(gin[out_at(il, d)]) + dtb;
+            }
             float colp = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int ii = row0 + e;
-                if (ii < L) {
-                    const int64_t o = out_at(ii, d);
-                    float sq = 0.f, sk = 0.f;
+                const bool valid = ii < L;
+                float sq = 0.f, sk = 0.f;
 #pragma unroll
-                    for (int g2 = 0; g2 < kMainQ; ++g2) { sq += sm.rs[0][g2][ii]; sk += sm.rs[1][g2][ii]; }
-                    const float rq = rqv[ii], rk = rkv[ii];
-                    dqo[o] = rq * (dqh[c][e] - sq * qh[ii][d]);
-                    dko[o] = rk * (dkh[c][e] - sk * kh[ii][d]);
-                    const float xg = bf16_bits_to_f32(gin[o]) + dtb;
-                    const float z = nA * softplus_fast(xg);
-                    const float da = sm.Z[ii][d];
-                    float dx = 0.f;
-                    if (z > a.lower_bound) {
-                        dx = da * nA * sigmoid_fast(xg);
-                        pa += da * z;
-                    }
+                for (int g2 = 0; g2 < kMainQ; ++g2) { sq += sm.rs[0][g2][ii]; sk += sm.rs[1][g2][ii]; }
+                const float dq = rqe[e] * (dqh[c][e] - sq * qh[ii][d]);
+                const float dk = rke[e] * (dkh[c][e] - sk * kh[ii][d]);
+                const float z = nA * softplus_fast(xg[e]);
+                const float da = sm.Z[ii][d];
+                const bool open = valid && z > a.lower_bound;  // the gate is not clamped
+                const float dx = open ? da * nA * sigmoid_fast(xg[e]) : 0.f;
+                pa += open ? da * z : 0.f;
+                colp += dx;
+                if (valid) {
+                    const int64_t o = out_at(ii, d);
+                    dqo[o] = dq;
+                    dko[o] = dk;
                     dgo[o] = dx;
-                    colp += dx;
                 }
             }
             colp = sum4g(colp);
