@@ -468,7 +468,7 @@ namespace {
 
 struct BwdLayout {
     WorkspaceLayout fwd;  // the forward's intermediates (unsplit, two-kernel)
-    size_t off_hs, off_dhs, off_dUt, off_qn, off_kn, off_G, off_rq, off_rk, off_bb, off_Mk, off_Tm, off_part,
+    size_t off_hs, off_dhs, off_dUt, off_G, off_rq, off_rk, off_bb, off_Mk, off_Tm, off_part,
         off_co;
     size_t total;
 };
@@ -489,8 +489,6 @@ BwdLayout make_bwd_layout(const Geometry &g) {
     L.off_hs = o;   o = align_up(o + per * kK * kV * 4, 256);
     L.off_dhs = o;  o = align_up(o + per * kK * kV * 4, 256);
     L.off_dUt = o;  o = align_up(o + per * kChunk * kV * 4, 256);
-    L.off_qn = o;   o = align_up(o + per * kChunk * kK * 4, 256);
-    L.off_kn = o;   o = align_up(o + per * kChunk * kK * 4, 256);
     L.off_G = o;    o = align_up(o + per * kChunk * kK * 4, 256);
     L.off_rq = o;   o = align_up(o + per * kChunk * 4, 256);
     L.off_rk = o;   o = align_up(o + per * kChunk * 4, 256);
@@ -615,8 +613,6 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
     ba.Wf = ia.Wf; ba.Qf = ia.Qf; ba.Kf = ia.Kf; ba.Af = ia.Af; ba.gn = ia.gn;
     ba.dhs = reinterpret_cast<float *>(ws + lay.off_dhs);
     ba.dUt = reinterpret_cast<float *>(ws + lay.off_dUt);
-    ba.qn = reinterpret_cast<float *>(ws + lay.off_qn);
-    ba.kn = reinterpret_cast<float *>(ws + lay.off_kn);
     ba.G = reinterpret_cast<float *>(ws + lay.off_G);
     ba.rq = reinterpret_cast<float *>(ws + lay.off_rq);
     ba.rk = reinterpret_cast<float *>(ws + lay.off_rk);

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
     _Float16 *WT = reinterpret_cast<_Float16 *>(co + kCoW);
     _Float16 *QgT = reinterpret_cast<_Float16 *>(co + kCoQ);
     float *gno = reinterpret_cast<float *>(co + kCoGn);
-    float *qn = a.qn + ws * (kChunk * kK), *kn = a.kn + ws * (kChunk * kK), *Go = a.G + ws * (kChunk * kK);
+    float *Go = a.G + ws * (kChunk * kK);
 
     // rows, norms, b and the per-channel log-decay; a quarter row per thread.
     // qhat and khat go out as they are; the first pass's half goes to LDS, and
@@ -219,12 +219,6 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
             qv[e] *= rq;
             kv[e] *= rk;
             gv[e] = valid ? fmaxf(a.lower_bound, nA * softplus_fast(gv[e] + dtb[e])) : 0.f;
-        }
-        float *qo = qn + row * kK + 32 * qt, *ko = kn + row * kK + 32 * qt;
-#pragma unroll
-        for (int e = 0; e < 32; e += 4) {
-            *reinterpret_cast<float4 *>(qo + e) = make_float4(qv[e], qv[e + 1], qv[e + 2], qv[e + 3]);
-            *reinterpret_cast<float4 *>(ko + e) = make_float4(kv[e], kv[e + 1], kv[e + 2], kv[e + 3]);
         }
         if (qt < 2) {
 #pragma unroll
@@ -713,6 +707,7 @@ struct MainSmem {
         uint16_t D[kChunk][136];     // dO, bf16 (P4-P6)
     } t;
     float b[kChunk];
+    float rq[kChunk], rk[kChunk];  // reciprocal norms of the rows of q and k (0 past the end)
     float db[kMainQ][kChunk];      // per column group
     float rs[2][kMainQ][kChunk];   // row sums qhat . dqhat and khat . dkhat, per column group
     float red[4][kK];       // column sums per row block
@@ -770,6 +765,29 @@ __device__ __forceinline__ void pin(f4 (&x)[kN]) {
     for (int i = 0; i < kN; ++i) asm volatile("" : "+v"(x[i]));
 }
 
+// One thread's share of a [64][128] tile of normalised rows, x_i / |x_i| from the
+// bf16 input rows and the reciprocal norms: row tid / 16, columns 8 (tid % 16) .. + 7.
+// Rows past the end read row 0 (in bounds) and have a reciprocal norm of 0.
+struct NormRow {
+    uint4 raw;
+    int row, c8;
+    __device__ __forceinline__ void load(const uint16_t *x, int64_t t0, int64_t H, int64_t h, int L, int tid) {
+        row = tid >> 4;
+        c8 = 8 * (tid & 15);
+        raw = *reinterpret_cast<const uint4 *>(x + ((t0 + (row < L ? row : 0)) * H + h) * kK + c8);
+    }
+    // the 8 values times rn, each times f[e] when given
+    __device__ __forceinline__ void store(float (*dst)[kRP], float rn, const float *f = nullptr) const {
+        float x[8];
+        unpack_bf16x8(raw, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = x[e] * rn;
+            dst[row][c8 + e] = f ? v * f[e] : v;
+        }
+    }
+};
+
 __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a) {
     __shared__ MainSmem sm;
     const int64_t ws = a.unit_base + blockIdx.x;
@@ -787,11 +805,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     const float *__restrict__ S = a.hs + ws * (int64_t)(kK * kV);
     const float *__restrict__ dSp = a.dhs + ws * (int64_t)(kK * kV);
     const float *__restrict__ dUt = a.dUt + ws * (int64_t)(kChunk * kV);
-    const float *__restrict__ qn_all = a.qn + ws * (kChunk * kK);
-    const float *__restrict__ kn_all = a.kn + ws * (kChunk * kK);
     const float *__restrict__ G_all = a.G + ws * (kChunk * kK);
-    const float *__restrict__ qn = qn_all;
-    const float *__restrict__ kn = kn_all;
     const float *__restrict__ G = G_all;
     const float *__restrict__ Mk = a.Mk + ws * (kChunk * kChunk);
     const float *__restrict__ Tm = a.Tm + ws * (kChunk * kChunk);
@@ -841,26 +855,26 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     {
         static_assert(kChunk * kChunk == 4 * kMainThreads, "one float4 of T per thread");
         const float4 tv = *reinterpret_cast<const float4 *>(Tm + 4 * tid);
-        const float bv = tid < kChunk ? bbv[tid] : 0.f;
-        RowStage<kChunk> ks, gs;
+        float bv = 0.f, rqr = 0.f, rkr = 0.f;
+        if (tid < kChunk) { bv = bbv[tid]; rqr = rqv[tid]; rkr = rkv[tid]; }
+        NormRow kr;
+        kr.load(a.k, t0, H, h, L, tid);
+        const float rkn = rkv[kr.row];
+        const float4 g0 = *reinterpret_cast<const float4 *>(G + kr.row * kK + kr.c8);
+        const float4 g1 = *reinterpret_cast<const float4 *>(G + kr.row * kK + kr.c8 + 4);
         RowStage<kK> ss;
-        ks.load(kn, tid);
-        gs.load(G, tid);
         ss.load(S, tid);
         *reinterpret_cast<float4 *>(&sm.t.T[tid >> 4][4 * (tid & 15)]) = tv;
         if (tid < kChunk) {
             sm.b[tid] = bv;
+            sm.rq[tid] = rqr;
+            sm.rk[tid] = rkr;
 #pragma unroll
             for (int g2 = 0; g2 < kMainQ; ++g2) sm.db[g2][tid] = 0.f;
         }
-#pragma unroll
-        for (int n = 0; n < RowStage<kChunk>::kN; ++n) {
-            ks.v[n].x *= __expf(gs.v[n].x);
-            ks.v[n].y *= __expf(gs.v[n].y);
-            ks.v[n].z *= __expf(gs.v[n].z);
-            ks.v[n].w *= __expf(gs.v[n].w);
-        }
-        ks.store(sm.U, tid);
+        const float gam[8] = {__expf(g0.x), __expf(g0.y), __expf(g0.z), __expf(g0.w),
+                              __expf(g1.x), __expf(g1.y), __expf(g1.z), __expf(g1.w)};
+        kr.store(sm.U, rkn, gam);  // gamma khat
         ss.store(sm.SB, tid);
     }
     __syncthreads();
@@ -993,7 +1007,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     __syncthreads();
     // P4: dQg = scale dO S^T and Zw = -Z S^T
     {
-        gfloat *__restrict__ qn = opaque(qn_all), *__restrict__ kn = opaque(kn_all), *__restrict__ G = opaque(G_all);
+        gfloat *__restrict__ G = opaque(G_all);
         f4 aq[kMainNC], az[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) { aq[c] = f4{0, 0, 0, 0}; az[c] = aq[c]; }
@@ -1023,7 +1037,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int ii = row0 + e, d = 16 * (kMainNC * cq + c) + r;
-                const float qh = qn[ii * kK + d], kh = kn[ii * kK + d];
+                const int64_t xi = ((t0 + (ii < L ? ii : 0)) * H + h) * kK + d;  // row 0 past the end
+                const float qh = bf16_bits_to_f32(a.q[xi]) * sm.rq[ii], kh = bf16_bits_to_f32(a.k[xi]) * sm.rk[ii];
                 const float gam = __expf(G[ii * kK + d]);
                 const float bi = sm.b[ii];
                 const float dQg = scale * aq[c][e], Zw = -az[c][e];
@@ -1044,15 +1059,16 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         }
     }
     __syncthreads();
-    // dS' into LDS; exp(G_n) sum_v S[d][v] dS'[d][v] on the way (kMainTPR threads per state row)
+    // dS' into LDS, over S; exp(G_n) sum_v S[d][v] dS'[d][v] on the way (kMainTPR threads per
+    // state row, each reading S from LDS where it then writes dS')
     {
         constexpr int kCols = kV / kMainTPR;
         const int d = tid / kMainTPR, qt = tid % kMainTPR;
-        const float *sr = S + d * kV + kCols * qt, *dr = dSp + d * kV + kCols * qt;
+        const float *dr = dSp + d * kV + kCols * qt;
         float s = 0.f;
 #pragma unroll
         for (int c4 = 0; c4 < kCols; c4 += 4) {
-            const float4 x = *reinterpret_cast<const float4 *>(sr + c4);
+            const float4 x = *reinterpret_cast<const float4 *>(&sm.SB[d][kCols * qt + c4]);
             const float4 y = *reinterpret_cast<const float4 *>(dr + c4);
             s += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
             sm.SB[d][kCols * qt + c4] = y.x;
@@ -1067,7 +1083,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     __syncthreads();
     // P5: dKbar = Ut dS'^T
     {
-        gfloat *__restrict__ qn = opaque(qn_all), *__restrict__ kn = opaque(kn_all), *__restrict__ G = opaque(G_all);
+        gfloat *__restrict__ G = opaque(G_all);
         f4 acc[kMainNC];
 #pragma unroll
         for (int c = 0; c < kMainNC; ++c) acc[c] = f4{0, 0, 0, 0};
@@ -1094,7 +1110,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
             for (int e = 0; e < 4; ++e) {
                 const int ii = row0 + e;
                 const float eK = __expf(Gn - G[ii * kK + d]);
-                const float kb = eK * kn[ii * kK + d];
+                const int64_t xi = ((t0 + (ii < L ? ii : 0)) * H + h) * kK + d;  // row 0 past the end
+                const float kb = eK * (bf16_bits_to_f32(a.k[xi]) * sm.rk[ii]);
                 const float dkb = acc[c][e];
                 dkh[c][e] += eK * dkb;
                 dG[c][e] -= kb * dkb;
@@ -1157,13 +1174,14 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
     __syncthreads();
     // khat, G and qhat into LDS for the Gram gradients
     {
-        RowStage<kChunk> ks, gs, qs;
-        ks.load(kn, tid);
+        NormRow kr, qr;
+        kr.load(a.k, t0, H, h, L, tid);
+        qr.load(a.q, t0, H, h, L, tid);
+        RowStage<kChunk> gs;
         gs.load(G, tid);
-        qs.load(qn, tid);
-        ks.store(sm.U, tid);
+        kr.store(sm.U, sm.rk[kr.row]);
+        qr.store(&sm.SB[kChunk], sm.rq[qr.row]);
         gs.store(sm.Z, tid);
-        qs.store(&sm.SB[kChunk], tid);
     }
     __syncthreads();
     // P7: the decayed Gram matrices P[i][j] = sum_d x_i y_j exp(G_i - G_j): for M
@@ -1297,8 +1315,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int il = row0 + e < L ? row0 + e : 0;
-            rqe[e] = rqv[il];
-            rke[e] = rkv[il];
+            rqe[e] = sm.rq[il];
+            rke[e] = sm.rk[il];
         }
         float pa = 0.f;
 #pragma unroll

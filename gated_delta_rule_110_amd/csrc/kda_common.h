@@ -148,12 +148,13 @@ struct DecodeArgs {
 // the workspace holds, besides the forward's fragment intermediates:
 //   hs, dhs [ws][K][V] fp32   state entering the chunk / gradient of the state leaving it
 //   dUt     [ws][64][V] fp32  gradient of the chunk's pseudo-values Ut = U - W S
-//   qn, kn, G [ws][64][K] fp32  normalised q and k, cumulative log-decay within the chunk
-//   rq, rk, bb [ws][64] fp32    reciprocal norms of q and k, b = sigmoid(beta)
+//   G [ws][64][K] fp32          cumulative log-decay within the chunk
+//   rq, rk, bb [ws][64] fp32    reciprocal norms of q and k (the normalised rows are
+//                               recomputed from q and k where needed), b = sigmoid(beta)
 //   Mk, Tm [ws][64][64] fp32    decayed key Gram (strictly lower, without b) and T = (I + Diag(b) Mk)^-1
 //   part [ws][K + 1] fp32       this chunk's share of ddt_bias (K) and of dA_log (1)
 //   co [ws][64000 B]            the reverse chain's fp16 operands (layout in kda_bwd.hip)
-// Rows past the end of a ragged chunk are zero in qn, kn, bb and keep G constant.
+// Rows past the end of a ragged chunk are zero in rq, rk, bb and keep G constant.
 constexpr int64_t kBwdChainOperandBytes = 64000;  // per (chunk, head): the reverse chain's fp16 operands
 
 struct BwdArgs {
@@ -168,7 +169,7 @@ struct BwdArgs {
     int64_t T, H, N, nc_fixed, slots;
     const _Float16 *Wf, *Qf, *Kf, *Af;      // the forward's intermediates
     const float *gn;
-    float *hs, *dhs, *dUt, *qn, *kn, *G, *rq, *rk, *bb, *Mk, *Tm, *part;
+    float *hs, *dhs, *dUt, *G, *rq, *rk, *bb, *Mk, *Tm, *part;
     unsigned char *co;                      // [ws][64000 B] the reverse chain's fp16 operands
     float *dq, *dk, *dv, *dg, *dbeta;       // [B,T,H,K] / [B,T,H,V] / [B,T,H] fp32
     float *dh0;                             // [N,H,K,V] fp32 or nullptr
