@@ -119,16 +119,16 @@ KERNEL_SOURCES = {
     "kda_chain_kernel": ["kda_chain.hip"],
     "kda_chain_x2_kernel": ["kda_chain.hip"],
     "kda_chunk_table_kernel": ["kda_chain.hip"],
-    "split_chain": ["kda_chain.hip", "kda_segment.hip", "kda_api.hip"],
+    "split_chain": ["kda_chain.hip", "kda_segment.hip", "kda_api.hip", "kda_bwd_args.h"],
     "kda_decode_kernel": ["kda_decode.hip"],
     "kda_decode_stream_kernel": ["kda_decode.hip"],
     "kda_decode_split2_kernel": ["kda_decode.hip"],
     "kda_decode_split4_kernel": ["kda_decode.hip"],
     "kda_chain_save_kernel": ["kda_chain.hip"],
-    "kda_bwd_prep_kernel": ["kda_bwd.hip"],
-    "kda_bwd_chain_kernel": ["kda_bwd.hip"],
-    "kda_bwd_main_kernel": ["kda_bwd.hip"],
-    "kda_bwd_params_kernel": ["kda_bwd.hip"],
+    "kda_bwd_prep_kernel": ["kda_bwd.hip", "kda_bwd_args.h"],
+    "kda_bwd_chain_kernel": ["kda_bwd.hip", "kda_bwd_args.h"],
+    "kda_bwd_main_kernel": ["kda_bwd.hip", "kda_bwd_args.h"],
+    "kda_bwd_params_kernel": ["kda_bwd.hip", "kda_bwd_args.h"],
 }
 # The library's choice of decode kernel, mirrored to name it: states of this
 # many bytes or more are streamed past the Infinity Cache; otherwise each head

@@ -8,7 +8,7 @@
 #include <stdlib.h>
 #include <mutex>
 #include <vector>
-#include "kda_common.h"
+#include "kda_bwd_args.h"
 #include "kda.h"
 
 using namespace kda;

@@ -44,7 +44,7 @@
 // row of each 16-row block (row 16 w + 8): with the log-decay >= -5 both
 // halves stay within exp(+-40) for the rows of the block, and rows of earlier
 // blocks only ever meet a factor <= 1.
-#include "kda_common.h"
+#include "kda_bwd_args.h"
 
 using namespace kda;
 
