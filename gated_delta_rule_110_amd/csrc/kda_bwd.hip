@@ -213,12 +213,23 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
         const float rq = valid ? 1.0f / sqrtf(sq + 1e-6f) : 0.f;
         const float rk = valid ? 1.0f / sqrtf(sk + 1e-6f) : 0.f;
         const float nA = -expf(a.A_log[h]);
-        const float *dtb = a.dt_bias + h * kK + 32 * qt;
+        float dtb[32];  // loaded together, kept in registers (not reloaded inside the loop below)
+#pragma unroll
+        for (int e = 0; e < 32; e += 4) {
+            const float4 x = *reinterpret_cast<const float4 *>(a.dt_bias + h * kK + 32 * qt + e);
+            dtb[e] = x.x; dtb[e + 1] = x.y; dtb[e + 2] = x.z; dtb[e + 3] = x.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 32; ++e) asm volatile("" : "+v"(dtb[e]));
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
             qv[e] *= rq;
             kv[e] *= rk;
-            gv[e] = valid ? fmaxf(a.lower_bound, nA * softplus_fast(gv[e] + dtb[e])) : 0.f;
+            // the gate of every row, then the selection: under a per-element branch on the row's
+            // validity the 32 exp / log chains would run one after another
+            float z = fmaxf(a.lower_bound, nA * softplus_fast(gv[e] + dtb[e]));
+            asm volatile("" : "+v"(z));
+            gv[e] = valid ? z : 0.f;
         }
         if (qt < 2) {
 #pragma unroll
