@@ -572,6 +572,12 @@ def main(argv=None) -> int:
         return ALG_SHARE_BYTES["chain"] * tok_heads + state_bytes(w)
 
     achieved = alg_bytes / (kernels[dom] / 1e3) / 1e9
+    # Which roofline bounds the path: the larger of its two floor times, the
+    # algorithmic bytes at the HBM peak and the algorithmic FLOPs at the dense
+    # fp16 / bf16 MFMA peak (the path's products are fp16 / bf16 MFMAs).
+    floor_hbm_us = alg_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    floor_mfma_us = F_ALG * tok_heads / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6
+    bound = "hbm" if floor_hbm_us >= floor_mfma_us else "mfma"
     copy_gbs = copy_bandwidth(dev)
     per_kernel = {}
     counter_total = 0
@@ -614,8 +620,13 @@ def main(argv=None) -> int:
         "kernel_ms": dict(([("kda_chunk_table_kernel", round(table_ms, 5))] if packed else [])
                           + [("kda_intra_kernel", round(intra_ms, 5)), (chain_key, round(chain_ms, 5))]),
         "kernel_ms_samples": len(evs),
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"kernel": dom, "bound": bound,
+                     **({"achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4)} if bound == "hbm" else
+                        {"achieved": round(F_ALG * tok_heads / (kernels[dom] / 1e3) / 1e12, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(F_ALG * tok_heads / (kernels[dom] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}),
+                     "floor_us": {"hbm": round(floor_hbm_us, 1), "mfma": round(floor_mfma_us, 1)},
                      "alg_bytes": alg_bytes, "traffic": traffic,
                      "traffic_ratio": None if counter_total is None else round(counter_total / alg_bytes, 3),
                      "frac_interface": round(dom_iface / HBM_PEAK_GBS, 4),
