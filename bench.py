@@ -1,6 +1,6 @@
 """Throughput of the KDA chunked forward pass on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline] [--bwd]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline] [--bwd [--keep-intermediates]]
 
 One step = one kda_fwd call (chunk table when packed, intra-chunk kernel,
 state-chain kernel) over the whole workload, with inputs already resident in
@@ -113,13 +113,13 @@ def cpu_baseline(w, target_s: float = 10.0):
 # The files each kernel's code and launch depend on: its own source (which
 # holds its launcher and grid), the shared header, the public header and the
 # build flags; for split chains also kda_api.hip, which chooses the segments.
-_COMMON_SOURCES = ["kda_common.h", "../../include/kda.h", "../_build.py"]
+_COMMON_SOURCES = ["kda_common.h", "../_build.py"]
 KERNEL_SOURCES = {
     "kda_intra_kernel": ["kda_intra.hip", "kda_intra_body.h"],
     "kda_chain_kernel": ["kda_chain.hip"],
     "kda_chain_x2_kernel": ["kda_chain.hip"],
     "kda_chunk_table_kernel": ["kda_chain.hip"],
-    "split_chain": ["kda_chain.hip", "kda_segment.hip", "kda_api.hip", "kda_bwd_args.h"],
+    "split_chain": ["kda_chain.hip", "kda_segment.hip", "kda_api.hip", "kda_bwd_args.h", "../../include/kda.h"],
     "kda_decode_kernel": ["kda_decode.hip"],
     "kda_decode_stream_kernel": ["kda_decode.hip"],
     "kda_decode_split2_kernel": ["kda_decode.hip"],
@@ -316,11 +316,19 @@ def bench_bwd(kda, args, dev, wname) -> int:
         e.record(stream)
     torch.cuda.synchronize(dev)
     ev_arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in ev])
+    fws = None
+    if args.keep_intermediates:
+        # a training step's backward: the forward ran once (untimed) and its workspace was kept
+        fws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.N, chain_segments=segs_req), dtype=torch.uint8,
+                          device=dev)
+        kda.fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, None, w.A_log, w.dt_bias, w.lower_bound, w.initial_state,
+                None, w.cu_seqlens, workspace=fws, chain_segments=segs_req)
 
     def step(events=None):
         return kda.bwd(w.q, w.k, w.v, w.g, w.beta, w.scale, w.A_log, w.dt_bias, w.lower_bound, d_out,
                        d_final_state=d_fin, initial_state=w.initial_state, cu_seqlens=w.cu_seqlens,
-                       workspace=workspace, phase_events=events, chain_segments=segs_req)
+                       workspace=workspace, phase_events=events, chain_segments=segs_req,
+                       forward_workspace=fws)
 
     for _ in range(args.warmup):
         step()
@@ -347,12 +355,14 @@ def bench_bwd(kda, args, dev, wname) -> int:
     sb = state_bytes(w) + (0 if d_fin is None else w.N * w.H * 128 * 128 * 4) + w.N * w.H * 128 * 128 * 4
     alg_bytes = BYTES_BWD * tok_heads + sb
     result = {
-        "metric": "KDA backward tokens/s (gradient of the prefill, recomputing the forward)",
+        "metric": ("KDA backward tokens/s (gradient of the prefill, from the forward's kept intermediates)"
+                   if fws is not None else
+                   "KDA backward tokens/s (gradient of the prefill, recomputing the forward)"),
         "value": round(w.B * w.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 in, fp32 gradients", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V, "num_seqs": w.N,
-                   "chain_segments": segs},
+                   "chain_segments": segs, "forward_intermediates": "kept" if fws is not None else "recomputed"},
         "kernel_ms": kernel_ms,
         "tflops_alg": round(F_BWD * tok_heads / (ms / 1e3) / 1e12, 2),
         "gbs_alg": round(alg_bytes / (ms / 1e3) / 1e9, 1),
@@ -442,6 +452,8 @@ def main(argv=None) -> int:
                          "chosen workload's head count, fp32 state updated in place, and exit")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (kda_bwd) on the chosen workload and exit")
+    ap.add_argument("--keep-intermediates", action="store_true",
+                    help="with --bwd: the backward reads the intermediates of a forward call's kept workspace")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV folders in DIR and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

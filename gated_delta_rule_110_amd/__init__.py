@@ -66,7 +66,8 @@ class KdaDesc(ctypes.Structure):
                 ("initial_state_dtype", ctypes.c_int32), ("final_state_dtype", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("phase_events", ctypes.c_void_p), ("chain_segments", ctypes.c_int64),
-                ("launch_piece", ctypes.c_int64), ("pipeline", ctypes.c_int64)]
+                ("launch_piece", ctypes.c_int64), ("pipeline", ctypes.c_int64),
+                ("forward_workspace", ctypes.c_void_p)]
 
 
 _lock = threading.Lock()
@@ -113,7 +114,7 @@ def library() -> ctypes.CDLL:
 def _desc(B, T, H, N, h0_dtype=0, ht_dtype=0, workspace=None, nbytes=0, chain_segments=0,
           launch_piece=0, pipeline=0) -> KdaDesc:
     return KdaDesc(B, T, H, HEAD_DIM, HEAD_DIM, N, h0_dtype, ht_dtype,
-                   ctypes.c_void_p(workspace), nbytes, None, chain_segments, launch_piece, pipeline)
+                   ctypes.c_void_p(workspace), nbytes, None, chain_segments, launch_piece, pipeline, None)
 
 
 def workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None, chain_segments: int = 0,
@@ -289,7 +290,8 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         d_out: torch.Tensor, d_final_state: Optional[torch.Tensor] = None,
         initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None, launch_piece: int = 0, chain_segments: int = 0,
-        with_d_initial: bool = True, phase_events=None, outputs: Optional[dict] = None) -> dict:
+        with_d_initial: bool = True, phase_events=None, outputs: Optional[dict] = None,
+        forward_workspace: Optional[torch.Tensor] = None) -> dict:
     """Gradient of ``fwd`` (``kda_bwd``) on the current HIP stream: for the loss
     gradients ``d_out`` (bf16 [B,T,H,128]) and ``d_final_state`` (bf16 or fp32
     [N,H,128,128], or None for zeros) returns a dict of fp32 tensors dq, dk, dg
@@ -299,7 +301,10 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     reverse chains split as the forward's do); phase_events: None or the
     address of a caller-owned array of 6 hipEvent_t (instrumentation);
     outputs: None, or a dict of caller-allocated fp32 tensors of those names and
-    shapes that the call writes into (what graph capture needs)."""
+    shapes that the call writes into (what graph capture needs);
+    forward_workspace: None, or the ``workspace`` tensor of an earlier ``fwd``
+    call on the same inputs, untouched since (its intermediates are read
+    instead of recomputed: ``kda_desc_t::forward_workspace``)."""
     lib = library()
     d, dev, d_out = _check_fwd_args(q, k, v, g, beta, d_out, A_log, dt_bias, initial_state, d_final_state,
                                     cu_seqlens, chain_segments, launch_piece, allocate_out=False)
@@ -331,6 +336,15 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         d.workspace = ctypes.c_void_p(workspace.data_ptr())
         d.workspace_bytes = workspace.numel() * workspace.element_size()
         d.phase_events = phase_events
+        if forward_workspace is not None:
+            # the intermediates end where the unsplit two-kernel forward's workspace does
+            fd = KdaDesc.from_buffer_copy(d)
+            fd.chain_segments = 1
+            fd.pipeline = 0
+            if forward_workspace.device != dev or \
+                    forward_workspace.numel() * forward_workspace.element_size() < int(lib.kda_fwd_workspace_size(ctypes.byref(fd))):
+                raise ValueError("forward_workspace must be the workspace of a fwd call on these shapes")
+            d.forward_workspace = ctypes.c_void_p(forward_workspace.data_ptr())
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
                          _ptr(dt_bias), float(lower_bound), _ptr(initial_state), _ptr(cu_seqlens), _ptr(d_out),
@@ -347,19 +361,27 @@ class KdaFunction(torch.autograd.Function):
     (q, k, v, g, beta bf16; A_log, dt_bias fp32; initial_state bf16, fp32 or
     None); ``final_dtype`` is the dtype of the returned final state, or None for
     no final state.  The gradients come from one ``kda_bwd`` call, in fp32,
-    cast to each input's dtype."""
+    cast to each input's dtype.  With ``keep_intermediates`` the forward's
+    workspace (about 72.5 KiB per 64-token chunk and head) is held until the
+    backward, which then reads the intra-chunk intermediates from it instead of
+    recomputing them (``kda_desc_t::forward_workspace``)."""
 
     @staticmethod
     def forward(ctx, q, k, v, g, beta, A_log, dt_bias, initial_state, scale, lower_bound, cu_seqlens,
-                final_dtype, chain_segments):
+                final_dtype, chain_segments, keep_intermediates=False):
         final = None
+        B, T, H, K = q.shape
+        N = B if cu_seqlens is None else cu_seqlens.numel() - 1
         if final_dtype is not None:
-            B, T, H, K = q.shape
-            N = B if cu_seqlens is None else cu_seqlens.numel() - 1
             final = torch.empty((N, H, K, v.shape[-1]), dtype=final_dtype, device=q.device)
+        ws = None
+        if keep_intermediates:
+            ws = torch.empty(max(workspace_size(B, T, H, N, chain_segments=chain_segments), 1),
+                             dtype=torch.uint8, device=q.device)
         out, fin = fwd(q, k, v, g, beta, scale, None, A_log, dt_bias, lower_bound, initial_state, final,
-                       cu_seqlens, chain_segments=chain_segments)
+                       cu_seqlens, workspace=ws, chain_segments=chain_segments)
         ctx.save_for_backward(q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens)
+        ctx.fwd_ws = ws
         ctx.scale, ctx.lower_bound, ctx.chain_segments = float(scale), float(lower_bound), int(chain_segments)
         return out, fin
 
@@ -374,24 +396,27 @@ class KdaFunction(torch.autograd.Function):
         want_h0 = initial_state is not None and ctx.needs_input_grad[7]
         res = bwd(q, k, v, g, beta, ctx.scale, A_log, dt_bias, ctx.lower_bound, d_out, d_final_state=d_fin,
                   initial_state=initial_state, cu_seqlens=cu_seqlens, chain_segments=ctx.chain_segments,
-                  with_d_initial=want_h0)
+                  with_d_initial=want_h0, forward_workspace=ctx.fwd_ws)
+        ctx.fwd_ws = None
         d_h0 = res["d_initial_state"].to(initial_state.dtype) if want_h0 else None
         return (res["dq"].to(q.dtype), res["dk"].to(k.dtype), res["dv"].to(v.dtype), res["dg"].to(g.dtype),
                 res["dbeta"].to(beta.dtype), res["dA_log"], res["ddt_bias"], d_h0,
-                None, None, None, None, None)
+                None, None, None, None, None, None)
 
 
 def kda_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                   scale: float, A_log: torch.Tensor, dt_bias: torch.Tensor, lower_bound: float,
                   initial_state: Optional[torch.Tensor] = None, final_state_dtype: Optional[torch.dtype] = None,
                   cu_seqlens: Optional[torch.Tensor] = None,
-                  chain_segments: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  chain_segments: int = 0,
+                  keep_intermediates: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """The KDA forward as an autograd operation (``KdaFunction``): returns
     ``(out, final_state)``, the final state in ``final_state_dtype`` (bf16 or
     fp32) or None, and backpropagates into q, k, v, g, beta, A_log, dt_bias and
-    the initial state through ``kda_bwd``."""
+    the initial state through ``kda_bwd``.  keep_intermediates: hold the
+    forward's workspace until the backward (more memory, a shorter backward)."""
     return KdaFunction.apply(q, k, v, g, beta, A_log, dt_bias, initial_state, scale, lower_bound, cu_seqlens,
-                             final_state_dtype, chain_segments)
+                             final_state_dtype, chain_segments, keep_intermediates)
 
 
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

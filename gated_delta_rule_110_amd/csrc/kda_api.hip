@@ -550,6 +550,12 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
         if (st != KDA_OK) return st;
     }
     const BwdLayout lay = make_bwd_layout(geo);
+    // the forward's intermediates: recomputed into this call's workspace, or
+    // those of the kda_fwd call that left them in desc->forward_workspace (the
+    // intermediates sit at the same offsets in both layouts: make_layout puts
+    // them before the parts that depend on split chains or the pipelined forward)
+    char *fw = static_cast<char *>(const_cast<void *>(desc->forward_workspace));
+    if (fw && !aligned(fw, 256)) return KDA_ERR_ALIGN;
     char *ws = static_cast<char *>(desc->workspace);
     bool owned = false;
     if (ws) {
@@ -577,14 +583,15 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
     ia.A_log = A_log; ia.dt_bias = dt_bias; ia.lower_bound = lower_bound;
     ia.cu = cu_seqlens; ia.chunk_off = chunk_off;
     ia.T = geo.T; ia.H = geo.H; ia.N = geo.N; ia.nc_fixed = geo.nc_fixed;
-    ia.Wf = reinterpret_cast<_Float16 *>(ws + fl.off_Wf);
-    ia.Qf = reinterpret_cast<_Float16 *>(ws + fl.off_Qf);
-    ia.Kf = reinterpret_cast<_Float16 *>(ws + fl.off_Kf);
-    ia.Af = reinterpret_cast<_Float16 *>(ws + fl.off_Af);
-    ia.Uf = reinterpret_cast<_Float16 *>(ws + fl.off_Uf);
-    ia.gn = reinterpret_cast<float *>(ws + fl.off_gn);
+    char *fbase = fw ? fw : ws;
+    ia.Wf = reinterpret_cast<_Float16 *>(fbase + fl.off_Wf);
+    ia.Qf = reinterpret_cast<_Float16 *>(fbase + fl.off_Qf);
+    ia.Kf = reinterpret_cast<_Float16 *>(fbase + fl.off_Kf);
+    ia.Af = reinterpret_cast<_Float16 *>(fbase + fl.off_Af);
+    ia.Uf = reinterpret_cast<_Float16 *>(fbase + fl.off_Uf);
+    ia.gn = reinterpret_cast<float *>(fbase + fl.off_gn);
     ia.piece_cap = desc->launch_piece;
-    if (err == hipSuccess && geo.T > 0) err = kda_launch_intra(ia, geo.slots, stream);
+    if (err == hipSuccess && geo.T > 0 && !fw) err = kda_launch_intra(ia, geo.slots, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[1], stream);
     BwdArgs ba{};
     ba.hs = reinterpret_cast<float *>(ws + lay.off_hs);

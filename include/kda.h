@@ -116,6 +116,18 @@ typedef struct {
      * not the default.  Other values are KDA_ERR_PARAM.  The two give the same
      * bits. */
     int64_t pipeline;
+    /* kda_bwd only (every other call ignores it): NULL, or the workspace of an
+     * earlier kda_fwd call on the same inputs, shapes and cu_seqlens, still
+     * holding what that call wrote (nothing may have reused it since).  kda_bwd
+     * then reads the forward's intra-chunk intermediates from it instead of
+     * recomputing them -- its intra-chunk pass is skipped, the gradients are
+     * the same bits -- so a training step that keeps the forward's workspace
+     * (about 72.5 KiB per 64-token chunk and head) until the backward saves
+     * that pass.  It must be 256-byte aligned (else KDA_ERR_ALIGN); it is only
+     * read.  The results are undefined if it does not hold that call's
+     * intermediates.  kda_fwd_noalloc's scratch cannot serve: later calls
+     * reuse it. */
+    const void *forward_workspace;
 } kda_desc_t;
 
 /* Bytes of workspace kda_fwd needs for these shapes (0 if the shapes are
@@ -269,7 +281,9 @@ size_t kda_bwd_workspace_size(const kda_desc_t *desc);
  * gradient of
  *     L = <d_out, out> + <d_final_state, final_state>
  * with respect to every input.  The forward is recomputed inside the call
- * (nothing from an earlier kda_fwd is needed).
+ * (nothing from an earlier kda_fwd is needed), or, with
+ * desc->forward_workspace set, only its state chain is: the intra-chunk
+ * intermediates come from that kda_fwd call's workspace.
  *
  *   q ... lower_bound, initial_state, cu_seqlens : as for kda_fwd (the same
  *                      shapes, dtypes and rules; desc->initial_state_dtype
@@ -297,7 +311,8 @@ size_t kda_bwd_workspace_size(const kda_desc_t *desc);
  * is the same function of the inputs either way, up to rounding;
  * desc->pipeline is ignored;
  * desc->phase_events, when set, is an array of 6 events recorded before the
- * first kernel (0), after the forward's intra-chunk kernel (1) and state
+ * first kernel (0), after the forward's intra-chunk kernel (1; right after 0
+ * when desc->forward_workspace is set) and state
  * chain (2), after the gradient's preparation kernel (3), its reverse state
  * chain (4) and its per-chunk kernel with the parameter sum (5);
  * launch_piece and the workspace rules are as for kda_fwd, with

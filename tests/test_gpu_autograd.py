@@ -12,8 +12,10 @@ from tests.parity import say
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("keep", [True, False])
 @pytest.mark.parametrize("case", ["fixed", "packed", "nostate", "split"])
-def test_autograd_matches_bwd(case):
+def test_autograd_matches_bwd(case, keep):
+    # keep: the backward reads the forward's intermediates from its kept workspace
     if case == "fixed":
         w = W.make("ag_fixed", 2, 150, 3, 7301, init="fp32", final="fp32")
         fin, segs = "fp32", 0
@@ -26,7 +28,7 @@ def test_autograd_matches_bwd(case):
     else:
         w = W.make("ag_split", 2, 64 * 12 + 5, 2, 7304, init="fp32", final="fp32")
         fin, segs = "fp32", 3
-    say("autograd %s: B=%d T=%d H=%d N=%d" % (case, w.B, w.T, w.H, w.N))
+    say("autograd %s keep=%s: B=%d T=%d H=%d N=%d" % (case, keep, w.B, w.T, w.H, w.N))
     d_out, d_fin = W.loss_grads(w, 7401, final=fin)
     wd = w.to("cuda")
     d_out, d_fin = d_out.cuda(), None if d_fin is None else d_fin.cuda()
@@ -36,7 +38,8 @@ def test_autograd_matches_bwd(case):
     out, final = kda.kda_attention(leaves["q"], leaves["k"], leaves["v"], leaves["g"], leaves["beta"], w.scale,
                                    leaves["A_log"], leaves["dt_bias"], w.lower_bound, initial_state=h0,
                                    final_state_dtype=None if d_fin is None else d_fin.dtype,
-                                   cu_seqlens=wd.cu_seqlens, chain_segments=segs)
+                                   cu_seqlens=wd.cu_seqlens, chain_segments=segs,
+                                   keep_intermediates=keep)
     loss = (out.float() * d_out.float()).sum()
     if final is not None:
         loss = loss + (final.float() * d_fin.float()).sum()

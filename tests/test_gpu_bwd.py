@@ -286,3 +286,44 @@ def test_bwd_split_chains(segs, states):
         a, b = got[name], unsplit[name]
         scale_ = max(float(np.abs(b).max()), 1e-30)
         assert float(np.abs(a - b).max()) / scale_ <= 2e-3, (name, segs)
+
+
+_FWD_WS_CASES = {
+    # (workload, loss-gradient seed and final-state dtype, forward keywords, backward keywords)
+    "fixed": lambda: CASES["fixed"]() + ({}, {}),
+    "packed": lambda: CASES["packed"]() + ({}, {}),
+    "split": lambda: (W.make("bwd_fws_split", 2, 64 * 40 + 17, 2, 7014, init="fp32", final="fp32"), 7114,
+                      "fp32", {"chain_segments": 3}, {"chain_segments": 3}),
+    # a forward left unsplit, a backward split in 3: the intermediates do not depend on the split
+    "split_unsplit": lambda: (W.make("bwd_fws_split", 2, 64 * 40 + 17, 2, 7014, init="fp32", final="fp32"),
+                              7114, "fp32", {"chain_segments": 1}, {"chain_segments": 3}),
+    # the pipelined forward writes the same intermediates
+    "pipelined": lambda: (W.make("bwd_fws_pipe", 1, 300, 8, 7015, init="bf16", final="fp32"), 7115, "fp32",
+                          {"pipeline": 1}, {}),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_FWD_WS_CASES))
+def test_bwd_reads_forward_workspace(case):
+    # kda_desc_t::forward_workspace: the backward reads the intra-chunk intermediates a forward
+    # call left in its workspace instead of recomputing them, and returns the same bits
+    w, seed, fin, fkw, bkw = _FWD_WS_CASES[case]()
+    if "pipeline" in fkw:
+        assert kda.pipelined_for(w.B, w.T, w.H, pipeline=1)
+    d_out, d_fin = W.loss_grads(w, seed, final=fin)
+    wd = w.to("cuda")
+    ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.N, **fkw), dtype=torch.uint8, device="cuda")
+    say("bwd forward_workspace %s: B=%d T=%d H=%d N=%d" % (case, w.B, w.T, w.H, w.N))
+    kda.fwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, None, wd.A_log, wd.dt_bias, w.lower_bound,
+            wd.initial_state, None, wd.cu_seqlens, workspace=ws, **fkw)
+    ref = _gpu(w, d_out, d_fin, **bkw)
+    got = _gpu(w, d_out, d_fin, forward_workspace=ws, **bkw)
+    for name in NAMES:
+        if ref[name] is None:
+            assert got[name] is None, name
+            continue
+        assert np.array_equal(got[name], ref[name]), (case, name)
+    # the intermediates are read, not recomputed: zeros in their place change the gradient
+    zeros = torch.zeros_like(ws)
+    bad = _gpu(w, d_out, d_fin, forward_workspace=zeros, **bkw)
+    assert not np.array_equal(bad["dq"], ref["dq"]), case

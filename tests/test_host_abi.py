@@ -246,6 +246,8 @@ def test_bwd_validation_errors(lib):
         assert _call_bwd(lib, _desc(), align=n) == 6, n
     d = _desc(workspace=ctypes.c_void_p(0x100000), workspace_bytes=1024)
     assert _call_bwd(lib, d) == 7
+    d = _desc(forward_workspace=ctypes.c_void_p(0x100010))  # not 256-aligned
+    assert _call_bwd(lib, d) == 6
     d = _desc(initial_state_dtype=9)
     assert lib.kda_bwd(*([ctypes.c_void_p(FAKE)] * 5), 0.1, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), -5.0,
                        ctypes.c_void_p(FAKE), None, ctypes.c_void_p(FAKE), None,
