@@ -317,18 +317,37 @@ def bench_bwd(kda, args, dev, wname) -> int:
     torch.cuda.synchronize(dev)
     ev_arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in ev])
     fws = None
+    fwd_keep_ms = None
     if args.keep_intermediates:
-        # a training step's backward: the forward ran once (untimed) and its workspace was kept
-        fws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.N, chain_segments=segs_req), dtype=torch.uint8,
-                          device=dev)
-        kda.fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, None, w.A_log, w.dt_bias, w.lower_bound, w.initial_state,
-                None, w.cu_seqlens, workspace=fws, chain_segments=segs_req)
+        # a training step's backward: the forward kept its workspace, with the state entering
+        # every chunk, and the backward recomputes nothing; that forward is timed here too
+        fws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.N, chain_segments=segs_req, save_states=True),
+                          dtype=torch.uint8, device=dev)
+        fin_t = None if w.final_state_dtype is None else \
+            torch.empty((w.N, w.H, 128, 128), dtype=w.final_state_dtype, device=dev)
+        out_t = torch.empty(w.v.shape, dtype=torch.bfloat16, device=dev)
+
+        def fwd_keep():
+            kda.fwd(w.q, w.k, w.v, w.g, w.beta, w.scale, out_t, w.A_log, w.dt_bias, w.lower_bound,
+                    w.initial_state, fin_t, w.cu_seqlens, workspace=fws, chain_segments=segs_req,
+                    save_states=True)
+
+        for _ in range(max(args.warmup, 1)):
+            fwd_keep()
+        torch.cuda.synchronize(dev)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(args.steps):
+            fwd_keep()
+        f1.record(stream)
+        torch.cuda.synchronize(dev)
+        fwd_keep_ms = f0.elapsed_time(f1) / args.steps
 
     def step(events=None):
         return kda.bwd(w.q, w.k, w.v, w.g, w.beta, w.scale, w.A_log, w.dt_bias, w.lower_bound, d_out,
                        d_final_state=d_fin, initial_state=w.initial_state, cu_seqlens=w.cu_seqlens,
                        workspace=workspace, phase_events=events, chain_segments=segs_req,
-                       forward_workspace=fws)
+                       forward_workspace=fws, forward_states=fws is not None)
 
     for _ in range(args.warmup):
         step()
@@ -355,7 +374,8 @@ def bench_bwd(kda, args, dev, wname) -> int:
     sb = state_bytes(w) + (0 if d_fin is None else w.N * w.H * 128 * 128 * 4) + w.N * w.H * 128 * 128 * 4
     alg_bytes = BYTES_BWD * tok_heads + sb
     result = {
-        "metric": ("KDA backward tokens/s (gradient of the prefill, from the forward's kept intermediates)"
+        "metric": ("KDA backward tokens/s (gradient of the prefill, from the forward's kept intermediates "
+                   "and states)"
                    if fws is not None else
                    "KDA backward tokens/s (gradient of the prefill, recomputing the forward)"),
         "value": round(w.B * w.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -364,6 +384,9 @@ def bench_bwd(kda, args, dev, wname) -> int:
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V, "num_seqs": w.N,
                    "chain_segments": segs, "forward_intermediates": "kept" if fws is not None else "recomputed"},
         "kernel_ms": kernel_ms,
+        # with kept intermediates: the forward that keeps them, and forward + backward
+        "forward_keep_ms": None if fwd_keep_ms is None else round(fwd_keep_ms, 5),
+        "train_step_ms": None if fwd_keep_ms is None else round(fwd_keep_ms + ms, 5),
         "tflops_alg": round(F_BWD * tok_heads / (ms / 1e3) / 1e12, 2),
         "gbs_alg": round(alg_bytes / (ms / 1e3) / 1e9, 1),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFLOPS,
@@ -453,7 +476,8 @@ def main(argv=None) -> int:
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (kda_bwd) on the chosen workload and exit")
     ap.add_argument("--keep-intermediates", action="store_true",
-                    help="with --bwd: the backward reads the intermediates of a forward call's kept workspace")
+                    help="with --bwd: the backward reads the intermediates and states of a forward call's "
+                         "kept workspace (that forward is timed too)")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSV folders in DIR and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

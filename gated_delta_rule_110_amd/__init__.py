@@ -67,7 +67,7 @@ class KdaDesc(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("phase_events", ctypes.c_void_p), ("chain_segments", ctypes.c_int64),
                 ("launch_piece", ctypes.c_int64), ("pipeline", ctypes.c_int64),
-                ("forward_workspace", ctypes.c_void_p)]
+                ("forward_workspace", ctypes.c_void_p), ("save_states", ctypes.c_int64)]
 
 
 _lock = threading.Lock()
@@ -112,15 +112,18 @@ def library() -> ctypes.CDLL:
 
 
 def _desc(B, T, H, N, h0_dtype=0, ht_dtype=0, workspace=None, nbytes=0, chain_segments=0,
-          launch_piece=0, pipeline=0) -> KdaDesc:
+          launch_piece=0, pipeline=0, save_states=0) -> KdaDesc:
     return KdaDesc(B, T, H, HEAD_DIM, HEAD_DIM, N, h0_dtype, ht_dtype,
-                   ctypes.c_void_p(workspace), nbytes, None, chain_segments, launch_piece, pipeline, None)
+                   ctypes.c_void_p(workspace), nbytes, None, chain_segments, launch_piece, pipeline, None,
+                   save_states)
 
 
 def workspace_size(B: int, T: int, H: int, num_seqs: Optional[int] = None, chain_segments: int = 0,
-                   pipeline: int = 0) -> int:
-    """Workspace bytes ``fwd`` needs for these shapes (and chain split)."""
-    d = _desc(B, T, H, B if num_seqs is None else num_seqs, chain_segments=chain_segments, pipeline=pipeline)
+                   pipeline: int = 0, save_states: bool = False) -> int:
+    """Workspace bytes ``fwd`` needs for these shapes (and chain split, and
+    the saved states with ``save_states``)."""
+    d = _desc(B, T, H, B if num_seqs is None else num_seqs, chain_segments=chain_segments, pipeline=pipeline,
+              save_states=int(bool(save_states)))
     return int(library().kda_fwd_workspace_size(ctypes.byref(d)))
 
 
@@ -214,7 +217,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None,
         phase_events=None, chain_segments: int = 0,
-        launch_piece: int = 0, pipeline: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        launch_piece: int = 0, pipeline: int = 0,
+        save_states: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """KDA forward on the current HIP stream.  Returns ``(out, final_state)``.
 
     q, k, g: bf16 [B,T,H,128]; v: bf16 [B,T,H,128]; beta: bf16 logits [B,T,H];
@@ -227,12 +231,16 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     chain_segments: 0 (automatic), 1 (never) or the number of segments each
     sequence's state chain is split into (batches without cu_seqlens);
     launch_piece: kda_desc_t::launch_piece (0: the library's launch size);
-    pipeline: kda_desc_t::pipeline (0: the two-kernel forward, 1: the pipelined one where it applies).
+    pipeline: kda_desc_t::pipeline (0: the two-kernel forward, 1: the pipelined one where it applies);
+    save_states: also store the state entering every chunk in the workspace,
+    for ``bwd(..., forward_workspace=workspace, forward_states=True)``
+    (``kda_desc_t::save_states``).
     """
     lib = library()
     d, dev, out = _check_fwd_args(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state,
                                   cu_seqlens, chain_segments, launch_piece, allocate_out=True,
                                   pipeline=pipeline)
+    d.save_states = int(bool(save_states))
     need = int(lib.kda_fwd_workspace_size(ctypes.byref(d)))
     with torch.cuda.device(dev):
         if workspace is None:
@@ -291,7 +299,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None, launch_piece: int = 0, chain_segments: int = 0,
         with_d_initial: bool = True, phase_events=None, outputs: Optional[dict] = None,
-        forward_workspace: Optional[torch.Tensor] = None) -> dict:
+        forward_workspace: Optional[torch.Tensor] = None, forward_states: bool = False) -> dict:
     """Gradient of ``fwd`` (``kda_bwd``) on the current HIP stream: for the loss
     gradients ``d_out`` (bf16 [B,T,H,128]) and ``d_final_state`` (bf16 or fp32
     [N,H,128,128], or None for zeros) returns a dict of fp32 tensors dq, dk, dg
@@ -304,7 +312,9 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
     shapes that the call writes into (what graph capture needs);
     forward_workspace: None, or the ``workspace`` tensor of an earlier ``fwd``
     call on the same inputs, untouched since (its intermediates are read
-    instead of recomputed: ``kda_desc_t::forward_workspace``)."""
+    instead of recomputed: ``kda_desc_t::forward_workspace``);
+    forward_states: that call ran with ``save_states`` and the same
+    chain_segments, and its states are read as well (``kda_desc_t::save_states``)."""
     lib = library()
     d, dev, d_out = _check_fwd_args(q, k, v, g, beta, d_out, A_log, dt_bias, initial_state, d_final_state,
                                     cu_seqlens, chain_segments, launch_piece, allocate_out=False)
@@ -337,14 +347,19 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta
         d.workspace_bytes = workspace.numel() * workspace.element_size()
         d.phase_events = phase_events
         if forward_workspace is not None:
-            # the intermediates end where the unsplit two-kernel forward's workspace does
+            # the intermediates end where the unsplit two-kernel forward's workspace does;
+            # with the states, the forward's whole workspace
             fd = KdaDesc.from_buffer_copy(d)
-            fd.chain_segments = 1
+            if forward_states:
+                fd.save_states = 1
+            else:
+                fd.chain_segments = 1
             fd.pipeline = 0
             if forward_workspace.device != dev or \
                     forward_workspace.numel() * forward_workspace.element_size() < int(lib.kda_fwd_workspace_size(ctypes.byref(fd))):
                 raise ValueError("forward_workspace must be the workspace of a fwd call on these shapes")
             d.forward_workspace = ctypes.c_void_p(forward_workspace.data_ptr())
+            d.save_states = int(bool(forward_states))
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
                          _ptr(dt_bias), float(lower_bound), _ptr(initial_state), _ptr(cu_seqlens), _ptr(d_out),
@@ -361,10 +376,11 @@ class KdaFunction(torch.autograd.Function):
     (q, k, v, g, beta bf16; A_log, dt_bias fp32; initial_state bf16, fp32 or
     None); ``final_dtype`` is the dtype of the returned final state, or None for
     no final state.  The gradients come from one ``kda_bwd`` call, in fp32,
-    cast to each input's dtype.  With ``keep_intermediates`` the forward's
-    workspace (about 72.5 KiB per 64-token chunk and head) is held until the
-    backward, which then reads the intra-chunk intermediates from it instead of
-    recomputing them (``kda_desc_t::forward_workspace``)."""
+    cast to each input's dtype.  With ``keep_intermediates`` the forward also
+    stores the state entering every chunk and its workspace (about 136.5 KiB
+    per 64-token chunk and head) is held until the backward, which then reads
+    the intermediates and the states from it instead of recomputing the
+    forward (``kda_desc_t::forward_workspace``, ``kda_desc_t::save_states``)."""
 
     @staticmethod
     def forward(ctx, q, k, v, g, beta, A_log, dt_bias, initial_state, scale, lower_bound, cu_seqlens,
@@ -376,10 +392,10 @@ class KdaFunction(torch.autograd.Function):
             final = torch.empty((N, H, K, v.shape[-1]), dtype=final_dtype, device=q.device)
         ws = None
         if keep_intermediates:
-            ws = torch.empty(max(workspace_size(B, T, H, N, chain_segments=chain_segments), 1),
+            ws = torch.empty(max(workspace_size(B, T, H, N, chain_segments=chain_segments, save_states=True), 1),
                              dtype=torch.uint8, device=q.device)
         out, fin = fwd(q, k, v, g, beta, scale, None, A_log, dt_bias, lower_bound, initial_state, final,
-                       cu_seqlens, workspace=ws, chain_segments=chain_segments)
+                       cu_seqlens, workspace=ws, chain_segments=chain_segments, save_states=ws is not None)
         ctx.save_for_backward(q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens)
         ctx.fwd_ws = ws
         ctx.scale, ctx.lower_bound, ctx.chain_segments = float(scale), float(lower_bound), int(chain_segments)
@@ -396,7 +412,7 @@ class KdaFunction(torch.autograd.Function):
         want_h0 = initial_state is not None and ctx.needs_input_grad[7]
         res = bwd(q, k, v, g, beta, ctx.scale, A_log, dt_bias, ctx.lower_bound, d_out, d_final_state=d_fin,
                   initial_state=initial_state, cu_seqlens=cu_seqlens, chain_segments=ctx.chain_segments,
-                  with_d_initial=want_h0, forward_workspace=ctx.fwd_ws)
+                  with_d_initial=want_h0, forward_workspace=ctx.fwd_ws, forward_states=ctx.fwd_ws is not None)
         ctx.fwd_ws = None
         d_h0 = res["d_initial_state"].to(initial_state.dtype) if want_h0 else None
         return (res["dq"].to(q.dtype), res["dk"].to(k.dtype), res["dv"].to(v.dtype), res["dg"].to(g.dtype),

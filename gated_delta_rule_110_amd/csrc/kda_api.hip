@@ -80,8 +80,10 @@ kda_status_t make_geometry(const kda_desc_t *d, bool varlen, Geometry &g) {
     }
     if (g.slots > 0x7fffffffLL || g.N > 0x7fffffffLL) return KDA_ERR_SHAPE;
     if (d->pipeline < 0 || d->pipeline > 1) return KDA_ERR_PARAM;
+    if (d->save_states < 0 || d->save_states > 1) return KDA_ERR_PARAM;
     const kda_status_t st = choose_segments(d, g);
-    g.fused = st == KDA_OK && g.segs == 1 && d->pipeline == 1 && kda_fused_applies(g.N, g.H, g.varlen);
+    g.fused = st == KDA_OK && g.segs == 1 && d->pipeline == 1 && d->save_states == 0 &&
+              kda_fused_applies(g.N, g.H, g.varlen);
     return st;
 }
 
@@ -115,6 +117,17 @@ WorkspaceLayout make_layout(const Geometry &g) {
     return L;
 }
 
+// Bytes of the fp32 states entering every chunk slot that kda_fwd stores past
+// the end of its layout with kda_desc_t::save_states = 1.
+size_t saved_states_bytes(const Geometry &g) {
+    return align_up((size_t)g.slots * (size_t)g.H * (size_t)(kK * kV) * 4, 256);
+}
+
+// kda_fwd's workspace: its layout, and the saved states after it.
+size_t fwd_workspace_bytes(const kda_desc_t *d, const Geometry &g) {
+    return make_layout(g).total + (d->save_states == 1 ? saved_states_bytes(g) : 0);
+}
+
 // With KDA_VALIDATE=1 in the environment, kda_fwd reads cu_seqlens back to the
 // host (synchronising `stream`) and refuses contents that would send the
 // kernels outside the token tensors.  Off by default: it costs a device
@@ -144,9 +157,9 @@ extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc) {
     Geometry g;
     size_t need = 0;
     bool ok = false;
-    if (make_geometry(desc, false, g) == KDA_OK) { need = make_layout(g).total; ok = true; }
+    if (make_geometry(desc, false, g) == KDA_OK) { need = fwd_workspace_bytes(desc, g); ok = true; }
     if (desc->B == 1 && make_geometry(desc, true, g) == KDA_OK) {
-        const size_t p = make_layout(g).total;
+        const size_t p = fwd_workspace_bytes(desc, g);
         need = p > need ? p : need;
         ok = true;
     }
@@ -247,10 +260,15 @@ hipError_t launch_chains(const ChainArgs &ca, const Geometry &geo, const Workspa
 // reverse scan with the transposed forward maps (the gradient leaving every
 // segment, into sin, and the gradient of the initial state), and the reverse
 // chain of every segment from the gradient leaving it.
+// The segment table and the forward's segment maps come from `fws`, the
+// workspace the forward's chains ran in (the call's own, or the kept forward
+// workspace when that call's states are read).
 hipError_t launch_bwd_chains(const BwdArgs &ba, const Geometry &geo, const WorkspaceLayout &lay, char *ws,
-                             hipStream_t stream) {
+                             char *fws, hipStream_t stream) {
     if (geo.segs <= 1) return kda_launch_bwd_chain(ba, stream);
-    const SegmentView sv = segment_view(lay, ws);
+    SegmentView sv = segment_view(lay, ws);
+    const SegmentView fv = segment_view(lay, fws);
+    sv.cu = fv.cu; sv.off = fv.off; sv.mapM = fv.mapM;
     BwdArgs seg = ba;
     seg.cu = sv.cu; seg.chunk_off = sv.off; seg.seq_order = nullptr;
     seg.N = geo.B * geo.segs; seg.nc_fixed = 0;
@@ -299,7 +317,9 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
         st = validate_cu_seqlens(cu_seqlens, geo.N, geo.T, stream);
         if (st != KDA_OK) return st;
     }
+    if (noalloc && desc->save_states != 0) return KDA_ERR_PARAM;
     const WorkspaceLayout lay = make_layout(geo);
+    const size_t need = fwd_workspace_bytes(desc, geo);
     char *ws = noalloc ? nullptr : static_cast<char *>(desc->workspace);
     bool owned = false;
     if (noalloc) {
@@ -310,10 +330,10 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
         if (!ws) return KDA_ERR_HIP;
     } else if (ws) {
         if (!aligned(ws, 256)) return KDA_ERR_ALIGN;
-        if (desc->workspace_bytes < lay.total) return KDA_ERR_WORKSPACE;
-    } else if (lay.total > 0) {
+        if (desc->workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    } else if (need > 0) {
         void *p = nullptr;
-        if (hipMallocAsync(&p, lay.total, stream) != hipSuccess) return KDA_ERR_HIP;
+        if (hipMallocAsync(&p, need, stream) != hipSuccess) return KDA_ERR_HIP;
         ws = static_cast<char *>(p);
         owned = true;
     }
@@ -375,6 +395,8 @@ kda_status_t fwd_impl(const void *q, const void *k, const void *v, const void *g
     ca.h0_bf16 = desc->initial_state_dtype == KDA_BF16;
     ca.ht_bf16 = desc->final_state_dtype == KDA_BF16;
     ca.out = static_cast<uint16_t *>(out);
+    // save_states: the chain also stores the state entering every chunk (past the layout's end)
+    ca.hs = desc->save_states == 1 ? reinterpret_cast<float *>(ws + lay.total) : nullptr;
     ca.piece_cap = desc->launch_piece;
     if (err == hipSuccess) err = launch_chains(ca, geo, lay, ws, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[3], stream);
@@ -476,8 +498,10 @@ struct BwdLayout {
 // Geometry of a backward call: the forward's (split chains by the same rule),
 // never pipelined.
 kda_status_t make_bwd_geometry(const kda_desc_t *d, bool varlen, Geometry &g) {
+    if (d->save_states < 0 || d->save_states > 1) return KDA_ERR_PARAM;
     kda_desc_t e = *d;
     e.pipeline = 0;
+    e.save_states = 0;
     return make_geometry(&e, varlen, g);
 }
 
@@ -556,6 +580,7 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
     // them before the parts that depend on split chains or the pipelined forward)
     char *fw = static_cast<char *>(const_cast<void *>(desc->forward_workspace));
     if (fw && !aligned(fw, 256)) return KDA_ERR_ALIGN;
+    const bool fw_states = fw && desc->save_states == 1;  // the chunks' entering states too
     char *ws = static_cast<char *>(desc->workspace);
     bool owned = false;
     if (ws) {
@@ -594,8 +619,9 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
     if (err == hipSuccess && geo.T > 0 && !fw) err = kda_launch_intra(ia, geo.slots, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[1], stream);
     BwdArgs ba{};
-    ba.hs = reinterpret_cast<float *>(ws + lay.off_hs);
-    if (geo.T > 0) {
+    // the forward's states: from the kept workspace, past the end of its layout
+    ba.hs = reinterpret_cast<float *>(fw_states ? fw + fl.total : ws + lay.off_hs);
+    if (geo.T > 0 && !fw_states) {
         ChainArgs ca{};
         ca.Wf = ia.Wf; ca.Qf = ia.Qf; ca.Kf = ia.Kf; ca.Af = ia.Af; ca.Uf = ia.Uf; ca.gn = ia.gn;
         ca.cu = cu_seqlens; ca.chunk_off = chunk_off; ca.seq_order = seq_order;
@@ -633,7 +659,7 @@ extern "C" kda_status_t kda_bwd(const void *q, const void *k, const void *v, con
     ba.piece_cap = desc->launch_piece;
     if (err == hipSuccess) err = kda_launch_bwd_prep(ba, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[3], stream);
-    if (err == hipSuccess) err = launch_bwd_chains(ba, geo, fl, ws, stream);
+    if (err == hipSuccess) err = launch_bwd_chains(ba, geo, fl, ws, fw_states ? fw : ws, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[4], stream);
     if (err == hipSuccess) err = kda_launch_bwd_grad(ba, stream);
     if (ev && err == hipSuccess) err = hipEventRecord(ev[5], stream);

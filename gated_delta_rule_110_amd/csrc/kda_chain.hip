@@ -318,11 +318,11 @@ __device__ __forceinline__ void out_wave(ChainSmem<kCB> &sm, const ChainArgs &a,
 
 // The chain kernel's body; kMap selects map mode (ChainArgs::map_mode), which
 // is a kernel of its own so that the ordinary chain is compiled without it;
-// kSave stores the state entering every chunk to ChainArgs::hs and writes no
-// outputs (the backward's forward pass, which needs the states only), also a
-// kernel of its own: its output waves only keep the barrier count, and its L2
-// prefetch, like map mode's, skips Qg and A_qk.
-template <bool kMap, int kCB, bool kSave = false>
+// kSave stores the state entering every chunk to ChainArgs::hs; without kOut
+// it writes no outputs (the backward's forward pass, which needs the states
+// only): its output waves only keep the barrier count, and its L2 prefetch,
+// like map mode's, skips Qg and A_qk.  Both are kernels of their own.
+template <bool kMap, int kCB, bool kSave = false, bool kOut = !kSave>
 __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &a) {
     using Sh = Shape<kCB>;
 
@@ -393,7 +393,7 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
 #pragma unroll
                         for (int e = 0; e < 4; ++e) hs[(16 * ct + 4 * g + e) * kV] = S[ct][e];
                 }
-                if (!kMap) chain_step<kCB, false, !kSave>(sm, S, rs, (int)(s & 1), c, lane);
+                if (!kMap) chain_step<kCB, false, kOut>(sm, S, rs, (int)(s & 1), c, lane);
                 else if (linear_part) chain_step<kCB, true, false>(sm, S, rs, (int)(s & 1), c, lane);
                 else chain_step<kCB, false, false>(sm, S, rs, (int)(s & 1), c, lane);
                 rs = rs + 1 == Sh::kSlots ? 0 : rs + 1;
@@ -417,7 +417,7 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
         }
     } else if (wave < 2 * kCB) {
         // ---- outputs: row tiles of every block of the workgroup -------------
-        if constexpr (kSave) {
+        if constexpr (!kOut) {
             if (nchunks > 0) {  // no outputs: the prologue barrier and one per chunk
                 lds_barrier();
                 for (int64_t s = 0; s < nchunks; ++s) lds_barrier();
@@ -469,7 +469,7 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
             const int64_t nu = nchunks + kAhead - 1;
             bool prologue_done = false;
             for (int64_t u = 0; u < nu; ++u) {
-                touch_lines<kCB, kMap || kSave>(sm, a, wsof(u + 1), vb, lane);
+                touch_lines<kCB, kMap || !kOut>(sm, a, wsof(u + 1), vb, lane);
                 asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTouchInFlight) : "memory");
                 if (u >= kAhead - 1) {
                     if (!prologue_done) { lds_barrier(); prologue_done = true; }
@@ -497,6 +497,14 @@ __global__ __launch_bounds__(Shape<1>::kThreads, 1) void kda_chain_save_kernel(C
 __global__ __launch_bounds__(Shape<2>::kThreads, 1) void kda_chain_save_x2_kernel(ChainArgs a) {
     __shared__ ChainSmem<2> sm;
     chain_body<false, 2, true>(sm, a);
+}
+__global__ __launch_bounds__(Shape<1>::kThreads, 1) void kda_chain_out_save_kernel(ChainArgs a) {
+    __shared__ ChainSmem<1> sm;
+    chain_body<false, 1, true, true>(sm, a);
+}
+__global__ __launch_bounds__(Shape<2>::kThreads, 1) void kda_chain_out_save_x2_kernel(ChainArgs a) {
+    __shared__ ChainSmem<2> sm;
+    chain_body<false, 2, true, true>(sm, a);
 }
 __global__ __launch_bounds__(Shape<1>::kThreads, 1) void kda_chain_map_kernel(ChainArgs a) {
     __shared__ ChainSmem<1> sm;
@@ -593,6 +601,12 @@ hipError_t kda_launch_chain(const ChainArgs &a, hipStream_t s) {
                                dim3(Shape<2>::kThreads), 0, s, b);
         else if (a.map_mode)
             hipLaunchKernelGGL(kda_chain_map_kernel, dim3((unsigned)(ng * 8 * Shape<1>::kNVB)),
+                               dim3(Shape<1>::kThreads), 0, s, b);
+        else if (a.hs && a.out && wide)
+            hipLaunchKernelGGL(kda_chain_out_save_x2_kernel, dim3((unsigned)(ng * 8 * Shape<2>::kNVB)),
+                               dim3(Shape<2>::kThreads), 0, s, b);
+        else if (a.hs && a.out)
+            hipLaunchKernelGGL(kda_chain_out_save_kernel, dim3((unsigned)(ng * 8 * Shape<1>::kNVB)),
                                dim3(Shape<1>::kThreads), 0, s, b);
         else if (a.hs && wide)
             hipLaunchKernelGGL(kda_chain_save_x2_kernel, dim3((unsigned)(ng * 8 * Shape<2>::kNVB)),

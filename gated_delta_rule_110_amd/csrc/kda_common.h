@@ -104,9 +104,10 @@ struct ChainArgs {
     // offset and the linear part of the chain's affine map S -> M S + N.
     int map_mode;
     float *mapM, *mapN;
-    // With hs set (the backward's forward pass), the chain stores the fp32
-    // state entering every chunk, hs[chunk slot * H + h][K][V], and writes no
-    // outputs (out is not used).
+    // With hs set the chain stores the fp32 state entering every chunk,
+    // hs[chunk slot * H + h][K][V]; with out also set it writes the outputs
+    // as well (a forward that keeps the states for its backward), else none
+    // (the backward's own forward pass, which needs the states only).
     float *hs;
     int64_t chain_base;  // first chain (in dispatch order) of this launch; set by the launcher
     int64_t piece_cap;   // kda_desc_t::launch_piece (0: launch size by the default rule)

@@ -128,6 +128,16 @@ typedef struct {
      * intermediates.  kda_fwd_noalloc's scratch cannot serve: later calls
      * reuse it. */
     const void *forward_workspace;
+    /* kda_fwd: 0, or 1 to also store in the workspace the fp32 state entering
+     * every 64-token chunk (64 KiB per chunk and head more, which
+     * kda_fwd_workspace_size counts), for a later kda_bwd on the same inputs
+     * to read instead of recomputing.  The outputs are the same bits; the
+     * pipelined forward does not apply.  kda_fwd_noalloc: must be 0.
+     * kda_bwd: 1 when desc->forward_workspace holds such states too (a kda_fwd
+     * call with save_states = 1 and the same chain_segments); kda_bwd then
+     * runs none of the forward's kernels.  Ignored without forward_workspace.
+     * Other values are KDA_ERR_PARAM. */
+    int64_t save_states;
 } kda_desc_t;
 
 /* Bytes of workspace kda_fwd needs for these shapes (0 if the shapes are
@@ -283,7 +293,9 @@ size_t kda_bwd_workspace_size(const kda_desc_t *desc);
  * with respect to every input.  The forward is recomputed inside the call
  * (nothing from an earlier kda_fwd is needed), or, with
  * desc->forward_workspace set, only its state chain is: the intra-chunk
- * intermediates come from that kda_fwd call's workspace.
+ * intermediates come from that kda_fwd call's workspace; with
+ * desc->save_states = 1 as well, the states entering every chunk do too and
+ * none of the forward is recomputed.
  *
  *   q ... lower_bound, initial_state, cu_seqlens : as for kda_fwd (the same
  *                      shapes, dtypes and rules; desc->initial_state_dtype
@@ -313,7 +325,7 @@ size_t kda_bwd_workspace_size(const kda_desc_t *desc);
  * desc->phase_events, when set, is an array of 6 events recorded before the
  * first kernel (0), after the forward's intra-chunk kernel (1; right after 0
  * when desc->forward_workspace is set) and state
- * chain (2), after the gradient's preparation kernel (3), its reverse state
+ * chain (2; right after 1 when the states are read as well), after the gradient's preparation kernel (3), its reverse state
  * chain (4) and its per-chunk kernel with the parameter sum (5);
  * launch_piece and the workspace rules are as for kda_fwd, with
  * kda_bwd_workspace_size() in place of kda_fwd_workspace_size().  The

@@ -327,3 +327,53 @@ def test_bwd_reads_forward_workspace(case):
     zeros = torch.zeros_like(ws)
     bad = _gpu(w, d_out, d_fin, forward_workspace=zeros, **bkw)
     assert not np.array_equal(bad["dq"], ref["dq"]), case
+
+
+_FWD_STATES_CASES = {
+    "fixed": lambda: CASES["fixed"]() + ({}, {}),
+    "packed": lambda: CASES["packed"]() + ({}, {}),
+    "nostate": lambda: CASES["nostate"]() + ({}, {}),
+    "split": lambda: (W.make("bwd_fws_split", 2, 64 * 40 + 17, 2, 7014, init="fp32", final="fp32"), 7114,
+                      "fp32", {"chain_segments": 3}, {"chain_segments": 3}),
+    # a forward that asks for the pipelined form runs the two-kernel one when it saves states
+    "pipelined": lambda: (W.make("bwd_fws_pipe", 1, 300, 8, 7015, init="bf16", final="fp32"), 7115, "fp32",
+                          {"pipeline": 1}, {}),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_FWD_STATES_CASES))
+def test_bwd_reads_forward_states(case):
+    # kda_desc_t::save_states: the forward also stores the state entering every chunk, and the
+    # backward reads the states and the intermediates from its workspace and recomputes nothing;
+    # the forward's outputs and the gradients are the same bits as without
+    w, seed, fin, fkw, bkw = _FWD_STATES_CASES[case]()
+    d_out, d_fin = W.loss_grads(w, seed, final=fin)
+    wd = w.to("cuda")
+    nbytes = kda.workspace_size(w.B, w.T, w.H, w.N, save_states=True, **fkw)
+    assert nbytes > kda.workspace_size(w.B, w.T, w.H, w.N, **fkw)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    say("bwd forward states %s: B=%d T=%d H=%d N=%d" % (case, w.B, w.T, w.H, w.N))
+    fin_t = None if w.final_state_dtype is None else \
+        torch.empty((w.N, w.H, 128, 128), dtype=w.final_state_dtype, device="cuda")
+    o1, f1 = kda.fwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, None, wd.A_log, wd.dt_bias, w.lower_bound,
+                     wd.initial_state, fin_t, wd.cu_seqlens, workspace=ws, save_states=True, **fkw)
+    o2, f2 = kda.fwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, None, wd.A_log, wd.dt_bias, w.lower_bound,
+                     wd.initial_state, None if fin_t is None else torch.empty_like(fin_t), wd.cu_seqlens,
+                     **{k: v for k, v in fkw.items() if k != "pipeline"})
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    if f1 is not None:
+        assert torch.equal(f1, f2)
+    ref = _gpu(w, d_out, d_fin, **bkw)
+    got = _gpu(w, d_out, d_fin, forward_workspace=ws, forward_states=True, **bkw)
+    for name in NAMES:
+        if ref[name] is None:
+            assert got[name] is None, name
+            continue
+        assert np.array_equal(got[name], ref[name]), (case, name)
+    # the states are read, not recomputed: zeros in the workspace change the gradient (not with
+    # split chains, whose segment table the workspace holds too, nor for one chunk from a zero
+    # state, where the only state read is zero either way)
+    if "chain_segments" not in bkw and case != "nostate":
+        bad = _gpu(w, d_out, d_fin, forward_workspace=torch.zeros_like(ws), forward_states=True, **bkw)
+        assert not np.array_equal(bad["dq"], ref["dq"]), case

@@ -83,6 +83,12 @@ def test_validation_errors(lib):
     assert _call(lib, d) == 7
     d = _desc(workspace=ctypes.c_void_p(0x100010), workspace_bytes=ws)  # not 256-aligned
     assert _call(lib, d) == 6
+    assert _call(lib, _desc(save_states=-1)) == 4
+    assert _call(lib, _desc(save_states=2)) == 4
+    # the saved states need a larger workspace
+    d = _desc(B=2, num_seqs=2, save_states=1, workspace=ctypes.c_void_p(0x100000),
+              workspace_bytes=kda.workspace_size(2, 64, 2))
+    assert _call(lib, d) == 7
     # bad state dtype
     d = _desc(final_state_dtype=7)
     assert lib.kda_fwd(*([ctypes.c_void_p(FAKE)] * 5), 0.1, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), -5.0,
@@ -100,6 +106,9 @@ def test_workspace_size_monotone(lib):
     # about 72.5 KiB per (64-token chunk, head)
     per = (kda.workspace_size(4, 64 * 100, 8) - kda.workspace_size(4, 64 * 50, 8)) / (4 * 50 * 8)
     assert abs(per - 72.5 * 1024) < 512
+    # and 64 KiB more for the saved fp32 states
+    assert kda.workspace_size(4, 64 * 100, 8, save_states=True) - kda.workspace_size(4, 64 * 100, 8) == \
+        4 * 100 * 8 * 65536
 
 
 def test_chain_segments_rule(lib):
@@ -210,6 +219,7 @@ def test_noalloc_validation_and_limit(lib):
     assert call(_desc(K=64)) == 3
     assert call(_desc(), lb=0.5) == 4
     assert call(_desc(launch_piece=-1)) == 4
+    assert call(_desc(save_states=1)) == 4     # later calls reuse the scratch: nothing to keep
     big = _desc(T=8192, H=32)  # 4096 (chunk, head) pairs: about 290 MiB of workspace
     assert kda.workspace_size(1, 8192, 32) > cap
     assert call(big) == 9
@@ -248,6 +258,7 @@ def test_bwd_validation_errors(lib):
     assert _call_bwd(lib, d) == 7
     d = _desc(forward_workspace=ctypes.c_void_p(0x100010))  # not 256-aligned
     assert _call_bwd(lib, d) == 6
+    assert _call_bwd(lib, _desc(save_states=2)) == 4
     d = _desc(initial_state_dtype=9)
     assert lib.kda_bwd(*([ctypes.c_void_p(FAKE)] * 5), 0.1, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), -5.0,
                        ctypes.c_void_p(FAKE), None, ctypes.c_void_p(FAKE), None,
