@@ -766,6 +766,32 @@ struct RowStage {
     }
 };
 
+// Staging of the 128 x 128 fp32 state the forward's chain saved in its register
+// layout ([16-column block][16-row tile ct][lane][e]: lane (r, g) holds rows
+// 16 ct + 4 g + e of column 16 block + r) into an LDS tile of pitch kRP,
+// 16 bytes per thread and pass, loads first as in RowStage.
+struct StateStage {
+    static constexpr int kN = kK * kV / 4 / kMainThreads;
+    float4 v[kN];
+    __device__ __forceinline__ void load(const float *src, int tid) {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) v[n] = reinterpret_cast<const float4 *>(src)[tid + n * kMainThreads];
+    }
+    __device__ __forceinline__ void store(float (*dst)[kRP], int tid) const {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+            const int idx = tid + n * kMainThreads;
+            const int ln = idx & 63;
+            const int row = 16 * ((idx >> 6) & 7) + 4 * (ln >> 4), col = 16 * (idx >> 9) + (ln & 15);
+            dst[row][col] = v[n].x;
+            dst[row + 1][col] = v[n].y;
+            dst[row + 2][col] = v[n].z;
+            dst[row + 3][col] = v[n].w;
+        }
+    }
+};
+static_assert(StateStage::kN * kMainThreads * 4 == kK * kV, "StateStage covers the state exactly");
+
 // Keep the accumulators' current values in registers here: without this the
 // compiler sinks a phase's updates into the last phase that reads them, and
 // the operands it keeps alive for that (loaded values, products) run out of
@@ -873,7 +899,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void kda_bwd_main_kernel(BwdArgs a
         const float rkn = rkv[kr.row];
         const float4 g0 = *reinterpret_cast<const float4 *>(G + kr.row * kK + kr.c8);
         const float4 g1 = *reinterpret_cast<const float4 *>(G + kr.row * kK + kr.c8 + 4);
-        RowStage<kK> ss;
+        StateStage ss;
         ss.load(S, tid);
         *reinterpret_cast<float4 *>(&sm.t.T[tid >> 4][4 * (tid & 15)]) = tv;
         if (tid < kChunk) {

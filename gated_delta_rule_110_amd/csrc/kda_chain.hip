@@ -386,12 +386,13 @@ __device__ __forceinline__ void chain_body(ChainSmem<kCB> &sm, const ChainArgs &
             int rs = 0;     // ring slot of chunk s
             for (int64_t s = 0; s < nchunks; ++s) {
                 if constexpr (kSave) {
-                    // lane (r, g) holds rows 16 ct + 4 g + e of column col0 + r
-                    float *hs = a.hs + wsof(s) * (int64_t)(kK * kV) + col0 + r;
+                    // in this lane layout (lane (r, g) holds rows 16 ct + 4 g + e of column
+                    // col0 + r): [16-column block][ct][lane][e], one 16-byte store per ct
+                    // (the texture path's instruction rate bounds the step, not its bytes)
+                    f4 *hs = reinterpret_cast<f4 *>(a.hs + wsof(s) * (int64_t)(kK * kV)) +
+                             (col0 / kVB) * (8 * 64) + lane;
 #pragma unroll
-                    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) hs[(16 * ct + 4 * g + e) * kV] = S[ct][e];
+                    for (int ct = 0; ct < 8; ++ct) hs[ct * 64] = S[ct];
                 }
                 if (!kMap) chain_step<kCB, false, kOut>(sm, S, rs, (int)(s & 1), c, lane);
                 else if (linear_part) chain_step<kCB, true, false>(sm, S, rs, (int)(s & 1), c, lane);

@@ -105,7 +105,9 @@ struct ChainArgs {
     int map_mode;
     float *mapM, *mapN;
     // With hs set the chain stores the fp32 state entering every chunk,
-    // hs[chunk slot * H + h][K][V]; with out also set it writes the outputs
+    // hs[chunk slot * H + h][16-column block][ct][lane][e] = S[16 ct + 4 (lane / 16) + e]
+    // [16 block + lane % 16] (the chain's register layout, 16 bytes per lane and
+    // row tile); with out also set it writes the outputs
     // as well (a forward that keeps the states for its backward), else none
     // (the backward's own forward pass, which needs the states only).
     float *hs;
