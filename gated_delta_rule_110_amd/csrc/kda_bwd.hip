@@ -130,22 +130,31 @@ __device__ __forceinline__ bool chunk_rows(const BwdArgs &a, int64_t slot, int64
 // ---- 2. per-chunk preparation ------------------------------------------------
 
 // The reverse chain's operands of one (chunk, head), fp16, written by the
-// preparation kernel in the padded row-major layouts the chain reads them in
-// (every part a whole number of KiB, so the chain copies it with 1 KiB
-// global_load_lds instructions):
-//   Kn  [64][136]   Kbar[i][d] = exp(G_n[d] - G_i[d]) khat_i[d]
-//   AqT [64][72]    A_qk^T[j][i], A_qk[i][j] = sum_d qhat_i khat_j exp(G_i - G_j) (j <= i)
-//   WT  [128][72]   -W^T[d][i], W = T Diag(b) (gamma * Khat)
-//   QgT [128][72]   Qg^T[d][i], Qg = gamma * qhat
+// preparation kernel in the layouts the chain reads them in (every part a
+// whole number of KiB, so the chain copies it with 1 KiB global_load_lds
+// instructions):
+//   Kn  [64][128]   Kbar[i][d] = exp(G_n[d] - G_i[d]) khat_i[d]
+//   AqT [64][64]    A_qk^T[j][i], A_qk[i][j] = sum_d qhat_i khat_j exp(G_i - G_j) (j <= i)
+//   WT  [128][64]   -W^T[d][i], W = T Diag(b) (gamma * Khat)
+//   QgT [128][64]   Qg^T[d][i], Qg = gamma * qhat
 //   gn  [128] fp32  exp(G_n)
-constexpr int kKnP = 136, kTkP = 72;
+// Rows are unpadded, with their 8-byte units of four columns permuted by the
+// row's low four bits (co_idx), so that the chain's reads of four columns from
+// 16 consecutive rows meet 16 different pairs of LDS banks; padding the rows
+// instead cost a tenth more copies per chunk step.
+constexpr int kTkP = 72;  // row pitch of the chain's fp16 dO^T and dUt^T tiles in LDS
 constexpr int kCoKn = 0;
-constexpr int kCoAq = kCoKn + kChunk * kKnP * 2;   // 17408
-constexpr int kCoW = kCoAq + kChunk * kTkP * 2;    // 26624
-constexpr int kCoQ = kCoW + kK * kTkP * 2;         // 45056
-constexpr int kCoGn = kCoQ + kK * kTkP * 2;        // 63488
-constexpr int kCoBytes = kCoGn + kK * 4;           // 64000
+constexpr int kCoAq = kCoKn + kChunk * kK * 2;      // 16384
+constexpr int kCoW = kCoAq + kChunk * kChunk * 2;   // 24576
+constexpr int kCoQ = kCoW + kK * kChunk * 2;        // 40960
+constexpr int kCoGn = kCoQ + kK * kChunk * 2;       // 57344
+constexpr int kCoBytes = kCoGn + kK * 4;            // 57856
 static_assert(kCoGn % 1024 == 0 && kCoBytes == kBwdChainOperandBytes, "chain operand block layout");
+// element (row, col) of an operand part of kCols fp16 columns (64 or 128)
+template <int kCols>
+__device__ __forceinline__ int co_idx(int row, int col) {
+    return row * kCols + ((((col >> 2) ^ (row & 15)) << 2) | (col & 3));
+}
 
 // The preparation kernel holds 64 of the 128 channels of q-hat, k-hat and G in
 // LDS at a time (two passes), so that two workgroups fit on a CU (71 KB each):
@@ -299,14 +308,14 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
             for (int idx = tid; idx < kChunk * kHC; idx += kThreads) {
                 const int i = idx >> 6, d = idx & (kHC - 1);
                 Go[i * kK + c0 + d] = sm.G[i][d];
-                Kn[i * kKnP + c0 + d] = (_Float16)(__expf(Gn[d] - sm.G[i][d]) * sm.k[i][d]);
+                Kn[co_idx<kK>(i, c0 + d)] = (_Float16)(__expf(Gn[d] - sm.G[i][d]) * sm.k[i][d]);
             }
             for (int idx = tid; idx < kHC * (kChunk / 4); idx += kThreads) {
                 const int d = idx >> 4, i0 = 4 * (idx & 15);
                 h4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = (_Float16)(__expf(sm.G[i0 + e][d]) * sm.u.q[i0 + e][d]);
-                *reinterpret_cast<h4 *>(QgT + (c0 + d) * kTkP + i0) = v;
+                *reinterpret_cast<h4 *>(QgT + co_idx<kChunk>(c0 + d, i0)) = v;
             }
             if (tid < kHC) gno[c0 + tid] = __expf(Gn[tid]);
             // the first half's cumulated log-decay stays with the threads that hold its khat, for W
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
                 at[e] = (_Float16)(j <= i ? accA[t][e] : 0.f);
             }
             // A_qk^T[16 J + r][16 I + 4 gq .. + 3]
-            *reinterpret_cast<h4 *>(AqT + (16 * J + r) * kTkP + 16 * I + 4 * gq) = at;
+            *reinterpret_cast<h4 *>(AqT + co_idx<kChunk>(16 * J + r, 16 * I + 4 * gq)) = at;
         }
         // the tiles above the diagonal blocks are zero
         for (int idx = tid; idx < kChunk * kChunk; idx += kThreads) {
@@ -362,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
             if ((j >> 4) > (i >> 4)) {
                 sm.M[i][j] = 0.f;
                 Mk[idx] = 0.f;
-                AqT[j * kTkP + i] = (_Float16)0.f;
+                AqT[co_idx<kChunk>(j, i)] = (_Float16)0.f;
                 sm.u.T[i][j] = 0.f;
             }
         }
@@ -457,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
             h4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = (_Float16)(-acc[ct][e]);
-            *reinterpret_cast<h4 *>(WT + (c0 + 16 * ct + r) * kTkP + 16 * w + 4 * gq) = v;
+            *reinterpret_cast<h4 *>(WT + co_idx<kChunk>(c0 + 16 * ct + r, 16 * w + 4 * gq)) = v;
         }
     }
 }
@@ -545,7 +554,7 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
         // first, then the operand block is copied straight into LDS; dO^T is built
         // (bf16 -> fp16) after the step's second barrier, and the copies are waited
         // for only before its last one, so that neither is on the path of the
-        // compute waves' first two barriers.  (Issuing the 63 copies takes most of
+        // compute waves' first two barriers.  (Issuing the 57 copies takes most of
         // a step, the per-CU load path being the limit: splitting them over two
         // loader waves, more in flight, measured 12% slower.) ----------------------
         auto issue = [&](int64_t ci, int s, uint4 &p0, uint4 &p1) {
@@ -637,7 +646,7 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
                 const h4 bv = pack_h4(dS[t]);
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) {
-                    const h4 av = *reinterpret_cast<const h4 *>(Kn + (16 * jt + r) * kKnP + 16 * ct + 4 * g);
+                    const h4 av = *reinterpret_cast<const h4 *>(Kn + co_idx<kK>(16 * jt + r, 16 * ct + 4 * g));
                     acc[jt] = mfma16x16x16_f16(av, bv, acc[jt]);
                 }
             }
@@ -646,7 +655,7 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
                 f4 aq = f4{0, 0, 0, 0};
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const h4 av = *reinterpret_cast<const h4 *>(AqT + (16 * w + r) * kTkP + 16 * kb + 4 * g);
+                    const h4 av = *reinterpret_cast<const h4 *>(AqT + co_idx<kChunk>(16 * w + r, 16 * kb + 4 * g));
                     const h4 bv = *reinterpret_cast<const h4 *>(&sm.dOT[slot][r][16 * kb + 4 * g]);
                     aq = mfma16x16x16_f16(av, bv, aq);
                 }
@@ -677,10 +686,10 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void kda_bwd_chain_kernel(BwdA
                 for (int e = 0; e < 4; ++e) nd[e] = gn[16 * ct + 4 * g + e] * dS[t][e];
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const h4 aw = *reinterpret_cast<const h4 *>(WT + (16 * ct + r) * kTkP + 16 * kb + 4 * g);
+                    const h4 aw = *reinterpret_cast<const h4 *>(WT + co_idx<kChunk>(16 * ct + r, 16 * kb + 4 * g));
                     const h4 bu = *reinterpret_cast<const h4 *>(&sm.dUT[r][16 * kb + 4 * g]);
                     nd = mfma16x16x16_f16(aw, bu, nd);
-                    const h4 aq = *reinterpret_cast<const h4 *>(QgT + (16 * ct + r) * kTkP + 16 * kb + 4 * g);
+                    const h4 aq = *reinterpret_cast<const h4 *>(QgT + co_idx<kChunk>(16 * ct + r, 16 * kb + 4 * g));
                     const h4 bo = *reinterpret_cast<const h4 *>(&sm.dOT[slot][r][16 * kb + 4 * g]);
                     nq = mfma16x16x16_f16(aq, bo, nq);
                 }

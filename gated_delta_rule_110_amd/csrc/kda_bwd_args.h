@@ -15,9 +15,9 @@ namespace kda {
 //                               recomputed from q and k where needed), b = sigmoid(beta)
 //   Mk, Tm [ws][64][64] fp32    decayed key Gram (strictly lower, without b) and T = (I + Diag(b) Mk)^-1
 //   part [ws][K + 1] fp32       this chunk's share of ddt_bias (K) and of dA_log (1)
-//   co [ws][64000 B]            the reverse chain's fp16 operands (layout in kda_bwd.hip)
+//   co [ws][57856 B]            the reverse chain's fp16 operands (layout in kda_bwd.hip)
 // Rows past the end of a ragged chunk are zero in rq, rk, bb and keep G constant.
-constexpr int64_t kBwdChainOperandBytes = 64000;  // per (chunk, head): the reverse chain's fp16 operands
+constexpr int64_t kBwdChainOperandBytes = 57856;  // per (chunk, head): the reverse chain's fp16 operands
 
 struct BwdArgs {
     const uint16_t *q, *k, *v, *g, *beta;   // bf16 inputs
@@ -32,7 +32,7 @@ struct BwdArgs {
     const _Float16 *Wf, *Qf, *Kf, *Af;      // the forward's intermediates
     const float *gn;
     float *hs, *dhs, *dUt, *G, *rq, *rk, *bb, *Mk, *Tm, *part;
-    unsigned char *co;                      // [ws][64000 B] the reverse chain's fp16 operands
+    unsigned char *co;                      // [ws][57856 B] the reverse chain's fp16 operands
     float *dq, *dk, *dv, *dg, *dbeta;       // [B,T,H,K] / [B,T,H,V] / [B,T,H] fp32
     float *dh0;                             // [N,H,K,V] fp32 or nullptr
     float *dA_log, *ddt_bias;               // [H] / [H,K] fp32

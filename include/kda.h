@@ -275,7 +275,7 @@ kda_status_t kda_decode(const void *q, const void *k, const void *v, const void 
                         const kda_desc_t *desc, hipStream_t stream);
 
 /* Bytes of workspace kda_bwd needs for these shapes (0 if the shapes are
- * invalid).  Pure host arithmetic.  About 361 KiB per 64-token chunk and head
+ * invalid).  Pure host arithmetic.  About 355 KiB per 64-token chunk and head
  * (the forward's 72.5 KiB of intermediates, the fp32 state entering every
  * chunk and its gradient, 64 KiB each, 97 KiB of fp32 per-chunk quantities
  * and 62.5 KiB of fp16 operands for the reverse chain), plus kda_fwd's 192 KiB
