@@ -391,7 +391,8 @@ class KdaFunction(torch.autograd.Function):
         if final_dtype is not None:
             final = torch.empty((N, H, K, v.shape[-1]), dtype=final_dtype, device=q.device)
         ws = None
-        if keep_intermediates:
+        # only when a backward can follow (otherwise the plain, faster forward)
+        if keep_intermediates and any(ctx.needs_input_grad):
             ws = torch.empty(max(workspace_size(B, T, H, N, chain_segments=chain_segments, save_states=True), 1),
                              dtype=torch.uint8, device=q.device)
         out, fin = fwd(q, k, v, g, beta, scale, None, A_log, dt_bias, lower_bound, initial_state, final,

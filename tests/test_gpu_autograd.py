@@ -63,3 +63,17 @@ def test_autograd_matches_bwd(case, keep):
     assert torch.equal(out, o2)
     if final is not None:
         assert torch.equal(final, f2)
+
+
+def test_autograd_without_grad_runs_the_plain_forward():
+    # with nothing to differentiate, kda_attention keeps no workspace and returns kda_fwd's bits
+    w = W.make("ag_nograd", 1, 200, 2, 7305, init="fp32", final="fp32")
+    wd = w.to("cuda")
+    with torch.no_grad():
+        out, fin = kda.kda_attention(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, wd.A_log, wd.dt_bias,
+                                     w.lower_bound, initial_state=wd.initial_state,
+                                     final_state_dtype=torch.float32)
+    o2, f2 = kda.fwd(wd.q, wd.k, wd.v, wd.g, wd.beta, w.scale, None, wd.A_log, wd.dt_bias, w.lower_bound,
+                     wd.initial_state, torch.empty_like(fin))
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(fin, f2)
