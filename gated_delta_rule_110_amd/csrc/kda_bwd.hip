@@ -305,10 +305,20 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
         {
             // the cumulated log-decay, Kbar (natural), Qg^T (four rows per store), exp(G_n)
             const float *Gn = sm.G[L - 1];
-            for (int idx = tid; idx < kChunk * kHC; idx += kThreads) {
-                const int i = idx >> 6, d = idx & (kHC - 1);
-                Go[i * kK + c0 + d] = sm.G[i][d];
-                Kn[co_idx<kK>(i, c0 + d)] = (_Float16)(__expf(Gn[d] - sm.G[i][d]) * sm.k[i][d]);
+            // four consecutive channels per thread and pass: one 16-byte G store, one
+            // 8-byte Kbar store (four columns are one unit of co_idx's permutation)
+            for (int idx = tid; idx < kChunk * kHC / 4; idx += kThreads) {
+                const int i = idx / (kHC / 4), d = 4 * (idx % (kHC / 4));
+                float4 gv;
+                h4 kv;
+                float *gp = &gv.x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    gp[e] = sm.G[i][d + e];
+                    kv[e] = (_Float16)(__expf(Gn[d + e] - gp[e]) * sm.k[i][d + e]);
+                }
+                *reinterpret_cast<float4 *>(Go + i * kK + c0 + d) = gv;
+                *reinterpret_cast<h4 *>(Kn + co_idx<kK>(i, c0 + d)) = kv;
             }
             for (int idx = tid; idx < kHC * (kChunk / 4); idx += kThreads) {
                 const int d = idx >> 4, i0 = 4 * (idx & 15);
