@@ -376,13 +376,16 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
             *reinterpret_cast<h4 *>(AqT + co_idx<kChunk>(16 * J + r, 16 * I + 4 * gq)) = at;
         }
         // the tiles above the diagonal blocks are zero
-        for (int idx = tid; idx < kChunk * kChunk; idx += kThreads) {
-            const int i = idx >> 6, j = idx & 63;
+        for (int idx = tid; idx < kChunk * kChunk / 4; idx += kThreads) {  // four columns of one tile
+            const int i = idx >> 4, j = 4 * (idx & 15);
             if ((j >> 4) > (i >> 4)) {
-                sm.M[i][j] = 0.f;
-                Mk[idx] = 0.f;
-                AqT[co_idx<kChunk>(j, i)] = (_Float16)0.f;
-                sm.u.T[i][j] = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sm.M[i][j + e] = 0.f;
+                    AqT[co_idx<kChunk>(j + e, i)] = (_Float16)0.f;
+                    sm.u.T[i][j + e] = 0.f;
+                }
+                *reinterpret_cast<float4 *>(Mk + i * kChunk + j) = make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
     }
@@ -440,7 +443,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_bwd_prep_kernel(BwdArgs a) {
     __syncthreads();
     {
         float *Tm = a.Tm + ws * (kChunk * kChunk);
-        for (int idx = tid; idx < kChunk * kChunk; idx += kThreads) Tm[idx] = sm.u.T[idx >> 6][idx & 63];
+        for (int idx = tid; idx < kChunk * kChunk / 4; idx += kThreads) {  // 16 bytes per store
+            const int i = idx >> 4, j = 4 * (idx & 15);
+            *reinterpret_cast<float4 *>(Tm + i * kChunk + j) =
+                make_float4(sm.u.T[i][j], sm.u.T[i][j + 1], sm.u.T[i][j + 2], sm.u.T[i][j + 3]);
+        }
     }
     // W = T Diag(b) (gamma * Khat), stored as -W^T; T[i][j] = 0 for j > i.  The second
     // half's channels are in LDS; then the first half's come back from registers.
